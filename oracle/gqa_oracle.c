@@ -1,0 +1,330 @@
+/*
+ * gqa_oracle.c -- plain, slow, fp64 CPU oracle for grouped-query attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY. The tests, the smoke check and the benchmark's CPU-baseline leg are
+ * its only users; the product path (the HIP library) never links, loads or calls it, and this file
+ * includes nothing from that library.
+ *
+ * What it computes follows the pages' own definitions, written out directly:
+ *   - grouping: query head i belongs to group i / (h / g), the contiguous rule of the GQA lab page
+ *     ("Transformer -- attention by hand: reducing only the key/value heads", step 1 note
+ *     "split the query heads into groups"); a head count that does not divide is an error;
+ *   - fold: position-wise mean of the key/value heads inside each contiguous group (lab step 2);
+ *   - expand: adjacent repetition of the folded heads back to h heads, [A,B] -> [A,A,B,B]
+ *     (lab step 3), materialised as a copy;
+ *   - attend: for every query row, dot with every visible key row, multiply by the scale
+ *     (1/sqrt(head dim), lab step 4 and the course page "Week 7. Attention", step 1), subtract the
+ *     row maximum, exponentiate, normalise, and take the weighted average of the value rows;
+ *   - causal mask: keys after the query's position are excluded before the softmax (course page,
+ *     step 1: -inf before softmax). Alignment when Tq < Tkv is bottom-right: query t sits at
+ *     position t + (Tkv - Tq). The pages only show the square case; this is the plainest reading
+ *     that keeps the square case and makes a one-token decode see the whole cache.
+ *   - heads_out: fold and expand K, fold and expand V, then one attend per query head (lab step 5).
+ *
+ * Everything is computed in double precision. Inputs may be fp64, fp32 or bf16 bit patterns;
+ * widening any of them to double is exact. Two-pass softmax: first the maximum, then the
+ * exponentials and their sum; dot products are summed sequentially in index order.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F64 = 0, ORACLE_F32 = 1, ORACLE_BF16 = 2 };
+
+enum {
+  ORACLE_OK = 0,
+  ORACLE_ERR_GROUPING = 1, /* head count not divisible by the group count */
+  ORACLE_ERR_SHAPE = 2,    /* non-positive sizes, bad index, causal rows with no visible key */
+  ORACLE_ERR_ALLOC = 3
+};
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Exact widening of one element to double. */
+static double widen(const void* base, int dtype, int64_t idx) {
+  if (dtype == ORACLE_F64) return ((const double*)base)[idx];
+  if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
+  uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* Group index of query head `head` when h heads are split into g contiguous groups.
+ * Returns -1 when h is not divisible by g or the arguments are out of range. */
+int oracle_group_of(int head, int h, int g) {
+  if (h <= 0 || g <= 0 || h % g != 0 || head < 0 || head >= h) return -1;
+  return head / (h / g);
+}
+
+/* fold: src[B,T,H,d] (any input dtype) -> dst[B,T,g,d] fp64.
+ * dst[b,t,j,:] = (sum over the s = H/g heads j*s .. j*s+s-1 of src[b,t,head,:]) / s. */
+int oracle_fold(const void* src, int dtype, double* dst, int64_t B, int64_t T, int H, int g,
+                int d) {
+  if (B <= 0 || T <= 0 || H <= 0 || g <= 0 || d <= 0) return ORACLE_ERR_SHAPE;
+  if (H % g != 0) return ORACLE_ERR_GROUPING;
+  const int s = H / g;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t t = 0; t < T; ++t)
+      for (int j = 0; j < g; ++j) {
+        const int start = j * s;
+        for (int c = 0; c < d; ++c) {
+          double acc = 0.0;
+          for (int i = 0; i < s; ++i)
+            acc += widen(src, dtype, ((b * T + t) * H + (start + i)) * (int64_t)d + c);
+          dst[((b * T + t) * g + j) * (int64_t)d + c] = acc / (double)s;
+        }
+      }
+  return ORACLE_OK;
+}
+
+/* expand: src[B,T,g,d] fp64 -> dst[B,T,h,d] fp64 by adjacent repetition: the outer loop runs
+ * over the folded heads, the inner loop repeats each one h/g times, so [A,B] -> [A,A,B,B]. */
+int oracle_expand(const double* src, double* dst, int64_t B, int64_t T, int g, int h, int d) {
+  if (B <= 0 || T <= 0 || h <= 0 || g <= 0 || d <= 0) return ORACLE_ERR_SHAPE;
+  if (h % g != 0) return ORACLE_ERR_GROUPING;
+  const int rep = h / g;
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t t = 0; t < T; ++t) {
+      int out_head = 0;
+      for (int j = 0; j < g; ++j)
+        for (int r = 0; r < rep; ++r) {
+          memcpy(&dst[((b * T + t) * h + out_head) * (int64_t)d],
+                 &src[((b * T + t) * g + j) * (int64_t)d], sizeof(double) * (size_t)d);
+          ++out_head;
+        }
+    }
+  return ORACLE_OK;
+}
+
+/* One output row of single-head attention.
+ * q: d values; k, v: nvis rows of d values (contiguous); out: d values.
+ * Scores s_j = scale * sum_c q[c] k[j][c]; two-pass softmax; out = sum_j p_j v_j / sum_j p_j.
+ * A row that sees no key (nvis == 0) is defined as zeros. */
+static void attend_row(const double* q, const double* k, const double* v, int64_t nvis, int d,
+                       double scale, double* s, double* out) {
+  for (int c = 0; c < d; ++c) out[c] = 0.0;
+  if (nvis <= 0) return;
+  double m = -INFINITY;
+  for (int64_t j = 0; j < nvis; ++j) {
+    double dot = 0.0;
+    for (int c = 0; c < d; ++c) dot += q[c] * k[j * d + c];
+    s[j] = scale * dot;
+    if (s[j] > m) m = s[j];
+  }
+  double l = 0.0;
+  for (int64_t j = 0; j < nvis; ++j) {
+    const double p = exp(s[j] - m);
+    s[j] = p;
+    l += p;
+  }
+  for (int64_t j = 0; j < nvis; ++j)
+    for (int c = 0; c < d; ++c) out[c] += s[j] * v[j * d + c];
+  for (int c = 0; c < d; ++c) out[c] /= l;
+}
+
+/* Number of keys query t of a (Tq, Tkv) item sees. */
+static int64_t visible_keys(int64_t t, int64_t Tq, int64_t Tkv, int causal) {
+  if (!causal) return Tkv;
+  int64_t n = t + (Tkv - Tq) + 1;
+  if (n < 0) n = 0;
+  if (n > Tkv) n = Tkv;
+  return n;
+}
+
+/* Item table: a dense batch has B items of (Tq, Tkv); a packed batch (cu_seqlens) has nseq items
+ * of equal query and key length, laid out back to back in a single [1, total, H, d] tensor. */
+typedef struct {
+  int64_t q_row0, k_row0; /* first row of the item in the [rows, H, d] view */
+  int64_t Tq, Tkv;
+} item_t;
+
+static int make_items(int64_t B, int64_t Tq, int64_t Tkv, const int32_t* cu, int nseq,
+                      item_t** items, int* nitems) {
+  if (cu) {
+    if (nseq <= 0 || cu[0] != 0) return ORACLE_ERR_SHAPE;
+    *items = (item_t*)malloc(sizeof(item_t) * (size_t)nseq);
+    if (!*items) return ORACLE_ERR_ALLOC;
+    for (int s = 0; s < nseq; ++s) {
+      const int64_t len = (int64_t)cu[s + 1] - cu[s];
+      if (len < 0) { free(*items); return ORACLE_ERR_SHAPE; }
+      (*items)[s].q_row0 = cu[s];
+      (*items)[s].k_row0 = cu[s];
+      (*items)[s].Tq = len;
+      (*items)[s].Tkv = len;
+    }
+    *nitems = nseq;
+  } else {
+    *items = (item_t*)malloc(sizeof(item_t) * (size_t)B);
+    if (!*items) return ORACLE_ERR_ALLOC;
+    for (int64_t b = 0; b < B; ++b) {
+      (*items)[b].q_row0 = b * Tq;
+      (*items)[b].k_row0 = b * Tkv;
+      (*items)[b].Tq = Tq;
+      (*items)[b].Tkv = Tkv;
+    }
+    *nitems = (int)B;
+  }
+  return ORACLE_OK;
+}
+
+/* heads_out: full grouped-query attention.
+ *   q   [B, Tq, Hq, d]   (dtype_in)       or [1, total, Hq, d] with cu_seqlens
+ *   k,v [B, Tkv, Hkv, d] (dtype_in)       or [1, total, Hkv, d]
+ *   out [B, Tq, Hq, d]   fp64
+ * Steps: widen K and V to fp64; expand both to Hq heads (materialised copies, adjacent
+ * repetition); for every item, query head and query row, attend over the visible keys of the
+ * expanded head. Hkv == Hq reproduces per-head multi-head attention exactly. */
+int oracle_gqa_attention(const void* q, const void* k, const void* v, int dtype_in, double* out,
+                         int64_t B, int64_t Tq, int64_t Tkv, int Hq, int Hkv, int d, double scale,
+                         int causal, const int32_t* cu_seqlens, int nseq) {
+  if (Hq <= 0 || Hkv <= 0 || d <= 0) return ORACLE_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ORACLE_ERR_GROUPING;
+  item_t* items = NULL;
+  int nitems = 0;
+  int rc = make_items(B, Tq, Tkv, cu_seqlens, nseq, &items, &nitems);
+  if (rc) return rc;
+  const int64_t qrows = cu_seqlens ? cu_seqlens[nseq] : B * Tq;
+  const int64_t krows = cu_seqlens ? cu_seqlens[nseq] : B * Tkv;
+
+  double* kw = (double*)malloc(sizeof(double) * (size_t)(krows * Hkv * d));
+  double* vw = (double*)malloc(sizeof(double) * (size_t)(krows * Hkv * d));
+  double* ke = (double*)malloc(sizeof(double) * (size_t)(krows * Hq * d));
+  double* ve = (double*)malloc(sizeof(double) * (size_t)(krows * Hq * d));
+  if (!kw || !vw || !ke || !ve) {
+    free(kw); free(vw); free(ke); free(ve); free(items);
+    return ORACLE_ERR_ALLOC;
+  }
+  for (int64_t i = 0; i < krows * Hkv * d; ++i) {
+    kw[i] = widen(k, dtype_in, i);
+    vw[i] = widen(v, dtype_in, i);
+  }
+  oracle_expand(kw, ke, 1, krows, Hkv, Hq, d);
+  oracle_expand(vw, ve, 1, krows, Hkv, Hq, d);
+  free(kw);
+  free(vw);
+
+  int64_t max_tkv = 0;
+  for (int it = 0; it < nitems; ++it)
+    if (items[it].Tkv > max_tkv) max_tkv = items[it].Tkv;
+
+  int err = ORACLE_OK;
+#pragma omp parallel
+  {
+    double* qh = (double*)malloc(sizeof(double) * (size_t)d);
+    double* kh = (double*)malloc(sizeof(double) * (size_t)(max_tkv * d + 1));
+    double* vh = (double*)malloc(sizeof(double) * (size_t)(max_tkv * d + 1));
+    double* sc = (double*)malloc(sizeof(double) * (size_t)(max_tkv + 1));
+    double* orow = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!qh || !kh || !vh || !sc || !orow) {
+#pragma omp atomic write
+      err = ORACLE_ERR_ALLOC;
+    } else {
+#pragma omp for schedule(dynamic, 1) collapse(2)
+      for (int it = 0; it < nitems; ++it)
+        for (int h = 0; h < Hq; ++h) {
+          const item_t I = items[it];
+          /* the expanded head h of this item as contiguous [Tkv][d] tables */
+          for (int64_t j = 0; j < I.Tkv; ++j) {
+            memcpy(&kh[j * d], &ke[((I.k_row0 + j) * Hq + h) * (int64_t)d], sizeof(double) * d);
+            memcpy(&vh[j * d], &ve[((I.k_row0 + j) * Hq + h) * (int64_t)d], sizeof(double) * d);
+          }
+          for (int64_t t = 0; t < I.Tq; ++t) {
+            const int64_t row = I.q_row0 + t;
+            for (int c = 0; c < d; ++c) qh[c] = widen(q, dtype_in, (row * Hq + h) * (int64_t)d + c);
+            attend_row(qh, kh, vh, visible_keys(t, I.Tq, I.Tkv, causal), d, scale, sc, orow);
+            memcpy(&out[(row * Hq + h) * (int64_t)d], orow, sizeof(double) * d);
+          }
+        }
+    }
+    free(qh); free(kh); free(vh); free(sc); free(orow);
+  }
+  (void)qrows;
+  free(ke);
+  free(ve);
+  free(items);
+  return err;
+}
+
+/* The same attention for a chosen set of output rows only (rows are independent, so this is
+ * exact for those rows). rows: nrows triples (b, t, head) where for a packed batch b == 0 and t
+ * is the packed row. out: nrows x d fp64. For each row the expanded head is materialised by
+ * copying the K/V rows of the item for the group's key/value head, found with the same
+ * contiguous rule the expansion above realises: head / (Hq / Hkv). */
+int oracle_gqa_attention_rows(const void* q, const void* k, const void* v, int dtype_in,
+                              int64_t B, int64_t Tq, int64_t Tkv, int Hq, int Hkv, int d,
+                              double scale, int causal, const int32_t* cu_seqlens, int nseq,
+                              const int64_t* rows, int64_t nrows, double* out) {
+  if (Hq <= 0 || Hkv <= 0 || d <= 0) return ORACLE_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ORACLE_ERR_GROUPING;
+  item_t* items = NULL;
+  int nitems = 0;
+  int rc = make_items(B, Tq, Tkv, cu_seqlens, nseq, &items, &nitems);
+  if (rc) return rc;
+  int64_t max_tkv = 0;
+  for (int it = 0; it < nitems; ++it)
+    if (items[it].Tkv > max_tkv) max_tkv = items[it].Tkv;
+  /* validate and locate every row first */
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t b = rows[3 * r], t = rows[3 * r + 1], h = rows[3 * r + 2];
+    if (h < 0 || h >= Hq) { free(items); return ORACLE_ERR_SHAPE; }
+    if (cu_seqlens) {
+      if (b != 0 || t < 0 || t >= cu_seqlens[nseq]) { free(items); return ORACLE_ERR_SHAPE; }
+    } else if (b < 0 || b >= B || t < 0 || t >= Tq) {
+      free(items);
+      return ORACLE_ERR_SHAPE;
+    }
+  }
+  int err = ORACLE_OK;
+#pragma omp parallel
+  {
+    double* qh = (double*)malloc(sizeof(double) * (size_t)d);
+    double* kh = (double*)malloc(sizeof(double) * (size_t)(max_tkv * d + 1));
+    double* vh = (double*)malloc(sizeof(double) * (size_t)(max_tkv * d + 1));
+    double* sc = (double*)malloc(sizeof(double) * (size_t)(max_tkv + 1));
+    if (!qh || !kh || !vh || !sc) {
+#pragma omp atomic write
+      err = ORACLE_ERR_ALLOC;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t b = rows[3 * r], tglob = rows[3 * r + 1];
+        const int h = (int)rows[3 * r + 2];
+        item_t I;
+        int64_t t;
+        if (cu_seqlens) {
+          int s = 0;
+          while (!(tglob >= cu_seqlens[s] && tglob < cu_seqlens[s + 1])) ++s;
+          I = items[s];
+          t = tglob - I.q_row0;
+        } else {
+          I = items[b];
+          t = tglob;
+        }
+        const int kvh = oracle_group_of(h, Hq, Hkv);
+        for (int64_t j = 0; j < I.Tkv; ++j)
+          for (int c = 0; c < d; ++c) {
+            const int64_t src = ((I.k_row0 + j) * Hkv + kvh) * (int64_t)d + c;
+            kh[j * d + c] = widen(k, dtype_in, src);
+            vh[j * d + c] = widen(v, dtype_in, src);
+          }
+        const int64_t row = I.q_row0 + t;
+        for (int c = 0; c < d; ++c) qh[c] = widen(q, dtype_in, (row * Hq + h) * (int64_t)d + c);
+        attend_row(qh, kh, vh, visible_keys(t, I.Tq, I.Tkv, causal), d, scale, sc, &out[r * d]);
+      }
+    }
+    free(qh); free(kh); free(vh); free(sc);
+  }
+  free(items);
+  return err;
+}

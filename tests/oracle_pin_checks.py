@@ -1,0 +1,346 @@
+"""Pins that tie the fp64 oracle to what the pages and the mathematics fix.
+
+Each ``check_*`` function takes a bound oracle (``oracle.Oracle``) and raises AssertionError when
+the oracle disagrees with the fact it pins. ``test_oracle_pins.py`` runs them on the in-tree
+oracle; ``test_oracle_mutations.py`` runs them on copies of the oracle with a planted mistake and
+asserts that some pin fails.
+
+Sources of the facts (page, section):
+  * GQA lab page ("Transformer -- attention by hand: reducing only the key/value heads"):
+    step 1 (contiguous groups, worked example h=8, g=2), step 2 (fold = mean; g = h returns the
+    values unchanged; first-head or global mean only coincide at g = 1), step 3 (expand by
+    adjacent repetition, worked example [A,B] -> [A,A,B,B]; query head i reads
+    folded[group_of(i)]), step 4 (divide by sqrt(head dim), subtract the max, large inputs must
+    not overflow), step 5 (g = h equals multi-head exactly: first diff_table entry 0.0),
+    steps 6-8 (counts; cache ratio up to 8x, core multiplies the same for every g).
+  * Course page ("Week 7. Attention"): step 1 (scale 1/sqrt(d); -inf before softmax so each row
+    still sums to one over the past), step 2 (32/8 heads -> 4x smaller cache, MQA 32x),
+    "typical errors" (repeat_kv must repeat adjacently; attention must be causal), and the
+    check against torch's scaled_dot_product_attention.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _sdpa_reference(q, k, v, causal):
+    """torch CPU fp64 scaled_dot_product_attention with K/V expanded by repeat_interleave."""
+    import torch
+    import torch.nn.functional as F
+    G = q.shape[2] // k.shape[2]
+    qt = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float64)).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(np.ascontiguousarray(k, dtype=np.float64)).repeat_interleave(G, dim=2)
+    vt = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float64)).repeat_interleave(G, dim=2)
+    kt = kt.permute(0, 2, 1, 3).contiguous()
+    vt = vt.permute(0, 2, 1, 3).contiguous()
+    out = F.scaled_dot_product_attention(qt.contiguous(), kt, vt, is_causal=causal)
+    return out.permute(0, 2, 1, 3).numpy()
+
+
+# ------------------------------------------------------------------------------------------------
+# step 1: grouping
+# ------------------------------------------------------------------------------------------------
+
+def check_group_of_worked_example(orc):
+    with open(os.path.join(GOLDEN, "group_map_h8_g2.txt")) as f:
+        rows = [tuple(int(x) for x in ln.split()) for ln in f
+                if ln.strip() and not ln.startswith("#")]
+    assert rows, "fixture empty"
+    for h, g, head, grp in rows:
+        assert orc.group_of(head, h, g) == grp, (h, g, head)
+    # contiguous blocks: group sizes equal, each group a run of consecutive heads
+    for h in range(1, 9):
+        for g in [x for x in range(1, h + 1) if h % x == 0]:
+            mem = orc.group_members(h, g)
+            assert [x for grp in mem for x in grp] == list(range(h)), (h, g)
+            assert all(len(grp) == h // g for grp in mem)
+
+
+def check_group_of_rejects_uneven(orc):
+    for h, g in ((8, 3), (6, 4), (32, 5)):
+        try:
+            orc.group_members(h, g)
+        except ValueError:
+            continue
+        raise AssertionError(f"group_members({h},{g}) did not raise")
+
+
+# ------------------------------------------------------------------------------------------------
+# step 2: fold
+# ------------------------------------------------------------------------------------------------
+
+def check_fold_identity_when_g_is_h(orc):
+    x = _rng(1).standard_normal((2, 5, 8, 16)).astype(np.float32)
+    f = orc.fold_kv(x, 8)
+    assert np.array_equal(f, x.astype(np.float64))
+
+
+def check_fold_is_group_mean(orc):
+    # integer-valued inputs: every sum and the division by a power of two are exact
+    x = _rng(2).integers(-64, 64, size=(2, 3, 8, 4)).astype(np.float64)
+    for g in (4, 2, 1):
+        s = 8 // g
+        want = x.reshape(2, 3, g, s, 4).sum(axis=3) / s
+        assert np.array_equal(orc.fold_kv(x, g), want), g
+    # constant within each group -> that constant
+    c = np.repeat(np.arange(4.0)[None, None, :, None], 2, axis=2).reshape(1, 1, 8, 1)
+    c = np.broadcast_to(c, (1, 2, 8, 3)).copy()
+    assert np.array_equal(orc.fold_kv(c, 4), np.broadcast_to(np.arange(4.0)[None, None, :, None],
+                                                              (1, 2, 4, 3)))
+    # the lab: keeping the first head, or averaging everything, only agree with fold at g = 1
+    y = _rng(3).standard_normal((1, 4, 8, 4))
+    f2 = orc.fold_kv(y, 2)
+    assert not np.allclose(f2[:, :, 0], y[:, :, 0])
+    assert not np.allclose(f2[:, :, 0], y.mean(axis=2))
+    assert np.allclose(orc.fold_kv(y, 1)[:, :, 0], y.mean(axis=2), rtol=0, atol=1e-15)
+
+
+# ------------------------------------------------------------------------------------------------
+# step 3: expand
+# ------------------------------------------------------------------------------------------------
+
+def check_expand_worked_example(orc):
+    with open(os.path.join(GOLDEN, "expand_AB_to_4.txt")) as f:
+        line = [ln for ln in f if ln.strip() and not ln.startswith("#")][0]
+    src, h, want, wrong = [p.strip() for p in line.split("|")]
+    names = src.split(",")
+    h = int(h)
+    folded = np.arange(1.0, len(names) + 1.0).reshape(1, 1, len(names), 1)  # A=1, B=2
+    code = {n: float(i + 1) for i, n in enumerate(names)}
+    got = orc.expand_kv(folded, h)[0, 0, :, 0]
+    assert list(got) == [code[n] for n in want.split(",")]
+    assert list(got) != [code[n] for n in wrong.split(",")]
+
+
+def check_expand_reads_own_group(orc):
+    x = _rng(4).standard_normal((1, 3, 8, 5))
+    for g in (8, 4, 2, 1):
+        f = orc.fold_kv(x, g)
+        e = orc.expand_kv(f, 8)
+        members = orc.group_members(8, g)
+        for i in range(8):
+            gi = orc.group_of(i, 8, g)
+            assert np.array_equal(e[:, :, i], f[:, :, gi]), (g, i)
+            assert np.allclose(e[:, :, i], x[:, :, members[gi]].mean(axis=2), rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------------------------------------------------
+# step 4 / course step 1: attention
+# ------------------------------------------------------------------------------------------------
+
+def check_matches_torch_sdpa(orc):
+    """Library cross-check: every divisor Hkv of Hq <= 8, unmasked and square causal, plus a
+    bottom-right-free decode case (Tq = 1, unmasked)."""
+    rng = _rng(5)
+    for Hq in (1, 2, 3, 4, 6, 8):
+        for Hkv in [x for x in range(1, Hq + 1) if Hq % x == 0]:
+            for causal in (False, True):
+                q = rng.standard_normal((2, 7, Hq, 8))
+                k = rng.standard_normal((2, 7, Hkv, 8))
+                v = rng.standard_normal((2, 7, Hkv, 8))
+                got = orc.attention(q, k, v, causal=causal)
+                ref = _sdpa_reference(q, k, v, causal)
+                err = np.max(np.abs(got - ref))
+                assert err <= 1e-12, (Hq, Hkv, causal, err)
+    q = rng.standard_normal((3, 1, 8, 16))
+    k = rng.standard_normal((3, 33, 2, 16))
+    v = rng.standard_normal((3, 33, 2, 16))
+    assert np.max(np.abs(orc.attention(q, k, v) - _sdpa_reference(q, k, v, False))) <= 1e-12
+
+
+def check_scale_is_one_over_sqrt_d(orc):
+    # d = 16 -> scale 1/4. q = 4a e_0, k_1 = b e_0 with a*b = ln 3: scores 0 and ln 3, weights 1/4, 3/4
+    d = 16
+    q = np.zeros((1, 1, 1, d)); q[0, 0, 0, 0] = 4.0
+    k = np.zeros((1, 2, 1, d)); k[0, 1, 0, 0] = math.log(3.0)
+    v = np.zeros((1, 2, 1, d)); v[0, 0, 0, :] = 1.0; v[0, 1, 0, :] = 5.0
+    out = orc.attention(q, k, v)
+    assert np.allclose(out, 0.25 * 1.0 + 0.75 * 5.0, rtol=0, atol=1e-14), out[0, 0, 0, 0]
+    # default scale equals an explicit 1/sqrt(d)
+    x = _rng(6).standard_normal((1, 9, 2, d))
+    assert np.array_equal(orc.attention(x, x[:, :, :1], x[:, :, 1:]),
+                          orc.attention(x, x[:, :, :1], x[:, :, 1:], scale=0.25))
+
+
+def check_rows_sum_to_one(orc):
+    # V rows = unit basis vectors: the output row is the softmax weight vector itself
+    rng = _rng(7)
+    T, d = 12, 16
+    q = rng.standard_normal((1, T, 4, d)) * 3
+    k = rng.standard_normal((1, T, 2, d)) * 3
+    v = np.zeros((1, T, 2, d)); v[0, np.arange(T), :, np.arange(T)] = 1.0
+    for causal in (False, True):
+        w = orc.attention(q, k, v, causal=causal)
+        assert np.all(w >= 0)
+        assert np.allclose(w.sum(axis=-1), 1.0, rtol=0, atol=1e-14)
+        if causal:  # nothing after the query's own position
+            for t in range(T):
+                assert np.all(w[0, t, :, t + 1:T] == 0.0)
+
+
+def check_closed_forms(orc):
+    rng = _rng(8)
+    # V == 1 -> out == 1
+    q = rng.standard_normal((2, 6, 4, 8)); k = rng.standard_normal((2, 6, 2, 8))
+    assert np.allclose(orc.attention(q, k, np.ones((2, 6, 2, 8)), causal=True), 1.0, rtol=0,
+                       atol=1e-15)
+    # K == 0 -> uniform weights: prefix means (causal) or full mean (unmasked)
+    v = rng.standard_normal((1, 6, 2, 8))
+    z = np.zeros((1, 6, 2, 8)); q1 = rng.standard_normal((1, 6, 4, 8))
+    o_full = orc.attention(q1, z, v)
+    o_causal = orc.attention(q1, z, v, causal=True)
+    for i in range(4):
+        kv = i // 2
+        assert np.allclose(o_full[0, :, i], v[0, :, kv].mean(axis=0), rtol=0, atol=1e-14)
+        for t in range(6):
+            assert np.allclose(o_causal[0, t, i], v[0, :t + 1, kv].mean(axis=0), rtol=0,
+                               atol=1e-14)
+    # a single key -> out == v_0 exactly
+    v1 = rng.standard_normal((1, 1, 1, 8))
+    assert np.array_equal(orc.attention(rng.standard_normal((1, 3, 4, 8)),
+                                        rng.standard_normal((1, 1, 1, 8)), v1)[0, :, 0],
+                          np.repeat(v1[0, :, 0], 3, axis=0))
+    # one dominant key -> its value row
+    k2 = rng.standard_normal((1, 5, 1, 8)) * 0.1
+    qd = np.zeros((1, 1, 1, 8)); qd[0, 0, 0, 0] = 100.0
+    k2[0, 3, 0, 0] = 100.0
+    assert np.allclose(orc.attention(qd, k2, v[:, :5, :1])[0, 0, 0], v[0, 3, 0], rtol=0,
+                       atol=1e-12)
+
+
+def check_large_inputs_do_not_overflow(orc):
+    rng = _rng(9)
+    for mult in (1e3, 1e6):
+        q = rng.standard_normal((1, 8, 4, 16)) * mult
+        k = rng.standard_normal((1, 8, 2, 16)) * mult
+        v = rng.standard_normal((1, 8, 2, 16))
+        out = orc.attention(q, k, v, causal=True)
+        assert np.all(np.isfinite(out))
+        # at this scale every row is one-hot on its best visible key
+        G = 2
+        for t in range(8):
+            for i in range(4):
+                s = [float(q[0, t, i] @ k[0, j, i // G]) for j in range(t + 1)]
+                assert np.allclose(out[0, t, i], v[0, int(np.argmax(s)), i // G], rtol=0,
+                                   atol=1e-9)
+
+
+def check_causality(orc):
+    rng = _rng(10)
+    q = rng.standard_normal((1, 10, 4, 8)); k = rng.standard_normal((1, 10, 2, 8))
+    v = rng.standard_normal((1, 10, 2, 8))
+    base = orc.attention(q, k, v, causal=True)
+    for t in (0, 4, 8):
+        k2 = k.copy(); v2 = v.copy()
+        k2[0, t + 1:] += 7.0; v2[0, t + 1:] -= 3.0
+        o = orc.attention(q, k2, v2, causal=True)
+        assert np.array_equal(o[0, :t + 1], base[0, :t + 1]), t
+        assert not np.array_equal(o[0, t + 1:], base[0, t + 1:]), t
+
+
+def check_bottom_right_alignment(orc):
+    """Tq < Tkv with the causal flag equals the last Tq rows of square causal attention over Tkv
+    queries (square causal is pinned to torch above); a single query sees the whole cache."""
+    rng = _rng(11)
+    Tkv, Tq = 11, 4
+    qf = rng.standard_normal((2, Tkv, 4, 8))
+    k = rng.standard_normal((2, Tkv, 1, 8)); v = rng.standard_normal((2, Tkv, 1, 8))
+    full = orc.attention(qf, k, v, causal=True)
+    part = orc.attention(qf[:, Tkv - Tq:], k, v, causal=True)
+    assert np.array_equal(part, full[:, Tkv - Tq:])
+    one = orc.attention(qf[:, -1:], k, v, causal=True)
+    assert np.array_equal(one, orc.attention(qf[:, -1:], k, v, causal=False))
+
+
+# ------------------------------------------------------------------------------------------------
+# step 5: heads_out / max_gap
+# ------------------------------------------------------------------------------------------------
+
+def check_g_equals_h_is_mha(orc):
+    from oracle import max_gap
+    q = _rng(12).standard_normal((1, 6, 8, 4))
+    k = _rng(13).standard_normal((1, 6, 8, 4))
+    v = _rng(14).standard_normal((1, 6, 8, 4))
+    mha = np.concatenate([orc.attention(q[:, :, i:i + 1], k[:, :, i:i + 1], v[:, :, i:i + 1])
+                          for i in range(8)], axis=2)
+    gaps = [max_gap(orc.heads_out(q, k, v, g), mha) for g in (8, 4, 2, 1)]
+    assert gaps[0] == 0.0, gaps
+    assert all(gp > 0 for gp in gaps[1:]), gaps
+
+
+def check_packed_equals_separate(orc):
+    rng = _rng(15)
+    lens = (5, 1, 9, 3)
+    tot = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q = rng.standard_normal((1, tot, 4, 8)); k = rng.standard_normal((1, tot, 2, 8))
+    v = rng.standard_normal((1, tot, 2, 8))
+    packed = orc.attention(q, k, v, causal=True, cu_seqlens=cu)
+    for s in range(len(lens)):
+        a, b = cu[s], cu[s + 1]
+        sep = orc.attention(q[:, a:b], k[:, a:b], v[:, a:b], causal=True)
+        assert np.array_equal(packed[:, a:b], sep), s
+
+
+def check_rows_equal_full(orc):
+    rng = _rng(16)
+    q = rng.standard_normal((2, 9, 8, 8)).astype(np.float32)
+    k = rng.standard_normal((2, 9, 2, 8)).astype(np.float32)
+    v = rng.standard_normal((2, 9, 2, 8)).astype(np.float32)
+    full = orc.attention(q, k, v, causal=True)
+    rows = np.array([(0, 0, 0), (1, 8, 7), (1, 3, 2), (0, 5, 5)], dtype=np.int64)
+    got = orc.attention_rows(q, k, v, rows, causal=True)
+    for r, (b, t, h) in enumerate(rows):
+        assert np.array_equal(got[r], full[b, t, h]), (b, t, h)
+    lens = (3, 6)
+    cu = np.array([0, 3, 9], dtype=np.int32)
+    qp, kp, vp = q[:1], k[:1], v[:1]
+    fullp = orc.attention(qp, kp, vp, causal=True, cu_seqlens=cu)
+    rows = np.array([(0, 0, 1), (0, 2, 7), (0, 3, 0), (0, 8, 4)], dtype=np.int64)
+    got = orc.attention_rows(qp, kp, vp, rows, causal=True, cu_seqlens=cu)
+    for r, (b, t, h) in enumerate(rows):
+        assert np.array_equal(got[r], fullp[b, t, h]), (b, t, h)
+    del lens
+
+
+def check_bf16_widening_is_exact(orc):
+    bits = _rng(17).integers(0, 1 << 16, size=(1, 5, 4, 8), dtype=np.uint16)
+    bits[(bits & 0x7F80) == 0x7F80] = 0x3F80    # no inf/nan patterns
+    vals = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    vals = np.clip(vals, -1e3, 1e3)
+    bits = ((vals.astype(np.float32)).view(np.uint32) >> 16).astype(np.uint16)
+    vals = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    kb, vb = bits[:, :, :2], bits[:, :, 2:]
+    a = orc.attention(bits, np.ascontiguousarray(kb), np.ascontiguousarray(vb), causal=True)
+    b = orc.attention(vals, vals[:, :, :2], vals[:, :, 2:], causal=True)
+    assert np.array_equal(a, b)
+
+
+ALL_CHECKS = [
+    check_group_of_worked_example,
+    check_group_of_rejects_uneven,
+    check_fold_identity_when_g_is_h,
+    check_fold_is_group_mean,
+    check_expand_worked_example,
+    check_expand_reads_own_group,
+    check_matches_torch_sdpa,
+    check_scale_is_one_over_sqrt_d,
+    check_rows_sum_to_one,
+    check_closed_forms,
+    check_large_inputs_do_not_overflow,
+    check_causality,
+    check_bottom_right_alignment,
+    check_g_equals_h_is_mha,
+    check_packed_equals_separate,
+    check_rows_equal_full,
+    check_bf16_widening_is_exact,
+]

@@ -1,0 +1,56 @@
+"""Planted mistakes in the oracle (CPU only): each mutant is a copy of ``gqa_oracle.c`` with one
+plausible error, compiled into a temporary library; at least one pin must fail for every mutant.
+This shows the pins constrain the oracle and are not a restatement of it."""
+import os
+
+import pytest
+
+import oracle
+import oracle_pin_checks as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "gqa_oracle.c")
+
+MUTANTS = {
+    # step 1: interleaved instead of contiguous groups
+    "group_of_interleaved": ("return head / (h / g);", "return head % g;"),
+    # step 3: whole-list repetition [A,B,A,B] instead of adjacent repetition
+    "expand_tiled": ("&src[((b * T + t) * g + j) * (int64_t)d]",
+                     "&src[((b * T + t) * g + (out_head % g)) * (int64_t)d]"),
+    # step 2: divide by the head count instead of the group size
+    "fold_wrong_divisor": ("dst[((b * T + t) * g + j) * (int64_t)d + c] = acc / (double)s;",
+                           "dst[((b * T + t) * g + j) * (int64_t)d + c] = acc / (double)H;"),
+    # step 4: scale dropped
+    "no_scale": ("s[j] = scale * dot;", "s[j] = dot;"),
+    # step 4: max not subtracted
+    "no_max_subtraction": ("const double p = exp(s[j] - m);", "const double p = exp(s[j]);"),
+    # course step 1: mask one position too strict
+    "causal_off_by_one": ("int64_t n = t + (Tkv - Tq) + 1;", "int64_t n = t + (Tkv - Tq);"),
+    # top-left instead of bottom-right alignment when Tq < Tkv
+    "causal_top_left": ("int64_t n = t + (Tkv - Tq) + 1;", "int64_t n = t + 1;"),
+    # softmax not normalised
+    "no_normalisation": ("for (int c = 0; c < d; ++c) out[c] /= l;", "(void)l;"),
+    # value rows weighted by the wrong key
+    "value_index_shift": ("out[c] += s[j] * v[j * d + c];",
+                          "out[c] += s[j] * v[((j + 1) % nvis) * d + c];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor for {name} no longer in the oracle source"
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    import subprocess
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", str(mutated),
+                    "-o", str(lib), "-lm"], check=True)
+    orc = oracle.Oracle(str(lib))
+    failed = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(orc)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(check.__name__)
+    assert failed, f"no pin caught mutant {name}"
