@@ -1,0 +1,22 @@
+"""Grouped-query attention forward for AMD MI355X (gfx950).
+
+Python face of the C ABI declared in ``include/gqa_attn.h``; the work runs in hand-written HIP
+kernels in ``libgqa_attn.so``. Import fails if the library has not been built.
+"""
+from ._binding import (  # noqa: F401
+    ABI_VERSION,
+    GQAError,
+    GQAValueError,
+    gqa_attn_decode,
+    gqa_attn_decode_workspace_bytes,
+    gqa_attn_prefill,
+    gqa_fold_kv,
+    gqa_status_string,
+    header_functions,
+    load_library,
+    raw_library,
+)
+
+prefill = gqa_attn_prefill
+decode = gqa_attn_decode
+fold_kv = gqa_fold_kv

@@ -1,0 +1,213 @@
+"""ctypes binding of ``libgqa_attn.so`` (argument marshalling only).
+
+Every step of the attention runs in the library's HIP kernels; this module only checks that the
+library is present, turns torch tensors into pointers, sizes and a stream handle, and maps status
+codes to Python exceptions (ValueError for sizes and uneven head groups, like the GQA lab page's
+ValueError convention; RuntimeError otherwise). There is no fallback: if the library is missing,
+importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch  # loaded first so the library binds to the HIP runtime torch already mapped
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgqa_attn.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "gqa_attn.h")
+
+GQA_OK, GQA_ERR_NULL_PTR, GQA_ERR_SHAPE, GQA_ERR_GROUPING = 0, 1, 2, 3
+GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_ALIAS, GQA_ERR_HIP = 4, 5, 6, 7
+GQA_DTYPE_F32, GQA_DTYPE_BF16 = 0, 1
+
+
+class GQAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(msg)
+        self.code = code
+
+
+class GQAValueError(ValueError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(msg)
+        self.code = code
+
+
+def _hip_runtimes_mapped():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln and "/" in ln})
+    except OSError:
+        return []
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m grouped_query_softmax_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.gqa_attn_prefill.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P, I, I, P]
+    lib.gqa_attn_prefill.restype = I
+    lib.gqa_attn_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.gqa_attn_decode_workspace_bytes.restype = SZ
+    lib.gqa_attn_decode.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, SZ, I, P]
+    lib.gqa_attn_decode.restype = I
+    lib.gqa_fold_kv.argtypes = [P, P, I, I, I, I, I, I, P]
+    lib.gqa_fold_kv.restype = I
+    lib.gqa_status_string.argtypes = [I]
+    lib.gqa_status_string.restype = ctypes.c_char_p
+    lib.gqa_attn_abi_version.argtypes = []
+    lib.gqa_attn_abi_version.restype = I
+    return lib
+
+
+def header_functions(header: str = HEADER):
+    """Names of the functions ``include/gqa_attn.h`` declares."""
+    src = open(header).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", src)))
+
+
+_lib = load_library()
+_runtimes = _hip_runtimes_mapped()
+if len(_runtimes) > 1:
+    raise ImportError(f"more than one HIP runtime mapped into this process: {_runtimes}")
+
+ABI_VERSION = _lib.gqa_attn_abi_version()
+
+
+def gqa_status_string(code: int) -> str:
+    return _lib.gqa_status_string(code).decode()
+
+
+def _check(code: int, what: str):
+    if code == GQA_OK:
+        return
+    msg = f"{what}: {gqa_status_string(code)} (status {code})"
+    if code in (GQA_ERR_SHAPE, GQA_ERR_GROUPING):
+        raise GQAValueError(code, msg)
+    raise GQAError(code, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GQA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return GQA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    return t if t.is_contiguous() else t.contiguous()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def gqa_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                     scale: Optional[float] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                     max_seqlen: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """q [B,Tq,Hq,d], k/v [B,Tkv,Hkv,d] (or [1,total,H,d] with int32 device cu_seqlens)."""
+    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q[B,Tq,Hq,d] and k, v[B,Tkv,Hkv,d]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    B, Tq, Hq, d = q.shape
+    Bk, Tkv, Hkv, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError("q and k/v disagree on batch or head dim")
+    if scale is None:
+        scale = d ** -0.5
+    cu_ptr, nseq, msl = None, B, 0
+    if cu_seqlens is not None:
+        cu = _dev(cu_seqlens, "cu_seqlens")
+        if cu.dtype != torch.int32 or cu.dim() != 1 or cu.numel() < 2:
+            raise ValueError("cu_seqlens must be a 1-D int32 device tensor of nseq+1 offsets")
+        if B != 1:
+            raise ValueError("packed batches use q/k/v of shape [1, total, H, d]")
+        nseq = cu.numel() - 1
+        if max_seqlen is None:
+            max_seqlen = int((cu[1:] - cu[:-1]).max().item())
+        cu_ptr, msl = cu.data_ptr(), int(max_seqlen)
+        cu_seqlens = cu
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    rc = _lib.gqa_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               nseq, Tq, Tkv, Hq, Hkv, d, float(scale), int(bool(causal)),
+                               cu_ptr, msl, _dtype_code(q), _stream(stream))
+    _check(rc, "gqa_attn_prefill")
+    return out
+
+
+def gqa_attn_decode_workspace_bytes(B: int, Tkv: int, Hq: int, Hkv: int, d: int) -> int:
+    return int(_lib.gqa_attn_decode_workspace_bytes(B, Tkv, Hq, Hkv, d))
+
+
+def gqa_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    scale: Optional[float] = None, causal: bool = False,
+                    workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """q [B,1,Hq,d], caches [B,Tkv,Hkv,d]; workspace: a device tensor of at least
+    gqa_attn_decode_workspace_bytes(...) bytes (allocated here when None)."""
+    q, k, v = _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache")
+    if q.dim() != 4 or q.shape[1] != 1 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q[B,1,Hq,d] and k_cache, v_cache[B,Tkv,Hkv,d]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q and the caches must share a dtype")
+    B, _, Hq, d = q.shape
+    Bk, Tkv, Hkv, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError("q and the caches disagree on batch or head dim")
+    if scale is None:
+        scale = d ** -0.5
+    ws_ptr, ws_bytes = None, 0
+    if q.dtype == torch.bfloat16:
+        need = gqa_attn_decode_workspace_bytes(B, Tkv, Hq, Hkv, d)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    rc = _lib.gqa_attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Tkv,
+                              Hq, Hkv, d, float(scale), int(bool(causal)), ws_ptr, ws_bytes,
+                              _dtype_code(q), _stream(stream))
+    _check(rc, "gqa_attn_decode")
+    return out
+
+
+def gqa_fold_kv(src: torch.Tensor, g: int, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """src [B,T,H,d] -> [B,T,g,d], mean over contiguous groups of H/g heads."""
+    if not isinstance(src, torch.Tensor) or src.dim() != 4:
+        raise ValueError("expected src[B,T,H,d]")
+    B, T, H, d = src.shape
+    if g <= 0 or H % g != 0:
+        raise GQAValueError(GQA_ERR_GROUPING, f"{H} heads do not fold evenly into {g} groups")
+    src = _dev(src, "src")
+    if out is None:
+        out = torch.empty((B, T, g, d), dtype=src.dtype, device=src.device)
+    rc = _lib.gqa_fold_kv(src.data_ptr(), out.data_ptr(), B, T, H, g, d, _dtype_code(src),
+                          _stream(stream))
+    _check(rc, "gqa_fold_kv")
+    return out
+
+
+def raw_library() -> ctypes.CDLL:
+    return _lib

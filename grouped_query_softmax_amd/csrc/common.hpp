@@ -1,0 +1,106 @@
+// common.hpp -- device helpers and launcher declarations shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+// log2(e): exponentials are evaluated as 2^(x * log2 e) on the hardware base-2 exponential.
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// Round-to-nearest-even float -> bf16 bits (gfx950 converts in hardware).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Element type traits for the kernels that take either dtype.
+struct F32 {
+  typedef float T;
+  static constexpr int kBytes = 4;
+  __device__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ static float to_f32(float x) { return x; }
+  __device__ static float from_f32(float x) { return x; }
+};
+struct BF16 {
+  typedef uint16_t T;
+  static constexpr int kBytes = 2;
+  __device__ static float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  __device__ static float to_f32(uint16_t x) { return bf16_to_f32(x); }
+  __device__ static uint16_t from_f32(float x) { return f32_to_bf16(x); }
+};
+
+// Item geometry of a launch: a dense batch of B items of (Tq, Tkv), or a packed batch whose
+// item s spans rows cu[s] .. cu[s+1]-1 of both q and k/v.
+struct Items {
+  const int32_t* cu;  // device offsets or nullptr
+  int Tq, Tkv;        // dense item sizes (ignored when cu != nullptr)
+  __device__ __forceinline__ void get(int item, int64_t& q0, int64_t& k0, int& tq,
+                                      int& tkv) const {
+    if (cu) {
+      const int a = cu[item], b = cu[item + 1];
+      q0 = a;
+      k0 = a;
+      tq = b - a;
+      tkv = b - a;
+    } else {
+      q0 = static_cast<int64_t>(item) * Tq;
+      k0 = static_cast<int64_t>(item) * Tkv;
+      tq = Tq;
+      tkv = Tkv;
+    }
+  }
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int nitems;     // B, or number of packed sequences
+  int max_tq;     // longest query length of any item (grid size)
+  Items items;
+  int Hq, Hkv, d;
+  float scale;
+  int causal;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int B, Tkv, Hq, Hkv, d;
+  float scale;
+  float* ws;      // partial results
+  int nsplit;
+};
+
+// Launchers (return hipSuccess or the launch error). Shapes have been validated by the caller.
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_fold(const void* src, void* dst, int64_t BT, int H, int g, int d, int is_bf16,
+                       hipStream_t s);
+
+// Decode split planning (host): shared by the workspace query and the launcher.
+int decode_num_splits(int B, int Tkv, int Hq, int Hkv, int d);
+size_t decode_workspace_bytes(int B, int Tkv, int Hq, int Hkv, int d);
+
+}  // namespace gqa

@@ -1,0 +1,204 @@
+// gqa_attn_api.cpp -- the extern "C" boundary: argument validation and kernel dispatch.
+//
+// Every check runs before anything is enqueued, so an error status means nothing was written.
+// The error convention follows the GQA lab page ("Transformer -- attention by hand: reducing only
+// the key/value heads", steps 1-3 and 6-7): head counts that do not split evenly are an error
+// (GQA_ERR_GROUPING), never silently truncated.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/gqa_attn.h"
+#include "common.hpp"
+
+namespace {
+
+constexpr int kMaxGridYZ = 65535;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap (byte ranges)
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+size_t esize(gqa_dtype_t t) { return t == GQA_DTYPE_BF16 ? 2 : 4; }
+
+bool dtype_ok(gqa_dtype_t t) { return t == GQA_DTYPE_F32 || t == GQA_DTYPE_BF16; }
+
+bool attn_d_supported(gqa_dtype_t t, int d) {
+  if (t == GQA_DTYPE_BF16) return d == 64 || d == 128;
+  if (t == GQA_DTYPE_F32) return d == 16 || d == 32 || d == 64 || d == 128;
+  return false;
+}
+
+// Rows-per-workgroup geometry must match the launchers (bf16: 128 columns, f32: 256 rows).
+int64_t prefill_tiles(gqa_dtype_t t, int G, int max_tq) {
+  const int cols = t == GQA_DTYPE_BF16 ? 128 : 256;
+  const int hpw = G < cols ? G : cols;
+  const int ppw = cols / hpw;
+  return (static_cast<int64_t>(max_tq) + ppw - 1) / ppw;
+}
+int64_t head_tiles(gqa_dtype_t t, int G) {
+  const int cols = t == GQA_DTYPE_BF16 ? 128 : 256;
+  const int hpw = G < cols ? G : cols;
+  return (G + hpw - 1) / hpw;
+}
+
+gqa_status_t from_hip(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int gqa_attn_abi_version(void) { return GQA_ATTN_ABI_VERSION; }
+
+const char* gqa_status_string(gqa_status_t s) {
+  switch (s) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_NULL_PTR: return "a required pointer is NULL";
+    case GQA_ERR_SHAPE: return "invalid or inconsistent sizes (or causal with Tq > Tkv)";
+    case GQA_ERR_GROUPING: return "head count does not split evenly into groups";
+    case GQA_ERR_UNSUPPORTED: return "unsupported dtype / head dim, or pointer not 16-byte aligned";
+    case GQA_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case GQA_ERR_ALIAS: return "output overlaps an input";
+    case GQA_ERR_HIP: return "HIP runtime error while enqueueing";
+  }
+  return "unknown status";
+}
+
+gqa_status_t gqa_attn_prefill(const void* q, const void* k, const void* v, void* out, int B,
+                              int Tq, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
+                              const int32_t* cu_seqlens, int max_seqlen, gqa_dtype_t dtype,
+                              hipStream_t stream) {
+  if (!q || !k || !v || !out) return GQA_ERR_NULL_PTR;
+  if (B <= 0 || Tq <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_SHAPE;
+  if (!isfinite(scale)) return GQA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return GQA_ERR_GROUPING;
+  if (!dtype_ok(dtype) || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return GQA_ERR_UNSUPPORTED;
+  int nitems, max_tq;
+  if (cu_seqlens) {
+    if (Tq != Tkv || max_seqlen <= 0 || max_seqlen > Tq) return GQA_ERR_SHAPE;
+    nitems = B;
+    max_tq = max_seqlen;
+  } else {
+    if (causal && Tq > Tkv) return GQA_ERR_SHAPE;
+    nitems = B;
+    max_tq = Tq;
+  }
+  const int G = Hq / Hkv;
+  if (nitems > kMaxGridYZ || prefill_tiles(dtype, G, max_tq) > kMaxGridYZ ||
+      static_cast<int64_t>(Hkv) * head_tiles(dtype, G) > INT32_MAX)
+    return GQA_ERR_UNSUPPORTED;
+  const size_t es = esize(dtype);
+  const size_t rows_q = cu_seqlens ? static_cast<size_t>(Tq) : static_cast<size_t>(B) * Tq;
+  const size_t rows_k = cu_seqlens ? static_cast<size_t>(Tkv) : static_cast<size_t>(B) * Tkv;
+  const size_t nq = rows_q * Hq * d * es, nk = rows_k * Hkv * d * es;
+  if (overlap(out, nq, q, nq) || overlap(out, nq, k, nk) || overlap(out, nq, v, nk))
+    return GQA_ERR_ALIAS;
+
+  gqa::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.nitems = nitems;
+  a.max_tq = max_tq;
+  a.items.cu = cu_seqlens;
+  a.items.Tq = Tq;
+  a.items.Tkv = Tkv;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal ? 1 : 0;
+  return from_hip(dtype == GQA_DTYPE_BF16 ? gqa::launch_prefill_bf16(a, stream)
+                                          : gqa::launch_prefill_f32(a, stream));
+}
+
+size_t gqa_attn_decode_workspace_bytes(int B, int Tkv, int Hq, int Hkv, int d) {
+  if (B <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0) return 0;
+  return gqa::decode_workspace_bytes(B, Tkv, Hq, Hkv, d);
+}
+
+gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+                             int B, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
+                             void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
+                             hipStream_t stream) {
+  (void)causal;  // a single query at the last position sees the whole cache
+  if (!q || !k_cache || !v_cache || !out) return GQA_ERR_NULL_PTR;
+  if (B <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_SHAPE;
+  if (!isfinite(scale)) return GQA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return GQA_ERR_GROUPING;
+  if (!dtype_ok(dtype) || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return GQA_ERR_UNSUPPORTED;
+  if (B > kMaxGridYZ) return GQA_ERR_UNSUPPORTED;
+  const size_t es = esize(dtype);
+  const size_t nq = static_cast<size_t>(B) * Hq * d * es;
+  const size_t nk = static_cast<size_t>(B) * Tkv * Hkv * d * es;
+  if (overlap(out, nq, q, nq) || overlap(out, nq, k_cache, nk) || overlap(out, nq, v_cache, nk))
+    return GQA_ERR_ALIAS;
+
+  if (dtype == GQA_DTYPE_F32) {
+    // fp32: the vector-ALU prefill kernel with one query row per sequence; no workspace.
+    if (workspace && overlap(workspace, workspace_bytes, out, nq)) return GQA_ERR_ALIAS;
+    gqa::PrefillArgs a;
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.out = out;
+    a.nitems = B;
+    a.max_tq = 1;
+    a.items.cu = nullptr;
+    a.items.Tq = 1;
+    a.items.Tkv = Tkv;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.d = d;
+    a.scale = scale;
+    a.causal = 0;
+    return from_hip(gqa::launch_prefill_f32(a, stream));
+  }
+  const size_t need = gqa::decode_workspace_bytes(B, Tkv, Hq, Hkv, d);
+  if (!workspace || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GQA_ERR_UNSUPPORTED;
+  if (overlap(workspace, need, q, nq) || overlap(workspace, need, k_cache, nk) ||
+      overlap(workspace, need, v_cache, nk) || overlap(workspace, need, out, nq))
+    return GQA_ERR_ALIAS;
+  gqa::DecodeArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.out = out;
+  a.B = B;
+  a.Tkv = Tkv;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.scale = scale;
+  a.ws = static_cast<float*>(workspace);
+  a.nsplit = gqa::decode_num_splits(B, Tkv, Hq, Hkv, d);
+  if (Hq > kMaxGridYZ) return GQA_ERR_UNSUPPORTED;
+  return from_hip(gqa::launch_decode_bf16(a, stream));
+}
+
+gqa_status_t gqa_fold_kv(const void* src, void* dst, int B, int T, int H, int g, int d,
+                         gqa_dtype_t dtype, hipStream_t stream) {
+  if (!src || !dst) return GQA_ERR_NULL_PTR;
+  if (B <= 0 || T <= 0 || H <= 0 || g <= 0 || d <= 0) return GQA_ERR_SHAPE;
+  if (H % g != 0) return GQA_ERR_GROUPING;
+  if (!dtype_ok(dtype)) return GQA_ERR_UNSUPPORTED;
+  const size_t es = esize(dtype);
+  if ((static_cast<size_t>(d) * es) % 16 != 0) return GQA_ERR_UNSUPPORTED;
+  if (!aligned16(src) || !aligned16(dst)) return GQA_ERR_UNSUPPORTED;
+  const size_t ns = static_cast<size_t>(B) * T * H * d * es;
+  const size_t nd = static_cast<size_t>(B) * T * g * d * es;
+  if (overlap(src, ns, dst, nd)) return GQA_ERR_ALIAS;
+  return from_hip(gqa::launch_fold(src, dst, static_cast<int64_t>(B) * T, H, g, d,
+                                   dtype == GQA_DTYPE_BF16 ? 1 : 0, stream));
+}
+
+}  // extern "C"

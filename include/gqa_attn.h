@@ -1,0 +1,111 @@
+/*
+ * gqa_attn.h -- C ABI of the MI355X (gfx950) grouped-query attention forward library.
+ *
+ * One operation family: scaled-dot-product attention in which Hq query heads share Hkv key/value
+ * heads (multi-head when Hkv == Hq, multi-query when Hkv == 1, grouped-query in between).
+ *
+ * What is computed (sources are the pages this library follows):
+ *   - Query head i reads key/value head i / (Hq / Hkv): queries are grouped in contiguous blocks,
+ *     never round-robin (GQA lab page "Transformer -- attention by hand: reducing only the
+ *     key/value heads", steps 1 and 3; course page "Week 7. Attention", typical errors).
+ *   - For every query row: dot with every visible key row of its group's head, multiplied by
+ *     `scale` (normally 1/sqrt(d): lab step 4, course step 1), minus the row maximum, exponentiated,
+ *     normalised, and used to average the value rows (lab step 4).
+ *   - causal != 0: keys after the query's position are removed before the softmax (course step 1).
+ *     With Tq < Tkv the queries are the last Tq positions (query t sits at t + Tkv - Tq); a
+ *     one-token decode therefore sees the whole cache.
+ *   - gqa_fold_kv: position-wise mean of the key/value heads inside each contiguous group (lab
+ *     step 2), the head reduction GQA applies to a multi-head checkpoint.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are dense, row-major device buffers in the [batch, position, head, head_dim] layout
+ *     with head_dim contiguous; all pointers must be 16-byte aligned.
+ *   - The caller owns every buffer. The library allocates no device memory, keeps no pointer
+ *     after returning, and never synchronises: all work is enqueued on `stream` (a HIP stream,
+ *     NULL for the default stream) and completes asynchronously.
+ *   - Arguments are validated before anything is enqueued; on an error status nothing has been
+ *     written. Outputs must not overlap inputs. No C++ exception crosses this interface.
+ *   - Thread-safe: the library holds no mutable global state.
+ *   - Internal arithmetic is fp32 (bf16 inputs are widened exactly; products accumulate in fp32);
+ *     outputs are rounded to nearest-even in the input dtype.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GQA_OK = 0,
+  GQA_ERR_NULL_PTR = 1,    /* a required pointer is NULL */
+  GQA_ERR_SHAPE = 2,       /* a size is non-positive or inconsistent, or causal with Tq > Tkv */
+  GQA_ERR_GROUPING = 3,    /* Hq is not divisible by Hkv (or H by g): heads do not split evenly */
+  GQA_ERR_UNSUPPORTED = 4, /* (dtype, d) combination not built, or a pointer not 16-byte aligned */
+  GQA_ERR_WORKSPACE = 5,   /* decode workspace missing or smaller than required */
+  GQA_ERR_ALIAS = 6,       /* an output buffer overlaps an input buffer */
+  GQA_ERR_HIP = 7          /* the HIP runtime reported an error when enqueueing */
+} gqa_status_t;
+
+typedef enum { GQA_DTYPE_F32 = 0, GQA_DTYPE_BF16 = 1 } gqa_dtype_t;
+
+/* Supported head dimensions: bf16 d in {64, 128}; f32 d in {16, 32, 64, 128}. */
+
+/*
+ * Prefill (any number of query positions).
+ *   q   [B, Tq, Hq, d]     k, v [B, Tkv, Hkv, d]     out [B, Tq, Hq, d]     (all `dtype`)
+ * Packed variable-length batch: pass cu_seqlens != NULL, a DEVICE int32 array of B+1 cumulative
+ * sequence offsets (cu_seqlens[0] == 0, non-decreasing, cu_seqlens[B] == Tq). Then the tensors
+ * are q [1, Tq, Hq, d], k, v [1, Tkv, Hkv, d] with Tq == Tkv == total tokens; each sequence
+ * attends only to itself (causal within the sequence when causal != 0), and max_seqlen (host)
+ * must be >= the longest sequence: it sizes the launch grid. With cu_seqlens == NULL, max_seqlen
+ * is ignored.
+ */
+gqa_status_t gqa_attn_prefill(const void* q, const void* k, const void* v, void* out, int B,
+                              int Tq, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
+                              const int32_t* cu_seqlens, int max_seqlen, gqa_dtype_t dtype,
+                              hipStream_t stream);
+
+/*
+ * Decode: one query token per sequence against a key/value cache, split along the cache length.
+ *   q [B, 1, Hq, d]     k_cache, v_cache [B, Tkv, Hkv, d]     out [B, 1, Hq, d]
+ * Each split writes an fp32 partial result (running max, sum and unnormalised output) to
+ * `workspace`, and a second kernel merges the splits. `workspace` is caller-owned device memory
+ * of at least gqa_attn_decode_workspace_bytes(...) bytes (16-byte aligned); its contents on
+ * entry do not matter and are overwritten. Concurrent calls must use distinct workspaces.
+ * `causal` is accepted for symmetry with prefill: a single query at the last position sees the
+ * whole cache, so it changes nothing. bf16 uses the split-KV kernels; f32 runs the prefill
+ * kernel with Tq = 1 and needs no workspace (workspace may then be NULL).
+ */
+size_t gqa_attn_decode_workspace_bytes(int B, int Tkv, int Hq, int Hkv, int d);
+gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+                             int B, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
+                             void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
+                             hipStream_t stream);
+
+/*
+ * Fold key/value heads: src [B, T, H, d] -> dst [B, T, g, d] with
+ *   dst[b,t,j,:] = (sum of src[b,t,j*s + i,:] for i < s) / s,   s = H / g,
+ * summed in fp32 in head order, divided in fp32, rounded to `dtype`. g == H copies the input.
+ * H not divisible by g is GQA_ERR_GROUPING.
+ */
+gqa_status_t gqa_fold_kv(const void* src, void* dst, int B, int T, int H, int g, int d,
+                         gqa_dtype_t dtype, hipStream_t stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* gqa_status_string(gqa_status_t s);
+
+/* Interface version of this header: bumped on any incompatible change. */
+#define GQA_ATTN_ABI_VERSION 1
+int gqa_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

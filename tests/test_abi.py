@@ -1,0 +1,114 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header declares, and its
+argument validation returns the documented status codes before any HIP call is made (every
+call here fails validation, so nothing is enqueued and no GPU is needed)."""
+import ctypes
+import os
+
+import pytest
+
+import grouped_query_softmax_amd as gqa
+from grouped_query_softmax_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gqa.raw_library()
+
+
+def test_library_exports_every_header_function(lib):
+    names = gqa.header_functions()
+    assert set(names) >= {"gqa_attn_prefill", "gqa_attn_decode", "gqa_attn_decode_workspace_bytes",
+                          "gqa_fold_kv", "gqa_status_string", "gqa_attn_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.gqa_attn_abi_version() == 1
+
+
+def test_single_hip_runtime_in_process():
+    assert len(B._hip_runtimes_mapped()) <= 1
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = gqa.gqa_status_string(code)
+        assert s and s != "unknown status"
+    assert gqa.gqa_status_string(99) == "unknown status"
+
+
+# fake, 16-byte aligned, non-overlapping addresses; validation never dereferences them
+Q, K, V, O, W = (0x10000000 * i for i in (1, 2, 3, 4, 5))
+F32, BF16 = B.GQA_DTYPE_F32, B.GQA_DTYPE_BF16
+
+
+def pre(lib, q=Q, k=K, v=V, o=O, Bn=1, Tq=8, Tkv=8, Hq=8, Hkv=2, d=128, scale=0.1, causal=0,
+        cu=None, msl=0, dt=BF16):
+    return lib.gqa_attn_prefill(q, k, v, o, Bn, Tq, Tkv, Hq, Hkv, d, scale, causal, cu, msl, dt,
+                                None)
+
+
+def test_prefill_validation(lib):
+    assert pre(lib, q=None) == B.GQA_ERR_NULL_PTR
+    assert pre(lib, o=None) == B.GQA_ERR_NULL_PTR
+    assert pre(lib, Tq=0) == B.GQA_ERR_SHAPE
+    assert pre(lib, Hkv=-1) == B.GQA_ERR_SHAPE
+    assert pre(lib, Hq=8, Hkv=3) == B.GQA_ERR_GROUPING
+    assert pre(lib, d=96) == B.GQA_ERR_UNSUPPORTED
+    assert pre(lib, d=16) == B.GQA_ERR_UNSUPPORTED          # bf16 needs 64 or 128
+    assert pre(lib, dt=7) == B.GQA_ERR_UNSUPPORTED
+    assert pre(lib, q=Q + 8) == B.GQA_ERR_UNSUPPORTED       # misaligned
+    assert pre(lib, Tq=9, Tkv=8, causal=1) == B.GQA_ERR_SHAPE
+    assert pre(lib, scale=float("nan")) == B.GQA_ERR_SHAPE
+    assert pre(lib, o=Q + 64) == B.GQA_ERR_ALIAS             # out overlaps q
+    assert pre(lib, o=K) == B.GQA_ERR_ALIAS
+    # packed batch: Tq must equal Tkv, max_seqlen in (0, Tq]
+    assert pre(lib, cu=W, msl=0) == B.GQA_ERR_SHAPE
+    assert pre(lib, cu=W, Tq=8, Tkv=9, msl=4) == B.GQA_ERR_SHAPE
+    assert pre(lib, cu=W, msl=9) == B.GQA_ERR_SHAPE
+    # grid limits
+    assert pre(lib, Bn=70000) == B.GQA_ERR_UNSUPPORTED
+
+
+def test_decode_validation(lib):
+    need = lib.gqa_attn_decode_workspace_bytes(4, 1024, 32, 8, 128)
+    assert need > 0 and need % 16 == 0
+    assert lib.gqa_attn_decode_workspace_bytes(4, 1024, 32, 5, 128) == 0
+
+    def dec(q=Q, k=K, v=V, o=O, Bn=4, Tkv=1024, Hq=32, Hkv=8, d=128, ws=W, wsb=need, dt=BF16):
+        return lib.gqa_attn_decode(q, k, v, o, Bn, Tkv, Hq, Hkv, d, 0.1, 0, ws, wsb, dt, None)
+
+    assert dec(k=None) == B.GQA_ERR_NULL_PTR
+    assert dec(Tkv=0) == B.GQA_ERR_SHAPE
+    assert dec(Hkv=5) == B.GQA_ERR_GROUPING
+    assert dec(d=80) == B.GQA_ERR_UNSUPPORTED
+    assert dec(ws=None) == B.GQA_ERR_WORKSPACE
+    assert dec(wsb=need - 1) == B.GQA_ERR_WORKSPACE
+    assert dec(ws=W + 4) == B.GQA_ERR_UNSUPPORTED
+    assert dec(o=Q) == B.GQA_ERR_ALIAS
+    assert dec(ws=O) == B.GQA_ERR_ALIAS
+
+
+def test_fold_validation(lib):
+    def fold(s=Q, dst=O, Bn=1, T=4, H=8, g=2, d=16, dt=F32):
+        return lib.gqa_fold_kv(s, dst, Bn, T, H, g, d, dt, None)
+
+    assert fold(s=None) == B.GQA_ERR_NULL_PTR
+    assert fold(g=0) == B.GQA_ERR_SHAPE
+    assert fold(g=3) == B.GQA_ERR_GROUPING
+    assert fold(d=6) == B.GQA_ERR_UNSUPPORTED       # rows must be whole 16-byte vectors
+    assert fold(dst=Q + 16) == B.GQA_ERR_ALIAS
+
+
+def test_python_wrapper_raises_value_error_for_uneven_heads():
+    import torch
+    with pytest.raises(gqa.GQAValueError) as e:
+        gqa.gqa_fold_kv(torch.empty(1, 2, 8, 16), 3)
+    assert e.value.code == B.GQA_ERR_GROUPING
+
+
+def test_header_cites_and_documents_each_entry_point():
+    text = open(os.path.join(ROOT, "include", "gqa_attn.h")).read()
+    for n in ("gqa_attn_prefill", "gqa_attn_decode", "gqa_fold_kv"):
+        assert n in text
+    assert "GQA lab page" in text and "Week 7. Attention" in text

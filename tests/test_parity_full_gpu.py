@@ -1,0 +1,71 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times:
+the whole output is computed on the GPU, and a seeded sample of output rows (always including
+the first and last position of every batch item / packed sequence, for the first and last head,
+plus -- for the MQA workload -- a sample of the x30 rows) is recomputed one by one by the fp64
+oracle. Rows are independent, so each sampled row is an exact check of that row."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import assert_bf16_close, host_view, say, to_dev, to_f64
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module")
+def gqa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import grouped_query_softmax_amd as g
+    return g
+
+
+def _check_rows(w, q, k, v, cu, out, rows):
+    orc = oracle.default()
+    ref = orc.attention_rows(host_view(q), host_view(k), host_view(v), rows, causal=w.causal,
+                             cu_seqlens=cu)
+    o = out.cpu()
+    got = np.stack([to_f64(o[b, t, h]) for b, t, h in rows])
+    return assert_bf16_close(got, ref, what=w.name)
+
+
+@pytest.mark.parametrize("w", [workloads.LLAMA_PREFILL, workloads.MQA_PREFILL,
+                               workloads.VARLEN_PREFILL], ids=lambda w: w.name)
+def test_full_prefill_sampled_rows(gqa, w):
+    say(f"full-size prefill {w.name}: generating inputs")
+    q, k, v, cu = workloads.make_inputs(w)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    cud = to_dev(cu) if cu is not None else None
+    say(f"full-size prefill {w.name}: launching")
+    out = gqa.gqa_attn_prefill(qd, kd, vd, causal=w.causal, cu_seqlens=cud,
+                               max_seqlen=max(w.seqlens) if w.seqlens else None)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    rows = workloads.sample_rows(w, 160, seed=7)
+    if w.peaked_frac > 0:
+        pk = workloads.peaked_rows(w)
+        sel = np.random.default_rng(8).choice(pk, size=96, replace=False)
+        extra = np.stack([sel // (w.Tq * w.Hq), (sel // w.Hq) % w.Tq, sel % w.Hq], axis=1)
+        rows = np.unique(np.concatenate([rows, extra]), axis=0)
+    say(f"full-size prefill {w.name}: oracle on {len(rows)} rows")
+    err, rel = _check_rows(w, q, k, v, cu, out, rows)
+    say(f"full-size prefill {w.name}: max-abs {err:.3e} rel {rel:.3e}")
+
+
+def test_full_decode_sampled_rows(gqa):
+    w = workloads.DECODE
+    say("full-size decode: generating inputs")
+    q, k, v, _ = workloads.make_inputs(w)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    ws = torch.empty(gqa.gqa_attn_decode_workspace_bytes(w.B, w.Tkv, w.Hq, w.Hkv, w.d),
+                     dtype=torch.uint8, device="cuda")
+    say("full-size decode: launching")
+    out = gqa.gqa_attn_decode(qd, kd, vd, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    rows = workloads.sample_rows(w, 200, seed=9)
+    say(f"full-size decode: oracle on {len(rows)} rows")
+    err, rel = _check_rows(w, q, k, v, None, out, rows)
+    say(f"full-size decode: max-abs {err:.3e} rel {rel:.3e}")
