@@ -108,17 +108,17 @@ int oracle_expand(const double* src, double* dst, int64_t B, int64_t T, int g, i
 }
 
 /* One output row of single-head attention.
- * q: d values; k, v: nvis rows of d values (contiguous); out: d values.
+ * q: d values; key j's row starts at k + j*kstride (likewise v); out: d values.
  * Scores s_j = scale * sum_c q[c] k[j][c]; two-pass softmax; out = sum_j p_j v_j / sum_j p_j.
  * A row that sees no key (nvis == 0) is defined as zeros. */
-static void attend_row(const double* q, const double* k, const double* v, int64_t nvis, int d,
-                       double scale, double* s, double* out) {
+static void attend_row(const double* q, const double* k, const double* v, int64_t kstride,
+                       int64_t nvis, int d, double scale, double* s, double* out) {
   for (int c = 0; c < d; ++c) out[c] = 0.0;
   if (nvis <= 0) return;
   double m = -INFINITY;
   for (int64_t j = 0; j < nvis; ++j) {
     double dot = 0.0;
-    for (int c = 0; c < d; ++c) dot += q[c] * k[j * d + c];
+    for (int c = 0; c < d; ++c) dot += q[c] * k[j * kstride + c];
     s[j] = scale * dot;
     if (s[j] > m) m = s[j];
   }
@@ -129,7 +129,7 @@ static void attend_row(const double* q, const double* k, const double* v, int64_
     l += p;
   }
   for (int64_t j = 0; j < nvis; ++j)
-    for (int c = 0; c < d; ++c) out[c] += s[j] * v[j * d + c];
+    for (int c = 0; c < d; ++c) out[c] += s[j] * v[j * kstride + c];
   for (int c = 0; c < d; ++c) out[c] /= l;
 }
 
@@ -217,39 +217,41 @@ int oracle_gqa_attention(const void* q, const void* k, const void* v, int dtype_
   int64_t max_tkv = 0;
   for (int it = 0; it < nitems; ++it)
     if (items[it].Tkv > max_tkv) max_tkv = items[it].Tkv;
+  /* item of every query row, so the work can be spread over (row, head) pairs */
+  int* row_item = (int*)malloc(sizeof(int) * (size_t)(qrows > 0 ? qrows : 1));
+  if (!row_item) {
+    free(ke); free(ve); free(items);
+    return ORACLE_ERR_ALLOC;
+  }
+  for (int it = 0; it < nitems; ++it)
+    for (int64_t t = 0; t < items[it].Tq; ++t) row_item[items[it].q_row0 + t] = it;
 
   int err = ORACLE_OK;
 #pragma omp parallel
   {
     double* qh = (double*)malloc(sizeof(double) * (size_t)d);
-    double* kh = (double*)malloc(sizeof(double) * (size_t)(max_tkv * d + 1));
-    double* vh = (double*)malloc(sizeof(double) * (size_t)(max_tkv * d + 1));
     double* sc = (double*)malloc(sizeof(double) * (size_t)(max_tkv + 1));
-    double* orow = (double*)malloc(sizeof(double) * (size_t)d);
-    if (!qh || !kh || !vh || !sc || !orow) {
+    if (!qh || !sc) {
 #pragma omp atomic write
       err = ORACLE_ERR_ALLOC;
     } else {
-#pragma omp for schedule(dynamic, 1) collapse(2)
-      for (int it = 0; it < nitems; ++it)
-        for (int h = 0; h < Hq; ++h) {
-          const item_t I = items[it];
-          /* the expanded head h of this item as contiguous [Tkv][d] tables */
-          for (int64_t j = 0; j < I.Tkv; ++j) {
-            memcpy(&kh[j * d], &ke[((I.k_row0 + j) * Hq + h) * (int64_t)d], sizeof(double) * d);
-            memcpy(&vh[j * d], &ve[((I.k_row0 + j) * Hq + h) * (int64_t)d], sizeof(double) * d);
-          }
-          for (int64_t t = 0; t < I.Tq; ++t) {
-            const int64_t row = I.q_row0 + t;
-            for (int c = 0; c < d; ++c) qh[c] = widen(q, dtype_in, (row * Hq + h) * (int64_t)d + c);
-            attend_row(qh, kh, vh, visible_keys(t, I.Tq, I.Tkv, causal), d, scale, sc, orow);
-            memcpy(&out[(row * Hq + h) * (int64_t)d], orow, sizeof(double) * d);
-          }
-        }
+#pragma omp for schedule(dynamic, 8)
+      for (int64_t r = 0; r < qrows * Hq; ++r) {
+        const int64_t row = r / Hq;
+        const int h = (int)(r % Hq);
+        const item_t I = items[row_item[row]];
+        const int64_t t = row - I.q_row0;
+        for (int c = 0; c < d; ++c) qh[c] = widen(q, dtype_in, (row * Hq + h) * (int64_t)d + c);
+        /* head h of the expanded K/V: rows k_row0.. of the [krows][Hq][d] tables */
+        const double* kh = &ke[(I.k_row0 * Hq + h) * (int64_t)d];
+        const double* vh = &ve[(I.k_row0 * Hq + h) * (int64_t)d];
+        attend_row(qh, kh, vh, (int64_t)Hq * d, visible_keys(t, I.Tq, I.Tkv, causal), d, scale,
+                   sc, &out[(row * Hq + h) * (int64_t)d]);
+      }
     }
-    free(qh); free(kh); free(vh); free(sc); free(orow);
+    free(qh); free(sc);
   }
-  (void)qrows;
+  free(row_item);
   free(ke);
   free(ve);
   free(items);
@@ -320,7 +322,8 @@ int oracle_gqa_attention_rows(const void* q, const void* k, const void* v, int d
           }
         const int64_t row = I.q_row0 + t;
         for (int c = 0; c < d; ++c) qh[c] = widen(q, dtype_in, (row * Hq + h) * (int64_t)d + c);
-        attend_row(qh, kh, vh, visible_keys(t, I.Tq, I.Tkv, causal), d, scale, sc, &out[r * d]);
+        attend_row(qh, kh, vh, d, visible_keys(t, I.Tq, I.Tkv, causal), d, scale, sc,
+                   &out[r * d]);
       }
     }
     free(qh); free(kh); free(vh); free(sc);

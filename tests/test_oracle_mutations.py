@@ -30,8 +30,8 @@ MUTANTS = {
     # softmax not normalised
     "no_normalisation": ("for (int c = 0; c < d; ++c) out[c] /= l;", "(void)l;"),
     # value rows weighted by the wrong key
-    "value_index_shift": ("out[c] += s[j] * v[j * d + c];",
-                          "out[c] += s[j] * v[((j + 1) % nvis) * d + c];"),
+    "value_index_shift": ("out[c] += s[j] * v[j * kstride + c];",
+                          "out[c] += s[j] * v[((j + 1) % nvis) * kstride + c];"),
 }
 
 
