@@ -230,34 +230,35 @@ def main():
         extra["varlen_prefill"] = vl
         log(f"varlen: {vl['avg_ms']:.3f} ms, {vl['tflops']:.1f} TFLOP/s")
     if args.only == "decode" or (args.only is None and not args.no_decode):
-        dw = workloads.DECODE
-        dec = bench_decode(gqa, dw, args.steps, args.warmup, torch, 3000)
+        dec = bench_decode(gqa, workloads.DECODE, args.steps, args.warmup, torch, 3000)
         extra["decode"] = dec
         log(f"decode: {dec['avg_ms'] * 1e3:.1f} us, {dec['gbs']:.0f} GB/s")
-        if pre is None:
-            pre_line = {"metric": "GQA decode KV GB/s (% HBM peak)", "value": dec["gbs"],
-                        "unit": "GB/s"}
     sha = kernel_source_sha()
+    metric = "GQA prefill TFLOPS (% MFMA peak); decode KV GB/s (% HBM peak)"
+    if pre is None and args.only in ("mqa", "varlen"):
+        key = "mqa_prefill" if args.only == "mqa" else "varlen_prefill"
+        pre = extra.pop(key)
+        w = workloads.MQA_PREFILL if args.only == "mqa" else workloads.VARLEN_PREFILL
     if pre is not None:
         value, unit = pre["tflops"], "TFLOP/s"
         ms_per_step = pre["avg_ms"]
-        traffic = traffic_for(sha)
+        traffic = traffic_for(sha) if w is workloads.LLAMA_PREFILL else None
         roofline = {"bound": "mfma", "achieved": pre["tflops"], "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": pre["tflops"] / PEAK_BF16_TFLOPS,
-                    "traffic": traffic, "kernel": "prefill_bf16_kernel<128>",
+                    "traffic": traffic, "kernel": "prefill_bf16_kernel<128,8,1>",
                     "flops_per_launch": pre["flops_per_launch"],
                     "avg_launch_ms": pre["avg_ms"], "kernel_source_sha": sha}
-        metric = "GQA prefill TFLOPS (% MFMA peak); decode KV GB/s (% HBM peak)"
         config = {"workload": w.name, "B": w.B, "T": w.Tq, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
                   "causal": w.causal, "global_batch": w.B, "seq_len": w.Tq,
                   "parallelism": "single-gpu"}
+        if w.seqlens:
+            config["seqlens"] = list(w.seqlens)
     else:
-        dec = extra["decode"]
+        dec = extra.pop("decode")
         value, unit = dec["gbs"], "GB/s"
         ms_per_step = dec["avg_ms"]
         roofline = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": dec["frac_hbm"], "traffic": None}
-        metric = pre_line["metric"]
         dw = workloads.DECODE
         config = {"workload": dw.name, "B": dw.B, "Tkv": dw.Tkv, "Hq": dw.Hq, "Hkv": dw.Hkv,
                   "d": dw.d, "parallelism": "single-gpu"}
@@ -268,7 +269,7 @@ def main():
             "roofline": roofline}
     if extra:
         line["secondary"] = extra
-    if not args.no_cpu_baseline and pre is not None:
+    if not args.no_cpu_baseline and tensors is not None:
         log("cpu baseline: fp64 oracle on a sample")
         line["cpu_baseline"] = cpu_baseline(w, tensors, torch)
     else:

@@ -95,6 +95,7 @@ struct DecodeArgs {
 // Launchers (return hipSuccess or the launch error). Shapes have been validated by the caller.
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+int prefill_bf16_cols();  // (position, head) columns per bf16 prefill workgroup
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_fold(const void* src, void* dst, int64_t BT, int H, int g, int d, int is_bf16,
                        hipStream_t s);

@@ -32,15 +32,16 @@ bool attn_d_supported(gqa_dtype_t t, int d) {
   return false;
 }
 
-// Rows-per-workgroup geometry must match the launchers (bf16: 128 columns, f32: 256 rows).
+// Rows-per-workgroup geometry must match the launchers (f32: 256 rows).
+int cols_per_wg(gqa_dtype_t t) { return t == GQA_DTYPE_BF16 ? gqa::prefill_bf16_cols() : 256; }
 int64_t prefill_tiles(gqa_dtype_t t, int G, int max_tq) {
-  const int cols = t == GQA_DTYPE_BF16 ? 128 : 256;
+  const int cols = cols_per_wg(t);
   const int hpw = G < cols ? G : cols;
   const int ppw = cols / hpw;
   return (static_cast<int64_t>(max_tq) + ppw - 1) / ppw;
 }
 int64_t head_tiles(gqa_dtype_t t, int G) {
-  const int cols = t == GQA_DTYPE_BF16 ? 128 : 256;
+  const int cols = cols_per_wg(t);
   const int hpw = G < cols ? G : cols;
   return (G + hpw - 1) / hpw;
 }
@@ -73,7 +74,7 @@ gqa_status_t gqa_attn_prefill(const void* q, const void* k, const void* v, void*
                               hipStream_t stream) {
   if (!q || !k || !v || !out) return GQA_ERR_NULL_PTR;
   if (B <= 0 || Tq <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_SHAPE;
-  if (!isfinite(scale)) return GQA_ERR_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.f)) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0) return GQA_ERR_GROUPING;
   if (!dtype_ok(dtype) || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -130,7 +131,7 @@ gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_c
   (void)causal;  // a single query at the last position sees the whole cache
   if (!q || !k_cache || !v_cache || !out) return GQA_ERR_NULL_PTR;
   if (B <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_SHAPE;
-  if (!isfinite(scale)) return GQA_ERR_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.f)) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0) return GQA_ERR_GROUPING;
   if (!dtype_ok(dtype) || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))

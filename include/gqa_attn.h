@@ -26,6 +26,7 @@
  *   - Arguments are validated before anything is enqueued; on an error status nothing has been
  *     written. Outputs must not overlap inputs. No C++ exception crosses this interface.
  *   - Thread-safe: the library holds no mutable global state.
+ *   - `scale` must be finite and positive (normally 1/sqrt(d)); anything else is GQA_ERR_SHAPE.
  *   - Internal arithmetic is fp32 (bf16 inputs are widened exactly; products accumulate in fp32);
  *     outputs are rounded to nearest-even in the input dtype.
  */
