@@ -42,10 +42,17 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (needs ROCm)")
 
 
+# Per-file flags. The prefill kernel assumes finite (non-NaN) inputs: with NaN semantics
+# relaxed, maxima of matrix-core results compile to v_max3_f32 without a canonicalising
+# v_max_f32 per element. Infinities keep their meaning (masked scores are -inf).
+FILE_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str, extra: List[str]) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-    cmd = [_hipcc(), *HIPCC_FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    lang = ["-x", "hip"]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), *extra, *lang, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

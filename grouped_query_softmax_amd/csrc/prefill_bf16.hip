@@ -37,6 +37,16 @@
 namespace gqa {
 namespace {
 
+#ifndef GQA_PREFILL_ORDER
+#define GQA_PREFILL_ORDER 1
+#endif
+#ifndef GQA_PREFILL_NW
+#define GQA_PREFILL_NW 8  // waves per workgroup for d = 128
+#endif
+#ifndef GQA_PREFILL_QT
+#define GQA_PREFILL_QT 1  // 32-column query tiles per wave for d = 128
+#endif
+
 constexpr int kKT = 64;                // keys per tile
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
@@ -82,7 +92,8 @@ __device__ __forceinline__ void lds_write(char* base, int byte_off, T v) {
 
 template <int D, int NW, int QT>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a, int heads_per_wg,
-                                                                  int pos_per_wg, int head_tiles) {
+                                                                  int pos_per_wg, int head_tiles,
+                                                                  int gz) {
   using C = Cfg<D, NW, QT>;
   constexpr int NS = D / 16;   // MFMA k-steps over d for the scores
   constexpr int NMT = D / 32;  // 32-row d tiles of O^T
@@ -90,15 +101,25 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a,
   constexpr int VW = VD / 2;   // dwords per key of one V item
   __shared__ __attribute__((aligned(16))) char smem[2 * C::kStageBytes];
 
-  const int kvh = blockIdx.x / head_tiles;
-  const int ht = blockIdx.x % head_tiles;
-  const int item = blockIdx.y;
+  // 1-D grid: (key/value head, head tile) fastest, then the order of GQA_PREFILL_ORDER
+  const int gx = a.Hkv * head_tiles;
+  const int lin = blockIdx.x;
+  const int xi = lin % gx;
+  const int rest = lin / gx;
+#if GQA_PREFILL_ORDER == 0
+  const int item = rest % a.nitems;  // items, then query tiles
+  const int z = rest / a.nitems;
+#else
+  const int z = rest % gz;           // query tiles, then items
+  const int item = rest / gz;
+#endif
+  const int kvh = xi / head_tiles;
+  const int ht = xi % head_tiles;
   int64_t q0, k0;
   int tq, tkv;
   a.items.get(item, q0, k0, tq, tkv);
   const int ntiles = (tq + pos_per_wg - 1) / pos_per_wg;
   // causal: this workgroup takes the query tiles (ntiles-1-z, z); otherwise tile z alone
-  const int z = blockIdx.z;
   int tiles[2];
   int ntile_here;
   if (a.causal) {
@@ -277,11 +298,20 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a,
       bf16x8 pb[QT][4];
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        float tmax = -INFINITY;
+        // row max of the 32 scores this lane holds: a tree of three-input maxima
+        float r3[11];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[qt][t][i]);
+        for (int g = 0; g < 10; ++g) {
+          const int i0 = 3 * g, i1 = 3 * g + 1, i2 = 3 * g + 2;
+          r3[g] = fmaxf(fmaxf(sacc[qt][i0 >> 4][i0 & 15], sacc[qt][i1 >> 4][i1 & 15]),
+                        sacc[qt][i2 >> 4][i2 & 15]);
+        }
+        r3[10] = fmaxf(sacc[qt][1][14], sacc[qt][1][15]);
+        const float r4a = fmaxf(fmaxf(r3[0], r3[1]), r3[2]);
+        const float r4b = fmaxf(fmaxf(r3[3], r3[4]), r3[5]);
+        const float r4c = fmaxf(fmaxf(r3[6], r3[7]), r3[8]);
+        const float r4d = fmaxf(r3[9], r3[10]);
+        float tmax = fmaxf(fmaxf(r4a, r4b), fmaxf(r4c, r4d));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl2;  // both halves of the column agree
         // move the reference max only when it grows by more than the slack (or is unset)
         const bool move = tmax > m_run[qt] + kRescaleSlack;
@@ -301,14 +331,21 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a,
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
-            u32x4 w;
+            uint32_t pw[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float p0v = fast_exp2(fmaf(sacc[qt][t][8 * h2 + 2 * e], sl2, -mref));
               const float p1v = fast_exp2(fmaf(sacc[qt][t][8 * h2 + 2 * e + 1], sl2, -mref));
-              psum += p0v + p1v;
-              w[e] = pack_bf16x2(p0v, p1v);
+              pw[e] = pack_bf16x2(p0v, p1v);
             }
+            // the row sum adds the rounded weights the MFMA consumes, so the weights used for
+            // the output are exactly normalised by it
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]),
+                                                     __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                                     psum, false);
+            const u32x4 w = {pw[0], pw[1], pw[2], pw[3]};
             pb[qt][2 * t + h2] = __builtin_bit_cast(bf16x8, w);
           }
         l_run[qt] += psum;
@@ -361,20 +398,13 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
   const int head_tiles = (G + heads_per_wg - 1) / heads_per_wg;
   const int ntiles = (a.max_tq + pos_per_wg - 1) / pos_per_wg;
   const int gz = a.causal ? (ntiles + 1) / 2 : ntiles;
-  dim3 grid(a.Hkv * head_tiles, a.nitems, gz);
+  const dim3 grid(a.Hkv * head_tiles * a.nitems * gz);
   hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, QT>), grid, dim3(NW * 64), 0, s, a, heads_per_wg,
-                     pos_per_wg, head_tiles);
+                     pos_per_wg, head_tiles, gz);
   return hipGetLastError();
 }
 
 }  // namespace
-
-#ifndef GQA_PREFILL_NW
-#define GQA_PREFILL_NW 8  // waves per workgroup for d = 128
-#endif
-#ifndef GQA_PREFILL_QT
-#define GQA_PREFILL_QT 1  // 32-column query tiles per wave for d = 128
-#endif
 
 // Columns per workgroup of the launched configurations (the host validates the grid with it).
 int prefill_bf16_cols() { return Cfg<128, GQA_PREFILL_NW, GQA_PREFILL_QT>::kCols; }
