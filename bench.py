@@ -142,6 +142,23 @@ def bench_decode(gqa, w, steps, warmup, torch, seed):
             "min_ms": min(ms), "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "wall_s": wall}
 
 
+COPY_BYTES = 1 << 30
+
+
+def bench_copy(steps, warmup, torch):
+    """A plain device-to-device copy of COPY_BYTES: it reads and writes exactly COPY_BYTES each,
+    so the HBM byte counters it reports calibrate those of the attention kernels."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms, wall = time_launches(lambda: dst.copy_(src), steps, warmup, torch)
+    avg = sum(ms) / len(ms)
+    gbs = 2 * COPY_BYTES / (avg * 1e-3) / 1e9
+    return {"metric": "device copy GB/s (read + write)", "value": gbs, "unit": "GB/s",
+            "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": avg,
+            "higher_is_better": True, "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+            "config": {"workload": "copy_1GiB"}}
+
+
 def cpu_baseline(w, tensors, torch, target_s=15.0):
     """fp64 oracle on a bounded sample of the prefill workload: the first `ng` key/value heads
     with their G query heads each (the same grouping; every query position, every key)."""
@@ -190,8 +207,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "mqa", "varlen"], default=None,
-                    help="time a single workload (for profiling); still prints one JSON line")
+    ap.add_argument("--only", choices=["prefill", "decode", "mqa", "varlen", "copy"],
+                    default=None,
+                    help="time a single workload (for profiling); still prints one JSON line. "
+                         "'copy' times a plain 1 GiB device copy, the calibration kernel for "
+                         "the HBM byte counters")
     ap.add_argument("--all", action="store_true", help="also time the MQA and varlen prefills")
     args = ap.parse_args()
 
@@ -209,6 +229,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+
+    if args.only == "copy":
+        print(json.dumps(bench_copy(args.steps, args.warmup, torch)), flush=True)
+        return
 
     w = workloads.LLAMA_PREFILL
     extra = {}
@@ -245,7 +269,7 @@ def main():
         traffic = traffic_for(sha) if w is workloads.LLAMA_PREFILL else None
         roofline = {"bound": "mfma", "achieved": pre["tflops"], "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": pre["tflops"] / PEAK_BF16_TFLOPS,
-                    "traffic": traffic, "kernel": "prefill_bf16_kernel<128,8,1>",
+                    "traffic": traffic, "kernel": "prefill_pp_kernel<128>",
                     "flops_per_launch": pre["flops_per_launch"],
                     "avg_launch_ms": pre["avg_ms"], "kernel_source_sha": sha}
         config = {"workload": w.name, "B": w.B, "T": w.Tq, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,

@@ -7,7 +7,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/gqa_attn.h"
+#include "gqa_attn.h"
 #include "common.hpp"
 
 namespace {

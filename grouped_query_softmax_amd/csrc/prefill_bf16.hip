@@ -6,19 +6,19 @@
 // row maximum subtracted before exponentiating (lab step 4), causal keys removed before the
 // softmax (course page "Week 7. Attention", step 1), and the normalised weighted sum of value rows.
 //
-// How. One workgroup = NW waves = one key/value head x one tile of NC = NW*32*QT (position, head)
-// columns; all G query heads of the group sit in the same workgroup, so each K/V tile is read
-// from HBM into LDS once and consumed by every query head of the group.
+// How. One workgroup = 8 waves = one key/value head x one tile of 256 (position, head) columns;
+// all G query heads of the group sit in the same workgroup, so each K/V tile is read from HBM
+// into LDS once and consumed by every query head of the group.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: keys are the MFMA
 //     rows and queries the columns, so each lane owns one query column and the softmax row
-//     statistics are lane-local (one exchange with the partner lane l^32 per tile).
+//     statistics are lane-local (one v_permlane32_swap with the partner lane l^32 per tile).
 //   * The output is accumulated transposed as well, O^T += V^T P^T. P^T is the score accumulator
 //     rounded to bf16 in place; the contraction order of keys is permuted to follow the
 //     accumulator layout, and V is stored in LDS transposed ([d][keys]) in that same permuted key
 //     order, so both MFMA operands are single 16-byte LDS reads.
-//   * K/V tiles of 64 keys are double-buffered in LDS: the global loads of tile t+1 are issued
-//     into registers before tile t is computed and written to the other buffer afterwards, so one
-//     barrier per tile suffices and HBM latency hides behind the matrix work.
+//   * K/V tiles of 64 keys rotate through three LDS stages. Two groups of 4 waves share the
+//     SIMDs and run half a step apart (ping-pong): while one group's waves issue the matrix-core
+//     work of a tile, the other group's waves do the softmax of theirs on the vector ALUs.
 //   * Online softmax in fp32 in the base-2 domain: x = s*scale*log2(e) - m in one FMA, p = 2^x.
 //     The reference maximum m is only moved when a tile raises the row maximum by more than
 //     kRescaleSlack (in log2 units); otherwise O and the running sum keep the old reference,
@@ -28,49 +28,30 @@
 //     the diagonal are masked per element with bottom-right alignment. For balance each
 //     workgroup takes the query tile pair (i, n-1-i), so every workgroup does the same number of
 //     key tiles.
-//   * Grid: key/value heads fastest, so consecutive workgroups -- spread round-robin over the 8
-//     XCDs by the dispatcher -- keep one key/value head per XCD L2 when Hkv * items is 8.
+//   * Launch order: key/value heads fastest, then query tiles, then batch items / packed
+//     sequences. Consecutive workgroups are spread round-robin over the 8 XCDs, so with 8 key/
+//     value heads each XCD L2 serves one head, and the workgroups running together on an XCD
+//     stream the same head of the same sequence.
+//   * The kernel assumes finite inputs: it is built without NaN semantics so row maxima of
+//     matrix-core results compile to v_max3_f32 (infinities keep their meaning: masked scores
+//     are -inf).
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.hpp"
 
 namespace gqa {
 namespace {
 
-#ifndef GQA_PREFILL_ORDER
-#define GQA_PREFILL_ORDER 1
-#endif
-#ifndef GQA_PREFILL_NW
-#define GQA_PREFILL_NW 8  // waves per workgroup for d = 128
-#endif
-#ifndef GQA_PREFILL_QT
-#define GQA_PREFILL_QT 1  // 32-column query tiles per wave for d = 128
-#endif
-
 constexpr int kKT = 64;                // keys per tile
 constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr int kLdsAhead = 4;           // MFMA operand reads kept in flight
+constexpr int kCols = 256;             // (position, head) columns per workgroup
 
 // Buffer resource word 3 for raw (unformatted) buffer loads on CDNA; loads at or beyond
 // num_records bytes return zeros, which pads the last key tile without branches.
 constexpr int kBufWord3 = 0x00020000;
-
-template <int D, int NW, int QT>
-struct Cfg {
-  static constexpr int kThreads = NW * 64;
-  static constexpr int kCols = NW * 32 * QT;
-  static constexpr int kChunks = D / 8;                     // 16-byte chunks per key row
-  static constexpr int kKLoads = kKT * kChunks / kThreads;  // 16-byte K loads per thread
-  static constexpr int kVD = (kKT / 4) * D / kThreads;      // d values per V staging item
-  // LDS pitches: one 16-byte pad per row makes 16 consecutive rows read at the same column
-  // land in 16 distinct bank groups, and keeps every read address lane base + immediate.
-  static constexpr int kKPitch = D * 2 + 16;        // bytes per key row of the K tile
-  static constexpr int kVPitch = kKT * 2 + 16;      // bytes per d row of the V^T tile
-  static constexpr int kKBytes = kKT * kKPitch;
-  static constexpr int kVBytes = D * kVPitch;
-  static constexpr int kStageBytes = kKBytes + kVBytes;
-  static_assert(kKLoads >= 1 && kKT * kChunks % kThreads == 0, "K staging split");
-  static_assert(kVD == 8 || kVD == 4 || kVD == 2, "V staging split");
-};
 
 // V^T rows hold the 64 keys of a tile permuted inside each group of 16: key 8a + 4h + r
 // (a, h in {0,1}, r < 4) sits at position 8h + 4a + r. The 8 keys one lane feeds into one MFMA
@@ -90,36 +71,44 @@ __device__ __forceinline__ void lds_write(char* base, int byte_off, T v) {
   *reinterpret_cast<T*>(base + byte_off) = v;
 }
 
-template <int D, int NW, int QT>
-__global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a, int heads_per_wg,
-                                                                  int pos_per_wg, int head_tiles,
-                                                                  int gz) {
-  using C = Cfg<D, NW, QT>;
+template <int D>
+struct PPCfg {
+  static constexpr int kGroupThreads = 256;
+  static constexpr int kChunks = D / 8;
+  static constexpr int kKLoads = kKT * kChunks / kGroupThreads;  // 16-byte K loads per thread
+  static constexpr int kVD = (kKT / 4) * D / kGroupThreads;      // d values per V item
+  static constexpr int kKPitch = D * 2 + 16;
+  static constexpr int kVPitch = kKT * 2 + 16;
+  static constexpr int kKBytes = kKT * kKPitch;
+  static constexpr int kVBytes = D * kVPitch;
+  static constexpr int kVBase = 3 * kKBytes;  // LDS: [K stage 0..2][V^T stage 0..2]
+  static constexpr int kSmemBytes = 3 * (kKBytes + kVBytes);
+  static_assert(kVD == 8 || kVD == 4, "V staging split");
+  static_assert(kVBase < 65536 && 3 * kVBytes < 65536, "stage offsets fit LDS immediates");
+};
+
+template <int D>
+__global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int heads_per_wg,
+                                                         int pos_per_wg, int head_tiles, int gz) {
+  using C = PPCfg<D>;
   constexpr int NS = D / 16;   // MFMA k-steps over d for the scores
   constexpr int NMT = D / 32;  // 32-row d tiles of O^T
-  constexpr int VD = C::kVD;   // V staging: 4 keys x VD dims per thread
-  constexpr int VW = VD / 2;   // dwords per key of one V item
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kStageBytes];
+  constexpr int VD = C::kVD;
+  constexpr int VW = VD / 2;
+  __shared__ __attribute__((aligned(16))) char smem[C::kSmemBytes];
 
-  // 1-D grid: (key/value head, head tile) fastest, then the order of GQA_PREFILL_ORDER
   const int gx = a.Hkv * head_tiles;
   const int lin = blockIdx.x;
   const int xi = lin % gx;
   const int rest = lin / gx;
-#if GQA_PREFILL_ORDER == 0
-  const int item = rest % a.nitems;  // items, then query tiles
-  const int z = rest / a.nitems;
-#else
-  const int z = rest % gz;           // query tiles, then items
+  const int z = rest % gz;  // query tiles, then items
   const int item = rest / gz;
-#endif
   const int kvh = xi / head_tiles;
   const int ht = xi % head_tiles;
   int64_t q0, k0;
   int tq, tkv;
   a.items.get(item, q0, k0, tq, tkv);
   const int ntiles = (tq + pos_per_wg - 1) / pos_per_wg;
-  // causal: this workgroup takes the query tiles (ntiles-1-z, z); otherwise tile z alone
   int tiles[2];
   int ntile_here;
   if (a.causal) {
@@ -137,261 +126,313 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_bf16_kernel(PrefillArgs a,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n = lane & 31;   // query column inside a 32-column MFMA tile
-  const int hh = lane >> 5;  // which half of the k-slots / accumulator rows this lane holds
-  const int off = tkv - tq;  // bottom-right causal alignment
+  const bool grp_a = wave < 4;
+  const int gtid = tid & 255;  // thread index inside the group
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int off = tkv - tq;
   const float sl2 = a.scale * kLog2e;
 
   const uint16_t* __restrict__ Qp = static_cast<const uint16_t*>(a.q);
   uint16_t* __restrict__ Op = static_cast<uint16_t*>(a.out);
-  const int row_bytes = a.Hkv * D * 2;  // bytes between consecutive keys of one head
+  const int row_bytes = a.Hkv * D * 2;
   const uint16_t* kbase_ptr = static_cast<const uint16_t*>(a.k) + (k0 * a.Hkv + kvh) * D;
   const uint16_t* vbase_ptr = static_cast<const uint16_t*>(a.v) + (k0 * a.Hkv + kvh) * D;
 
-  // per-thread staging geometry (loop invariant)
+  // staging geometry of this thread inside its group (loop invariant)
   int k_src[C::kKLoads], k_dst[C::kKLoads];
 #pragma unroll
   for (int i = 0; i < C::kKLoads; ++i) {
-    const int idx = i * C::kThreads + tid;
+    const int idx = i * C::kGroupThreads + gtid;
     const int j = idx / C::kChunks, c = idx % C::kChunks;
     k_src[i] = j * row_bytes + 16 * c;
     k_dst[i] = j * C::kKPitch + 16 * c;
   }
-  constexpr int NPR = D / VD;  // V items per key row
-  const int v_c = tid % NPR, v_kg = tid / NPR;
+  // V items: 4 keys x VD dims; the key group runs fastest across lanes so 16 lanes write one
+  // V^T row (128 contiguous bytes) at once
+  const int v_kg = gtid % 16, v_c = gtid / 16;
   const int v_src = 4 * v_kg * row_bytes + 2 * VD * v_c;
-  const int v_dst = C::kKBytes + (VD * v_c) * C::kVPitch + 8 * vt_slot(v_kg);
-  // per-lane MFMA operand read bases
+  const int v_dst = (VD * v_c) * C::kVPitch + 8 * vt_slot(v_kg);
   const int k_rd = n * C::kKPitch + 16 * hh;
-  const int v_rd = C::kKBytes + n * C::kVPitch + 16 * hh;
+  const int v_rd = n * C::kVPitch + 16 * hh;
 
   for (int tt = 0; tt < ntile_here; ++tt) {
     const int tile = tiles[tt];
     const int p0 = tile * pos_per_wg;
 
-    // ---- per-lane column geometry ----
-    int pos[QT], hq[QT];
-    bool valid[QT];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const int col = (wave * QT + qt) * 32 + n;
-      const int pl = col / heads_per_wg;
-      const int hi = ht * heads_per_wg + col % heads_per_wg;
-      valid[qt] = pl < pos_per_wg && (p0 + pl) < tq && hi < G;
-      pos[qt] = min(p0 + pl, tq - 1);
-      hq[qt] = kvh * G + min(hi, G - 1);
-    }
+    const int col = wave * 32 + n;
+    const int pl = col / heads_per_wg;
+    const int hi = ht * heads_per_wg + col % heads_per_wg;
+    const bool valid = pl < pos_per_wg && (p0 + pl) < tq && hi < G;
+    const int pos = min(p0 + pl, tq - 1);
+    const int hq = kvh * G + min(hi, G - 1);
 
-    // ---- Q^T operands: lane holds q[col][16*s + 8*hh .. +8] for each k-step s ----
-    bf16x8 qf[QT][NS];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const uint16_t* qrow = Qp + ((q0 + pos[qt]) * a.Hq + hq[qt]) * D + 8 * hh;
+    bf16x8 qf[NS];
+    {
+      const uint16_t* qrow = Qp + ((q0 + pos) * a.Hq + hq) * D + 8 * hh;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        u32x4 w = valid[qt] ? *reinterpret_cast<const u32x4*>(qrow + 16 * s) : u32x4{0, 0, 0, 0};
-        qf[qt][s] = __builtin_bit_cast(bf16x8, w);
+        u32x4 w = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * s) : u32x4{0, 0, 0, 0};
+        qf[s] = __builtin_bit_cast(bf16x8, w);
       }
     }
-
-    f32x16 acc_o[QT][NMT];
-    float m_run[QT], l_run[QT];
+    f32x16 acc_o[NMT];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
+    for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc_o[qt][mt][i] = 0.f;
-      m_run[qt] = -INFINITY;
-      l_run[qt] = 0.f;
-    }
+      for (int i = 0; i < 16; ++i) acc_o[mt][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
 
     const int last = min(p0 + pos_per_wg, tq) - 1;
-    const int kend = a.causal ? min(tkv, last + off + 1) : tkv;  // keys this tile needs
+    const int kend = a.causal ? min(tkv, last + off + 1) : tkv;
     const int nkt = (kend + kKT - 1) / kKT;
-    // K/V rows past kend read as zeros
     const int nrec = (kend - 1) * row_bytes + D * 2;
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kbase_ptr), 0, nrec, kBufWord3);
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vbase_ptr), 0, nrec, kBufWord3);
 
-    u32x4 kreg[C::kKLoads];
-    uint32_t vreg[4][VW];
-    auto load_tile = [&](int kt) {
+    // one staging register file per thread: group B stages K tiles, group A stages V tiles
+    constexpr int kStageRegs = (4 * C::kKLoads > 4 * VW) ? 4 * C::kKLoads : 4 * VW;
+    uint32_t stg[kStageRegs];
+    auto load_k = [&](int kt) {
       const int soff = kt * kKT * row_bytes;
 #pragma unroll
-      for (int i = 0; i < C::kKLoads; ++i)
-        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_src[i], soff, 0);
+      for (int i = 0; i < C::kKLoads; ++i) {
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(krs, k_src[i], soff, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) stg[4 * i + e] = w[e];
+      }
+    };
+    auto store_k = [&](int stage) {
+      char* base = smem + stage * C::kKBytes;
+#pragma unroll
+      for (int i = 0; i < C::kKLoads; ++i) {
+        const u32x4 w = {stg[4 * i], stg[4 * i + 1], stg[4 * i + 2], stg[4 * i + 3]};
+        lds_write<u32x4>(base, k_dst[i], w);
+      }
+    };
+    auto load_v = [&](int kt) {
+      const int soff = kt * kKT * row_bytes;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if constexpr (VD == 8) {
           const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_src + r * row_bytes, soff, 0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vreg[r][e] = w[e];
-        } else if constexpr (VD == 4) {
-          const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(vrs, v_src + r * row_bytes, soff, 0);
-          vreg[r][0] = w[0];
-          vreg[r][1] = w[1];
+          for (int e = 0; e < 4; ++e) stg[VW * r + e] = w[e];
         } else {
-          vreg[r][0] = __builtin_amdgcn_raw_buffer_load_b32(vrs, v_src + r * row_bytes, soff, 0);
+          const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(vrs, v_src + r * row_bytes, soff, 0);
+          stg[VW * r] = w[0];
+          stg[VW * r + 1] = w[1];
         }
       }
     };
-    auto store_tile = [&](int stage) {
-      char* base = smem + stage * C::kStageBytes;
-#pragma unroll
-      for (int i = 0; i < C::kKLoads; ++i) lds_write<u32x4>(base, k_dst[i], kreg[i]);
+    auto store_v = [&](int stage) {
+      char* base = smem + C::kVBase + stage * C::kVBytes;
 #pragma unroll
       for (int e = 0; e < VD; ++e) {
-        // keys 4kg..4kg+3 at dim VD*c+e: the low or high halves of the dwords holding that dim
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
         u32x2 w;
-        w[0] = __builtin_amdgcn_perm(vreg[1][e >> 1], vreg[0][e >> 1], sel);
-        w[1] = __builtin_amdgcn_perm(vreg[3][e >> 1], vreg[2][e >> 1], sel);
+        w[0] = __builtin_amdgcn_perm(stg[VW * 1 + (e >> 1)], stg[VW * 0 + (e >> 1)], sel);
+        w[1] = __builtin_amdgcn_perm(stg[VW * 3 + (e >> 1)], stg[VW * 2 + (e >> 1)], sel);
         lds_write<u32x2>(base, v_dst + e * C::kVPitch, w);
       }
     };
 
-    __syncthreads();  // the previous query tile's readers are done with both stages
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int stage = kt & 1;
-      const int kbase = kt * kKT;
-      if (kt + 1 < nkt) load_tile(kt + 1);
-      const char* sm = smem + stage * C::kStageBytes;
-
-      // ---- S^T = K Q^T: 2 sub-tiles of 32 keys x QT query tiles ----
-      f32x16 sacc[QT][2];
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 kop = __builtin_bit_cast(
-              bf16x8, lds_read<u32x4>(sm, k_rd + t * 32 * C::kKPitch + 32 * s));
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt)
-            sacc[qt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                kop, qf[qt][s], s == 0 ? f32x16{} : sacc[qt][t], 0, 0, 0);
-        }
-
-      // ---- mask the tiles that cross the causal diagonal or the end of the keys ----
-      const bool need_mask = (kbase + kKT > tkv) || (a.causal && kbase + kKT - 1 > p0 + off);
-      if (need_mask) {
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          const int lim = a.causal ? min(tkv - 1, pos[qt] + off) : tkv - 1;  // last visible key
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = kbase + t * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-              sacc[qt][t][i] = key <= lim ? sacc[qt][t][i] : -INFINITY;
-            }
-        }
-      }
-
-      // ---- online softmax (per query tile) ----
-      bf16x8 pb[QT][4];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        // row max of the 32 scores this lane holds: a tree of three-input maxima
-        float r3[11];
-#pragma unroll
-        for (int g = 0; g < 10; ++g) {
-          const int i0 = 3 * g, i1 = 3 * g + 1, i2 = 3 * g + 2;
-          r3[g] = fmaxf(fmaxf(sacc[qt][i0 >> 4][i0 & 15], sacc[qt][i1 >> 4][i1 & 15]),
-                        sacc[qt][i2 >> 4][i2 & 15]);
-        }
-        r3[10] = fmaxf(sacc[qt][1][14], sacc[qt][1][15]);
-        const float r4a = fmaxf(fmaxf(r3[0], r3[1]), r3[2]);
-        const float r4b = fmaxf(fmaxf(r3[3], r3[4]), r3[5]);
-        const float r4c = fmaxf(fmaxf(r3[6], r3[7]), r3[8]);
-        const float r4d = fmaxf(r3[9], r3[10]);
-        float tmax = fmaxf(fmaxf(r4a, r4b), fmaxf(r4c, r4d));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * sl2;  // both halves of the column agree
-        // move the reference max only when it grows by more than the slack (or is unset)
-        const bool move = tmax > m_run[qt] + kRescaleSlack;
-        if (__any(move)) {
-          const float m_new = move ? tmax : m_run[qt];
-          const float alpha = fast_exp2(m_run[qt] - m_new);
-          l_run[qt] *= alpha;
-#pragma unroll
-          for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc_o[qt][mt][i] *= alpha;
-          m_run[qt] = m_new;
-        }
-        const float mref = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
-        float psum = 0.f;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            uint32_t pw[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float p0v = fast_exp2(fmaf(sacc[qt][t][8 * h2 + 2 * e], sl2, -mref));
-              const float p1v = fast_exp2(fmaf(sacc[qt][t][8 * h2 + 2 * e + 1], sl2, -mref));
-              pw[e] = pack_bf16x2(p0v, p1v);
-            }
-            // the row sum adds the rounded weights the MFMA consumes, so the weights used for
-            // the output are exactly normalised by it
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]),
-                                                     __builtin_bit_cast(bf16x2, 0x3f803f80u),
-                                                     psum, false);
-            const u32x4 w = {pw[0], pw[1], pw[2], pw[3]};
-            pb[qt][2 * t + h2] = __builtin_bit_cast(bf16x8, w);
-          }
-        l_run[qt] += psum;
-      }
-
-      // ---- O^T += V^T P^T ----
+    f32x16 sacc[2];
+    bf16x8 pb[4];
+    // M phase pieces: O += V(t-1) P(t-1) and S(t) = K(t) Q^T, operands read from LDS
+    auto pv = [&](int t) {
+      const char* sm = smem + C::kVBase + ((t + 2) % 3) * C::kVBytes;
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-        for (int kstep = 0; kstep < 4; ++kstep) {  // 16-key steps: (sub-tile, half)
+        for (int kstep = 0; kstep < 4; ++kstep) {
           const bf16x8 vop = __builtin_bit_cast(
               bf16x8, lds_read<u32x4>(sm, v_rd + mt * 32 * C::kVPitch + 32 * kstep));
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt)
-            acc_o[qt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[qt][kstep],
-                                                                    acc_o[qt][mt], 0, 0, 0);
+          acc_o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kstep], acc_o[mt], 0, 0, 0);
         }
-
-      if (kt + 1 < nkt) store_tile(stage ^ 1);
-      __syncthreads();
-    }
-
-    // ---- epilogue: combine the lane pair's sums, normalise, round, store ----
+    };
+    auto qk = [&](int t) {
+      const char* sm = smem + (t % 3) * C::kKBytes;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float inv = 1.f / (l_run[qt] + __shfl_xor(l_run[qt], 32));
-      if (valid[qt]) {
-        uint16_t* orow = Op + ((q0 + pos[qt]) * a.Hq + hq[qt]) * D;
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bf16x8 kop = __builtin_bit_cast(
+              bf16x8, lds_read<u32x4>(sm, k_rd + h * 32 * C::kKPitch + 32 * s));
+          sacc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[s], s == 0 ? f32x16{} : sacc[h],
+                                                            0, 0, 0);
+        }
+    };
+    // Ask the scheduler to keep kLdsAhead operand reads in flight ahead of the MFMAs that use
+    // them instead of waiting on each read right before its MFMA.
+    auto sched_stream = [&](auto nmfma_tag) {
+      constexpr int NM = decltype(nmfma_tag)::value;
+      constexpr int AHEAD = kLdsAhead < NM ? kLdsAhead : NM;
+      __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+      for (int i = 0; i < NM - AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+    };
+    auto m_full = [&](int t) {  // 1 <= t < nkt
+      pv(t);
+      qk(t);
+      sched_stream(std::integral_constant<int, 2 * NMT * 4>{});
+    };
+    auto m_first = [&]() {
+      qk(0);
+      sched_stream(std::integral_constant<int, 2 * NS>{});
+    };
+    auto m_last = [&](int t) {
+      pv(t);
+      sched_stream(std::integral_constant<int, NMT * 4>{});
+    };
+    // V phase: softmax of S(t) into P(t)
+    auto v_phase = [&](int t) {
+      const int kbase = t * kKT;
+      const bool need_mask = (kbase + kKT > tkv) || (a.causal && kbase + kKT - 1 > p0 + off);
+      if (need_mask) {
+        const int lim = a.causal ? min(tkv - 1, pos + off) : tkv - 1;
+        // key of element (h, i) is kbase + 4*hh + c(h, i) with a compile-time c; compare c
+        // against one per-lane remainder so no per-element offsets stay live across tiles
+        const int rem = lim - kbase - 4 * hh;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int c = h * 32 + (i >> 2) * 8 + (i & 3);
+            sacc[h][i] = c <= rem ? sacc[h][i] : -INFINITY;
+          }
+      }
+      float r3[11];
+#pragma unroll
+      for (int g = 0; g < 10; ++g) {
+        const int i0 = 3 * g, i1 = 3 * g + 1, i2 = 3 * g + 2;
+        r3[g] = fmaxf(fmaxf(sacc[i0 >> 4][i0 & 15], sacc[i1 >> 4][i1 & 15]), sacc[i2 >> 4][i2 & 15]);
+      }
+      r3[10] = fmaxf(sacc[1][14], sacc[1][15]);
+      const float r4a = fmaxf(fmaxf(r3[0], r3[1]), r3[2]);
+      const float r4b = fmaxf(fmaxf(r3[3], r3[4]), r3[5]);
+      const float r4c = fmaxf(fmaxf(r3[6], r3[7]), r3[8]);
+      const float r4d = fmaxf(r3[9], r3[10]);
+      float tmax = fmaxf(fmaxf(r4a, r4b), fmaxf(r4c, r4d));
+      tmax = pair_max32(tmax) * sl2;
+      const bool move = tmax > m_run + kRescaleSlack;
+      if (__any(move)) {
+        const float m_new = move ? tmax : m_run;
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int dd = mt * 32 + g4 * 8 + hh * 4;
-            u32x2 w;
-            w[0] = pack_bf16x2(acc_o[qt][mt][4 * g4 + 0] * inv, acc_o[qt][mt][4 * g4 + 1] * inv);
-            w[1] = pack_bf16x2(acc_o[qt][mt][4 * g4 + 2] * inv, acc_o[qt][mt][4 * g4 + 3] * inv);
-            *reinterpret_cast<u32x2*>(orow + dd) = w;
-          }
+          for (int i = 0; i < 16; ++i) acc_o[mt][i] *= alpha;
+        m_run = m_new;
       }
+      const float mref = m_run == -INFINITY ? 0.f : m_run;
+      float psum = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          uint32_t pw[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0v = fast_exp2(fmaf(sacc[h][8 * h2 + 2 * e], sl2, -mref));
+            const float p1v = fast_exp2(fmaf(sacc[h][8 * h2 + 2 * e + 1], sl2, -mref));
+            pw[e] = pack_bf16x2(p0v, p1v);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]),
+                                                   __builtin_bit_cast(bf16x2, 0x3f803f80u), psum,
+                                                   false);
+          const u32x4 w = {pw[0], pw[1], pw[2], pw[3]};
+          pb[2 * h + h2] = __builtin_bit_cast(bf16x8, w);
+        }
+      l_run += psum;
+    };
+
+    __syncthreads();  // the previous query tile's readers are done with every stage
+    if (grp_a) {
+      load_v(0);
+      store_v(0);
+      load_v(1);
+    } else {
+      load_k(0);
+      store_k(0);
+      load_k(1);
+    }
+    __syncthreads();
+    // Staging runs at the end of each group's matrix phase, which has slack, so waiting for
+    // the global loads does not lengthen the vector-ALU (softmax) phase that paces the loop.
+    // A writes V(t+1) in its M(t) at half-step 2t (V(t-2) is no longer read after 2t-1);
+    // B writes K(t+1) in its M(t) at half-step 2t+1 (read first by A at 2t+2).
+    // t = 0: only the scores of tile 0
+    if (grp_a) {
+      m_first();
+      store_v(1);
+      load_v(2);
+    }
+    __syncthreads();
+    if (grp_a) {
+      v_phase(0);
+    } else {
+      m_first();
+      store_k(1);
+      load_k(2);
+    }
+    __syncthreads();
+    for (int t = 1; t < nkt; ++t) {
+      const int st_next = (t + 1) % 3;
+      if (grp_a) {
+        m_full(t);
+        store_v(st_next);
+        load_v(t + 2);
+      } else {
+        v_phase(t - 1);
+      }
+      __syncthreads();
+      if (grp_a) {
+        v_phase(t);
+      } else {
+        m_full(t);
+        store_k(st_next);
+        load_k(t + 2);
+      }
+      __syncthreads();
+    }
+    // t = nkt: only O += V(nkt-1) P(nkt-1)
+    if (grp_a) {
+      m_last(nkt);
+    } else {
+      v_phase(nkt - 1);
+    }
+    __syncthreads();
+    if (!grp_a) m_last(nkt);
+
+    const float inv = 1.f / pair_sum32(l_run);
+    if (valid) {
+      uint16_t* orow = Op + ((q0 + pos) * a.Hq + hq) * D;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int dd = mt * 32 + g4 * 8 + hh * 4;
+          u32x2 w;
+          w[0] = pack_bf16x2(acc_o[mt][4 * g4 + 0] * inv, acc_o[mt][4 * g4 + 1] * inv);
+          w[1] = pack_bf16x2(acc_o[mt][4 * g4 + 2] * inv, acc_o[mt][4 * g4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + dd) = w;
+        }
     }
   }
 }
 
-template <int D, int NW, int QT>
-hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
-  constexpr int kCols = Cfg<D, NW, QT>::kCols;
+template <int D>
+hipError_t launch_pp(const PrefillArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int heads_per_wg = G < kCols ? G : kCols;
   const int pos_per_wg = kCols / heads_per_wg;
@@ -399,20 +440,19 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
   const int ntiles = (a.max_tq + pos_per_wg - 1) / pos_per_wg;
   const int gz = a.causal ? (ntiles + 1) / 2 : ntiles;
   const dim3 grid(a.Hkv * head_tiles * a.nitems * gz);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, QT>), grid, dim3(NW * 64), 0, s, a, heads_per_wg,
-                     pos_per_wg, head_tiles, gz);
+  hipLaunchKernelGGL(prefill_pp_kernel<D>, grid, dim3(512), 0, s, a, heads_per_wg, pos_per_wg,
+                     head_tiles, gz);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Columns per workgroup of the launched configurations (the host validates the grid with it).
-int prefill_bf16_cols() { return Cfg<128, GQA_PREFILL_NW, GQA_PREFILL_QT>::kCols; }
+int prefill_bf16_cols() { return kCols; }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   switch (a.d) {
-    case 64: return launch_cfg<64, GQA_PREFILL_NW, GQA_PREFILL_QT>(a, s);
-    case 128: return launch_cfg<128, GQA_PREFILL_NW, GQA_PREFILL_QT>(a, s);
+    case 64: return launch_pp<64>(a, s);
+    case 128: return launch_pp<128>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
