@@ -25,9 +25,15 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
 PEAK_HBM_GBS = 8000.0       # HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_llama3_8b_T4096_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "grouped_query_softmax_amd", "csrc", f)
-                  for f in ("prefill_bf16.hip", "common.hpp")]
+CSRC = os.path.join(ROOT, "grouped_query_softmax_amd", "csrc")
+# HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE counters (calibrated against a plain
+# copy), valid only for the kernel sources they were taken on (checked by hash)
+TRAFFIC = {
+    "prefill": (os.path.join(ROOT, "profiles", "prefill_bf16_llama3_8b_T4096_traffic.json"),
+                ("prefill_bf16.hip", "common.hpp")),
+    "decode": (os.path.join(ROOT, "profiles", "decode_bf16_B64_kv8192_traffic.json"),
+               ("decode.hip", "common.hpp")),
+}
 
 
 def log(msg):
@@ -50,10 +56,10 @@ def prefill_flops(w):
     return 4 * w.d * w.Hq * pairs
 
 
-def kernel_source_sha():
+def kernel_source_sha(which="prefill"):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
+    for name in TRAFFIC[which][1]:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -139,7 +145,8 @@ def bench_decode(gqa, w, steps, warmup, torch, seed):
     avg = sum(ms) / len(ms)
     gbs = (kv_bytes + qo_bytes) / (avg * 1e-3) / 1e9
     return {"workload": w.name, "bytes_per_launch": kv_bytes + qo_bytes, "avg_ms": avg,
-            "min_ms": min(ms), "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "wall_s": wall}
+            "min_ms": min(ms), "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "wall_s": wall,
+            "traffic": traffic_for("decode")}
 
 
 COPY_BYTES = 1 << 30
@@ -190,12 +197,14 @@ def cpu_baseline(w, tensors, torch, target_s=15.0):
                       f"{t:.1f} s, fp64"}
 
 
-def traffic_for(sha, launches_per_profile=None):
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_for(which):
+    """Calibrated HBM bytes per launch, or None when no counters exist for the current source."""
+    path = TRAFFIC[which][0]
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha") != sha:
+    if rec.get("kernel_source_sha") != kernel_source_sha(which):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -257,7 +266,7 @@ def main():
         dec = bench_decode(gqa, workloads.DECODE, args.steps, args.warmup, torch, 3000)
         extra["decode"] = dec
         log(f"decode: {dec['avg_ms'] * 1e3:.1f} us, {dec['gbs']:.0f} GB/s")
-    sha = kernel_source_sha()
+    sha = kernel_source_sha("prefill")
     metric = "GQA prefill TFLOPS (% MFMA peak); decode KV GB/s (% HBM peak)"
     if pre is None and args.only in ("mqa", "varlen"):
         key = "mqa_prefill" if args.only == "mqa" else "varlen_prefill"
@@ -266,7 +275,7 @@ def main():
     if pre is not None:
         value, unit = pre["tflops"], "TFLOP/s"
         ms_per_step = pre["avg_ms"]
-        traffic = traffic_for(sha) if w is workloads.LLAMA_PREFILL else None
+        traffic = traffic_for("prefill") if w is workloads.LLAMA_PREFILL else None
         roofline = {"bound": "mfma", "achieved": pre["tflops"], "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": pre["tflops"] / PEAK_BF16_TFLOPS,
                     "traffic": traffic, "kernel": "prefill_pp_kernel<128>",
@@ -282,7 +291,10 @@ def main():
         value, unit = dec["gbs"], "GB/s"
         ms_per_step = dec["avg_ms"]
         roofline = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": dec["frac_hbm"], "traffic": None}
+                    "frac": dec["frac_hbm"], "traffic": dec["traffic"],
+                    "kernel": "decode_split_kernel<128>", "bytes_per_launch":
+                    dec["bytes_per_launch"], "avg_launch_ms": dec["avg_ms"],
+                    "kernel_source_sha": kernel_source_sha("decode")}
         dw = workloads.DECODE
         config = {"workload": dw.name, "B": dw.B, "Tkv": dw.Tkv, "Hq": dw.Hq, "Hkv": dw.Hkv,
                   "d": dw.d, "parallelism": "single-gpu"}

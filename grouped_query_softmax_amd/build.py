@@ -42,10 +42,15 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (needs ROCm)")
 
 
-# Per-file flags. The prefill kernel assumes finite (non-NaN) inputs: with NaN semantics
+# Per-file flags. The bf16 attention kernels assume finite (non-NaN) inputs: with NaN semantics
 # relaxed, maxima of matrix-core results compile to v_max3_f32 without a canonicalising
 # v_max_f32 per element. Infinities keep their meaning (masked scores are -inf).
-FILE_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"]}
+FILE_FLAGS = {
+    "prefill_bf16.hip": ["-fno-honor-nans"],
+    # decode also keeps its matrix-core accumulators in ordinary VGPRs, so the occasional softmax
+    # rescale of the output accumulators needs no accumulator-register copies
+    "decode.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src: str, extra: List[str]) -> str:

@@ -107,7 +107,8 @@ struct DecodeArgs {
   int B, Tkv, Hq, Hkv, d;
   float scale;
   float* ws;      // partial results
-  int nsplit;
+  int nsplit;     // splits of the cache
+  int per;        // keys per split (a multiple of the kernel's key tile)
 };
 
 // Launchers (return hipSuccess or the launch error). Shapes have been validated by the caller.
@@ -120,6 +121,7 @@ hipError_t launch_fold(const void* src, void* dst, int64_t BT, int H, int g, int
 
 // Decode split planning (host): shared by the workspace query and the launcher.
 int decode_num_splits(int B, int Tkv, int Hq, int Hkv, int d);
+int decode_split_len(int Tkv, int nsplit);
 size_t decode_workspace_bytes(int B, int Tkv, int Hq, int Hkv, int d);
 
 }  // namespace gqa

@@ -7,14 +7,27 @@
 // attention by hand: reducing only the key/value heads", step 6: the cache element count has no
 // query-head term).
 //
-// Kernel 1 (split): one workgroup per (sequence, key/value head, head chunk, split of the cache).
-//   Every 16-lane group (8 for d = 64) reads one whole key row with 16-byte loads (256 contiguous
-//   bytes per row), so each cache element leaves HBM exactly once for all query heads of the
-//   group. The group dots its 8 dims with each query head, sums across its lanes, and keeps an
-//   online max-subtracted softmax per head in fp32. Groups are merged inside the workgroup and
-//   the split's partial (running max m, running sum l, unnormalised output o) goes to the
-//   workspace.
-// Kernel 2 (combine): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
+// Kernel 1 (split): one workgroup of 4 waves per (sequence, key/value head, chunk of up to 16
+// query heads, split of the cache). Each wave streams its own 32-key tiles of the split and keeps
+// the next tile's loads in flight while it computes the current one, so the vector and matrix
+// work hides under the HBM stream. Per tile, on the matrix cores (v_mfma_f32_16x16x32_bf16):
+//   * the tile's K and V rows are loaded whole (each load instruction covers complete 128-byte
+//     lines, with the non-temporal cache policy: every line is used exactly once) and written
+//     to per-wave LDS tiles; every cache element leaves HBM exactly once for all query heads;
+//   * scores S^T = K Q^T: K rows are the A operand read back from LDS, the query heads are the
+//     16 columns of B (unused columns are zero);
+//   * O^T += V^T P^T: V comes back from LDS transposed with ds_read_b64_tr_b16 (4 keys of one
+//     dimension per lane), P^T is the score accumulator rounded to bf16 in place, with the
+//     contraction order of keys following the accumulator layout.
+// Each lane owns one query head (one accumulator column), so the softmax reference and the
+// rescale factor are per lane; the row maximum of a tile is combined over the 4 lane groups that
+// hold that head's keys. Online softmax in the base-2 domain with a lazily moved reference
+// (moved only when a tile raises the maximum by more than 8 in log2 units; exact, since one
+// reference is used for both the output and the running sum). The 4 waves are merged in LDS and
+// the split's partial (reference m, running sum l, unnormalised output o) goes to the workspace,
+// or, when the cache is not split, the normalised output goes straight to `out`.
+// Kernel 2 (combine, only with more than one split):
+//   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
 #include <math.h>
 
 #include "common.hpp"
@@ -22,153 +35,279 @@
 namespace gqa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTargetBlocks = 2048;  // split count aims at this many workgroups
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTK = 32;              // keys per tile
+constexpr int kHeadCols = 16;        // query heads per workgroup (MFMA columns)
+// Splits are added only until the grid has this many workgroups: 2 per CU (the kernel's
+// register and LDS use allow 2 resident per CU) x 256 CUs, one full round with no tail.
+constexpr int kTargetBlocks = 512;
+// Cache policy of the key/value loads: non-temporal (each cache line is read exactly once).
+constexpr int kStreamLoad = 2;
+constexpr int kMinSplitKeys = 256;
+constexpr float kRescaleSlack = 8.0f;
+// Raw buffer resource word 3: loads at or past num_records bytes return zeros. Only the VGPR
+// offset is range checked (not the SGPR offset), so every offset goes in the VGPR operand.
+constexpr int kBufWord3 = 0x00020000;
 
-__device__ __forceinline__ void merge(float& m, float& l, float* o, float m2, float l2,
-                                      const float* o2, int n) {
-  const float M = fmaxf(m, m2);
-  const float a1 = (M == -INFINITY) ? 0.f : fast_exp2(m - M);
-  const float a2 = (M == -INFINITY) ? 0.f : fast_exp2(m2 - M);
-  l = l * a1 + l2 * a2;
-  for (int i = 0; i < n; ++i) o[i] = o[i] * a1 + o2[i] * a2;
-  m = M;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+template <int D>
+struct DecCfg {
+  static constexpr int kSteps = D / 32;   // MFMA k-steps over d for the scores
+  static constexpr int kDT = D / 16;      // 16-dimension tiles of O^T
+  // LDS row pitches (bytes), chosen so that the reads are free of bank conflicts: 16-byte K
+  // operand reads of 16 rows, and transposing 8-byte V reads of 8 rows per half wave
+  static constexpr int kPitch = 2 * D + 32;   // V tile
+  static constexpr int kKPitch = 2 * D + 16;  // K tile
+  static constexpr int kTileBytes = kTK * (kPitch + kKPitch);
+  static constexpr int kLPR = D / 8;          // lanes per key row in the full-row loads
+  static constexpr int kRPI = 64 / kLPR;      // key rows per load instruction
+  static constexpr int kVBytes = kWaves * kTileBytes;
+  static constexpr int kMergeBytes = kWaves * kHeadCols * (D + 2) * 4;
+  static constexpr int kSmemBytes = kVBytes > kMergeBytes ? kVBytes : kMergeBytes;
+};
+
+// Transposing LDS read: with lane 4r + t of a 16-lane group pointing at 4 consecutive bf16 of
+// row r (columns 4t .. 4t+3), lane j of the group receives column j of rows 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr(char* base, int byte_off) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)((__attribute__((address_space(3))) char*)base + byte_off));
+  return __builtin_bit_cast(u32x2, r);
 }
 
-template <int D, int GC>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, int head_chunks) {
-  constexpr int LPK = D / 8;               // lanes per key row
-  constexpr int SLOTS = kThreads / LPK;    // key rows in flight per workgroup step
-  __shared__ float sm[4][GC], sl[4][GC];
-  __shared__ float so[4][GC][D];
+// Keeps the compiler from moving LDS accesses across this point. The tile in LDS is written and
+// read back by the same wave, whose LDS instructions execute in program order, so no wait or
+// workgroup barrier is needed; only the compiler must not reorder them.
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y / head_chunks;
-  const int hc = blockIdx.y % head_chunks;
-  const int b = blockIdx.z;
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, int head_chunks) {
+  using C = DecCfg<D>;
+  constexpr int NS = C::kSteps;
+  constexpr int NDT = C::kDT;
+  __shared__ __attribute__((aligned(16))) char smem[C::kSmemBytes];
+
+  const int S = a.nsplit;
+  const int lin = blockIdx.x;
+  const int split = lin % S;
+  const int rest = lin / S;
+  const int y = rest % (a.Hkv * head_chunks);
+  const int b = rest / (a.Hkv * head_chunks);
+  const int kvh = y / head_chunks;
+  const int hc = y % head_chunks;
   const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int slot = tid / LPK;
-  const int lc = tid % LPK;
-  const int per = (a.Tkv + a.nsplit - 1) / a.nsplit;
-  const int kb = split * per;
-  const int ke = min(a.Tkv, kb + per);
-
-  const uint16_t* __restrict__ Qp = static_cast<const uint16_t*>(a.q);
-  const uint16_t* __restrict__ Kp = static_cast<const uint16_t*>(a.k);
-  const uint16_t* __restrict__ Vp = static_cast<const uint16_t*>(a.v);
-
-  float qv[GC][8], o[GC][8], m[GC], l[GC];
-#pragma unroll
-  for (int g = 0; g < GC; ++g) {
-    const int hi = hc * GC + g;
-    u32x4 w = {0, 0, 0, 0};
-    if (hi < G)
-      w = *reinterpret_cast<const u32x4*>(Qp + (static_cast<int64_t>(b) * a.Hq + kvh * G + hi) * D +
-                                          8 * lc);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qv[g][2 * e] = bf16_lo(w[e]);
-      qv[g][2 * e + 1] = bf16_hi(w[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
-    m[g] = -INFINITY;
-    l[g] = 0.f;
-  }
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int kb = split * a.per;
+  const int nkeys = min(a.Tkv, kb + a.per) - kb;  // >= 1 by the split plan
+  const int ntile = (nkeys + kTK - 1) / kTK;
+  const int row_bytes = a.Hkv * D * 2;
   const float sl2 = a.scale * kLog2e;
-  const int64_t kstride = static_cast<int64_t>(a.Hkv) * D;
-  const int64_t base = (static_cast<int64_t>(b) * a.Tkv * a.Hkv + kvh) * D + 8 * lc;
 
-#pragma unroll 2
-  for (int key = kb + slot; key < ke; key += SLOTS) {
-    const u32x4 kw = *reinterpret_cast<const u32x4*>(Kp + base + key * kstride);
-    const u32x4 vw = *reinterpret_cast<const u32x4*>(Vp + base + key * kstride);
-    float kf[8], vf[8];
+  // this lane's query head (accumulator column) and its B operand, loaded once
+  const int col = hc * kHeadCols + r16;
+  const bool col_ok = col < G;
+  bf16x8 qop[NS];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           (static_cast<int64_t>(b) * a.Hq + kvh * G + (col_ok ? col : 0)) * D +
+                           8 * g;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kf[2 * e] = bf16_lo(kw[e]);
-      kf[2 * e + 1] = bf16_hi(kw[e]);
-      vf[2 * e] = bf16_lo(vw[e]);
-      vf[2 * e + 1] = bf16_hi(vw[e]);
-    }
-    float s[GC];
-#pragma unroll
-    for (int g = 0; g < GC; ++g) {
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = fmaf(qv[g][e], kf[e], acc);
-      s[g] = acc;
-    }
-#pragma unroll
-    for (int off = LPK / 2; off > 0; off >>= 1)
-#pragma unroll
-      for (int g = 0; g < GC; ++g) s[g] += __shfl_xor(s[g], off);
-#pragma unroll
-    for (int g = 0; g < GC; ++g) {
-      const float t = s[g] * sl2;
-      const float mn = fmaxf(m[g], t);
-      const float al = fast_exp2(m[g] - mn);
-      const float p = fast_exp2(t - mn);
-      l[g] = l[g] * al + p;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[g][e] = fmaf(p, vf[e], o[g][e] * al);
-      m[g] = mn;
+    for (int s = 0; s < NS; ++s) {
+      const u32x4 w = col_ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * s) : u32x4{0, 0, 0, 0};
+      qop[s] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
-  // merge the key slots of this wave (lanes lc, lc+LPK, ...)
+  const int64_t split_elem = ((static_cast<int64_t>(b) * a.Tkv + kb) * a.Hkv + kvh) * D;
+  const int nrec = (nkeys - 1) * row_bytes + D * 2;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k) + split_elem), 0, nrec, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.v) + split_elem), 0, nrec, kBufWord3);
+
+  // Loads: kLPR lanes cover one whole key row (16 bytes each), so every load instruction reads
+  // whole 128-byte lines; K and V go to this wave's LDS tiles as they arrived. The K operand is
+  // read back as lane (g, r16) <- row r16, bytes 64s + 16g (dimensions 32s + 8g .. +7, the A
+  // operand slice of lane group g at k-step s); V is read back transposed.
+  char* vt = smem + wave * C::kTileBytes;
+  char* kt = vt + kTK * C::kPitch;
+  const int lrow = lane / C::kLPR, lcol = lane % C::kLPR;
+  const int foff = lrow * row_bytes + 16 * lcol;
+  const int k_wr = lrow * C::kKPitch + 16 * lcol;
+  const int v_wr = lrow * C::kPitch + 16 * lcol;
+  const int k_rd = r16 * C::kKPitch + 16 * g;
+  const int v_rd = (4 * g + (r16 >> 2)) * C::kPitch + 8 * (r16 & 3);
+
+  f32x4 acc_o[NDT];
 #pragma unroll
-  for (int off = LPK; off < 64; off <<= 1) {
+  for (int nt = 0; nt < NDT; ++nt) acc_o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Tiles at or past ntile read as zeros (past num_records) and are never processed.
+  auto load = [&](u32x4 (&kr)[2][NS], u32x4 (&vr)[2][NS], int t) {
+    const int soff = t * kTK * row_bytes;
 #pragma unroll
-    for (int g = 0; g < GC; ++g) {
-      const float m2 = __shfl_xor(m[g], off);
-      const float l2 = __shfl_xor(l[g], off);
-      float o2[8];
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(o[g][e], off);
-      merge(m[g], l[g], o[g], m2, l2, o2, 8);
-    }
-  }
-  if (lane < LPK) {
-#pragma unroll
-    for (int g = 0; g < GC; ++g) {
-      if (lane == 0) {
-        sm[wave][g] = m[g];
-        sl[wave][g] = l[g];
+      for (int s = 0; s < NS; ++s) {
+        const int off = foff + soff + (blk * NS + s) * C::kRPI * row_bytes;
+        kr[blk][s] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, kStreamLoad);
+        vr[blk][s] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kStreamLoad);
       }
+  };
+
+  auto process = [&](const u32x4 (&kr)[2][NS], const u32x4 (&vr)[2][NS], int t) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) so[wave][g][8 * lc + e] = o[g][e];
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int row = (blk * NS + s) * C::kRPI;
+        *reinterpret_cast<u32x4*>(kt + k_wr + row * C::kKPitch) = kr[blk][s];
+        *reinterpret_cast<u32x4*>(vt + v_wr + row * C::kPitch) = vr[blk][s];
+      }
+    lds_order();
+    // S^T for the 2 blocks of 16 keys: lane (g, r16) gets keys 16 blk + 4g + i of head r16
+    f32x4 sc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      sc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const u32x4 kw =
+            *reinterpret_cast<const u32x4*>(kt + k_rd + blk * 16 * C::kKPitch + 64 * s);
+        sc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw),
+                                                          qop[s], sc[blk], 0, 0, 0);
+      }
     }
+    const int k0 = t * kTK;
+    if (k0 + kTK > nkeys) {
+      const int rem = nkeys - 1 - k0 - 4 * g;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[blk][i] = (16 * blk + i <= rem) ? sc[blk][i] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = pair_max32(mx) * sl2;
+    const bool move = mx > m_run + kRescaleSlack;
+    if (__any(move)) {
+      const float m_new = move ? mx : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int nt = 0; nt < NDT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_o[nt][i] *= alpha;
+      m_run = m_new;
+    }
+    uint32_t pw[4];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        pw[2 * blk + e] = pack_bf16x2(fast_exp2(fmaf(sc[blk][2 * e], sl2, -m_run)),
+                                      fast_exp2(fmaf(sc[blk][2 * e + 1], sl2, -m_run)));
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]),
+                                             __builtin_bit_cast(bf16x2, 0x3f803f80u), psum, false);
+    l_run += psum;
+    const bf16x8 pop = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+    lds_order();
+#pragma unroll
+    for (int nt = 0; nt < NDT; ++nt) {
+      const u32x2 lo = lds_read_tr(vt, v_rd + 32 * nt);                  // keys 4g .. 4g+3
+      const u32x2 hi = lds_read_tr(vt, v_rd + 16 * C::kPitch + 32 * nt);  // keys 16+4g ..
+      const bf16x8 vop = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      acc_o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, acc_o[nt], 0, 0, 0);
+    }
+    lds_order();
+  };
+
+  {
+    // two register sets: the loads of the next tile are in flight while a tile is processed
+    // (a fixed trip count and no early exit, so the compiler's wait analysis sees only the
+    // other set's loads in flight at the top of the loop)
+    u32x4 ka[2][NS], va[2][NS], kbuf[2][NS], vbuf[2][NS];
+    const int mine = wave < ntile ? (ntile - wave + kWaves - 1) / kWaves : 0;
+    load(ka, va, wave);
+    int t = wave;
+    for (int i = 0; i < mine / 2; ++i) {
+      load(kbuf, vbuf, t + kWaves);
+      process(ka, va, t);
+      load(ka, va, t + 2 * kWaves);
+      process(kbuf, vbuf, t + kWaves);
+      t += 2 * kWaves;
+    }
+    if (mine & 1) process(ka, va, t);
   }
+
+  // this wave's running sum: the 4 lane groups hold different keys of the same head
+  l_run += __shfl_xor(l_run, 16);
+  l_run = pair_sum32(l_run);
+
+  // merge the 4 waves in LDS: m, l per head, then o[head][dim]
+  __syncthreads();  // every wave is done with its V tile
+  float* mm = reinterpret_cast<float*>(smem);
+  float* ll = mm + kWaves * kHeadCols;
+  float* oo = ll + kWaves * kHeadCols;
+  if (g == 0) {
+    mm[wave * kHeadCols + r16] = m_run;
+    ll[wave * kHeadCols + r16] = l_run;
+  }
+#pragma unroll
+  for (int nt = 0; nt < NDT; ++nt)
+    *reinterpret_cast<f32x4*>(oo + (wave * kHeadCols + r16) * D + 16 * nt + 4 * g) = acc_o[nt];
   __syncthreads();
-  if (wave == 0 && lane < LPK) {
+  constexpr int kDimsPerThread = kHeadCols * D / kThreads;  // 8 at d = 128, 4 at d = 64
+  const int h = tid / (D / kDimsPerThread);
+  const int d0 = (tid % (D / kDimsPerThread)) * kDimsPerThread;
+  const int hq_in = hc * kHeadCols + h;
+  if (hq_in < G) {
+    float M = -INFINITY;
 #pragma unroll
-    for (int g = 0; g < GC; ++g) {
-      float mm = sm[0][g], ll = sl[0][g];
-      float oo[8];
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mm[w * kHeadCols + h]);
+    float L = 0.f, o[kDimsPerThread];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) oo[e] = so[0][g][8 * lc + e];
-      for (int w = 1; w < 4; ++w) {
-        float o2[8];
+    for (int e = 0; e < kDimsPerThread; ++e) o[e] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o2[e] = so[w][g][8 * lc + e];
-        merge(mm, ll, oo, sm[w][g], sl[w][g], o2, 8);
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = mm[w * kHeadCols + h];
+      const float aw = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+      L = fmaf(aw, ll[w * kHeadCols + h], L);
+#pragma unroll
+      for (int e = 0; e < kDimsPerThread; ++e)
+        o[e] = fmaf(aw, oo[(w * kHeadCols + h) * D + d0 + e], o[e]);
+    }
+    const int64_t idx = (static_cast<int64_t>(b) * a.Hq + kvh * G + hq_in) * S + split;
+    if (S == 1) {  // the whole cache in one split: finish here, no combine pass
+      uint16_t* orow = static_cast<uint16_t*>(a.out) + idx * D + d0;
+#pragma unroll
+      for (int e = 0; e < kDimsPerThread; e += 4) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[e] / L, o[e + 1] / L);
+        w[1] = pack_bf16x2(o[e + 2] / L, o[e + 3] / L);
+        *reinterpret_cast<u32x2*>(orow + e) = w;
       }
-      const int hi = hc * GC + g;
-      if (hi < G) {
-        const int64_t idx = (static_cast<int64_t>(b) * a.Hq + kvh * G + hi) * a.nsplit + split;
-        float* wo = a.ws + idx * D + 8 * lc;
+      return;
+    }
+    float* wo = a.ws + idx * D + d0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wo[e] = oo[e];
-        if (lc == 0) {
-          const int64_t nbh = static_cast<int64_t>(a.B) * a.Hq * a.nsplit;
-          a.ws[nbh * D + idx] = mm;
-          a.ws[nbh * D + nbh + idx] = ll;
-        }
-      }
+    for (int e = 0; e < kDimsPerThread; e += 4)
+      *reinterpret_cast<f32x4*>(wo + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
+    if (d0 == 0) {
+      const int64_t nbh = static_cast<int64_t>(a.B) * a.Hq * S;
+      a.ws[nbh * D + idx] = M;
+      a.ws[nbh * D + nbh + idx] = L;
     }
   }
 }
@@ -193,28 +332,15 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
   out[static_cast<int64_t>(bh) * D + d] = f32_to_bf16(num / den);
 }
 
-int head_chunk_size(int G) { return G >= 8 ? 8 : (G >= 4 ? 4 : (G >= 2 ? 2 : 1)); }
-
-template <int D, int GC>
-hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
-  const int G = a.Hq / a.Hkv;
-  const int head_chunks = (G + GC - 1) / GC;
-  dim3 grid(a.nsplit, a.Hkv * head_chunks, a.B);
-  hipLaunchKernelGGL((decode_split_kernel<D, GC>), grid, dim3(kThreads), 0, s, a, head_chunks);
-  return hipGetLastError();
-}
+int head_chunks_of(int G) { return (G + kHeadCols - 1) / kHeadCols; }
 
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
-  const int G = a.Hq / a.Hkv;
-  hipError_t e;
-  switch (head_chunk_size(G)) {
-    case 8: e = launch_split<D, 8>(a, s); break;
-    case 4: e = launch_split<D, 4>(a, s); break;
-    case 2: e = launch_split<D, 2>(a, s); break;
-    default: e = launch_split<D, 1>(a, s); break;
-  }
-  if (e != hipSuccess) return e;
+  const int hcs = head_chunks_of(a.Hq / a.Hkv);
+  const dim3 grid(a.nsplit * a.Hkv * hcs * a.B);
+  hipLaunchKernelGGL(decode_split_kernel<D>, grid, dim3(kThreads), 0, s, a, hcs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.B * a.Hq), dim3(D), 0, s, a.ws,
                      static_cast<uint16_t*>(a.out), a.B * a.Hq, a.nsplit);
   return hipGetLastError();
@@ -222,16 +348,21 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
 
 }  // namespace
 
+int decode_split_len(int Tkv, int nsplit) {
+  const int per = (Tkv + nsplit - 1) / nsplit;
+  return (per + kTK - 1) / kTK * kTK;
+}
+
 int decode_num_splits(int B, int Tkv, int Hq, int Hkv, int d) {
   (void)d;
-  const int G = Hq / Hkv;
-  const int gc = head_chunk_size(G);
-  const int64_t units = static_cast<int64_t>(B) * Hkv * ((G + gc - 1) / gc);
+  const int64_t units = static_cast<int64_t>(B) * Hkv * head_chunks_of(Hq / Hkv);
   int64_t s = (kTargetBlocks + units - 1) / units;
-  const int64_t max_s = Tkv / 256 > 1 ? Tkv / 256 : 1;  // at least 256 keys per split
+  const int64_t max_s = Tkv / kMinSplitKeys > 1 ? Tkv / kMinSplitKeys : 1;
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
-  return static_cast<int>(s);
+  // splits are whole tiles; recount so that every split holds at least one key
+  const int per = decode_split_len(Tkv, static_cast<int>(s));
+  return (Tkv + per - 1) / per;
 }
 
 size_t decode_workspace_bytes(int B, int Tkv, int Hq, int Hkv, int d) {

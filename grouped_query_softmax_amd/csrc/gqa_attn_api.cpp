@@ -13,6 +13,9 @@
 namespace {
 
 constexpr int kMaxGridYZ = 65535;
+// a flat grid must keep blockIdx.x * blockDim.x below 2^32
+constexpr int64_t kMaxFlatWorkgroups512 = (int64_t{1} << 32) / 512 - 1;
+constexpr int64_t kMaxFlatWorkgroups256 = (int64_t{1} << 32) / 256 - 1;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -90,10 +93,19 @@ gqa_status_t gqa_attn_prefill(const void* q, const void* k, const void* v, void*
     max_tq = Tq;
   }
   const int G = Hq / Hkv;
-  if (nitems > kMaxGridYZ || prefill_tiles(dtype, G, max_tq) > kMaxGridYZ ||
-      static_cast<int64_t>(Hkv) * head_tiles(dtype, G) > INT32_MAX)
-    return GQA_ERR_UNSUPPORTED;
   const size_t es = esize(dtype);
+  if (dtype == GQA_DTYPE_BF16) {
+    // one flat grid of 512-thread workgroups; key/value offsets inside an item are 32-bit
+    const int64_t tiles = prefill_tiles(dtype, G, max_tq);
+    const int64_t wgs = static_cast<int64_t>(Hkv) * head_tiles(dtype, G) * nitems *
+                        (causal ? (tiles + 1) / 2 : tiles);
+    const int64_t item_kv_bytes =
+        static_cast<int64_t>(cu_seqlens ? max_tq : Tkv) * Hkv * d * static_cast<int64_t>(es);
+    if (wgs > kMaxFlatWorkgroups512 || item_kv_bytes > INT32_MAX) return GQA_ERR_UNSUPPORTED;
+  } else if (nitems > kMaxGridYZ || prefill_tiles(dtype, G, max_tq) > INT32_MAX ||
+             static_cast<int64_t>(Hkv) * head_tiles(dtype, G) > kMaxGridYZ) {
+    return GQA_ERR_UNSUPPORTED;
+  }
   const size_t rows_q = cu_seqlens ? static_cast<size_t>(Tq) : static_cast<size_t>(B) * Tq;
   const size_t rows_k = cu_seqlens ? static_cast<size_t>(Tkv) : static_cast<size_t>(B) * Tkv;
   const size_t nq = rows_q * Hq * d * es, nk = rows_k * Hkv * d * es;
@@ -136,7 +148,17 @@ gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_c
   if (!dtype_ok(dtype) || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return GQA_ERR_UNSUPPORTED;
-  if (B > kMaxGridYZ) return GQA_ERR_UNSUPPORTED;
+  if (dtype == GQA_DTYPE_F32 && B > kMaxGridYZ) return GQA_ERR_UNSUPPORTED;
+  if (dtype == GQA_DTYPE_BF16) {
+    // one flat grid of 256-thread workgroups; cache offsets inside a sequence are 32-bit
+    const int G = Hq / Hkv;
+    const int64_t wgs = static_cast<int64_t>(gqa::decode_num_splits(B, Tkv, Hq, Hkv, d)) * Hkv *
+                        ((G + 15) / 16) * B;
+    const int64_t cache_item_bytes = static_cast<int64_t>(Tkv) * Hkv * d * 2;
+    if (wgs > kMaxFlatWorkgroups256 || cache_item_bytes > INT32_MAX ||
+        static_cast<int64_t>(B) * Hq > INT32_MAX)
+      return GQA_ERR_UNSUPPORTED;
+  }
   const size_t es = esize(dtype);
   const size_t nq = static_cast<size_t>(B) * Hq * d * es;
   const size_t nk = static_cast<size_t>(B) * Tkv * Hkv * d * es;
@@ -182,7 +204,7 @@ gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_c
   a.scale = scale;
   a.ws = static_cast<float*>(workspace);
   a.nsplit = gqa::decode_num_splits(B, Tkv, Hq, Hkv, d);
-  if (Hq > kMaxGridYZ) return GQA_ERR_UNSUPPORTED;
+  a.per = gqa::decode_split_len(Tkv, a.nsplit);
   return from_hip(gqa::launch_decode_bf16(a, stream));
 }
 

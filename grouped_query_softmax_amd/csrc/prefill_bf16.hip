@@ -50,7 +50,9 @@ constexpr int kLdsAhead = 4;           // MFMA operand reads kept in flight
 constexpr int kCols = 256;             // (position, head) columns per workgroup
 
 // Buffer resource word 3 for raw (unformatted) buffer loads on CDNA; loads at or beyond
-// num_records bytes return zeros, which pads the last key tile without branches.
+// num_records bytes return zeros, which pads the last key tile without branches. Only the
+// VGPR offset takes part in that range check (the SGPR offset does not), so tile offsets are
+// added to the VGPR offset.
 constexpr int kBufWord3 = 0x00020000;
 
 // V^T rows hold the 64 keys of a tile permuted inside each group of 16: key 8a + 4h + r
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
       const int soff = kt * kKT * row_bytes;
 #pragma unroll
       for (int i = 0; i < C::kKLoads; ++i) {
-        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(krs, k_src[i], soff, 0);
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(krs, k_src[i] + soff, 0, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) stg[4 * i + e] = w[e];
       }
@@ -217,11 +219,13 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if constexpr (VD == 8) {
-          const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_src + r * row_bytes, soff, 0);
+          const u32x4 w =
+              __builtin_amdgcn_raw_buffer_load_b128(vrs, v_src + r * row_bytes + soff, 0, 0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) stg[VW * r + e] = w[e];
         } else {
-          const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(vrs, v_src + r * row_bytes, soff, 0);
+          const u32x2 w =
+              __builtin_amdgcn_raw_buffer_load_b64(vrs, v_src + r * row_bytes + soff, 0, 0);
           stg[VW * r] = w[0];
           stg[VW * r + 1] = w[1];
         }

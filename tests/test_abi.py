@@ -66,8 +66,10 @@ def test_prefill_validation(lib):
     assert pre(lib, cu=W, msl=0) == B.GQA_ERR_SHAPE
     assert pre(lib, cu=W, Tq=8, Tkv=9, msl=4) == B.GQA_ERR_SHAPE
     assert pre(lib, cu=W, msl=9) == B.GQA_ERR_SHAPE
-    # grid limits
-    assert pre(lib, Bn=70000) == B.GQA_ERR_UNSUPPORTED
+    # launch limits: f32 runs a 3-D grid (at most 65535 items); bf16 addresses one item's keys
+    # and values with 32-bit offsets (at most 2 GiB per item)
+    assert pre(lib, Bn=70000, d=16, dt=F32) == B.GQA_ERR_UNSUPPORTED
+    assert pre(lib, Tkv=1 << 22, Hq=8, Hkv=8) == B.GQA_ERR_UNSUPPORTED
 
 
 def test_decode_validation(lib):
@@ -87,6 +89,8 @@ def test_decode_validation(lib):
     assert dec(ws=W + 4) == B.GQA_ERR_UNSUPPORTED
     assert dec(o=Q) == B.GQA_ERR_ALIAS
     assert dec(ws=O) == B.GQA_ERR_ALIAS
+    # one sequence's cache beyond 2 GiB (32-bit offsets) is refused before anything else
+    assert dec(Tkv=1 << 22) == B.GQA_ERR_UNSUPPORTED
 
 
 def test_fold_validation(lib):

@@ -191,6 +191,10 @@ DECODE_CASES = [
     (5, 4096, 32, 8, 128),
     (4, 300, 12, 4, 128),   # G = 3
     (1, 1, 4, 2, 128),      # a single cached key
+    (2, 33, 16, 1, 128),    # G = 16: every head column used; one key past a tile
+    (1, 5000, 40, 2, 128),  # G = 20: a second, partial chunk of query heads
+    (3, 31, 4, 1, 64),      # shorter than one key tile
+    (2, 8192, 8, 8, 64),    # G = 1 (multi-head)
 ]
 
 
@@ -205,6 +209,21 @@ def test_bf16_decode_vs_oracle(gqa, orc, case):
     torch.cuda.synchronize()
     ref = orc.attention(host_view(q), host_view(k), host_view(v), causal=True)
     assert_bf16_close(to_f64(out), ref, what=str(case))
+
+
+def test_bf16_decode_growing_logits(gqa, orc):
+    """Key norms grow along the cache, so the running maximum keeps rising from tile to tile and
+    the softmax reference is moved many times; the result must still match the two-pass oracle."""
+    say("bf16 decode growing logits")
+    B, Tkv, Hq, Hkv, d = 2, 3000, 8, 2, 128
+    q = workloads.randn_bf16((B, 1, Hq, d), 54)
+    ramp = 0.2 + 4.0 * torch.arange(Tkv, dtype=torch.float32).reshape(1, Tkv, 1, 1) / Tkv
+    k = workloads.to_bf16(workloads.randn_f32((B, Tkv, Hkv, d), 55) * ramp)
+    v = workloads.randn_bf16((B, Tkv, Hkv, d), 56)
+    out = gqa.gqa_attn_decode(to_dev(q), to_dev(k), to_dev(v))
+    torch.cuda.synchronize()
+    ref = orc.attention(host_view(q), host_view(k), host_view(v), causal=True)
+    assert_bf16_close(to_f64(out), ref, what="growing logits")
 
 
 def test_f32_decode_vs_oracle(gqa, orc):
