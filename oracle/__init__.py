@@ -68,10 +68,11 @@ def _bind(lib):
     lib.oracle_fold.restype = I
     lib.oracle_expand.argtypes = [P, P, I64, I64, I, I, I]
     lib.oracle_expand.restype = I
-    lib.oracle_gqa_attention.argtypes = [P, P, P, I, P, I64, I64, I64, I, I, I, D, I, P, I]
+    lib.oracle_gqa_attention.argtypes = [P, P, P, I, P, I64, I64, I64, I, I, I, D, I, P, I, I64,
+                                         I64]
     lib.oracle_gqa_attention.restype = I
     lib.oracle_gqa_attention_rows.argtypes = [P, P, P, I, I64, I64, I64, I, I, I, D, I, P, I, P,
-                                              I64, P]
+                                              I64, P, I64, I64]
     lib.oracle_gqa_attention_rows.restype = I
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = I
@@ -170,20 +171,25 @@ class Oracle:
         return q, k, v, dq, B, Tq, Tkv, Hq, Hkv, d, float(scale), cu, nseq
 
     def attention(self, q, k, v, scale: Optional[float] = None, causal: bool = False,
-                  cu_seqlens=None) -> np.ndarray:
-        """Grouped-query attention forward (``heads_out``): float64 out[B,Tq,Hq,d]."""
+                  cu_seqlens=None, window: int = 0, n_sink: int = 0) -> np.ndarray:
+        """Grouped-query attention forward (``heads_out``): float64 out[B,Tq,Hq,d].
+
+        ``window`` > 0 (causal only) limits each query at position p to keys p-window+1 .. p,
+        plus the ``n_sink`` first keys (course page "Week 7. Attention", step 3)."""
         q, k, v, dt, B, Tq, Tkv, Hq, Hkv, d, scale, cu, nseq = self._common(q, k, v, scale,
                                                                             cu_seqlens)
         out = np.empty((B, Tq, Hq, d), dtype=np.float64)
         rc = self.lib.oracle_gqa_attention(q.ctypes.data, k.ctypes.data, v.ctypes.data, dt,
                                            out.ctypes.data, B, Tq, Tkv, Hq, Hkv, d, scale,
                                            int(bool(causal)),
-                                           cu.ctypes.data if cu is not None else None, nseq)
+                                           cu.ctypes.data if cu is not None else None, nseq,
+                                           int(window), int(n_sink))
         self._check(rc)
         return out
 
     def attention_rows(self, q, k, v, rows: np.ndarray, scale: Optional[float] = None,
-                       causal: bool = False, cu_seqlens=None) -> np.ndarray:
+                       causal: bool = False, cu_seqlens=None, window: int = 0,
+                       n_sink: int = 0) -> np.ndarray:
         """Selected output rows only. rows: int64 [n, 3] of (b, t, head); returns float64 [n, d]."""
         q, k, v, dt, B, Tq, Tkv, Hq, Hkv, d, scale, cu, nseq = self._common(q, k, v, scale,
                                                                             cu_seqlens)
@@ -192,7 +198,8 @@ class Oracle:
         rc = self.lib.oracle_gqa_attention_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, dt,
                                                 B, Tq, Tkv, Hq, Hkv, d, scale, int(bool(causal)),
                                                 cu.ctypes.data if cu is not None else None, nseq,
-                                                r.ctypes.data, r.shape[0], out.ctypes.data)
+                                                r.ctypes.data, r.shape[0], out.ctypes.data,
+                                                int(window), int(n_sink))
         self._check(rc)
         return out
 

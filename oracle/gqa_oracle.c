@@ -109,28 +109,46 @@ int oracle_expand(const double* src, double* dst, int64_t B, int64_t T, int g, i
 
 /* One output row of single-head attention.
  * q: d values; key j's row starts at k + j*kstride (likewise v); out: d values.
- * Scores s_j = scale * sum_c q[c] k[j][c]; two-pass softmax; out = sum_j p_j v_j / sum_j p_j.
- * A row that sees no key (nvis == 0) is defined as zeros. */
+ * Keys 0 .. nvis-1 are candidates; candidate j is visible unless lo <= j is false and j is not
+ * a sink (j >= n_sink), i.e. visible iff j >= lo or j < n_sink (lo = 0: every candidate).
+ * Scores s_j = scale * sum_c q[c] k[j][c]; two-pass softmax over the visible keys;
+ * out = sum_j p_j v_j / sum_j p_j. A row that sees no key is defined as zeros. */
 static void attend_row(const double* q, const double* k, const double* v, int64_t kstride,
-                       int64_t nvis, int d, double scale, double* s, double* out) {
+                       int64_t nvis, int64_t lo, int64_t n_sink, int d, double scale, double* s,
+                       double* out) {
   for (int c = 0; c < d; ++c) out[c] = 0.0;
-  if (nvis <= 0) return;
   double m = -INFINITY;
+  int64_t seen = 0;
   for (int64_t j = 0; j < nvis; ++j) {
+    if (j < lo && j >= n_sink) continue;
     double dot = 0.0;
     for (int c = 0; c < d; ++c) dot += q[c] * k[j * kstride + c];
     s[j] = scale * dot;
     if (s[j] > m) m = s[j];
+    ++seen;
   }
+  if (seen == 0) return;
   double l = 0.0;
   for (int64_t j = 0; j < nvis; ++j) {
+    if (j < lo && j >= n_sink) continue;
     const double p = exp(s[j] - m);
     s[j] = p;
     l += p;
   }
-  for (int64_t j = 0; j < nvis; ++j)
+  for (int64_t j = 0; j < nvis; ++j) {
+    if (j < lo && j >= n_sink) continue;
     for (int c = 0; c < d; ++c) out[c] += s[j] * v[j * kstride + c];
+  }
   for (int c = 0; c < d; ++c) out[c] /= l;
+}
+
+/* First key of the sliding window of query t (bottom-right aligned): with a window of W keys
+ * the query at position p = t + (Tkv - Tq) sees keys p - W + 1 .. p, plus the sink keys
+ * 0 .. n_sink-1 (course page "Week 7. Attention", step 3: sliding window and attention sinks).
+ * window <= 0 means no window (returns 0). */
+static int64_t window_lo(int64_t t, int64_t Tq, int64_t Tkv, int64_t window) {
+  if (window <= 0) return 0;
+  return t + (Tkv - Tq) - window + 1;
 }
 
 /* Number of keys query t of a (Tq, Tkv) item sees. */
@@ -187,8 +205,10 @@ static int make_items(int64_t B, int64_t Tq, int64_t Tkv, const int32_t* cu, int
  * expanded head. Hkv == Hq reproduces per-head multi-head attention exactly. */
 int oracle_gqa_attention(const void* q, const void* k, const void* v, int dtype_in, double* out,
                          int64_t B, int64_t Tq, int64_t Tkv, int Hq, int Hkv, int d, double scale,
-                         int causal, const int32_t* cu_seqlens, int nseq) {
+                         int causal, const int32_t* cu_seqlens, int nseq, int64_t window,
+                         int64_t n_sink) {
   if (Hq <= 0 || Hkv <= 0 || d <= 0) return ORACLE_ERR_SHAPE;
+  if ((window > 0 || n_sink > 0) && !causal) return ORACLE_ERR_SHAPE;  /* windows are causal */
   if (Hq % Hkv != 0) return ORACLE_ERR_GROUPING;
   item_t* items = NULL;
   int nitems = 0;
@@ -245,8 +265,9 @@ int oracle_gqa_attention(const void* q, const void* k, const void* v, int dtype_
         /* head h of the expanded K/V: rows k_row0.. of the [krows][Hq][d] tables */
         const double* kh = &ke[(I.k_row0 * Hq + h) * (int64_t)d];
         const double* vh = &ve[(I.k_row0 * Hq + h) * (int64_t)d];
-        attend_row(qh, kh, vh, (int64_t)Hq * d, visible_keys(t, I.Tq, I.Tkv, causal), d, scale,
-                   sc, &out[(row * Hq + h) * (int64_t)d]);
+        attend_row(qh, kh, vh, (int64_t)Hq * d, visible_keys(t, I.Tq, I.Tkv, causal),
+                   window_lo(t, I.Tq, I.Tkv, window), n_sink, d, scale, sc,
+                   &out[(row * Hq + h) * (int64_t)d]);
       }
     }
     free(qh); free(sc);
@@ -266,8 +287,10 @@ int oracle_gqa_attention(const void* q, const void* k, const void* v, int dtype_
 int oracle_gqa_attention_rows(const void* q, const void* k, const void* v, int dtype_in,
                               int64_t B, int64_t Tq, int64_t Tkv, int Hq, int Hkv, int d,
                               double scale, int causal, const int32_t* cu_seqlens, int nseq,
-                              const int64_t* rows, int64_t nrows, double* out) {
+                              const int64_t* rows, int64_t nrows, double* out, int64_t window,
+                              int64_t n_sink) {
   if (Hq <= 0 || Hkv <= 0 || d <= 0) return ORACLE_ERR_SHAPE;
+  if ((window > 0 || n_sink > 0) && !causal) return ORACLE_ERR_SHAPE;  /* windows are causal */
   if (Hq % Hkv != 0) return ORACLE_ERR_GROUPING;
   item_t* items = NULL;
   int nitems = 0;
@@ -322,8 +345,8 @@ int oracle_gqa_attention_rows(const void* q, const void* k, const void* v, int d
           }
         const int64_t row = I.q_row0 + t;
         for (int c = 0; c < d; ++c) qh[c] = widen(q, dtype_in, (row * Hq + h) * (int64_t)d + c);
-        attend_row(qh, kh, vh, d, visible_keys(t, I.Tq, I.Tkv, causal), d, scale, sc,
-                   &out[r * d]);
+        attend_row(qh, kh, vh, d, visible_keys(t, I.Tq, I.Tkv, causal),
+                   window_lo(t, I.Tq, I.Tkv, window), n_sink, d, scale, sc, &out[r * d]);
       }
     }
     free(qh); free(kh); free(vh); free(sc);

@@ -16,7 +16,8 @@ Sources of the facts (page, section):
   * Course page ("Week 7. Attention"): step 1 (scale 1/sqrt(d); -inf before softmax so each row
     still sums to one over the past), step 2 (32/8 heads -> 4x smaller cache, MQA 32x),
     "typical errors" (repeat_kv must repeat adjacently; attention must be causal), and the
-    check against torch's scaled_dot_product_attention.
+    check against torch's scaled_dot_product_attention; step 3 (sliding window and attention
+    sinks: the window bounds what a query sees, the first tokens stay visible).
 """
 from __future__ import annotations
 
@@ -325,6 +326,70 @@ def check_bf16_widening_is_exact(orc):
     assert np.array_equal(a, b)
 
 
+# ------------------------------------------------------------------------------------------------
+# course step 3: sliding window and attention sinks
+# ------------------------------------------------------------------------------------------------
+
+def _window_mask(Tq, Tkv, window, n_sink):
+    """Boolean [Tq, Tkv] table built from the definition: query t sits at p = t + Tkv - Tq and
+    sees key j iff j <= p and (j > p - window or j < n_sink)."""
+    m = np.zeros((Tq, Tkv), dtype=bool)
+    for t in range(Tq):
+        p = t + Tkv - Tq
+        for j in range(Tkv):
+            m[t, j] = j <= p and (j > p - window or j < n_sink)
+    return m
+
+
+def check_window_matches_masked_sdpa(orc):
+    """Library cross-check: torch CPU fp64 scaled_dot_product_attention with an explicit mask
+    table (K/V expanded by repeat_interleave), for windows with and without sink keys."""
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(18)
+    for (Tq, Tkv, W, S) in [(9, 9, 3, 0), (9, 9, 3, 2), (5, 12, 4, 1), (12, 12, 1, 3),
+                            (7, 7, 20, 0), (1, 30, 8, 4), (16, 16, 5, 5)]:
+        for Hq, Hkv in ((4, 2), (3, 1), (2, 2)):
+            q = rng.standard_normal((2, Tq, Hq, 8))
+            k = rng.standard_normal((2, Tkv, Hkv, 8))
+            v = rng.standard_normal((2, Tkv, Hkv, 8))
+            got = orc.attention(q, k, v, causal=True, window=W, n_sink=S)
+            G = Hq // Hkv
+            qt = torch.from_numpy(q).permute(0, 2, 1, 3).contiguous()
+            kt = torch.from_numpy(k).repeat_interleave(G, dim=2).permute(0, 2, 1, 3).contiguous()
+            vt = torch.from_numpy(v).repeat_interleave(G, dim=2).permute(0, 2, 1, 3).contiguous()
+            mask = torch.from_numpy(_window_mask(Tq, Tkv, W, S))
+            ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+            err = np.max(np.abs(got - ref.permute(0, 2, 1, 3).numpy()))
+            assert err <= 1e-12, (Tq, Tkv, W, S, Hq, Hkv, err)
+
+
+def check_window_limits(orc):
+    """A window covering the whole past (or sinks covering it) is plain causal attention; a
+    one-key window returns each query's own value row; windows need the causal flag."""
+    rng = _rng(19)
+    q = rng.standard_normal((2, 6, 4, 8)); k = rng.standard_normal((2, 10, 2, 8))
+    v = rng.standard_normal((2, 10, 2, 8))
+    causal = orc.attention(q, k, v, causal=True)
+    assert np.array_equal(orc.attention(q, k, v, causal=True, window=10), causal)
+    assert np.array_equal(orc.attention(q, k, v, causal=True, window=3, n_sink=10), causal)
+    one = orc.attention(q, k, v, causal=True, window=1)
+    for t in range(6):
+        for h in range(4):
+            assert np.array_equal(one[:, t, h], v[:, t + 4, h // 2]), (t, h)
+    rows = np.array([(0, 0, 0), (1, 5, 3), (0, 3, 2)], dtype=np.int64)
+    full = orc.attention(q, k, v, causal=True, window=3, n_sink=2)
+    got = orc.attention_rows(q, k, v, rows, causal=True, window=3, n_sink=2)
+    for r, (b, t, h) in enumerate(rows):
+        assert np.array_equal(got[r], full[b, t, h]), (b, t, h)
+    try:
+        orc.attention(q, k, v, causal=False, window=3)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a window without the causal flag must be rejected")
+
+
 ALL_CHECKS = [
     check_group_of_worked_example,
     check_group_of_rejects_uneven,
@@ -338,6 +403,8 @@ ALL_CHECKS = [
     check_closed_forms,
     check_large_inputs_do_not_overflow,
     check_causality,
+    check_window_matches_masked_sdpa,
+    check_window_limits,
     check_bottom_right_alignment,
     check_g_equals_h_is_mha,
     check_packed_equals_separate,

@@ -29,6 +29,10 @@ MUTANTS = {
     "causal_top_left": ("int64_t n = t + (Tkv - Tq) + 1;", "int64_t n = t + 1;"),
     # softmax not normalised
     "no_normalisation": ("for (int c = 0; c < d; ++c) out[c] /= l;", "(void)l;"),
+    # course step 3: window one key too wide
+    "window_off_by_one": ("return t + (Tkv - Tq) - window + 1;", "return t + (Tkv - Tq) - window;"),
+    # course step 3: sink keys dropped from the window
+    "sinks_ignored": ("if (j < lo && j >= n_sink) continue;", "if (j < lo) continue;"),
     # value rows weighted by the wrong key
     "value_index_shift": ("out[c] += s[j] * v[j * kstride + c];",
                           "out[c] += s[j] * v[((j + 1) % nvis) * kstride + c];"),
