@@ -48,8 +48,21 @@ def visible_pairs(Tq, Tkv, causal):
     return Tq * (off + 1) + Tq * (Tq - 1) // 2
 
 
+def visible_pairs_window(T, window, n_sink):
+    """Unmasked (query, key) pairs of one head of a square causal item with a sliding window of
+    `window` keys plus `n_sink` sink keys below it."""
+    pairs = 0
+    for t in range(T):
+        below = t + 1 - window  # keys 0 .. below-1 lie under the window
+        pairs += min(t + 1, window) + (min(n_sink, below) if below > 0 else 0)
+    return pairs
+
+
 def prefill_flops(w):
-    if w.seqlens is not None:
+    if w.window > 0:
+        assert w.seqlens is None and w.Tq == w.Tkv
+        pairs = w.B * visible_pairs_window(w.Tq, w.window, w.n_sink)
+    elif w.seqlens is not None:
         pairs = sum(visible_pairs(n, n, w.causal) for n in w.seqlens)
     else:
         pairs = w.B * visible_pairs(w.Tq, w.Tkv, w.causal)
@@ -111,7 +124,10 @@ def bench_prefill(gqa, w, steps, warmup, torch, seed):
     msl = max(w.seqlens) if w.seqlens else None
 
     def step():
-        gqa.gqa_attn_prefill(q, k, v, causal=w.causal, cu_seqlens=cu, max_seqlen=msl, out=out)
+        if w.window > 0:
+            gqa.gqa_attn_prefill_window(q, k, v, window=w.window, n_sink=w.n_sink, out=out)
+        else:
+            gqa.gqa_attn_prefill(q, k, v, causal=w.causal, cu_seqlens=cu, max_seqlen=msl, out=out)
 
     ms, wall = time_launches(step, steps, warmup, torch)
     flops = prefill_flops(w)
@@ -132,21 +148,28 @@ def bench_decode(gqa, w, steps, warmup, torch, seed):
     ws = torch.empty(gqa.gqa_attn_decode_workspace_bytes(w.B, w.Tkv, w.Hq, w.Hkv, w.d),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty_like(sets[0][0])
+    lens = None
+    if w.cache_lens is not None:
+        lens = torch.tensor(w.cache_lens, dtype=torch.int32, device="cuda")
     it = [0]
 
     def step():
         q, k, v = sets[it[0] & 1]
         it[0] += 1
-        gqa.gqa_attn_decode(q, k, v, workspace=ws, out=out)
+        if lens is not None:
+            gqa.gqa_attn_decode_ragged(q, k, v, cache_lens=lens, workspace=ws, out=out)
+        else:
+            gqa.gqa_attn_decode(q, k, v, workspace=ws, out=out)
 
     ms, wall = time_launches(step, steps, warmup, torch)
-    kv_bytes = 2 * w.B * w.Tkv * w.Hkv * w.d * 2
+    entries = sum(w.cache_lens) if w.cache_lens is not None else w.B * w.Tkv
+    kv_bytes = 2 * entries * w.Hkv * w.d * 2
     qo_bytes = 2 * w.B * w.Hq * w.d * 2
     avg = sum(ms) / len(ms)
     gbs = (kv_bytes + qo_bytes) / (avg * 1e-3) / 1e9
     return {"workload": w.name, "bytes_per_launch": kv_bytes + qo_bytes, "avg_ms": avg,
             "min_ms": min(ms), "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "wall_s": wall,
-            "traffic": traffic_for("decode")}
+            "traffic": traffic_for("decode") if w.cache_lens is None else None}
 
 
 COPY_BYTES = 1 << 30
@@ -216,7 +239,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "mqa", "varlen", "copy"],
+    ap.add_argument("--only", choices=["prefill", "decode", "mqa", "varlen", "window",
+                                       "ragged", "copy"],
                     default=None,
                     help="time a single workload (for profiling); still prints one JSON line. "
                          "'copy' times a plain 1 GiB device copy, the calibration kernel for "
@@ -262,16 +286,26 @@ def main():
         vl["frac_mfma"] = vl["tflops"] / PEAK_BF16_TFLOPS
         extra["varlen_prefill"] = vl
         log(f"varlen: {vl['avg_ms']:.3f} ms, {vl['tflops']:.1f} TFLOP/s")
+    if args.only == "window" or args.all:
+        wp, _ = bench_prefill(gqa, workloads.WINDOW_PREFILL, args.steps, args.warmup, torch, 6000)
+        wp["frac_mfma"] = wp["tflops"] / PEAK_BF16_TFLOPS
+        extra["window_prefill"] = wp
+        log(f"window prefill: {wp['avg_ms'] * 1e3:.1f} us, {wp['tflops']:.1f} TFLOP/s")
+    if args.only == "ragged" or args.all:
+        rd = bench_decode(gqa, workloads.RAGGED_DECODE, args.steps, args.warmup, torch, 7000)
+        extra["ragged_decode"] = rd
+        log(f"ragged decode: {rd['avg_ms'] * 1e3:.1f} us, {rd['gbs']:.0f} GB/s")
     if args.only == "decode" or (args.only is None and not args.no_decode):
         dec = bench_decode(gqa, workloads.DECODE, args.steps, args.warmup, torch, 3000)
         extra["decode"] = dec
         log(f"decode: {dec['avg_ms'] * 1e3:.1f} us, {dec['gbs']:.0f} GB/s")
     sha = kernel_source_sha("prefill")
     metric = "GQA prefill TFLOPS (% MFMA peak); decode KV GB/s (% HBM peak)"
-    if pre is None and args.only in ("mqa", "varlen"):
-        key = "mqa_prefill" if args.only == "mqa" else "varlen_prefill"
+    if pre is None and args.only in ("mqa", "varlen", "window"):
+        key, w = {"mqa": ("mqa_prefill", workloads.MQA_PREFILL),
+                  "varlen": ("varlen_prefill", workloads.VARLEN_PREFILL),
+                  "window": ("window_prefill", workloads.WINDOW_PREFILL)}[args.only]
         pre = extra.pop(key)
-        w = workloads.MQA_PREFILL if args.only == "mqa" else workloads.VARLEN_PREFILL
     if pre is not None:
         value, unit = pre["tflops"], "TFLOP/s"
         ms_per_step = pre["avg_ms"]
@@ -286,8 +320,11 @@ def main():
                   "parallelism": "single-gpu"}
         if w.seqlens:
             config["seqlens"] = list(w.seqlens)
+        if w.window > 0:
+            config["window"], config["n_sink"] = w.window, w.n_sink
     else:
-        dec = extra.pop("decode")
+        dw = workloads.RAGGED_DECODE if args.only == "ragged" else workloads.DECODE
+        dec = extra.pop("ragged_decode" if args.only == "ragged" else "decode")
         value, unit = dec["gbs"], "GB/s"
         ms_per_step = dec["avg_ms"]
         roofline = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -295,7 +332,6 @@ def main():
                     "kernel": "decode_split_kernel<128>", "bytes_per_launch":
                     dec["bytes_per_launch"], "avg_launch_ms": dec["avg_ms"],
                     "kernel_source_sha": kernel_source_sha("decode")}
-        dw = workloads.DECODE
         config = {"workload": dw.name, "B": dw.B, "Tkv": dw.Tkv, "Hq": dw.Hq, "Hkv": dw.Hkv,
                   "d": dw.d, "parallelism": "single-gpu"}
     line = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,

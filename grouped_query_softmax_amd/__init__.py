@@ -8,8 +8,10 @@ from ._binding import (  # noqa: F401
     GQAError,
     GQAValueError,
     gqa_attn_decode,
+    gqa_attn_decode_ragged,
     gqa_attn_decode_workspace_bytes,
     gqa_attn_prefill,
+    gqa_attn_prefill_window,
     gqa_fold_kv,
     gqa_status_string,
     header_functions,

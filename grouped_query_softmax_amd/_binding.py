@@ -55,6 +55,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_attn_decode_workspace_bytes.restype = SZ
     lib.gqa_attn_decode.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, SZ, I, P]
     lib.gqa_attn_decode.restype = I
+    lib.gqa_attn_prefill_window.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, P, I, I, P]
+    lib.gqa_attn_prefill_window.restype = I
+    lib.gqa_attn_decode_ragged.argtypes = [P, P, P, P, I, I, I, I, I, F, P, I, I, P, SZ, I, P]
+    lib.gqa_attn_decode_ragged.restype = I
     lib.gqa_fold_kv.argtypes = [P, P, I, I, I, I, I, I, P]
     lib.gqa_fold_kv.restype = I
     lib.gqa_status_string.argtypes = [I]
@@ -116,11 +120,7 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
-def gqa_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
-                     scale: Optional[float] = None, cu_seqlens: Optional[torch.Tensor] = None,
-                     max_seqlen: Optional[int] = None, out: Optional[torch.Tensor] = None,
-                     stream=None) -> torch.Tensor:
-    """q [B,Tq,Hq,d], k/v [B,Tkv,Hkv,d] (or [1,total,H,d] with int32 device cu_seqlens)."""
+def _prefill_args(q, k, v, scale, cu_seqlens, max_seqlen, out):
     q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("expected q[B,Tq,Hq,d] and k, v[B,Tkv,Hkv,d]")
@@ -143,16 +143,37 @@ def gqa_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: 
         if max_seqlen is None:
             max_seqlen = int((cu[1:] - cu[:-1]).max().item())
         cu_ptr, msl = cu.data_ptr(), int(max_seqlen)
-        cu_seqlens = cu
     if out is None:
         out = torch.empty_like(q)
-    else:
-        if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-            raise ValueError("out must be a contiguous tensor shaped and typed like q")
-    rc = _lib.gqa_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                               nseq, Tq, Tkv, Hq, Hkv, d, float(scale), int(bool(causal)),
-                               cu_ptr, msl, _dtype_code(q), _stream(stream))
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    return q, k, v, out, (nseq, Tq, Tkv, Hq, Hkv, d, float(scale)), cu_ptr, msl
+
+
+def gqa_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                     scale: Optional[float] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                     max_seqlen: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """q [B,Tq,Hq,d], k/v [B,Tkv,Hkv,d] (or [1,total,H,d] with int32 device cu_seqlens)."""
+    q, k, v, out, dims, cu_ptr, msl = _prefill_args(q, k, v, scale, cu_seqlens, max_seqlen, out)
+    rc = _lib.gqa_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), *dims,
+                               int(bool(causal)), cu_ptr, msl, _dtype_code(q), _stream(stream))
     _check(rc, "gqa_attn_prefill")
+    return out
+
+
+def gqa_attn_prefill_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: int,
+                            n_sink: int = 0, scale: Optional[float] = None,
+                            cu_seqlens: Optional[torch.Tensor] = None,
+                            max_seqlen: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """Causal prefill where the query at position p sees keys p-window+1 .. p and the first
+    n_sink keys (window 0: plain causal). Shapes as for :func:`gqa_attn_prefill`; bf16 only."""
+    q, k, v, out, dims, cu_ptr, msl = _prefill_args(q, k, v, scale, cu_seqlens, max_seqlen, out)
+    rc = _lib.gqa_attn_prefill_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      *dims, int(window), int(n_sink), cu_ptr, msl,
+                                      _dtype_code(q), _stream(stream))
+    _check(rc, "gqa_attn_prefill_window")
     return out
 
 
@@ -160,12 +181,7 @@ def gqa_attn_decode_workspace_bytes(B: int, Tkv: int, Hq: int, Hkv: int, d: int)
     return int(_lib.gqa_attn_decode_workspace_bytes(B, Tkv, Hq, Hkv, d))
 
 
-def gqa_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                    scale: Optional[float] = None, causal: bool = False,
-                    workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                    stream=None) -> torch.Tensor:
-    """q [B,1,Hq,d], caches [B,Tkv,Hkv,d]; workspace: a device tensor of at least
-    gqa_attn_decode_workspace_bytes(...) bytes (allocated here when None)."""
+def _decode_args(q, k_cache, v_cache, scale, workspace, out):
     q, k, v = _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache")
     if q.dim() != 4 or q.shape[1] != 1 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("expected q[B,1,Hq,d] and k_cache, v_cache[B,Tkv,Hkv,d]")
@@ -185,10 +201,44 @@ def gqa_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     if out is None:
         out = torch.empty_like(q)
-    rc = _lib.gqa_attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Tkv,
-                              Hq, Hkv, d, float(scale), int(bool(causal)), ws_ptr, ws_bytes,
-                              _dtype_code(q), _stream(stream))
+    return q, k, v, out, (B, Tkv, Hq, Hkv, d, float(scale)), ws_ptr, ws_bytes, workspace
+
+
+def gqa_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    scale: Optional[float] = None, causal: bool = False,
+                    workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """q [B,1,Hq,d], caches [B,Tkv,Hkv,d]; workspace: a device tensor of at least
+    gqa_attn_decode_workspace_bytes(...) bytes (allocated here when None)."""
+    q, k, v, out, dims, ws_ptr, ws_bytes, _ = _decode_args(q, k_cache, v_cache, scale, workspace,
+                                                           out)
+    rc = _lib.gqa_attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), *dims,
+                              int(bool(causal)), ws_ptr, ws_bytes, _dtype_code(q),
+                              _stream(stream))
     _check(rc, "gqa_attn_decode")
+    return out
+
+
+def gqa_attn_decode_ragged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           cache_lens: Optional[torch.Tensor] = None, window: int = 0,
+                           n_sink: int = 0, scale: Optional[float] = None,
+                           workspace: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode where sequence b uses cache entries 0 .. cache_lens[b]-1 (int32 device tensor;
+    None: all), optionally limited to its last `window` entries plus the first n_sink; bf16."""
+    q, k, v, out, dims, ws_ptr, ws_bytes, _ = _decode_args(q, k_cache, v_cache, scale, workspace,
+                                                           out)
+    lens_ptr = None
+    if cache_lens is not None:
+        lens = _dev(cache_lens, "cache_lens")
+        if lens.dtype != torch.int32 or lens.dim() != 1 or lens.numel() != q.shape[0]:
+            raise ValueError("cache_lens must be a 1-D int32 device tensor with one entry per "
+                             "sequence")
+        lens_ptr = lens.data_ptr()
+    rc = _lib.gqa_attn_decode_ragged(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     *dims, lens_ptr, int(window), int(n_sink), ws_ptr, ws_bytes,
+                                     _dtype_code(q), _stream(stream))
+    _check(rc, "gqa_attn_decode_ragged")
     return out
 
 

@@ -97,6 +97,8 @@ struct PrefillArgs {
   int Hq, Hkv, d;
   float scale;
   int causal;
+  int window;  // > 0: causal sliding window of this many keys (0: none)
+  int n_sink;  // keys 0 .. n_sink-1 stay visible below the window
 };
 
 struct DecodeArgs {
@@ -109,6 +111,9 @@ struct DecodeArgs {
   float* ws;      // partial results
   int nsplit;     // splits of the cache
   int per;        // keys per split (a multiple of the kernel's key tile)
+  const int32_t* lens;  // device per-sequence cache lengths, or nullptr (all Tkv)
+  int window;     // > 0: the query sees only the last `window` cache entries (plus sinks)
+  int n_sink;     // cache entries 0 .. n_sink-1 stay visible below the window
 };
 
 // Launchers (return hipSuccess or the launch error). Shapes have been validated by the caller.

@@ -19,6 +19,10 @@
 //   * O^T += V^T P^T: V comes back from LDS transposed with ds_read_b64_tr_b16 (4 keys of one
 //     dimension per lane), P^T is the score accumulator rounded to bf16 in place, with the
 //     contraction order of keys following the accumulator layout.
+// Ragged caches and sliding windows (course page "Week 7. Attention", step 3): sequence b uses
+// its first lens[b] cache entries; with a window it sees only the last `window` of them plus the
+// first n_sink (sink) entries. The visible entries form one list (sinks, then window) over which
+// the splits and tiles run, so nothing outside it is read.
 // Each lane owns one query head (one accumulator column), so the softmax reference and the
 // rescale factor are per lane; the row maximum of a tile is combined over the 4 lane groups that
 // hold that head's keys. Online softmax in the base-2 domain with a lazily moved reference
@@ -103,9 +107,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int r16 = lane & 15;
   const int g = lane >> 4;
+  // The visible cache entries of this sequence, as one list: the sink entries below the window
+  // [0, a_end) followed by the window [w_start, L). Splits and tiles run over list positions.
+  const int L = a.lens ? min(max(a.lens[b], 1), a.Tkv) : a.Tkv;
+  const int w_start = a.window > 0 ? max(0, L - a.window) : 0;
+  const int a_end = min(a.n_sink, w_start);
+  const int nvis = a_end + (L - w_start);
   const int kb = split * a.per;
-  const int nkeys = min(a.Tkv, kb + a.per) - kb;  // >= 1 by the split plan
-  const int ntile = (nkeys + kTK - 1) / kTK;
+  const int nkeys = min(nvis, kb + a.per) - kb;  // <= 0: nothing of this sequence in the split
+  const int ntile = nkeys > 0 ? (nkeys + kTK - 1) / kTK : 0;
   const int row_bytes = a.Hkv * D * 2;
   const float sl2 = a.scale * kLog2e;
 
@@ -124,12 +134,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
     }
   }
 
-  const int64_t split_elem = ((static_cast<int64_t>(b) * a.Tkv + kb) * a.Hkv + kvh) * D;
-  const int nrec = (nkeys - 1) * row_bytes + D * 2;
+  const int64_t seq_elem = (static_cast<int64_t>(b) * a.Tkv * a.Hkv + kvh) * D;
+  const int nrec = (L - 1) * row_bytes + D * 2;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k) + split_elem), 0, nrec, kBufWord3);
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k) + seq_elem), 0, nrec, kBufWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.v) + split_elem), 0, nrec, kBufWord3);
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.v) + seq_elem), 0, nrec, kBufWord3);
+  const int vend = kb + max(nkeys, 0);    // list positions of this split: [kb, vend)
+  const int shift = w_start - a_end;      // list position -> cache entry, past the sinks
 
   // Loads: kLPR lanes cover one whole key row (16 bytes each), so every load instruction reads
   // whole 128-byte lines; K and V go to this wave's LDS tiles as they arrived. The K operand is
@@ -138,7 +150,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   char* vt = smem + wave * C::kTileBytes;
   char* kt = vt + kTK * C::kPitch;
   const int lrow = lane / C::kLPR, lcol = lane % C::kLPR;
-  const int foff = lrow * row_bytes + 16 * lcol;
   const int k_wr = lrow * C::kKPitch + 16 * lcol;
   const int v_wr = lrow * C::kPitch + 16 * lcol;
   const int k_rd = r16 * C::kKPitch + 16 * g;
@@ -149,14 +160,19 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   for (int nt = 0; nt < NDT; ++nt) acc_o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Tiles at or past ntile read as zeros (past num_records) and are never processed.
+  // Rows past the split's list positions are pointed past num_records and read as zeros; tiles
+  // at or past ntile are never processed.
   auto load = [&](u32x4 (&kr)[2][NS], u32x4 (&vr)[2][NS], int t) {
-    const int soff = t * kTK * row_bytes;
+    const int v0 = kb + t * kTK + lrow;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int off = foff + soff + (blk * NS + s) * C::kRPI * row_bytes;
+        const int vpos = v0 + (blk * NS + s) * C::kRPI;
+        const int entry = vpos < a_end ? vpos : vpos + shift;
+        const int off = vpos < vend
+                            ? static_cast<int>(static_cast<unsigned>(entry) * row_bytes) + 16 * lcol
+                            : nrec;
         kr[blk][s] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, kStreamLoad);
         vr[blk][s] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kStreamLoad);
       }
@@ -200,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
     const bool move = mx > m_run + kRescaleSlack;
     if (__any(move)) {
       const float m_new = move ? mx : m_run;
-      const float alpha = fast_exp2(m_run - m_new);
+      const float alpha = move ? fast_exp2(m_run - m_new) : 1.f;
       l_run *= alpha;
 #pragma unroll
       for (int nt = 0; nt < NDT; ++nt)

@@ -71,15 +71,17 @@ const char* gqa_status_string(gqa_status_t s) {
   return "unknown status";
 }
 
-gqa_status_t gqa_attn_prefill(const void* q, const void* k, const void* v, void* out, int B,
-                              int Tq, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
-                              const int32_t* cu_seqlens, int max_seqlen, gqa_dtype_t dtype,
-                              hipStream_t stream) {
+static gqa_status_t prefill_impl(const void* q, const void* k, const void* v, void* out, int B,
+                                 int Tq, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
+                                 int window, int n_sink, const int32_t* cu_seqlens, int max_seqlen,
+                                 gqa_dtype_t dtype, hipStream_t stream) {
   if (!q || !k || !v || !out) return GQA_ERR_NULL_PTR;
   if (B <= 0 || Tq <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_SHAPE;
   if (!isfinite(scale) || !(scale > 0.f)) return GQA_ERR_SHAPE;
+  if (window < 0 || n_sink < 0) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0) return GQA_ERR_GROUPING;
   if (!dtype_ok(dtype) || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
+  if ((window > 0 || n_sink > 0) && dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return GQA_ERR_UNSUPPORTED;
   int nitems, max_tq;
@@ -127,8 +129,26 @@ gqa_status_t gqa_attn_prefill(const void* q, const void* k, const void* v, void*
   a.d = d;
   a.scale = scale;
   a.causal = causal ? 1 : 0;
+  a.window = window;
+  a.n_sink = window > 0 ? n_sink : 0;  // without a window every past key is visible anyway
   return from_hip(dtype == GQA_DTYPE_BF16 ? gqa::launch_prefill_bf16(a, stream)
                                           : gqa::launch_prefill_f32(a, stream));
+}
+
+gqa_status_t gqa_attn_prefill(const void* q, const void* k, const void* v, void* out, int B,
+                              int Tq, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
+                              const int32_t* cu_seqlens, int max_seqlen, gqa_dtype_t dtype,
+                              hipStream_t stream) {
+  return prefill_impl(q, k, v, out, B, Tq, Tkv, Hq, Hkv, d, scale, causal, 0, 0, cu_seqlens,
+                      max_seqlen, dtype, stream);
+}
+
+gqa_status_t gqa_attn_prefill_window(const void* q, const void* k, const void* v, void* out,
+                                     int B, int Tq, int Tkv, int Hq, int Hkv, int d, float scale,
+                                     int window, int n_sink, const int32_t* cu_seqlens,
+                                     int max_seqlen, gqa_dtype_t dtype, hipStream_t stream) {
+  return prefill_impl(q, k, v, out, B, Tq, Tkv, Hq, Hkv, d, scale, 1, window, n_sink, cu_seqlens,
+                      max_seqlen, dtype, stream);
 }
 
 size_t gqa_attn_decode_workspace_bytes(int B, int Tkv, int Hq, int Hkv, int d) {
@@ -136,16 +156,18 @@ size_t gqa_attn_decode_workspace_bytes(int B, int Tkv, int Hq, int Hkv, int d) {
   return gqa::decode_workspace_bytes(B, Tkv, Hq, Hkv, d);
 }
 
-gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
-                             int B, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
-                             void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
-                             hipStream_t stream) {
-  (void)causal;  // a single query at the last position sees the whole cache
+static gqa_status_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                                void* out, int B, int Tkv, int Hq, int Hkv, int d, float scale,
+                                const int32_t* cache_lens, int window, int n_sink, void* workspace,
+                                size_t workspace_bytes, gqa_dtype_t dtype, hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !out) return GQA_ERR_NULL_PTR;
   if (B <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_SHAPE;
   if (!isfinite(scale) || !(scale > 0.f)) return GQA_ERR_SHAPE;
+  if (window < 0 || n_sink < 0) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0) return GQA_ERR_GROUPING;
   if (!dtype_ok(dtype) || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
+  if ((cache_lens || window > 0 || n_sink > 0) && dtype != GQA_DTYPE_BF16)
+    return GQA_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return GQA_ERR_UNSUPPORTED;
   if (dtype == GQA_DTYPE_F32 && B > kMaxGridYZ) return GQA_ERR_UNSUPPORTED;
@@ -183,6 +205,8 @@ gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_c
     a.d = d;
     a.scale = scale;
     a.causal = 0;
+    a.window = 0;
+    a.n_sink = 0;
     return from_hip(gqa::launch_prefill_f32(a, stream));
   }
   const size_t need = gqa::decode_workspace_bytes(B, Tkv, Hq, Hkv, d);
@@ -205,7 +229,28 @@ gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_c
   a.ws = static_cast<float*>(workspace);
   a.nsplit = gqa::decode_num_splits(B, Tkv, Hq, Hkv, d);
   a.per = gqa::decode_split_len(Tkv, a.nsplit);
+  a.lens = cache_lens;
+  a.window = window;
+  a.n_sink = window > 0 ? n_sink : 0;
   return from_hip(gqa::launch_decode_bf16(a, stream));
+}
+
+gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+                             int B, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
+                             void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
+                             hipStream_t stream) {
+  (void)causal;  // a single query at the last position sees the whole cache
+  return decode_impl(q, k_cache, v_cache, out, B, Tkv, Hq, Hkv, d, scale, nullptr, 0, 0,
+                     workspace, workspace_bytes, dtype, stream);
+}
+
+gqa_status_t gqa_attn_decode_ragged(const void* q, const void* k_cache, const void* v_cache,
+                                    void* out, int B, int Tmax, int Hq, int Hkv, int d,
+                                    float scale, const int32_t* cache_lens, int window,
+                                    int n_sink, void* workspace, size_t workspace_bytes,
+                                    gqa_dtype_t dtype, hipStream_t stream) {
+  return decode_impl(q, k_cache, v_cache, out, B, Tmax, Hq, Hkv, d, scale, cache_lens, window,
+                     n_sink, workspace, workspace_bytes, dtype, stream);
 }
 
 gqa_status_t gqa_fold_kv(const void* src, void* dst, int B, int T, int H, int g, int d,

@@ -25,7 +25,9 @@
 //     which is exact (the final O / l uses one reference throughout) and skips the O rescale.
 //     p is then at most 2^kRescaleSlack, far inside fp32 and bf16 range.
 //   * Causal: key tiles past the workgroup's last visible key are never loaded; tiles crossing
-//     the diagonal are masked per element with bottom-right alignment. For balance each
+//     the diagonal are masked per element with bottom-right alignment. With a sliding window
+//     (course page "Week 7. Attention", step 3) only the sink tiles and the tiles from the
+//     window start of the workgroup's first row are visited, and the window edge is masked. For balance each
 //     workgroup takes the query tile pair (i, n-1-i), so every workgroup does the same number of
 //     key tiles.
 //   * Launch order: key/value heads fastest, then query tiles, then batch items / packed
@@ -187,7 +189,17 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
 
     const int last = min(p0 + pos_per_wg, tq) - 1;
     const int kend = a.causal ? min(tkv, last + off + 1) : tkv;
-    const int nkt = (kend + kKT - 1) / kKT;
+    // Key tiles of this query tile: with a sliding window, the sink tiles [0, nst) and then the
+    // window tiles from wt0 up; loop step t works on key tile ktile(t). Steps past the end map
+    // past kend, where the loads return zeros.
+    const int kt_end = (kend + kKT - 1) / kKT;
+    int nst = 0, wt0 = 0;
+    if (a.window > 0) {
+      wt0 = max(0, p0 + off - a.window + 1) / kKT;
+      nst = min((min(a.n_sink, kend) + kKT - 1) / kKT, wt0);
+    }
+    const int nkt = nst + (kt_end - wt0);
+    auto ktile = [&](int t) { return t < nst ? t : t - nst + wt0; };
     const int nrec = (kend - 1) * row_bytes + D * 2;
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kbase_ptr), 0, nrec, kBufWord3);
@@ -197,8 +209,8 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
     // one staging register file per thread: group B stages K tiles, group A stages V tiles
     constexpr int kStageRegs = (4 * C::kKLoads > 4 * VW) ? 4 * C::kKLoads : 4 * VW;
     uint32_t stg[kStageRegs];
-    auto load_k = [&](int kt) {
-      const int soff = kt * kKT * row_bytes;
+    auto load_k = [&](int t) {
+      const int soff = ktile(t) * kKT * row_bytes;
 #pragma unroll
       for (int i = 0; i < C::kKLoads; ++i) {
         const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(krs, k_src[i] + soff, 0, 0);
@@ -214,8 +226,8 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
         lds_write<u32x4>(base, k_dst[i], w);
       }
     };
-    auto load_v = [&](int kt) {
-      const int soff = kt * kKT * row_bytes;
+    auto load_v = [&](int t) {
+      const int soff = ktile(t) * kKT * row_bytes;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if constexpr (VD == 8) {
@@ -297,19 +309,25 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
     };
     // V phase: softmax of S(t) into P(t)
     auto v_phase = [&](int t) {
-      const int kbase = t * kKT;
-      const bool need_mask = (kbase + kKT > tkv) || (a.causal && kbase + kKT - 1 > p0 + off);
+      const int kbase = ktile(t) * kKT;
+      const bool below_window =
+          a.window > 0 && kbase < last + off - a.window + 1 && kbase + kKT > a.n_sink;
+      const bool need_mask =
+          (kbase + kKT > tkv) || (a.causal && kbase + kKT - 1 > p0 + off) || below_window;
       if (need_mask) {
         const int lim = a.causal ? min(tkv - 1, pos + off) : tkv - 1;
         // key of element (h, i) is kbase + 4*hh + c(h, i) with a compile-time c; compare c
-        // against one per-lane remainder so no per-element offsets stay live across tiles
+        // against per-lane remainders so no per-element offsets stay live across tiles. The key
+        // is visible if it is at most lim and (inside the window or a sink key).
         const int rem = lim - kbase - 4 * hh;
+        const int rlo = a.window > 0 ? pos + off - a.window + 1 - kbase - 4 * hh : -kKT;
+        const int rsk = a.n_sink - kbase - 4 * hh;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int c = h * 32 + (i >> 2) * 8 + (i & 3);
-            sacc[h][i] = c <= rem ? sacc[h][i] : -INFINITY;
+            sacc[h][i] = (c <= rem && (c >= rlo || c < rsk)) ? sacc[h][i] : -INFINITY;
           }
       }
       float r3[11];
@@ -328,7 +346,9 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
       const bool move = tmax > m_run + kRescaleSlack;
       if (__any(move)) {
         const float m_new = move ? tmax : m_run;
-        const float alpha = fast_exp2(m_run - m_new);
+        // lanes that keep their reference keep their sums (their m may still be -inf, since
+        // with a sliding window a row can see nothing in the first tiles of the workgroup)
+        const float alpha = move ? fast_exp2(m_run - m_new) : 1.f;
         l_run *= alpha;
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)

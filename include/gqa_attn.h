@@ -73,6 +73,20 @@ gqa_status_t gqa_attn_prefill(const void* q, const void* k, const void* v, void*
                               hipStream_t stream);
 
 /*
+ * Prefill with a causal sliding window and attention sinks (course page "Week 7. Attention",
+ * step 3: the window bounds what each query sees; the first tokens stay visible as sinks).
+ * Same tensors, layout, packing and errors as gqa_attn_prefill with causal = 1; the query at
+ * position p (bottom-right aligned, as there) sees key j iff j <= p and (j > p - window or
+ * j < n_sink). window = 0 means no window (plain causal attention; n_sink is then irrelevant);
+ * window and n_sink must be >= 0 (else GQA_ERR_SHAPE). bf16 only (else GQA_ERR_UNSUPPORTED).
+ * Only the sink and window key tiles are read.
+ */
+gqa_status_t gqa_attn_prefill_window(const void* q, const void* k, const void* v, void* out,
+                                     int B, int Tq, int Tkv, int Hq, int Hkv, int d, float scale,
+                                     int window, int n_sink, const int32_t* cu_seqlens,
+                                     int max_seqlen, gqa_dtype_t dtype, hipStream_t stream);
+
+/*
  * Decode: one query token per sequence against a key/value cache, split along the cache length.
  *   q [B, 1, Hq, d]     k_cache, v_cache [B, Tkv, Hkv, d]     out [B, 1, Hq, d]
  * Each split writes an fp32 partial result (running max, sum and unnormalised output) to
@@ -88,6 +102,25 @@ gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_c
                              int B, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
                              void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
                              hipStream_t stream);
+
+/*
+ * Decode against a ragged cache, optionally with a sliding window and sinks (course page
+ * "Week 7. Attention", step 3).
+ *   q [B, 1, Hq, d]     k_cache, v_cache [B, Tmax, Hkv, d] (Tmax = allocated entries per
+ *   sequence)     out [B, 1, Hq, d]
+ * cache_lens: DEVICE int32[B] (or NULL: every sequence uses all Tmax entries); sequence b uses its
+ * entries 0 .. cache_lens[b]-1 and its query sits at position cache_lens[b]-1. Lengths outside
+ * [1, Tmax] are clamped into it. With window > 0 the query sees only its last `window` entries
+ * plus entries 0 .. n_sink-1; window = 0 means the whole (ragged) cache. Only visible entries
+ * are read. Workspace as for gqa_attn_decode, sized by
+ * gqa_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, d). bf16 only (else GQA_ERR_UNSUPPORTED);
+ * negative window or n_sink is GQA_ERR_SHAPE.
+ */
+gqa_status_t gqa_attn_decode_ragged(const void* q, const void* k_cache, const void* v_cache,
+                                    void* out, int B, int Tmax, int Hq, int Hkv, int d,
+                                    float scale, const int32_t* cache_lens, int window,
+                                    int n_sink, void* workspace, size_t workspace_bytes,
+                                    gqa_dtype_t dtype, hipStream_t stream);
 
 /*
  * Fold key/value heads: src [B, T, H, d] -> dst [B, T, g, d] with

@@ -72,6 +72,27 @@ def test_prefill_validation(lib):
     assert pre(lib, Tkv=1 << 22, Hq=8, Hkv=8) == B.GQA_ERR_UNSUPPORTED
 
 
+def test_window_and_ragged_validation(lib):
+    def prew(window=4, n_sink=0, dt=BF16, d=128):
+        return lib.gqa_attn_prefill_window(Q, K, V, O, 1, 8, 8, 8, 2, d, 0.1, window, n_sink,
+                                           None, 0, dt, None)
+    assert prew(window=-1) == B.GQA_ERR_SHAPE
+    assert prew(n_sink=-2) == B.GQA_ERR_SHAPE
+    assert prew(dt=F32, d=16) == B.GQA_ERR_UNSUPPORTED     # windows are bf16 only
+    assert lib.gqa_attn_prefill_window(Q, K, V, O, 1, 9, 8, 8, 2, 128, 0.1, 4, 0, None, 0, BF16,
+                                       None) == B.GQA_ERR_SHAPE   # causal needs Tq <= Tkv
+    need = lib.gqa_attn_decode_workspace_bytes(4, 1024, 32, 8, 128)
+
+    def rag(window=0, n_sink=0, dt=BF16, d=128, lens=W + 4096, ws=W, wsb=need, Tmax=1024):
+        return lib.gqa_attn_decode_ragged(Q, K, V, O, 4, Tmax, 32, 8, d, 0.1, lens, window,
+                                          n_sink, ws, wsb, dt, None)
+    assert rag(window=-3) == B.GQA_ERR_SHAPE
+    assert rag(n_sink=-1) == B.GQA_ERR_SHAPE
+    assert rag(dt=F32, d=16) == B.GQA_ERR_UNSUPPORTED
+    assert rag(ws=None) == B.GQA_ERR_WORKSPACE
+    assert rag(Tmax=1 << 22) == B.GQA_ERR_UNSUPPORTED
+
+
 def test_decode_validation(lib):
     need = lib.gqa_attn_decode_workspace_bytes(4, 1024, 32, 8, 128)
     assert need > 0 and need % 16 == 0

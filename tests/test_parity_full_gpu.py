@@ -69,3 +69,47 @@ def test_full_decode_sampled_rows(gqa):
     say(f"full-size decode: oracle on {len(rows)} rows")
     err, rel = _check_rows(w, q, k, v, None, out, rows)
     say(f"full-size decode: max-abs {err:.3e} rel {rel:.3e}")
+
+
+def test_full_window_prefill_sampled_rows(gqa):
+    w = workloads.WINDOW_PREFILL
+    say(f"full-size window prefill {w.name}: generating inputs")
+    q, k, v, _ = workloads.make_inputs(w)
+    say(f"full-size window prefill {w.name}: launching")
+    out = gqa.gqa_attn_prefill_window(to_dev(q), to_dev(k), to_dev(v), window=w.window,
+                                      n_sink=w.n_sink)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    rows = workloads.sample_rows(w, 160, seed=10)
+    say(f"full-size window prefill: oracle on {len(rows)} rows")
+    ref = oracle.default().attention_rows(host_view(q), host_view(k), host_view(v), rows,
+                                          causal=True, window=w.window, n_sink=w.n_sink)
+    o = out.cpu()
+    got = np.stack([to_f64(o[b, t, h]) for b, t, h in rows])
+    err, rel = assert_bf16_close(got, ref, what=w.name)
+    say(f"full-size window prefill: max-abs {err:.3e} rel {rel:.3e}")
+
+
+def test_full_ragged_decode_sampled_sequences(gqa):
+    w = workloads.RAGGED_DECODE
+    say(f"full-size ragged decode {w.name}: generating inputs")
+    q, k, v, _ = workloads.make_inputs(w)
+    lens = torch.tensor(w.cache_lens, dtype=torch.int32).cuda()
+    ws = torch.empty(gqa.gqa_attn_decode_workspace_bytes(w.B, w.Tkv, w.Hq, w.Hkv, w.d),
+                     dtype=torch.uint8, device="cuda")
+    say("full-size ragged decode: launching")
+    out = gqa.gqa_attn_decode_ragged(to_dev(q), to_dev(k), to_dev(v), cache_lens=lens,
+                                     workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    got = to_f64(out)
+    qh, kh, vh = host_view(q), host_view(k), host_view(v)
+    # the shortest and longest sequences plus a seeded sample of the rest, all heads
+    pick = sorted({0, w.B - 1, *np.random.default_rng(11).choice(w.B, 6, replace=False).tolist()})
+    say(f"full-size ragged decode: oracle on sequences {pick}")
+    orc = oracle.default()
+    for b in pick:
+        L = w.cache_lens[b]
+        ref = orc.attention(qh[b:b + 1], np.ascontiguousarray(kh[b:b + 1, :L]),
+                            np.ascontiguousarray(vh[b:b + 1, :L]), causal=True)
+        assert_bf16_close(got[b:b + 1], ref, what=f"{w.name} seq {b} len {L}")

@@ -102,6 +102,9 @@ class Workload:
     peaked_frac: float = 0.0                    # fraction of q rows multiplied by peaked_scale
     peaked_scale: float = 1.0
     peaked_seed: int = 0
+    window: int = 0                             # causal sliding window (0: none)
+    n_sink: int = 0                             # sink keys kept visible below the window
+    cache_lens: Optional[Tuple[int, ...]] = None  # ragged decode: entries used per sequence
 
     @property
     def G(self) -> int:
@@ -140,8 +143,31 @@ VARLEN_PREFILL = Workload("varlen_causal_prefill_16k_8k_4k_1k", B=1, Tq=29696, T
                           Hkv=8, d=128, dtype="bf16", causal=True,
                           seqlens=(16384, 8192, 4096, 1024), seeds=(5000, 5001, 5002))
 
+
+
+def ragged_lengths(B: int, Tmax: int, seed: int) -> Tuple[int, ...]:
+    """Seeded per-sequence cache lengths, uniform on 1 .. Tmax (a serving batch at mixed
+    progress), with the extremes 1 and Tmax always present."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, Tmax + 1, size=B)
+    lens[0], lens[-1] = 1, Tmax
+    return tuple(int(x) for x in lens)
+
+
+# Llama-3-8B-shaped prefill with a causal sliding window of 1024 keys and 4 sink keys (course
+# page "Week 7. Attention", step 3) over an 8192-token sequence.
+WINDOW_PREFILL = Workload("window_prefill_T8192_W1024_S4", B=1, Tq=8192, Tkv=8192, Hq=32, Hkv=8,
+                          d=128, dtype="bf16", causal=True, seeds=(6000, 6001, 6002),
+                          window=1024, n_sink=4)
+# Batched decode against a ragged cache: 64 sequences with lengths uniform on 1 .. 8192 in
+# caches allocated for 8192 entries.
+RAGGED_DECODE = Workload("ragged_decode_B64_max8192", B=64, Tq=1, Tkv=8192, Hq=32, Hkv=8, d=128,
+                         dtype="bf16", causal=False, seeds=(7000, 7001, 7002),
+                         cache_lens=ragged_lengths(64, 8192, 7003))
+
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in
-                                  (TINY, LLAMA_PREFILL, DECODE, MQA_PREFILL, VARLEN_PREFILL)}
+                                  (TINY, LLAMA_PREFILL, DECODE, MQA_PREFILL, VARLEN_PREFILL,
+                                   WINDOW_PREFILL, RAGGED_DECODE)}
 
 
 def tiny_lab_inputs(x1000: bool = False) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
