@@ -69,10 +69,10 @@ def _bind(lib):
     lib.oracle_expand.argtypes = [P, P, I64, I64, I, I, I]
     lib.oracle_expand.restype = I
     lib.oracle_gqa_attention.argtypes = [P, P, P, I, P, I64, I64, I64, I, I, I, D, I, P, I, I64,
-                                         I64]
+                                         I64, P, P, I64, I]
     lib.oracle_gqa_attention.restype = I
     lib.oracle_gqa_attention_rows.argtypes = [P, P, P, I, I64, I64, I64, I, I, I, D, I, P, I, P,
-                                              I64, P, I64, I64]
+                                              I64, P, I64, I64, P, P, I64, I]
     lib.oracle_gqa_attention_rows.restype = I
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = I
@@ -170,36 +170,56 @@ class Oracle:
                 raise ValueError("packed batch needs q,k,v as [1,total,H,d] with total == cu[-1]")
         return q, k, v, dq, B, Tq, Tkv, Hq, Hkv, d, float(scale), cu, nseq
 
+    @staticmethod
+    def _rope(rope, rope_mode, d):
+        """rope: None or (cos, sin) float32 tables [n_pos, d/2]; rope_mode "qk" rotates queries
+        and keys, "q" only the queries (keys already rotated, as in a cache)."""
+        if rope is None:
+            return None, None, 0, 0, ()
+        cos_t = np.ascontiguousarray(rope[0], dtype=np.float32)
+        sin_t = np.ascontiguousarray(rope[1], dtype=np.float32)
+        if cos_t.shape != sin_t.shape or cos_t.ndim != 2 or cos_t.shape[1] * 2 != d:
+            raise ValueError("rope tables must both be [n_pos, d/2]")
+        mode = {"qk": 3, "q": 1}[rope_mode]
+        return cos_t.ctypes.data, sin_t.ctypes.data, cos_t.shape[0], mode, (cos_t, sin_t)
+
     def attention(self, q, k, v, scale: Optional[float] = None, causal: bool = False,
-                  cu_seqlens=None, window: int = 0, n_sink: int = 0) -> np.ndarray:
+                  cu_seqlens=None, window: int = 0, n_sink: int = 0, rope=None,
+                  rope_mode: str = "qk") -> np.ndarray:
         """Grouped-query attention forward (``heads_out``): float64 out[B,Tq,Hq,d].
 
         ``window`` > 0 (causal only) limits each query at position p to keys p-window+1 .. p,
-        plus the ``n_sink`` first keys (course page "Week 7. Attention", step 3)."""
+        plus the ``n_sink`` first keys; ``rope`` = (cos, sin) tables rotates query t at position
+        t + Tkv - Tq and key j at position j before the scores (course page "Week 7. Attention",
+        step 3)."""
         q, k, v, dt, B, Tq, Tkv, Hq, Hkv, d, scale, cu, nseq = self._common(q, k, v, scale,
                                                                             cu_seqlens)
+        cp, sp, npos, mode, keep = self._rope(rope, rope_mode, d)
         out = np.empty((B, Tq, Hq, d), dtype=np.float64)
         rc = self.lib.oracle_gqa_attention(q.ctypes.data, k.ctypes.data, v.ctypes.data, dt,
                                            out.ctypes.data, B, Tq, Tkv, Hq, Hkv, d, scale,
                                            int(bool(causal)),
                                            cu.ctypes.data if cu is not None else None, nseq,
-                                           int(window), int(n_sink))
+                                           int(window), int(n_sink), cp, sp, npos, mode)
+        del keep
         self._check(rc)
         return out
 
     def attention_rows(self, q, k, v, rows: np.ndarray, scale: Optional[float] = None,
                        causal: bool = False, cu_seqlens=None, window: int = 0,
-                       n_sink: int = 0) -> np.ndarray:
+                       n_sink: int = 0, rope=None, rope_mode: str = "qk") -> np.ndarray:
         """Selected output rows only. rows: int64 [n, 3] of (b, t, head); returns float64 [n, d]."""
         q, k, v, dt, B, Tq, Tkv, Hq, Hkv, d, scale, cu, nseq = self._common(q, k, v, scale,
                                                                             cu_seqlens)
         r = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+        cp, sp, npos, mode, keep = self._rope(rope, rope_mode, d)
         out = np.empty((r.shape[0], d), dtype=np.float64)
         rc = self.lib.oracle_gqa_attention_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, dt,
                                                 B, Tq, Tkv, Hq, Hkv, d, scale, int(bool(causal)),
                                                 cu.ctypes.data if cu is not None else None, nseq,
                                                 r.ctypes.data, r.shape[0], out.ctypes.data,
-                                                int(window), int(n_sink))
+                                                int(window), int(n_sink), cp, sp, npos, mode)
+        del keep
         self._check(rc)
         return out
 

@@ -35,6 +35,9 @@
 
 enum { ORACLE_F64 = 0, ORACLE_F32 = 1, ORACLE_BF16 = 2 };
 
+/* rotary embedding modes: which of q and k are rotated */
+enum { ROPE_Q = 1, ROPE_K = 2 };
+
 enum {
   ORACLE_OK = 0,
   ORACLE_ERR_GROUPING = 1, /* head count not divisible by the group count */
@@ -160,6 +163,21 @@ static int64_t visible_keys(int64_t t, int64_t Tq, int64_t Tkv, int causal) {
   return n;
 }
 
+/* Rotary position embedding of one head row in place (course page "Week 7. Attention", step 3:
+ * each pair of coordinates is turned by the angle pos * theta_i; in complex form the pair
+ * (x[2i], x[2i+1]) is the number x[2i] + i x[2i+1] multiplied by e^{i pos theta_i}).
+ * cos_t / sin_t: tables [n_pos][d/2] (fp32, as the caller passes them) holding cos and sin of
+ * pos * theta_i. */
+static void rope_row(double* x, int d, const float* cos_t, const float* sin_t, int64_t pos) {
+  for (int i = 0; i < d / 2; ++i) {
+    const double c = (double)cos_t[pos * (d / 2) + i];
+    const double s = (double)sin_t[pos * (d / 2) + i];
+    const double re = x[2 * i], im = x[2 * i + 1];
+    x[2 * i] = re * c - im * s;
+    x[2 * i + 1] = re * s + im * c;
+  }
+}
+
 /* Item table: a dense batch has B items of (Tq, Tkv); a packed batch (cu_seqlens) has nseq items
  * of equal query and key length, laid out back to back in a single [1, total, H, d] tensor. */
 typedef struct {
@@ -206,9 +224,11 @@ static int make_items(int64_t B, int64_t Tq, int64_t Tkv, const int32_t* cu, int
 int oracle_gqa_attention(const void* q, const void* k, const void* v, int dtype_in, double* out,
                          int64_t B, int64_t Tq, int64_t Tkv, int Hq, int Hkv, int d, double scale,
                          int causal, const int32_t* cu_seqlens, int nseq, int64_t window,
-                         int64_t n_sink) {
+                         int64_t n_sink, const float* rope_cos, const float* rope_sin,
+                         int64_t rope_npos, int rope_mode) {
   if (Hq <= 0 || Hkv <= 0 || d <= 0) return ORACLE_ERR_SHAPE;
   if ((window > 0 || n_sink > 0) && !causal) return ORACLE_ERR_SHAPE;  /* windows are causal */
+  if (rope_mode && (!rope_cos || !rope_sin || d % 2 != 0)) return ORACLE_ERR_SHAPE;
   if (Hq % Hkv != 0) return ORACLE_ERR_GROUPING;
   item_t* items = NULL;
   int nitems = 0;
@@ -228,6 +248,18 @@ int oracle_gqa_attention(const void* q, const void* k, const void* v, int dtype_
   for (int64_t i = 0; i < krows * Hkv * d; ++i) {
     kw[i] = widen(k, dtype_in, i);
     vw[i] = widen(v, dtype_in, i);
+  }
+  if (rope_mode & ROPE_K) {
+    /* key j of an item sits at position j */
+    for (int it = 0; it < nitems; ++it)
+      for (int64_t j = 0; j < items[it].Tkv; ++j) {
+        if (j >= rope_npos) {
+          free(kw); free(vw); free(ke); free(ve); free(items);
+          return ORACLE_ERR_SHAPE;
+        }
+        for (int h = 0; h < Hkv; ++h)
+          rope_row(&kw[((items[it].k_row0 + j) * Hkv + h) * (int64_t)d], d, rope_cos, rope_sin, j);
+      }
   }
   oracle_expand(kw, ke, 1, krows, Hkv, Hq, d);
   oracle_expand(vw, ve, 1, krows, Hkv, Hq, d);
@@ -262,6 +294,16 @@ int oracle_gqa_attention(const void* q, const void* k, const void* v, int dtype_
         const item_t I = items[row_item[row]];
         const int64_t t = row - I.q_row0;
         for (int c = 0; c < d; ++c) qh[c] = widen(q, dtype_in, (row * Hq + h) * (int64_t)d + c);
+        if (rope_mode & ROPE_Q) {
+          /* query t sits at position t + (Tkv - Tq), the same alignment as the causal mask */
+          const int64_t qpos = t + (I.Tkv - I.Tq);
+          if (qpos < 0 || qpos >= rope_npos) {
+#pragma omp atomic write
+            err = ORACLE_ERR_SHAPE;
+            continue;
+          }
+          rope_row(qh, d, rope_cos, rope_sin, qpos);
+        }
         /* head h of the expanded K/V: rows k_row0.. of the [krows][Hq][d] tables */
         const double* kh = &ke[(I.k_row0 * Hq + h) * (int64_t)d];
         const double* vh = &ve[(I.k_row0 * Hq + h) * (int64_t)d];
@@ -288,9 +330,11 @@ int oracle_gqa_attention_rows(const void* q, const void* k, const void* v, int d
                               int64_t B, int64_t Tq, int64_t Tkv, int Hq, int Hkv, int d,
                               double scale, int causal, const int32_t* cu_seqlens, int nseq,
                               const int64_t* rows, int64_t nrows, double* out, int64_t window,
-                              int64_t n_sink) {
+                              int64_t n_sink, const float* rope_cos, const float* rope_sin,
+                              int64_t rope_npos, int rope_mode) {
   if (Hq <= 0 || Hkv <= 0 || d <= 0) return ORACLE_ERR_SHAPE;
   if ((window > 0 || n_sink > 0) && !causal) return ORACLE_ERR_SHAPE;  /* windows are causal */
+  if (rope_mode && (!rope_cos || !rope_sin || d % 2 != 0)) return ORACLE_ERR_SHAPE;
   if (Hq % Hkv != 0) return ORACLE_ERR_GROUPING;
   item_t* items = NULL;
   int nitems = 0;
@@ -337,14 +381,23 @@ int oracle_gqa_attention_rows(const void* q, const void* k, const void* v, int d
           t = tglob;
         }
         const int kvh = oracle_group_of(h, Hq, Hkv);
-        for (int64_t j = 0; j < I.Tkv; ++j)
+        const int64_t qpos = t + (I.Tkv - I.Tq);
+        if (rope_mode && (I.Tkv > rope_npos || qpos < 0 || qpos >= rope_npos)) {
+#pragma omp atomic write
+          err = ORACLE_ERR_SHAPE;
+          continue;
+        }
+        for (int64_t j = 0; j < I.Tkv; ++j) {
           for (int c = 0; c < d; ++c) {
             const int64_t src = ((I.k_row0 + j) * Hkv + kvh) * (int64_t)d + c;
             kh[j * d + c] = widen(k, dtype_in, src);
             vh[j * d + c] = widen(v, dtype_in, src);
           }
+          if (rope_mode & ROPE_K) rope_row(&kh[j * d], d, rope_cos, rope_sin, j);
+        }
         const int64_t row = I.q_row0 + t;
         for (int c = 0; c < d; ++c) qh[c] = widen(q, dtype_in, (row * Hq + h) * (int64_t)d + c);
+        if (rope_mode & ROPE_Q) rope_row(qh, d, rope_cos, rope_sin, qpos);
         attend_row(qh, kh, vh, d, visible_keys(t, I.Tq, I.Tkv, causal),
                    window_lo(t, I.Tq, I.Tkv, window), n_sink, d, scale, sc, &out[r * d]);
       }

@@ -17,7 +17,9 @@ Sources of the facts (page, section):
     still sums to one over the past), step 2 (32/8 heads -> 4x smaller cache, MQA 32x),
     "typical errors" (repeat_kv must repeat adjacently; attention must be causal), and the
     check against torch's scaled_dot_product_attention; step 3 (sliding window and attention
-    sinks: the window bounds what a query sees, the first tokens stay visible).
+    sinks: the window bounds what a query sees, the first tokens stay visible; rotary position
+    embedding: pairs of coordinates turned by pos * theta_i, theta_i = base^(-2i/d), the pair
+    being one complex number, so scores depend only on position differences).
 """
 from __future__ import annotations
 
@@ -390,6 +392,89 @@ def check_window_limits(orc):
         raise AssertionError("a window without the causal flag must be rejected")
 
 
+# ------------------------------------------------------------------------------------------------
+# course step 3: rotary position embedding
+# ------------------------------------------------------------------------------------------------
+
+def rope_tables(npos, d, base=10000.0):
+    """cos / sin of p * theta_i with theta_i = base^(-2i/d), computed in float64 and stored as
+    float32 [npos, d/2] (the course page's formula, step 3)."""
+    i = np.arange(d // 2, dtype=np.float64)
+    theta = base ** (-2.0 * i / d)
+    ang = np.arange(npos, dtype=np.float64)[:, None] * theta[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def check_rope_worked_example(orc):
+    """d = 2 (theta_0 = 1 rad per position): q = (1, 0) at position 1 turns to (cos 1, sin 1);
+    key 0 = (0, 1) stays, key 1 = (1, 0) turns with q. Scores sin(1)/sqrt(2) and 1/sqrt(2), so
+    out = softmax-weighted v0 = (1, 0), v1 = (0, 1) in closed form. A turn in the other direction
+    would give the first score the opposite sign."""
+    cos_t, sin_t = rope_tables(2, 2)
+    q = np.array([1.0, 0.0]).reshape(1, 1, 1, 2)
+    k = np.array([[0.0, 1.0], [1.0, 0.0]]).reshape(1, 2, 1, 2)
+    v = np.array([[1.0, 0.0], [0.0, 1.0]]).reshape(1, 2, 1, 2)
+    got = orc.attention(q, k, v, causal=True, rope=(cos_t, sin_t))
+    c1, s1 = float(cos_t[1, 0]), float(sin_t[1, 0])
+    sc = 1.0 / math.sqrt(2.0)
+    s0v, s1v = sc * s1, sc * (c1 * c1 + s1 * s1)
+    p0 = 1.0 / (1.0 + math.exp(s1v - s0v))
+    assert abs(got[0, 0, 0, 0] - p0) <= 1e-14 and abs(got[0, 0, 0, 1] - (1 - p0)) <= 1e-14, got
+
+
+def check_rope_matches_complex_torch(orc):
+    """Library cross-check: rotate q and k by complex multiplication in torch (the page's complex
+    form: adjacent coordinates are the real and imaginary part), then torch fp64 SDPA."""
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(20)
+    for (Tq, Tkv, Hq, Hkv, d, causal) in [(7, 7, 4, 2, 8, True), (3, 11, 2, 1, 16, True),
+                                          (5, 5, 3, 3, 4, False)]:
+        cos_t, sin_t = rope_tables(Tkv + 2, d)
+        q = rng.standard_normal((2, Tq, Hq, d)); k = rng.standard_normal((2, Tkv, Hkv, d))
+        v = rng.standard_normal((2, Tkv, Hkv, d))
+        got = orc.attention(q, k, v, causal=causal, rope=(cos_t, sin_t))
+        rot = torch.complex(torch.from_numpy(cos_t.astype(np.float64)),
+                            torch.from_numpy(sin_t.astype(np.float64)))
+
+        def turn(x, pos0):
+            z = torch.view_as_complex(torch.from_numpy(x).reshape(*x.shape[:-1], d // 2, 2))
+            z = z * rot[pos0:pos0 + x.shape[1]][None, :, None, :]
+            return torch.view_as_real(z).reshape(x.shape)
+        G = Hq // Hkv
+        qt = turn(q, Tkv - Tq).permute(0, 2, 1, 3).contiguous()
+        kt = turn(k, 0).repeat_interleave(G, dim=2).permute(0, 2, 1, 3).contiguous()
+        vt = torch.from_numpy(v).repeat_interleave(G, dim=2).permute(0, 2, 1, 3).contiguous()
+        mask = None
+        if causal:
+            mask = torch.from_numpy(_window_mask(Tq, Tkv, Tkv + 1, 0))
+        ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+        err = np.max(np.abs(got - ref.permute(0, 2, 1, 3).numpy()))
+        assert err <= 1e-12, (Tq, Tkv, d, causal, err)
+        # queries only (keys already turned, as in a cache)
+        k_turned = turn(k, 0).numpy()
+        got_q = orc.attention(q, k_turned, v, causal=causal, rope=(cos_t, sin_t), rope_mode="q")
+        assert np.max(np.abs(got_q - got)) <= 1e-12
+
+
+def check_rope_relative_positions(orc):
+    """Scores depend on positions only through m - n (the page's derivation): moving every
+    position by the same amount (tables read from a later row) leaves the output unchanged up
+    to the fp32 rounding of the tables; zero angles are no rotation at all."""
+    rng = _rng(21)
+    d = 16
+    cos_t, sin_t = rope_tables(64, d)
+    q = rng.standard_normal((1, 9, 4, d)); k = rng.standard_normal((1, 9, 2, d))
+    v = rng.standard_normal((1, 9, 2, d))
+    a = orc.attention(q, k, v, causal=True, rope=(cos_t, sin_t))
+    b = orc.attention(q, k, v, causal=True, rope=(cos_t[37:], sin_t[37:]))
+    assert np.max(np.abs(a - b)) <= 1e-5, np.max(np.abs(a - b))
+    assert np.max(np.abs(a - orc.attention(q, k, v, causal=True))) > 1e-3
+    ones, zeros = np.ones_like(cos_t), np.zeros_like(sin_t)
+    assert np.array_equal(orc.attention(q, k, v, causal=True, rope=(ones, zeros)),
+                          orc.attention(q, k, v, causal=True))
+
+
 ALL_CHECKS = [
     check_group_of_worked_example,
     check_group_of_rejects_uneven,
@@ -405,6 +490,9 @@ ALL_CHECKS = [
     check_causality,
     check_window_matches_masked_sdpa,
     check_window_limits,
+    check_rope_worked_example,
+    check_rope_matches_complex_torch,
+    check_rope_relative_positions,
     check_bottom_right_alignment,
     check_g_equals_h_is_mha,
     check_packed_equals_separate,

@@ -33,6 +33,10 @@ MUTANTS = {
     "window_off_by_one": ("return t + (Tkv - Tq) - window + 1;", "return t + (Tkv - Tq) - window;"),
     # course step 3: sink keys dropped from the window
     "sinks_ignored": ("if (j < lo && j >= n_sink) continue;", "if (j < lo) continue;"),
+    # course step 3: rotation turned the wrong way
+    "rope_wrong_direction": ("x[2 * i] = re * c - im * s;", "x[2 * i] = re * c + im * s;"),
+    # course step 3: query position not aligned with the keys (top-left)
+    "rope_query_top_left": ("const int64_t qpos = t + (I.Tkv - I.Tq);", "const int64_t qpos = t;"),
     # value rows weighted by the wrong key
     "value_index_shift": ("out[c] += s[j] * v[j * kstride + c];",
                           "out[c] += s[j] * v[((j + 1) % nvis) * kstride + c];"),
