@@ -118,13 +118,21 @@ def time_launches(fn, steps, warmup, torch):
     return ms, wall
 
 
-def bench_prefill(gqa, w, steps, warmup, torch, seed):
+def bench_prefill(gqa, w, steps, warmup, torch, seed, rope=False):
+    """rope: turn q and k inside the kernel with (cos, sin) tables (rotary embedding)."""
     q, k, v, cu = device_inputs(w, torch, seed)
     out = torch.empty_like(q)
     msl = max(w.seqlens) if w.seqlens else None
+    tables = None
+    if rope:
+        import workloads
+        tables = tuple(torch.from_numpy(t).cuda() for t in workloads.rope_tables(w.Tkv, w.d))
 
     def step():
-        if w.window > 0:
+        if tables is not None:
+            gqa.gqa_attn_prefill_ex(q, k, v, causal=w.causal, window=w.window, n_sink=w.n_sink,
+                                    rope=tables, out=out)
+        elif w.window > 0:
             gqa.gqa_attn_prefill_window(q, k, v, window=w.window, n_sink=w.n_sink, out=out)
         else:
             gqa.gqa_attn_prefill(q, k, v, causal=w.causal, cu_seqlens=cu, max_seqlen=msl, out=out)
@@ -240,7 +248,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "mqa", "varlen", "window",
-                                       "ragged", "copy"],
+                                       "ragged", "rope", "copy"],
                     default=None,
                     help="time a single workload (for profiling); still prints one JSON line. "
                          "'copy' times a plain 1 GiB device copy, the calibration kernel for "
@@ -291,6 +299,13 @@ def main():
         wp["frac_mfma"] = wp["tflops"] / PEAK_BF16_TFLOPS
         extra["window_prefill"] = wp
         log(f"window prefill: {wp['avg_ms'] * 1e3:.1f} us, {wp['tflops']:.1f} TFLOP/s")
+    if args.only == "rope" or args.all:
+        rp, _ = bench_prefill(gqa, workloads.LLAMA_PREFILL, args.steps, args.warmup, torch, 2000,
+                              rope=True)
+        rp["frac_mfma"] = rp["tflops"] / PEAK_BF16_TFLOPS
+        rp["workload"] = workloads.LLAMA_PREFILL.name + "+rope"
+        extra["rope_prefill"] = rp
+        log(f"rope prefill: {rp['avg_ms'] * 1e3:.1f} us, {rp['tflops']:.1f} TFLOP/s")
     if args.only == "ragged" or args.all:
         rd = bench_decode(gqa, workloads.RAGGED_DECODE, args.steps, args.warmup, torch, 7000)
         extra["ragged_decode"] = rd
@@ -301,10 +316,11 @@ def main():
         log(f"decode: {dec['avg_ms'] * 1e3:.1f} us, {dec['gbs']:.0f} GB/s")
     sha = kernel_source_sha("prefill")
     metric = "GQA prefill TFLOPS (% MFMA peak); decode KV GB/s (% HBM peak)"
-    if pre is None and args.only in ("mqa", "varlen", "window"):
+    if pre is None and args.only in ("mqa", "varlen", "window", "rope"):
         key, w = {"mqa": ("mqa_prefill", workloads.MQA_PREFILL),
                   "varlen": ("varlen_prefill", workloads.VARLEN_PREFILL),
-                  "window": ("window_prefill", workloads.WINDOW_PREFILL)}[args.only]
+                  "window": ("window_prefill", workloads.WINDOW_PREFILL),
+                  "rope": ("rope_prefill", workloads.LLAMA_PREFILL)}[args.only]
         pre = extra.pop(key)
     if pre is not None:
         value, unit = pre["tflops"], "TFLOP/s"

@@ -7,10 +7,13 @@ from ._binding import (  # noqa: F401
     ABI_VERSION,
     GQAError,
     GQAValueError,
+    AttnOptions,
     gqa_attn_decode,
+    gqa_attn_decode_ex,
     gqa_attn_decode_ragged,
     gqa_attn_decode_workspace_bytes,
     gqa_attn_prefill,
+    gqa_attn_prefill_ex,
     gqa_attn_prefill_window,
     gqa_fold_kv,
     gqa_status_string,

@@ -44,6 +44,24 @@ def _hip_runtimes_mapped():
         return []
 
 
+class AttnOptions(ctypes.Structure):
+    """``gqa_attn_options_t``: sliding window, sinks and rotary tables of the extended calls."""
+    _fields_ = [("window", ctypes.c_int), ("n_sink", ctypes.c_int),
+                ("rope_cos", ctypes.c_void_p), ("rope_sin", ctypes.c_void_p),
+                ("rope_rows", ctypes.c_int)]
+
+
+def _options(window: int, n_sink: int, rope, d: int) -> AttnOptions:
+    o = AttnOptions(int(window), int(n_sink), None, None, 0)
+    if rope is not None:
+        cos_t, sin_t = (_dev(t, name) for t, name in zip(rope, ("rope cos", "rope sin")))
+        if (cos_t.dtype != torch.float32 or sin_t.dtype != torch.float32 or cos_t.dim() != 2
+                or cos_t.shape != sin_t.shape or cos_t.shape[1] * 2 != d):
+            raise ValueError("rope tables must be float32 device tensors [rows, d/2]")
+        o.rope_cos, o.rope_sin, o.rope_rows = cos_t.data_ptr(), sin_t.data_ptr(), cos_t.shape[0]
+    return o
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m grouped_query_softmax_amd.build`")
@@ -59,6 +77,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_attn_prefill_window.restype = I
     lib.gqa_attn_decode_ragged.argtypes = [P, P, P, P, I, I, I, I, I, F, P, I, I, P, SZ, I, P]
     lib.gqa_attn_decode_ragged.restype = I
+    OP = ctypes.POINTER(AttnOptions)
+    lib.gqa_attn_prefill_ex.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P, I, OP, I, P]
+    lib.gqa_attn_prefill_ex.restype = I
+    lib.gqa_attn_decode_ex.argtypes = [P, P, P, P, I, I, I, I, I, F, P, OP, P, SZ, I, P]
+    lib.gqa_attn_decode_ex.restype = I
     lib.gqa_fold_kv.argtypes = [P, P, I, I, I, I, I, I, P]
     lib.gqa_fold_kv.restype = I
     lib.gqa_status_string.argtypes = [I]
@@ -177,6 +200,22 @@ def gqa_attn_prefill_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, w
     return out
 
 
+def gqa_attn_prefill_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                        window: int = 0, n_sink: int = 0, rope=None,
+                        scale: Optional[float] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                        max_seqlen: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """:func:`gqa_attn_prefill` with a sliding window / sinks and rotary embedding of q and k
+    inside the kernel; rope = (cos, sin) float32 device tables [rows, d/2]. bf16 only."""
+    q, k, v, out, dims, cu_ptr, msl = _prefill_args(q, k, v, scale, cu_seqlens, max_seqlen, out)
+    opt = _options(window, n_sink, rope, q.shape[-1])
+    rc = _lib.gqa_attn_prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  *dims, int(bool(causal)), cu_ptr, msl, ctypes.byref(opt),
+                                  _dtype_code(q), _stream(stream))
+    _check(rc, "gqa_attn_prefill_ex")
+    return out
+
+
 def gqa_attn_decode_workspace_bytes(B: int, Tkv: int, Hq: int, Hkv: int, d: int) -> int:
     return int(_lib.gqa_attn_decode_workspace_bytes(B, Tkv, Hq, Hkv, d))
 
@@ -239,6 +278,30 @@ def gqa_attn_decode_ragged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                                      *dims, lens_ptr, int(window), int(n_sink), ws_ptr, ws_bytes,
                                      _dtype_code(q), _stream(stream))
     _check(rc, "gqa_attn_decode_ragged")
+    return out
+
+
+def gqa_attn_decode_ex(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       cache_lens: Optional[torch.Tensor] = None, window: int = 0,
+                       n_sink: int = 0, rope=None, scale: Optional[float] = None,
+                       workspace: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """:func:`gqa_attn_decode_ragged` plus rotary embedding of the query (the cache holds
+    turned keys); rope = (cos, sin) float32 device tables [rows >= Tmax, d/2]. bf16 only."""
+    q, k, v, out, dims, ws_ptr, ws_bytes, _ = _decode_args(q, k_cache, v_cache, scale, workspace,
+                                                           out)
+    lens_ptr = None
+    if cache_lens is not None:
+        lens = _dev(cache_lens, "cache_lens")
+        if lens.dtype != torch.int32 or lens.dim() != 1 or lens.numel() != q.shape[0]:
+            raise ValueError("cache_lens must be a 1-D int32 device tensor with one entry per "
+                             "sequence")
+        lens_ptr = lens.data_ptr()
+    opt = _options(window, n_sink, rope, q.shape[-1])
+    rc = _lib.gqa_attn_decode_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), *dims,
+                                 lens_ptr, ctypes.byref(opt), ws_ptr, ws_bytes, _dtype_code(q),
+                                 _stream(stream))
+    _check(rc, "gqa_attn_decode_ex")
     return out
 
 

@@ -99,6 +99,9 @@ struct PrefillArgs {
   int causal;
   int window;  // > 0: causal sliding window of this many keys (0: none)
   int n_sink;  // keys 0 .. n_sink-1 stay visible below the window
+  const float* rope_cos;  // rotary tables [rope_rows][d/2] (device), or nullptr
+  const float* rope_sin;
+  int rope_rows;
 };
 
 struct DecodeArgs {
@@ -114,7 +117,20 @@ struct DecodeArgs {
   const int32_t* lens;  // device per-sequence cache lengths, or nullptr (all Tkv)
   int window;     // > 0: the query sees only the last `window` cache entries (plus sinks)
   int n_sink;     // cache entries 0 .. n_sink-1 stay visible below the window
+  const float* rope_cos;  // rotary tables for the query [rope_rows][d/2] (device), or nullptr
+  const float* rope_sin;
+  int rope_rows;
 };
+// Rotary embedding of one 16-byte chunk of a head row in place: 4 pairs (2i, 2i+1), each turned
+// by the angle whose cos / sin are given (the pair is one complex number times e^{i angle}).
+__device__ __forceinline__ u32x4 rope_chunk(u32x4 w, f32x4 c, f32x4 s) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float re = bf16_lo(w[e]), im = bf16_hi(w[e]);
+    w[e] = pack_bf16x2(fmaf(re, c[e], -im * s[e]), fmaf(re, s[e], im * c[e]));
+  }
+  return w;
+}
 
 // Launchers (return hipSuccess or the launch error). Shapes have been validated by the caller.
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);

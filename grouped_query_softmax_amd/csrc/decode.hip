@@ -129,7 +129,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
                            8 * g;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const u32x4 w = col_ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * s) : u32x4{0, 0, 0, 0};
+      u32x4 w = col_ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * s) : u32x4{0, 0, 0, 0};
+      if (a.rope_cos) {
+        // rotary embedding of the query at its position L - 1 (the cache holds turned keys);
+        // this lane's dimensions 32s + 8g .. +7 are the pairs 16s + 4g .. +3
+        const int ti = (L - 1) * (D / 2) + 16 * s + 4 * g;
+        w = rope_chunk(w, *reinterpret_cast<const f32x4*>(a.rope_cos + ti),
+                       *reinterpret_cast<const f32x4*>(a.rope_sin + ti));
+      }
       qop[s] = __builtin_bit_cast(bf16x8, w);
     }
   }

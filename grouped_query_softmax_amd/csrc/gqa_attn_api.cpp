@@ -71,17 +71,35 @@ const char* gqa_status_string(gqa_status_t s) {
   return "unknown status";
 }
 
+// Options shared by the extended entry points; a null pointer means none of them.
+static gqa_status_t check_options(const gqa_attn_options_t* o, gqa_dtype_t dtype, int rows_needed) {
+  if (!o) return GQA_OK;
+  if (o->window < 0 || o->n_sink < 0) return GQA_ERR_SHAPE;
+  const bool rope = o->rope_cos || o->rope_sin;
+  if (rope && (!o->rope_cos || !o->rope_sin)) return GQA_ERR_NULL_PTR;
+  if ((o->window > 0 || o->n_sink > 0 || rope) && dtype != GQA_DTYPE_BF16)
+    return GQA_ERR_UNSUPPORTED;
+  if (rope) {
+    if (!aligned16(o->rope_cos) || !aligned16(o->rope_sin)) return GQA_ERR_UNSUPPORTED;
+    if (o->rope_rows < rows_needed) return GQA_ERR_SHAPE;
+  }
+  return GQA_OK;
+}
+
 static gqa_status_t prefill_impl(const void* q, const void* k, const void* v, void* out, int B,
                                  int Tq, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
-                                 int window, int n_sink, const int32_t* cu_seqlens, int max_seqlen,
-                                 gqa_dtype_t dtype, hipStream_t stream) {
+                                 const gqa_attn_options_t* opt, const int32_t* cu_seqlens,
+                                 int max_seqlen, gqa_dtype_t dtype, hipStream_t stream) {
   if (!q || !k || !v || !out) return GQA_ERR_NULL_PTR;
   if (B <= 0 || Tq <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_SHAPE;
   if (!isfinite(scale) || !(scale > 0.f)) return GQA_ERR_SHAPE;
-  if (window < 0 || n_sink < 0) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0) return GQA_ERR_GROUPING;
   if (!dtype_ok(dtype) || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
-  if ((window > 0 || n_sink > 0) && dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+  if (const gqa_status_t st = check_options(opt, dtype, cu_seqlens ? max_seqlen : Tkv))
+    return st;
+  const int window = opt ? opt->window : 0;
+  const int n_sink = opt ? opt->n_sink : 0;
+  if ((window > 0 || n_sink > 0) && !causal) return GQA_ERR_SHAPE;  // windows are causal
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return GQA_ERR_UNSUPPORTED;
   int nitems, max_tq;
@@ -131,6 +149,9 @@ static gqa_status_t prefill_impl(const void* q, const void* k, const void* v, vo
   a.causal = causal ? 1 : 0;
   a.window = window;
   a.n_sink = window > 0 ? n_sink : 0;  // without a window every past key is visible anyway
+  a.rope_cos = opt ? opt->rope_cos : nullptr;
+  a.rope_sin = opt ? opt->rope_sin : nullptr;
+  a.rope_rows = opt ? opt->rope_rows : 0;
   return from_hip(dtype == GQA_DTYPE_BF16 ? gqa::launch_prefill_bf16(a, stream)
                                           : gqa::launch_prefill_f32(a, stream));
 }
@@ -139,7 +160,7 @@ gqa_status_t gqa_attn_prefill(const void* q, const void* k, const void* v, void*
                               int Tq, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
                               const int32_t* cu_seqlens, int max_seqlen, gqa_dtype_t dtype,
                               hipStream_t stream) {
-  return prefill_impl(q, k, v, out, B, Tq, Tkv, Hq, Hkv, d, scale, causal, 0, 0, cu_seqlens,
+  return prefill_impl(q, k, v, out, B, Tq, Tkv, Hq, Hkv, d, scale, causal, nullptr, cu_seqlens,
                       max_seqlen, dtype, stream);
 }
 
@@ -147,7 +168,17 @@ gqa_status_t gqa_attn_prefill_window(const void* q, const void* k, const void* v
                                      int B, int Tq, int Tkv, int Hq, int Hkv, int d, float scale,
                                      int window, int n_sink, const int32_t* cu_seqlens,
                                      int max_seqlen, gqa_dtype_t dtype, hipStream_t stream) {
-  return prefill_impl(q, k, v, out, B, Tq, Tkv, Hq, Hkv, d, scale, 1, window, n_sink, cu_seqlens,
+  gqa_attn_options_t o = {window, n_sink, nullptr, nullptr, 0};
+  return prefill_impl(q, k, v, out, B, Tq, Tkv, Hq, Hkv, d, scale, 1, &o, cu_seqlens, max_seqlen,
+                      dtype, stream);
+}
+
+gqa_status_t gqa_attn_prefill_ex(const void* q, const void* k, const void* v, void* out, int B,
+                                 int Tq, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
+                                 const int32_t* cu_seqlens, int max_seqlen,
+                                 const gqa_attn_options_t* options, gqa_dtype_t dtype,
+                                 hipStream_t stream) {
+  return prefill_impl(q, k, v, out, B, Tq, Tkv, Hq, Hkv, d, scale, causal, options, cu_seqlens,
                       max_seqlen, dtype, stream);
 }
 
@@ -158,16 +189,18 @@ size_t gqa_attn_decode_workspace_bytes(int B, int Tkv, int Hq, int Hkv, int d) {
 
 static gqa_status_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
                                 void* out, int B, int Tkv, int Hq, int Hkv, int d, float scale,
-                                const int32_t* cache_lens, int window, int n_sink, void* workspace,
-                                size_t workspace_bytes, gqa_dtype_t dtype, hipStream_t stream) {
+                                const int32_t* cache_lens, const gqa_attn_options_t* opt,
+                                void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
+                                hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !out) return GQA_ERR_NULL_PTR;
   if (B <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_SHAPE;
   if (!isfinite(scale) || !(scale > 0.f)) return GQA_ERR_SHAPE;
-  if (window < 0 || n_sink < 0) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0) return GQA_ERR_GROUPING;
   if (!dtype_ok(dtype) || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
-  if ((cache_lens || window > 0 || n_sink > 0) && dtype != GQA_DTYPE_BF16)
-    return GQA_ERR_UNSUPPORTED;
+  if (const gqa_status_t st = check_options(opt, dtype, Tkv)) return st;
+  if (cache_lens && dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+  const int window = opt ? opt->window : 0;
+  const int n_sink = opt ? opt->n_sink : 0;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return GQA_ERR_UNSUPPORTED;
   if (dtype == GQA_DTYPE_F32 && B > kMaxGridYZ) return GQA_ERR_UNSUPPORTED;
@@ -207,6 +240,8 @@ static gqa_status_t decode_impl(const void* q, const void* k_cache, const void* 
     a.causal = 0;
     a.window = 0;
     a.n_sink = 0;
+    a.rope_cos = a.rope_sin = nullptr;
+    a.rope_rows = 0;
     return from_hip(gqa::launch_prefill_f32(a, stream));
   }
   const size_t need = gqa::decode_workspace_bytes(B, Tkv, Hq, Hkv, d);
@@ -232,6 +267,9 @@ static gqa_status_t decode_impl(const void* q, const void* k_cache, const void* 
   a.lens = cache_lens;
   a.window = window;
   a.n_sink = window > 0 ? n_sink : 0;
+  a.rope_cos = opt ? opt->rope_cos : nullptr;
+  a.rope_sin = opt ? opt->rope_sin : nullptr;
+  a.rope_rows = opt ? opt->rope_rows : 0;
   return from_hip(gqa::launch_decode_bf16(a, stream));
 }
 
@@ -240,7 +278,7 @@ gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_c
                              void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
                              hipStream_t stream) {
   (void)causal;  // a single query at the last position sees the whole cache
-  return decode_impl(q, k_cache, v_cache, out, B, Tkv, Hq, Hkv, d, scale, nullptr, 0, 0,
+  return decode_impl(q, k_cache, v_cache, out, B, Tkv, Hq, Hkv, d, scale, nullptr, nullptr,
                      workspace, workspace_bytes, dtype, stream);
 }
 
@@ -249,8 +287,18 @@ gqa_status_t gqa_attn_decode_ragged(const void* q, const void* k_cache, const vo
                                     float scale, const int32_t* cache_lens, int window,
                                     int n_sink, void* workspace, size_t workspace_bytes,
                                     gqa_dtype_t dtype, hipStream_t stream) {
-  return decode_impl(q, k_cache, v_cache, out, B, Tmax, Hq, Hkv, d, scale, cache_lens, window,
-                     n_sink, workspace, workspace_bytes, dtype, stream);
+  gqa_attn_options_t o = {window, n_sink, nullptr, nullptr, 0};
+  return decode_impl(q, k_cache, v_cache, out, B, Tmax, Hq, Hkv, d, scale, cache_lens, &o,
+                     workspace, workspace_bytes, dtype, stream);
+}
+
+gqa_status_t gqa_attn_decode_ex(const void* q, const void* k_cache, const void* v_cache,
+                                void* out, int B, int Tmax, int Hq, int Hkv, int d, float scale,
+                                const int32_t* cache_lens, const gqa_attn_options_t* options,
+                                void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
+                                hipStream_t stream) {
+  return decode_impl(q, k_cache, v_cache, out, B, Tmax, Hq, Hkv, d, scale, cache_lens, options,
+                     workspace, workspace_bytes, dtype, stream);
 }
 
 gqa_status_t gqa_fold_kv(const void* src, void* dst, int B, int T, int H, int g, int d,

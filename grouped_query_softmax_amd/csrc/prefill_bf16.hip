@@ -91,7 +91,7 @@ struct PPCfg {
   static_assert(kVBase < 65536 && 3 * kVBytes < 65536, "stage offsets fit LDS immediates");
 };
 
-template <int D>
+template <int D, bool ROPE>
 __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int heads_per_wg,
                                                          int pos_per_wg, int head_tiles, int gz) {
   using C = PPCfg<D>;
@@ -177,6 +177,12 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         u32x4 w = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * s) : u32x4{0, 0, 0, 0};
+        if constexpr (ROPE) {
+          // query at position pos + off (the causal mask's alignment); pairs 8s + 4hh .. +3
+          const int ti = (pos + off) * (D / 2) + 8 * s + 4 * hh;
+          w = rope_chunk(w, *reinterpret_cast<const f32x4*>(a.rope_cos + ti),
+                         *reinterpret_cast<const f32x4*>(a.rope_sin + ti));
+        }
         qf[s] = __builtin_bit_cast(bf16x8, w);
       }
     }
@@ -209,6 +215,18 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
     // one staging register file per thread: group B stages K tiles, group A stages V tiles
     constexpr int kStageRegs = (4 * C::kKLoads > 4 * VW) ? 4 * C::kKLoads : 4 * VW;
     uint32_t stg[kStageRegs];
+    // rotary embedding of the staged keys: key j of the item sits at position j; the tables are
+    // read through a range-checked resource (rows past the table read as 0: those keys are the
+    // zero padding of the last tile)
+    [[maybe_unused]] f32x4 rc[ROPE ? C::kKLoads : 1], rs[ROPE ? C::kKLoads : 1];
+    [[maybe_unused]] __amdgpu_buffer_rsrc_t crs, srs;
+    if constexpr (ROPE) {
+      const int tbytes = a.rope_rows * (D / 2) * 4;
+      crs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.rope_cos), 0, tbytes,
+                                              kBufWord3);
+      srs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.rope_sin), 0, tbytes,
+                                              kBufWord3);
+    }
     auto load_k = [&](int t) {
       const int soff = ktile(t) * kKT * row_bytes;
 #pragma unroll
@@ -218,11 +236,26 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
         for (int e = 0; e < 4; ++e) stg[4 * i + e] = w[e];
       }
     };
+    // the table rows of the keys staged next; issued at the start of a matrix phase so they
+    // arrive by its end, where the keys are turned and written to LDS
+    auto load_rope = [&](int t) {
+      if constexpr (ROPE) {
+#pragma unroll
+        for (int i = 0; i < C::kKLoads; ++i) {
+          const int idx = i * C::kGroupThreads + gtid;
+          const int key = ktile(t) * kKT + idx / C::kChunks;
+          const int toff = (key * (D / 2) + 4 * (idx % C::kChunks)) * 4;
+          rc[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, toff, 0, 0));
+          rs[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, toff, 0, 0));
+        }
+      }
+    };
     auto store_k = [&](int stage) {
       char* base = smem + stage * C::kKBytes;
 #pragma unroll
       for (int i = 0; i < C::kKLoads; ++i) {
-        const u32x4 w = {stg[4 * i], stg[4 * i + 1], stg[4 * i + 2], stg[4 * i + 3]};
+        u32x4 w = {stg[4 * i], stg[4 * i + 1], stg[4 * i + 2], stg[4 * i + 3]};
+        if constexpr (ROPE) w = rope_chunk(w, rc[i], rs[i]);
         lds_write<u32x4>(base, k_dst[i], w);
       }
     };
@@ -387,6 +420,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
       load_v(1);
     } else {
       load_k(0);
+      load_rope(0);
       store_k(0);
       load_k(1);
     }
@@ -405,6 +439,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
     if (grp_a) {
       v_phase(0);
     } else {
+      load_rope(1);
       m_first();
       store_k(1);
       load_k(2);
@@ -423,6 +458,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
       if (grp_a) {
         v_phase(t);
       } else {
+        load_rope(t + 1);
         m_full(t);
         store_k(st_next);
         load_k(t + 2);
@@ -455,7 +491,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
   }
 }
 
-template <int D>
+template <int D, bool ROPE>
 hipError_t launch_pp(const PrefillArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int heads_per_wg = G < kCols ? G : kCols;
@@ -464,7 +500,7 @@ hipError_t launch_pp(const PrefillArgs& a, hipStream_t s) {
   const int ntiles = (a.max_tq + pos_per_wg - 1) / pos_per_wg;
   const int gz = a.causal ? (ntiles + 1) / 2 : ntiles;
   const dim3 grid(a.Hkv * head_tiles * a.nitems * gz);
-  hipLaunchKernelGGL(prefill_pp_kernel<D>, grid, dim3(512), 0, s, a, heads_per_wg, pos_per_wg,
+  hipLaunchKernelGGL((prefill_pp_kernel<D, ROPE>), grid, dim3(512), 0, s, a, heads_per_wg, pos_per_wg,
                      head_tiles, gz);
   return hipGetLastError();
 }
@@ -475,8 +511,8 @@ int prefill_bf16_cols() { return kCols; }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   switch (a.d) {
-    case 64: return launch_pp<64>(a, s);
-    case 128: return launch_pp<128>(a, s);
+    case 64: return a.rope_cos ? launch_pp<64, true>(a, s) : launch_pp<64, false>(a, s);
+    case 128: return a.rope_cos ? launch_pp<128, true>(a, s) : launch_pp<128, false>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

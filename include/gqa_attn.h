@@ -73,6 +73,38 @@ gqa_status_t gqa_attn_prefill(const void* q, const void* k, const void* v, void*
                               hipStream_t stream);
 
 /*
+ * Options of the extended entry points (course page "Week 7. Attention", step 3). A NULL
+ * options pointer means all defaults (no window, no rotation).
+ *   window, n_sink: causal sliding window and sink keys, as for gqa_attn_prefill_window
+ *                   (needs causal != 0 in gqa_attn_prefill_ex).
+ *   rope_cos, rope_sin: rotary position embedding, DEVICE fp32 tables [rope_rows][d/2], row p
+ *                   holding cos / sin of p * theta_i (theta_i = base^(-2i/d) normally; any table
+ *                   is accepted). Coordinates (2i, 2i+1) form one pair (a complex number turned
+ *                   by p * theta_i). Both NULL: no rotation; exactly one NULL: GQA_ERR_NULL_PTR.
+ *                   16-byte aligned. Prefill turns query t at position t + (Tkv - Tq) and key j
+ *                   at position j (per sequence in a packed batch), inside the kernel; decode
+ *                   turns the query at position cache_lens[b] - 1 and expects the cache to hold
+ *                   keys already turned at their positions.
+ *   rope_rows:      rows of the tables; must cover every position used (>= Tkv, >= max_seqlen
+ *                   for packed batches, >= Tmax for decode), else GQA_ERR_SHAPE.
+ * Windows and rotation are bf16 only (GQA_ERR_UNSUPPORTED for f32).
+ */
+typedef struct {
+  int window;
+  int n_sink;
+  const float* rope_cos;
+  const float* rope_sin;
+  int rope_rows;
+} gqa_attn_options_t;
+
+/* gqa_attn_prefill with options (window, sinks, rotary embedding). */
+gqa_status_t gqa_attn_prefill_ex(const void* q, const void* k, const void* v, void* out, int B,
+                                 int Tq, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
+                                 const int32_t* cu_seqlens, int max_seqlen,
+                                 const gqa_attn_options_t* options, gqa_dtype_t dtype,
+                                 hipStream_t stream);
+
+/*
  * Prefill with a causal sliding window and attention sinks (course page "Week 7. Attention",
  * step 3: the window bounds what each query sees; the first tokens stay visible as sinks).
  * Same tensors, layout, packing and errors as gqa_attn_prefill with causal = 1; the query at
@@ -121,6 +153,13 @@ gqa_status_t gqa_attn_decode_ragged(const void* q, const void* k_cache, const vo
                                     float scale, const int32_t* cache_lens, int window,
                                     int n_sink, void* workspace, size_t workspace_bytes,
                                     gqa_dtype_t dtype, hipStream_t stream);
+
+/* gqa_attn_decode_ragged with options (window, sinks, rotary embedding of the query). */
+gqa_status_t gqa_attn_decode_ex(const void* q, const void* k_cache, const void* v_cache,
+                                void* out, int B, int Tmax, int Hq, int Hkv, int d, float scale,
+                                const int32_t* cache_lens, const gqa_attn_options_t* options,
+                                void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
+                                hipStream_t stream);
 
 /*
  * Fold key/value heads: src [B, T, H, d] -> dst [B, T, g, d] with

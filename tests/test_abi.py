@@ -93,6 +93,28 @@ def test_window_and_ragged_validation(lib):
     assert rag(Tmax=1 << 22) == B.GQA_ERR_UNSUPPORTED
 
 
+def test_extended_options_validation(lib):
+    Opt = B.AttnOptions
+    T = W + 8192   # fake 16-byte aligned table addresses
+
+    def pex(opt, causal=1, dt=BF16, d=128, Tkv=8):
+        return lib.gqa_attn_prefill_ex(Q, K, V, O, 1, 8, Tkv, 8, 2, d, 0.1, causal, None, 0,
+                                       ctypes.byref(opt) if opt is not None else None, dt, None)
+    assert pex(Opt(0, 0, T, None, 8)) == B.GQA_ERR_NULL_PTR          # one table missing
+    assert pex(Opt(0, 0, T, T + 4096, 7)) == B.GQA_ERR_SHAPE         # fewer rows than keys
+    assert pex(Opt(0, 0, T + 4, T + 4096, 8)) == B.GQA_ERR_UNSUPPORTED  # misaligned table
+    assert pex(Opt(0, 0, T, T + 4096, 8), dt=F32, d=16) == B.GQA_ERR_UNSUPPORTED
+    assert pex(Opt(3, 0, None, None, 0), causal=0) == B.GQA_ERR_SHAPE  # windows are causal
+    assert pex(Opt(-1, 0, None, None, 0)) == B.GQA_ERR_SHAPE
+    need = lib.gqa_attn_decode_workspace_bytes(4, 1024, 32, 8, 128)
+
+    def dex(opt, Tmax=1024):
+        return lib.gqa_attn_decode_ex(Q, K, V, O, 4, Tmax, 32, 8, 128, 0.1, None,
+                                      ctypes.byref(opt), W, need, BF16, None)
+    assert dex(Opt(0, 0, T, T + 4096, 1023)) == B.GQA_ERR_SHAPE      # rows must cover Tmax
+    assert dex(Opt(0, 0, None, T, 1024)) == B.GQA_ERR_NULL_PTR
+
+
 def test_decode_validation(lib):
     need = lib.gqa_attn_decode_workspace_bytes(4, 1024, 32, 8, 128)
     assert need > 0 and need % 16 == 0

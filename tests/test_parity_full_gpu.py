@@ -113,3 +113,24 @@ def test_full_ragged_decode_sampled_sequences(gqa):
         ref = orc.attention(qh[b:b + 1], np.ascontiguousarray(kh[b:b + 1, :L]),
                             np.ascontiguousarray(vh[b:b + 1, :L]), causal=True)
         assert_bf16_close(got[b:b + 1], ref, what=f"{w.name} seq {b} len {L}")
+
+
+def test_full_rope_prefill_sampled_rows(gqa):
+    """The headline prefill with the rotary embedding fused into the kernel."""
+    w = workloads.LLAMA_PREFILL
+    say("full-size rope prefill: generating inputs")
+    q, k, v, _ = workloads.make_inputs(w)
+    cos_t, sin_t = workloads.rope_tables(w.Tkv, w.d)
+    say("full-size rope prefill: launching")
+    out = gqa.gqa_attn_prefill_ex(to_dev(q), to_dev(k), to_dev(v), causal=True,
+                                  rope=(to_dev(cos_t), to_dev(sin_t)))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    rows = workloads.sample_rows(w, 160, seed=12)
+    say(f"full-size rope prefill: oracle on {len(rows)} rows")
+    ref = oracle.default().attention_rows(host_view(q), host_view(k), host_view(v), rows,
+                                          causal=True, rope=(cos_t, sin_t))
+    o = out.cpu()
+    got = np.stack([to_f64(o[b, t, h]) for b, t, h in rows])
+    err, rel = assert_bf16_close(got, ref, what="rope prefill")
+    say(f"full-size rope prefill: max-abs {err:.3e} rel {rel:.3e}")

@@ -145,6 +145,15 @@ VARLEN_PREFILL = Workload("varlen_causal_prefill_16k_8k_4k_1k", B=1, Tq=29696, T
 
 
 
+def rope_tables(npos: int, d: int, base: float = 10000.0) -> Tuple[np.ndarray, np.ndarray]:
+    """Rotary-embedding input tables as a caller would pass them: cos / sin of p * theta_i with
+    theta_i = base^(-2i/d) (course page "Week 7. Attention", step 3), evaluated in float64 and
+    stored as float32 arrays [npos, d/2]."""
+    i = np.arange(d // 2, dtype=np.float64)
+    ang = np.arange(npos, dtype=np.float64)[:, None] * (base ** (-2.0 * i / d))[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 def ragged_lengths(B: int, Tmax: int, seed: int) -> Tuple[int, ...]:
     """Seeded per-sequence cache lengths, uniform on 1 .. Tmax (a serving batch at mixed
     progress), with the extremes 1 and Tmax always present."""
