@@ -74,6 +74,9 @@ def _bind(lib):
     lib.oracle_gqa_attention_rows.argtypes = [P, P, P, I, I64, I64, I64, I, I, I, D, I, P, I, P,
                                               I64, P, I64, I64, P, P, I64, I]
     lib.oracle_gqa_attention_rows.restype = I
+    lib.oracle_gqa_attention_bwd.argtypes = [P, P, P, P, I, P, P, P, I64, I64, I64, I, I, I, D,
+                                             I, I64, I64]
+    lib.oracle_gqa_attention_bwd.restype = I
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = I
     return lib
@@ -222,6 +225,24 @@ class Oracle:
         del keep
         self._check(rc)
         return out
+
+    def attention_bwd(self, q, k, v, dout, scale: Optional[float] = None, causal: bool = False,
+                      window: int = 0, n_sink: int = 0):
+        """Gradients (dq, dk, dv) of sum(out * dout) for the forward :meth:`attention`, float64.
+        dk / dv sum the contributions of the G query heads that share each key/value head."""
+        q, k, v, dt, B, Tq, Tkv, Hq, Hkv, d, scale, _, _ = self._common(q, k, v, scale, None)
+        g, dtg = self._prep(dout)
+        if dtg != dt or g.shape != q.shape:
+            raise ValueError("dout must match q in shape and dtype")
+        dq = np.empty((B, Tq, Hq, d), dtype=np.float64)
+        dk = np.empty((B, Tkv, Hkv, d), dtype=np.float64)
+        dv = np.empty((B, Tkv, Hkv, d), dtype=np.float64)
+        rc = self.lib.oracle_gqa_attention_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                               g.ctypes.data, dt, dq.ctypes.data, dk.ctypes.data,
+                                               dv.ctypes.data, B, Tq, Tkv, Hq, Hkv, d, scale,
+                                               int(bool(causal)), int(window), int(n_sink))
+        self._check(rc)
+        return dq, dk, dv
 
     def heads_out(self, q, k, v, g: int, causal: bool = False) -> np.ndarray:
         """The lab's three-way protocol: fold K and V to g heads, then attend with all query heads."""

@@ -407,3 +407,127 @@ int oracle_gqa_attention_rows(const void* q, const void* k, const void* v, int d
   free(items);
   return err;
 }
+
+/* Backward of grouped-query attention, written out from the chain rule in fp64.
+ *   q, dout [B, Tq, Hq, d]; k, v [B, Tkv, Hkv, d] (dtype_in); dq [B, Tq, Hq, d] and
+ *   dk, dv [B, Tkv, Hkv, d] fp64 outputs (dense batches).
+ * For every query row (b, t, head h) with visible keys J (the forward's rule, incl. window):
+ *   s_j = scale q.k_j, P_j = exp(s_j - max) / sum (two-pass, as the forward),
+ *   dP_j = dout.v_j, D = sum_j P_j dP_j, dS_j = P_j (dP_j - D),
+ *   dq = scale sum_j dS_j k_j;  expanded head h: dk_e[j] += scale dS_j q, dv_e[j] += P_j dout.
+ * The key/value heads were replicated G = Hq/Hkv times into the expanded heads (adjacent
+ * copies), so their gradients are the SUM over the G copies (K3 notes, section 4, backward:
+ * the backward of a replication sums, it does not average). */
+int oracle_gqa_attention_bwd(const void* q, const void* k, const void* v, const void* dout,
+                             int dtype_in, double* dq, double* dk, double* dv, int64_t B,
+                             int64_t Tq, int64_t Tkv, int Hq, int Hkv, int d, double scale,
+                             int causal, int64_t window, int64_t n_sink) {
+  if (B <= 0 || Tq <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return ORACLE_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ORACLE_ERR_GROUPING;
+  if ((window > 0 || n_sink > 0) && !causal) return ORACLE_ERR_SHAPE;
+  const int G = Hq / Hkv;
+  const int64_t krows = B * Tkv;
+  double* kw = (double*)malloc(sizeof(double) * (size_t)(krows * Hkv * d));
+  double* vw = (double*)malloc(sizeof(double) * (size_t)(krows * Hkv * d));
+  double* ke = (double*)malloc(sizeof(double) * (size_t)(krows * Hq * d));
+  double* ve = (double*)malloc(sizeof(double) * (size_t)(krows * Hq * d));
+  double* dke = (double*)calloc((size_t)(krows * Hq * d), sizeof(double));
+  double* dve = (double*)calloc((size_t)(krows * Hq * d), sizeof(double));
+  if (!kw || !vw || !ke || !ve || !dke || !dve) {
+    free(kw); free(vw); free(ke); free(ve); free(dke); free(dve);
+    return ORACLE_ERR_ALLOC;
+  }
+  for (int64_t i = 0; i < krows * Hkv * d; ++i) {
+    kw[i] = widen(k, dtype_in, i);
+    vw[i] = widen(v, dtype_in, i);
+  }
+  oracle_expand(kw, ke, 1, krows, Hkv, Hq, d);
+  oracle_expand(vw, ve, 1, krows, Hkv, Hq, d);
+  free(kw);
+  free(vw);
+
+  int err = ORACLE_OK;
+  /* one (batch item, expanded head) per task: each task owns its dk_e / dv_e head slice */
+#pragma omp parallel
+  {
+    double* qh = (double*)malloc(sizeof(double) * (size_t)d);
+    double* gh = (double*)malloc(sizeof(double) * (size_t)d);
+    double* p = (double*)malloc(sizeof(double) * (size_t)Tkv);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)Tkv);
+    if (!qh || !gh || !p || !dp) {
+#pragma omp atomic write
+      err = ORACLE_ERR_ALLOC;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t task = 0; task < B * Hq; ++task) {
+        const int64_t b = task / Hq;
+        const int h = (int)(task % Hq);
+        const int64_t kstride = (int64_t)Hq * d;
+        const double* kh = &ke[(b * Tkv * Hq + h) * (int64_t)d];
+        const double* vh = &ve[(b * Tkv * Hq + h) * (int64_t)d];
+        double* dkh = &dke[(b * Tkv * Hq + h) * (int64_t)d];
+        double* dvh = &dve[(b * Tkv * Hq + h) * (int64_t)d];
+        for (int64_t t = 0; t < Tq; ++t) {
+          const int64_t row = (b * Tq + t) * Hq + h;
+          for (int c = 0; c < d; ++c) {
+            qh[c] = widen(q, dtype_in, row * (int64_t)d + c);
+            gh[c] = widen(dout, dtype_in, row * (int64_t)d + c);
+          }
+          const int64_t nvis = visible_keys(t, Tq, Tkv, causal);
+          const int64_t lo = window_lo(t, Tq, Tkv, window);
+          double* dqr = &dq[row * (int64_t)d];
+          for (int c = 0; c < d; ++c) dqr[c] = 0.0;
+          /* forward probabilities, two-pass */
+          double m = -INFINITY;
+          for (int64_t j = 0; j < nvis; ++j) {
+            if (j < lo && j >= n_sink) continue;
+            double dot = 0.0;
+            for (int c = 0; c < d; ++c) dot += qh[c] * kh[j * kstride + c];
+            p[j] = scale * dot;
+            if (p[j] > m) m = p[j];
+          }
+          if (m == -INFINITY) continue; /* no visible key: no gradient */
+          double l = 0.0;
+          for (int64_t j = 0; j < nvis; ++j) {
+            if (j < lo && j >= n_sink) continue;
+            p[j] = exp(p[j] - m);
+            l += p[j];
+          }
+          double D = 0.0;
+          for (int64_t j = 0; j < nvis; ++j) {
+            if (j < lo && j >= n_sink) continue;
+            p[j] /= l;
+            double dot = 0.0;
+            for (int c = 0; c < d; ++c) dot += gh[c] * vh[j * kstride + c];
+            dp[j] = dot;
+            D += p[j] * dp[j];
+          }
+          for (int64_t j = 0; j < nvis; ++j) {
+            if (j < lo && j >= n_sink) continue;
+            const double ds = p[j] * (dp[j] - D);
+            for (int c = 0; c < d; ++c) {
+              dqr[c] += scale * ds * kh[j * kstride + c];
+              dkh[j * kstride + c] += scale * ds * qh[c];
+              dvh[j * kstride + c] += p[j] * gh[c];
+            }
+          }
+        }
+      }
+    }
+    free(qh); free(gh); free(p); free(dp);
+  }
+  /* fold the expanded-head gradients back: sum over the G copies of each key/value head */
+  for (int64_t r = 0; r < krows; ++r)
+    for (int j = 0; j < Hkv; ++j)
+      for (int c = 0; c < d; ++c) {
+        double sk = 0.0, sv = 0.0;
+        for (int g = 0; g < G; ++g) {
+          sk += dke[(r * Hq + j * G + g) * (int64_t)d + c];
+          sv += dve[(r * Hq + j * G + g) * (int64_t)d + c];
+        }
+        dk[(r * Hkv + j) * (int64_t)d + c] = sk;
+        dv[(r * Hkv + j) * (int64_t)d + c] = sv;
+      }
+  free(ke); free(ve); free(dke); free(dve);
+  return err;
+}

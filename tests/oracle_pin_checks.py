@@ -475,6 +475,81 @@ def check_rope_relative_positions(orc):
                           orc.attention(q, k, v, causal=True))
 
 
+# ------------------------------------------------------------------------------------------------
+# backward (K3 notes, section 4: the gradient of a replicated head is the sum over its copies)
+# ------------------------------------------------------------------------------------------------
+
+def check_bwd_matches_torch_autograd(orc):
+    """Library cross-check: torch fp64 autograd through repeat_interleave + SDPA (an explicit
+    mask table for the causal cases, bottom-right aligned)."""
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(22)
+    for (Tq, Tkv, Hq, Hkv, causal, W, S) in [(6, 6, 4, 2, False, 0, 0), (6, 6, 4, 1, True, 0, 0),
+                                             (4, 9, 6, 3, True, 0, 0), (7, 7, 2, 2, True, 3, 1),
+                                             (5, 5, 8, 2, True, 0, 0)]:
+        d = 8
+        q = rng.standard_normal((2, Tq, Hq, d)); k = rng.standard_normal((2, Tkv, Hkv, d))
+        v = rng.standard_normal((2, Tkv, Hkv, d)); g = rng.standard_normal((2, Tq, Hq, d))
+        dq, dk, dv = orc.attention_bwd(q, k, v, g, causal=causal, window=W, n_sink=S)
+        G = Hq // Hkv
+        qt, kt, vt = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+        mask = torch.from_numpy(_window_mask(Tq, Tkv, W if W > 0 else Tkv + 1, S)) if causal \
+            else None
+        out = F.scaled_dot_product_attention(
+            qt.permute(0, 2, 1, 3), kt.repeat_interleave(G, dim=2).permute(0, 2, 1, 3),
+            vt.repeat_interleave(G, dim=2).permute(0, 2, 1, 3), attn_mask=mask)
+        (out.permute(0, 2, 1, 3) * torch.from_numpy(g)).sum().backward()
+        for name, a, b in (("dq", dq, qt.grad), ("dk", dk, kt.grad), ("dv", dv, vt.grad)):
+            err = np.max(np.abs(a - b.numpy()))
+            assert err <= 1e-12, (name, Tq, Tkv, Hq, Hkv, causal, W, S, err)
+
+
+def check_bwd_finite_differences(orc):
+    """Central differences of L = sum(out * g) through the (pinned) forward oracle."""
+    rng = _rng(23)
+    q = rng.standard_normal((1, 4, 4, 4)); k = rng.standard_normal((1, 5, 2, 4))
+    v = rng.standard_normal((1, 5, 2, 4)); g = rng.standard_normal((1, 4, 4, 4))
+    dq, dk, dv = orc.attention_bwd(q, k, v, g, causal=True)
+    h = 1e-6
+
+    def loss(qq, kk, vv):
+        return float(np.sum(orc.attention(qq, kk, vv, causal=True) * g))
+    for arr, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        for idx in [(0, 0, 0, 0), (0, 3, 1, 2), (0, 2, 0, 3), (0, 1, 1, 1)]:
+            if idx[2] >= arr.shape[2] or idx[1] >= arr.shape[1]:
+                continue
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += h
+            minus[idx] -= h
+            args_p = [q, k, v]; args_m = [q, k, v]
+            args_p[which] = plus; args_m[which] = minus
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - grad[idx]) <= 1e-7, (which, idx, fd, grad[idx])
+
+
+def check_bwd_invariants(orc):
+    """Each row's dS sums to zero over its keys, so the key gradients sum to zero; the value
+    gradients sum to the sum of dout (the weights of a row sum to one); constant value rows give
+    zero query and key gradients; the G-fold sum rule for key/value heads."""
+    rng = _rng(24)
+    q = rng.standard_normal((2, 7, 6, 8)); k = rng.standard_normal((2, 7, 2, 8))
+    v = rng.standard_normal((2, 7, 2, 8)); g = rng.standard_normal((2, 7, 6, 8))
+    dq, dk, dv = orc.attention_bwd(q, k, v, g, causal=True)
+    assert np.max(np.abs(dk.sum(axis=1))) <= 1e-12
+    gsum = g.reshape(2, 7, 2, 3, 8).sum(axis=(1, 3))          # per key/value head group
+    assert np.max(np.abs(dv.sum(axis=1) - gsum)) <= 1e-12
+    vc = np.broadcast_to(rng.standard_normal((2, 1, 2, 8)), v.shape).copy()
+    dq0, dk0, _ = orc.attention_bwd(q, k, vc, g, causal=True)
+    assert np.max(np.abs(dq0)) <= 1e-13 and np.max(np.abs(dk0)) <= 1e-13
+    # sum rule: GQA gradients = MHA gradients of the expanded heads, summed over each group
+    ke, ve = np.repeat(k, 3, axis=2), np.repeat(v, 3, axis=2)
+    dqm, dkm, dvm = orc.attention_bwd(q, ke, ve, g, causal=True)
+    assert np.max(np.abs(dqm - dq)) <= 1e-12
+    assert np.max(np.abs(dkm.reshape(2, 7, 2, 3, 8).sum(axis=3) - dk)) <= 1e-12
+    assert np.max(np.abs(dvm.reshape(2, 7, 2, 3, 8).sum(axis=3) - dv)) <= 1e-12
+
+
 ALL_CHECKS = [
     check_group_of_worked_example,
     check_group_of_rejects_uneven,
@@ -493,6 +568,9 @@ ALL_CHECKS = [
     check_rope_worked_example,
     check_rope_matches_complex_torch,
     check_rope_relative_positions,
+    check_bwd_matches_torch_autograd,
+    check_bwd_finite_differences,
+    check_bwd_invariants,
     check_bottom_right_alignment,
     check_g_equals_h_is_mha,
     check_packed_equals_separate,

@@ -37,6 +37,14 @@ MUTANTS = {
     "rope_wrong_direction": ("x[2 * i] = re * c - im * s;", "x[2 * i] = re * c + im * s;"),
     # course step 3: query position not aligned with the keys (top-left)
     "rope_query_top_left": ("const int64_t qpos = t + (I.Tkv - I.Tq);", "const int64_t qpos = t;"),
+    # backward: replicated key/value heads averaged instead of summed
+    "bwd_fold_mean": ("dk[(r * Hkv + j) * (int64_t)d + c] = sk;",
+                      "dk[(r * Hkv + j) * (int64_t)d + c] = sk / G;"),
+    # backward: softmax Jacobian without the row term D
+    "bwd_no_row_term": ("const double ds = p[j] * (dp[j] - D);", "const double ds = p[j] * dp[j];"),
+    # backward: query gradient without the scale
+    "bwd_dq_no_scale": ("dqr[c] += scale * ds * kh[j * kstride + c];",
+                        "dqr[c] += ds * kh[j * kstride + c];"),
     # value rows weighted by the wrong key
     "value_index_shift": ("out[c] += s[j] * v[j * kstride + c];",
                           "out[c] += s[j] * v[((j + 1) % nvis) * kstride + c];"),
