@@ -146,6 +146,29 @@ def bench_prefill(gqa, w, steps, warmup, torch, seed, rope=False):
     return res, (q, k, v, cu)
 
 
+def bench_backward(gqa, w, steps, warmup, torch, seed):
+    """Backward of the causal prefill (dq, dk, dv): algorithmic work is 10*d flops per unmasked
+    (query, key, head) triple (recomputed scores, dP, dV, dK, dQ), 2.5x the forward's."""
+    q, k, v, _ = device_inputs(w, torch, seed)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 7)
+    dout = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    out = gqa.gqa_attn_prefill_ex(q, k, v, causal=w.causal, lse=lse)
+    ws = torch.empty(gqa.raw_library().gqa_attn_backward_workspace_bytes(w.B, w.Tq, w.Hq),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        gqa.gqa_attn_backward(q, k, v, out, dout, lse, causal=w.causal, workspace=ws)
+
+    ms, wall = time_launches(step, steps, warmup, torch)
+    flops = prefill_flops(w) * 10 // 4
+    avg = sum(ms) / len(ms)
+    return {"workload": w.name + "+backward", "flops_per_launch": flops, "avg_ms": avg,
+            "min_ms": min(ms), "tflops": flops / (avg * 1e-3) / 1e12,
+            "frac_mfma": flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "wall_s": wall}
+
+
 def bench_decode(gqa, w, steps, warmup, torch, seed):
     """Alternates two distinct caches (4 GiB together) so no run rides the previous one's
     last-level cache."""
@@ -248,7 +271,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "mqa", "varlen", "window",
-                                       "ragged", "rope", "copy"],
+                                       "ragged", "rope", "backward", "copy"],
                     default=None,
                     help="time a single workload (for profiling); still prints one JSON line. "
                          "'copy' times a plain 1 GiB device copy, the calibration kernel for "
@@ -306,6 +329,10 @@ def main():
         rp["workload"] = workloads.LLAMA_PREFILL.name + "+rope"
         extra["rope_prefill"] = rp
         log(f"rope prefill: {rp['avg_ms'] * 1e3:.1f} us, {rp['tflops']:.1f} TFLOP/s")
+    if args.only == "backward" or args.all:
+        bw = bench_backward(gqa, workloads.LLAMA_PREFILL, args.steps, args.warmup, torch, 2000)
+        extra["backward"] = bw
+        log(f"backward: {bw['avg_ms'] * 1e3:.1f} us, {bw['tflops']:.1f} TFLOP/s")
     if args.only == "ragged" or args.all:
         rd = bench_decode(gqa, workloads.RAGGED_DECODE, args.steps, args.warmup, torch, 7000)
         extra["ragged_decode"] = rd
@@ -316,11 +343,12 @@ def main():
         log(f"decode: {dec['avg_ms'] * 1e3:.1f} us, {dec['gbs']:.0f} GB/s")
     sha = kernel_source_sha("prefill")
     metric = "GQA prefill TFLOPS (% MFMA peak); decode KV GB/s (% HBM peak)"
-    if pre is None and args.only in ("mqa", "varlen", "window", "rope"):
+    if pre is None and args.only in ("mqa", "varlen", "window", "rope", "backward"):
         key, w = {"mqa": ("mqa_prefill", workloads.MQA_PREFILL),
                   "varlen": ("varlen_prefill", workloads.VARLEN_PREFILL),
                   "window": ("window_prefill", workloads.WINDOW_PREFILL),
-                  "rope": ("rope_prefill", workloads.LLAMA_PREFILL)}[args.only]
+                  "rope": ("rope_prefill", workloads.LLAMA_PREFILL),
+                  "backward": ("backward", workloads.LLAMA_PREFILL)}[args.only]
         pre = extra.pop(key)
     if pre is not None:
         value, unit = pre["tflops"], "TFLOP/s"
@@ -328,7 +356,10 @@ def main():
         traffic = traffic_for("prefill") if w is workloads.LLAMA_PREFILL else None
         roofline = {"bound": "mfma", "achieved": pre["tflops"], "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": pre["tflops"] / PEAK_BF16_TFLOPS,
-                    "traffic": traffic, "kernel": "prefill_pp_kernel<128>",
+                    "traffic": traffic,
+                    "kernel": {"backward": "bwd_rowdot + bwd_dkdv_kernel<128> + bwd_dq_kernel<128>",
+                               "rope": "prefill_pp_kernel<128, true>"}.get(
+                                   args.only, "prefill_pp_kernel<128, false>"),
                     "flops_per_launch": pre["flops_per_launch"],
                     "avg_launch_ms": pre["avg_ms"], "kernel_source_sha": sha}
         config = {"workload": w.name, "B": w.B, "T": w.Tq, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,

@@ -8,6 +8,7 @@ from ._binding import (  # noqa: F401
     GQAError,
     GQAValueError,
     AttnOptions,
+    gqa_attn_backward,
     gqa_attn_decode,
     gqa_attn_decode_ex,
     gqa_attn_decode_ragged,

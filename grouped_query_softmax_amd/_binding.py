@@ -48,11 +48,13 @@ class AttnOptions(ctypes.Structure):
     """``gqa_attn_options_t``: sliding window, sinks and rotary tables of the extended calls."""
     _fields_ = [("window", ctypes.c_int), ("n_sink", ctypes.c_int),
                 ("rope_cos", ctypes.c_void_p), ("rope_sin", ctypes.c_void_p),
-                ("rope_rows", ctypes.c_int)]
+                ("rope_rows", ctypes.c_int), ("lse", ctypes.c_void_p)]
 
 
-def _options(window: int, n_sink: int, rope, d: int) -> AttnOptions:
-    o = AttnOptions(int(window), int(n_sink), None, None, 0)
+def _options(window: int, n_sink: int, rope, d: int, lse=None) -> AttnOptions:
+    o = AttnOptions(int(window), int(n_sink), None, None, 0, None)
+    if lse is not None:
+        o.lse = lse.data_ptr()
     if rope is not None:
         cos_t, sin_t = (_dev(t, name) for t, name in zip(rope, ("rope cos", "rope sin")))
         if (cos_t.dtype != torch.float32 or sin_t.dtype != torch.float32 or cos_t.dim() != 2
@@ -82,6 +84,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_attn_prefill_ex.restype = I
     lib.gqa_attn_decode_ex.argtypes = [P, P, P, P, I, I, I, I, I, F, P, OP, P, SZ, I, P]
     lib.gqa_attn_decode_ex.restype = I
+    lib.gqa_attn_backward_workspace_bytes.argtypes = [I, I, I]
+    lib.gqa_attn_backward_workspace_bytes.restype = SZ
+    lib.gqa_attn_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, SZ, I,
+                                      P]
+    lib.gqa_attn_backward.restype = I
     lib.gqa_fold_kv.argtypes = [P, P, I, I, I, I, I, I, P]
     lib.gqa_fold_kv.restype = I
     lib.gqa_status_string.argtypes = [I]
@@ -204,11 +211,17 @@ def gqa_attn_prefill_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causa
                         window: int = 0, n_sink: int = 0, rope=None,
                         scale: Optional[float] = None, cu_seqlens: Optional[torch.Tensor] = None,
                         max_seqlen: Optional[int] = None, out: Optional[torch.Tensor] = None,
-                        stream=None) -> torch.Tensor:
+                        lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """:func:`gqa_attn_prefill` with a sliding window / sinks and rotary embedding of q and k
-    inside the kernel; rope = (cos, sin) float32 device tables [rows, d/2]. bf16 only."""
+    inside the kernel; rope = (cos, sin) float32 device tables [rows, d/2]; lse: optional float32
+    device output [B, Tq, Hq] receiving each row's log-sum-exp (for the backward). bf16 only."""
     q, k, v, out, dims, cu_ptr, msl = _prefill_args(q, k, v, scale, cu_seqlens, max_seqlen, out)
-    opt = _options(window, n_sink, rope, q.shape[-1])
+    if lse is not None:
+        lse = _dev(lse, "lse")
+        if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]) \
+                or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 device tensor [B, Tq, Hq]")
+    opt = _options(window, n_sink, rope, q.shape[-1], lse)
     rc = _lib.gqa_attn_prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                   *dims, int(bool(causal)), cu_ptr, msl, ctypes.byref(opt),
                                   _dtype_code(q), _stream(stream))
@@ -303,6 +316,36 @@ def gqa_attn_decode_ex(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                                  _stream(stream))
     _check(rc, "gqa_attn_decode_ex")
     return out
+
+
+def gqa_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                      dout: torch.Tensor, lse: torch.Tensor, causal: bool = False,
+                      scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None):
+    """Gradients (dq, dk, dv) of sum(out * dout) for a forward with the same arguments; lse from
+    :func:`gqa_attn_prefill_ex`. Dense bf16 batches."""
+    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    out, dout, lse = _dev(out, "out"), _dev(dout, "dout"), _dev(lse, "lse")
+    if q.dim() != 4 or k.shape != v.shape or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("expected q, out, dout [B,Tq,Hq,d] and k, v [B,Tkv,Hkv,d]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must be float32 [B, Tq, Hq]")
+    B, Tq, Hq, d = q.shape
+    Tkv, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = d ** -0.5
+    need = int(_lib.gqa_attn_backward_workspace_bytes(B, Tq, Hq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    rc = _lib.gqa_attn_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), B, Tq, Tkv, Hq, Hkv, d, float(scale),
+                                int(bool(causal)), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _dtype_code(q),
+                                _stream(stream))
+    _check(rc, "gqa_attn_backward")
+    return dq, dk, dv
 
 
 def gqa_fold_kv(src: torch.Tensor, g: int, out: Optional[torch.Tensor] = None,

@@ -1,0 +1,389 @@
+// backward.hip -- gradients of grouped-query attention (bf16 in, bf16 gradients, fp32 math).
+//
+// From the chain rule for one query row (softmax probabilities P recomputed from the forward's
+// row log-sum-exp L):  P_j = exp(s_j - L), dP_j = dout.v_j, D = dout.out (= sum_j P_j dP_j),
+// dS_j = P_j (dP_j - D);  dq = scale sum_j dS_j k_j,  dk_j = scale sum_i dS_ij q_i,
+// dv_j = sum_i P_ij dout_i. The key/value heads are shared by G query heads (copies of one
+// head), so their gradients are the sum over the G heads of the group (K3 notes, section 4,
+// backward: the backward of a replication is a sum over the copies).
+//
+// Three kernels:
+//   * bwd_rowdot: D = dout.out per query row (fp32).
+//   * bwd_dkdv: one workgroup of 4 waves per (sequence, key/value head, 128 keys); each wave owns
+//     32 keys and keeps their K^T, V^T operands and dK^T, dV^T accumulators in registers while
+//     32-row chunks of (q, dout, L, D) of every query head of the group stream through LDS.
+//     Per chunk: S = Q K^T and dP = dO V^T with the keys as MFMA columns, P and dS in fp32,
+//     then dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T read transposed from LDS
+//     (ds_read_b64_tr_b16) in the key order of the accumulators.
+//   * bwd_dq: one workgroup of 4 waves per (sequence, key/value head, 32 positions x 4 heads of
+//     the group ... 128 query rows); 32-key chunks of K and V stream through LDS. Per chunk:
+//     S^T = K Q^T and dP^T = V dO^T with the queries as columns, dS^T, then dQ^T += K^T dS^T.
+// All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+#include <math.h>
+
+#include "common.hpp"
+
+namespace gqa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32;  // rows of a streamed chunk
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposing LDS read: lane 4r + t of a 16-lane group points at 4 consecutive bf16 of row r;
+// lane j of the group receives column j of rows 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr(char* base, int byte_off) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)((__attribute__((address_space(3))) char*)base + byte_off));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+template <int D>
+struct BwdCfg {
+  static constexpr int kPitch = 2 * D + 16;        // bytes per LDS row of a [rows][D] chunk
+  static constexpr int kChunkBytes = kRows * kPitch;
+  static constexpr int kNS = D / 16;               // MFMA k-steps over d
+  static constexpr int kNMT = D / 32;              // 32-row d tiles
+  static constexpr int kLoadsPerRow = D / 8;       // 16-byte pieces per row
+  static constexpr int kChunkLoads = kRows * kLoadsPerRow / kThreads;  // per thread
+};
+
+// The A operand (8 bf16) of an MFMA whose rows are the d values base .. base+31 and whose k
+// values are the 16 chunk rows 16 ks .. 16 ks + 15 in the accumulator order
+// (rows 16ks+4hh+0..3, then 16ks+8+4hh+0..3), read transposed from a [rows][D] LDS chunk.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(char* chunk, int lane, int base, int ks) {
+  const int hh = lane >> 5, sub = (lane >> 4) & 1, j = lane & 15;
+  const int row = 16 * ks + 4 * hh + (j >> 2);
+  const int off = row * BwdCfg<D>::kPitch + 2 * (base + 16 * sub + 4 * (j & 3));
+  const u32x2 lo = lds_read_tr(chunk, off);
+  const u32x2 hi = lds_read_tr(chunk, off + 8 * BwdCfg<D>::kPitch);
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Packs accumulator values i = 8 ks .. 8 ks + 7 (rows 16ks+4hh+0..3 and 16ks+8+4hh+0..3 of the
+// lane's column) into a B operand.
+__device__ __forceinline__ bf16x8 pack_rows(const float* x, int ks) {
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[8 * ks + 2 * e], x[8 * ks + 2 * e + 1]);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// D = dout . out per row; rows = B*Tq*Hq, one 64-lane wave per 4 rows (16 lanes per row).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restrict__ out,
+                                                         const uint16_t* __restrict__ dout,
+                                                         float* __restrict__ Dr, int64_t rows) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const int64_t row = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) / LPR;
+  const int c = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 o = *reinterpret_cast<const u32x4*>(out + row * D + 8 * c);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(dout + row * D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(bf16_lo(o[e]), bf16_lo(g[e]), acc);
+      acc = fmaf(bf16_hi(o[e]), bf16_hi(g[e]), acc);
+    }
+  }
+#pragma unroll
+  for (int m = LPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
+  if (row < rows && c == 0) Dr[row] = acc;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_tiles) {
+  using C = BwdCfg<D>;
+  constexpr int NS = C::kNS, NMT = C::kNMT;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::kChunkBytes + 2 * kRows * 4];
+  char* sq = smem;                      // q chunk [32][D]
+  char* sg = smem + C::kChunkBytes;     // dout chunk [32][D]
+  float* sl = reinterpret_cast<float*>(smem + 2 * C::kChunkBytes);  // L of the rows (log2 units)
+  float* sd = sl + kRows;               // D of the rows
+
+  const int lin = blockIdx.x;
+  const int kt = lin % key_tiles;
+  const int kvh = (lin / key_tiles) % a.Hkv;
+  const int b = lin / (key_tiles * a.Hkv);
+  const int G = a.Hq / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hh = lane >> 5;
+  const int off = a.Tkv - a.Tq;
+  const float sl2 = a.scale * kLog2e;
+  const int kb0 = kt * kWaves * 32;
+  const int key = kb0 + 32 * wave + n;  // this lane's key column
+  const bool key_ok = key < a.Tkv;
+
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* V = static_cast<const uint16_t*>(a.v);
+  const uint16_t* GO = static_cast<const uint16_t*>(a.dout);
+
+  // K^T and V^T operands of this lane's key: dims 16 s + 8 hh .. +7
+  bf16x8 kop[NS], vop[NS];
+  {
+    const int64_t kr = ((static_cast<int64_t>(b) * a.Tkv + (key_ok ? key : 0)) * a.Hkv + kvh) * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const u32x4 wk = key_ok ? *reinterpret_cast<const u32x4*>(K + kr + 16 * s + 8 * hh)
+                              : u32x4{0, 0, 0, 0};
+      const u32x4 wv = key_ok ? *reinterpret_cast<const u32x4*>(V + kr + 16 * s + 8 * hh)
+                              : u32x4{0, 0, 0, 0};
+      kop[s] = __builtin_bit_cast(bf16x8, wk);
+      vop[s] = __builtin_bit_cast(bf16x8, wv);
+    }
+  }
+  f32x16 dk[NMT], dv[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dk[mt][i] = dv[mt][i] = 0.f;
+
+  // first query position that can see the tile's first key
+  const int qstart = a.causal ? max(0, kb0 - off) / kRows * kRows : 0;
+  const int nchunk = (a.Tq - qstart + kRows - 1) / kRows;
+  // staging: thread covers chunk row r = idx / LPR, piece c = idx % LPR for each of its loads
+  for (int h = 0; h < G; ++h) {
+    const int hq = kvh * G + h;
+    for (int ci = 0; ci < nchunk; ++ci) {
+      const int qc = qstart + ci * kRows;
+      __syncthreads();  // previous chunk fully consumed
+#pragma unroll
+      for (int i = 0; i < C::kChunkLoads; ++i) {
+        const int idx = i * kThreads + tid;
+        const int r = idx / C::kLoadsPerRow, c = idx % C::kLoadsPerRow;
+        const int p = qc + r;
+        u32x4 wq = {0, 0, 0, 0}, wg = {0, 0, 0, 0};
+        if (p < a.Tq) {
+          const int64_t src = ((static_cast<int64_t>(b) * a.Tq + p) * a.Hq + hq) * D + 8 * c;
+          wq = *reinterpret_cast<const u32x4*>(Q + src);
+          wg = *reinterpret_cast<const u32x4*>(GO + src);
+        }
+        *reinterpret_cast<u32x4*>(sq + r * C::kPitch + 16 * c) = wq;
+        *reinterpret_cast<u32x4*>(sg + r * C::kPitch + 16 * c) = wg;
+      }
+      if (tid < kRows) {
+        const int p = qc + tid;
+        const int64_t row = (static_cast<int64_t>(b) * a.Tq + p) * a.Hq + hq;
+        sl[tid] = p < a.Tq ? a.lse[row] * kLog2e : INFINITY;  // rows past the end get P = 0
+        sd[tid] = p < a.Tq ? a.Drow[row] : 0.f;
+      }
+      __syncthreads();
+
+      // S = Q K^T and dP = dO V^T: rows are the chunk's queries, columns this wave's keys
+      f32x16 s_acc = {}, p_acc = {};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 qa = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(sq + n * C::kPitch + 32 * s + 16 * hh));
+        const bf16x8 ga = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(sg + n * C::kPitch + 32 * s + 16 * hh));
+        s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[s], s_acc, 0, 0, 0);
+        p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vop[s], p_acc, 0, 0, 0);
+      }
+      float pr[16], ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = (i >> 2) * 8 + 4 * hh + (i & 3);
+        const int p = qc + r;
+        const bool vis = key_ok && (!a.causal || key <= p + off);
+        const float pv = vis ? fast_exp2(fmaf(s_acc[i], sl2, -sl[r])) : 0.f;
+        pr[i] = pv;
+        ds[i] = pv * (p_acc[i] - sd[r]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 pb = pack_rows(pr, ks);
+        const bf16x8 db = pack_rows(ds, ks);
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+          dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(sg, lane, 32 * mt, ks),
+                                                           pb, dv[mt], 0, 0, 0);
+          dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(sq, lane, 32 * mt, ks),
+                                                           db, dk[mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if (key_ok) {
+    uint16_t* DK = static_cast<uint16_t*>(a.dk);
+    uint16_t* DV = static_cast<uint16_t*>(a.dv);
+    const int64_t orow = ((static_cast<int64_t>(b) * a.Tkv + key) * a.Hkv + kvh) * D;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int dd = mt * 32 + g4 * 8 + hh * 4;
+        u32x2 wk, wv;
+        wk[0] = pack_bf16x2(dk[mt][4 * g4] * a.scale, dk[mt][4 * g4 + 1] * a.scale);
+        wk[1] = pack_bf16x2(dk[mt][4 * g4 + 2] * a.scale, dk[mt][4 * g4 + 3] * a.scale);
+        wv[0] = pack_bf16x2(dv[mt][4 * g4], dv[mt][4 * g4 + 1]);
+        wv[1] = pack_bf16x2(dv[mt][4 * g4 + 2], dv[mt][4 * g4 + 3]);
+        *reinterpret_cast<u32x2*>(DK + orow + dd) = wk;
+        *reinterpret_cast<u32x2*>(DV + orow + dd) = wv;
+      }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per_wg,
+                                                          int heads_per_wg, int head_tiles,
+                                                          int pos_tiles) {
+  using C = BwdCfg<D>;
+  constexpr int NS = C::kNS, NMT = C::kNMT;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::kChunkBytes];
+  char* sk = smem;                   // k chunk [32][D]
+  char* sv = smem + C::kChunkBytes;  // v chunk [32][D]
+
+  const int lin = blockIdx.x;
+  const int pt = lin % pos_tiles;
+  const int rest = lin / pos_tiles;
+  const int ht = rest % head_tiles;
+  const int kvh = (rest / head_tiles) % a.Hkv;
+  const int b = rest / (head_tiles * a.Hkv);
+  const int G = a.Hq / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hh = lane >> 5;
+  const int off = a.Tkv - a.Tq;
+  const float sl2 = a.scale * kLog2e;
+
+  // this lane's query column: 128 (position, head) columns per workgroup, heads fastest
+  const int col = wave * 32 + n;
+  const int p0 = pt * pos_per_wg;
+  const int pl = col / heads_per_wg;
+  const int hi = ht * heads_per_wg + col % heads_per_wg;
+  const bool valid = pl < pos_per_wg && p0 + pl < a.Tq && hi < G;
+  const int pos = min(p0 + pl, a.Tq - 1);
+  const int hq = kvh * G + min(hi, G - 1);
+  const int64_t qrow = (static_cast<int64_t>(b) * a.Tq + pos) * a.Hq + hq;
+
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* V = static_cast<const uint16_t*>(a.v);
+  const uint16_t* GO = static_cast<const uint16_t*>(a.dout);
+  bf16x8 qop[NS], gop[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const u32x4 wq = valid ? *reinterpret_cast<const u32x4*>(Q + qrow * D + 16 * s + 8 * hh)
+                           : u32x4{0, 0, 0, 0};
+    const u32x4 wg = valid ? *reinterpret_cast<const u32x4*>(GO + qrow * D + 16 * s + 8 * hh)
+                           : u32x4{0, 0, 0, 0};
+    qop[s] = __builtin_bit_cast(bf16x8, wq);
+    gop[s] = __builtin_bit_cast(bf16x8, wg);
+  }
+  const float Lr = valid ? a.lse[qrow] * kLog2e : INFINITY;
+  const float Dq = valid ? a.Drow[qrow] : 0.f;
+  f32x16 dq[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq[mt][i] = 0.f;
+
+  const int last = min(p0 + pos_per_wg, a.Tq) - 1;
+  const int kend = a.causal ? min(a.Tkv, last + off + 1) : a.Tkv;
+  const int nchunk = (kend + kRows - 1) / kRows;
+  for (int ci = 0; ci < nchunk; ++ci) {
+    const int kc = ci * kRows;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < C::kChunkLoads; ++i) {
+      const int idx = i * kThreads + tid;
+      const int r = idx / C::kLoadsPerRow, c = idx % C::kLoadsPerRow;
+      const int kk = kc + r;
+      u32x4 wk = {0, 0, 0, 0}, wv = {0, 0, 0, 0};
+      if (kk < a.Tkv) {
+        const int64_t src = ((static_cast<int64_t>(b) * a.Tkv + kk) * a.Hkv + kvh) * D + 8 * c;
+        wk = *reinterpret_cast<const u32x4*>(K + src);
+        wv = *reinterpret_cast<const u32x4*>(V + src);
+      }
+      *reinterpret_cast<u32x4*>(sk + r * C::kPitch + 16 * c) = wk;
+      *reinterpret_cast<u32x4*>(sv + r * C::kPitch + 16 * c) = wv;
+    }
+    __syncthreads();
+    // S^T = K Q^T and dP^T = V dO^T: rows are the chunk's keys, columns the queries
+    f32x16 s_acc = {}, p_acc = {};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 ka = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(sk + n * C::kPitch + 32 * s + 16 * hh));
+      const bf16x8 va = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(sv + n * C::kPitch + 32 * s + 16 * hh));
+      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[s], s_acc, 0, 0, 0);
+      p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gop[s], p_acc, 0, 0, 0);
+    }
+    float ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kk = kc + (i >> 2) * 8 + 4 * hh + (i & 3);
+      const bool vis = kk < a.Tkv && (!a.causal || kk <= pos + off);
+      const float pv = vis ? fast_exp2(fmaf(s_acc[i], sl2, -Lr)) : 0.f;
+      ds[i] = pv * (p_acc[i] - Dq);
+    }
+    // dQ^T += K^T dS^T (K^T read transposed in the accumulator's key order)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 db = pack_rows(ds, ks);
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+        dq[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(sk, lane, 32 * mt, ks), db,
+                                                         dq[mt], 0, 0, 0);
+    }
+  }
+  if (valid) {
+    uint16_t* DQ = static_cast<uint16_t*>(a.dq) + qrow * D;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int dd = mt * 32 + g4 * 8 + hh * 4;
+        u32x2 w;
+        w[0] = pack_bf16x2(dq[mt][4 * g4] * a.scale, dq[mt][4 * g4 + 1] * a.scale);
+        w[1] = pack_bf16x2(dq[mt][4 * g4 + 2] * a.scale, dq[mt][4 * g4 + 3] * a.scale);
+        *reinterpret_cast<u32x2*>(DQ + dd) = w;
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
+  const int64_t rows = static_cast<int64_t>(a.B) * a.Tq * a.Hq;
+  const int64_t rblocks = (rows * (D / 8) + 255) / 256;
+  hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3(static_cast<unsigned>(rblocks)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(a.out), static_cast<const uint16_t*>(a.dout),
+                     a.Drow, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int key_tiles = (a.Tkv + kWaves * 32 - 1) / (kWaves * 32);
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv * key_tiles), dim3(kThreads), 0, s, a,
+                     key_tiles);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int G = a.Hq / a.Hkv;
+  constexpr int kCols = kWaves * 32;
+  const int heads_per_wg = G < kCols ? G : kCols;
+  const int pos_per_wg = kCols / heads_per_wg;
+  const int head_tiles = (G + heads_per_wg - 1) / heads_per_wg;
+  const int pos_tiles = (a.Tq + pos_per_wg - 1) / pos_per_wg;
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.B * a.Hkv * head_tiles * pos_tiles), dim3(kThreads),
+                     0, s, a, pos_per_wg, heads_per_wg, head_tiles, pos_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_bf16(const BwdArgs& a, hipStream_t s) {
+  switch (a.d) {
+    case 64: return launch_bwd_d<64>(a, s);
+    case 128: return launch_bwd_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gqa

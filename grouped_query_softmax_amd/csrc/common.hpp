@@ -8,6 +8,7 @@ namespace gqa {
 
 // log2(e): exponentials are evaluated as 2^(x * log2 e) on the hardware base-2 exponential.
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
@@ -102,6 +103,7 @@ struct PrefillArgs {
   const float* rope_cos;  // rotary tables [rope_rows][d/2] (device), or nullptr
   const float* rope_sin;
   int rope_rows;
+  float* lse;  // optional output: natural-log log-sum-exp of each row's scaled scores
 };
 
 struct DecodeArgs {
@@ -132,11 +134,28 @@ __device__ __forceinline__ u32x4 rope_chunk(u32x4 w, f32x4 c, f32x4 s) {
   return w;
 }
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;  // [B, Tq, Hq] natural-log log-sum-exp of the forward rows
+  float* Drow;       // workspace [B, Tq, Hq]: dout . out
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Tq, Tkv, Hq, Hkv, d;
+  float scale;
+  int causal;
+};
+
 // Launchers (return hipSuccess or the launch error). Shapes have been validated by the caller.
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 int prefill_bf16_cols();  // (position, head) columns per bf16 prefill workgroup
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_backward_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_fold(const void* src, void* dst, int64_t BT, int H, int g, int d, int is_bf16,
                        hipStream_t s);
 

@@ -83,6 +83,7 @@ static gqa_status_t check_options(const gqa_attn_options_t* o, gqa_dtype_t dtype
     if (!aligned16(o->rope_cos) || !aligned16(o->rope_sin)) return GQA_ERR_UNSUPPORTED;
     if (o->rope_rows < rows_needed) return GQA_ERR_SHAPE;
   }
+  if (o->lse && dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
   return GQA_OK;
 }
 
@@ -152,6 +153,8 @@ static gqa_status_t prefill_impl(const void* q, const void* k, const void* v, vo
   a.rope_cos = opt ? opt->rope_cos : nullptr;
   a.rope_sin = opt ? opt->rope_sin : nullptr;
   a.rope_rows = opt ? opt->rope_rows : 0;
+  a.lse = opt ? opt->lse : nullptr;
+  if (a.lse && overlap(a.lse, rows_q * Hq * sizeof(float), q, nq)) return GQA_ERR_ALIAS;
   return from_hip(dtype == GQA_DTYPE_BF16 ? gqa::launch_prefill_bf16(a, stream)
                                           : gqa::launch_prefill_f32(a, stream));
 }
@@ -168,7 +171,7 @@ gqa_status_t gqa_attn_prefill_window(const void* q, const void* k, const void* v
                                      int B, int Tq, int Tkv, int Hq, int Hkv, int d, float scale,
                                      int window, int n_sink, const int32_t* cu_seqlens,
                                      int max_seqlen, gqa_dtype_t dtype, hipStream_t stream) {
-  gqa_attn_options_t o = {window, n_sink, nullptr, nullptr, 0};
+  gqa_attn_options_t o = {window, n_sink, nullptr, nullptr, 0, nullptr};
   return prefill_impl(q, k, v, out, B, Tq, Tkv, Hq, Hkv, d, scale, 1, &o, cu_seqlens, max_seqlen,
                       dtype, stream);
 }
@@ -242,6 +245,7 @@ static gqa_status_t decode_impl(const void* q, const void* k_cache, const void* 
     a.n_sink = 0;
     a.rope_cos = a.rope_sin = nullptr;
     a.rope_rows = 0;
+    a.lse = nullptr;
     return from_hip(gqa::launch_prefill_f32(a, stream));
   }
   const size_t need = gqa::decode_workspace_bytes(B, Tkv, Hq, Hkv, d);
@@ -287,7 +291,7 @@ gqa_status_t gqa_attn_decode_ragged(const void* q, const void* k_cache, const vo
                                     float scale, const int32_t* cache_lens, int window,
                                     int n_sink, void* workspace, size_t workspace_bytes,
                                     gqa_dtype_t dtype, hipStream_t stream) {
-  gqa_attn_options_t o = {window, n_sink, nullptr, nullptr, 0};
+  gqa_attn_options_t o = {window, n_sink, nullptr, nullptr, 0, nullptr};
   return decode_impl(q, k_cache, v_cache, out, B, Tmax, Hq, Hkv, d, scale, cache_lens, &o,
                      workspace, workspace_bytes, dtype, stream);
 }
@@ -299,6 +303,68 @@ gqa_status_t gqa_attn_decode_ex(const void* q, const void* k_cache, const void* 
                                 hipStream_t stream) {
   return decode_impl(q, k_cache, v_cache, out, B, Tmax, Hq, Hkv, d, scale, cache_lens, options,
                      workspace, workspace_bytes, dtype, stream);
+}
+
+size_t gqa_attn_backward_workspace_bytes(int B, int Tq, int Hq) {
+  if (B <= 0 || Tq <= 0 || Hq <= 0) return 0;
+  return (static_cast<size_t>(B) * Tq * Hq * sizeof(float) + 15) / 16 * 16;
+}
+
+gqa_status_t gqa_attn_backward(const void* q, const void* k, const void* v, const void* out,
+                               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                               int B, int Tq, int Tkv, int Hq, int Hkv, int d, float scale,
+                               int causal, void* workspace, size_t workspace_bytes,
+                               gqa_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return GQA_ERR_NULL_PTR;
+  if (B <= 0 || Tq <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.f)) return GQA_ERR_SHAPE;
+  if (causal && Tq > Tkv) return GQA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return GQA_ERR_GROUPING;
+  if (dtype != GQA_DTYPE_BF16 || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q, k, v, out, dout, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GQA_ERR_UNSUPPORTED;
+  const size_t need = gqa_attn_backward_workspace_bytes(B, Tq, Hq);
+  if (!workspace || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GQA_ERR_UNSUPPORTED;
+  const int64_t wgs = static_cast<int64_t>(B) * Hkv * ((Tkv + 127) / 128) +
+                      static_cast<int64_t>(B) * Tq * Hq / 128 + static_cast<int64_t>(B) * Hq;
+  if (wgs > kMaxFlatWorkgroups256 || static_cast<int64_t>(B) * Tq * Hq * d > INT32_MAX * 8LL)
+    return GQA_ERR_UNSUPPORTED;
+  const size_t nq = static_cast<size_t>(B) * Tq * Hq * d * 2;
+  const size_t nk = static_cast<size_t>(B) * Tkv * Hkv * d * 2;
+  const size_t nl = static_cast<size_t>(B) * Tq * Hq * sizeof(float);
+  // every output (and the workspace) must be disjoint from every input and from each other
+  const void* outs[] = {dq, dk, dv, workspace};
+  const size_t outn[] = {nq, nk, nk, need};
+  const void* ins[] = {q, k, v, out, dout, lse};
+  const size_t inn[] = {nq, nk, nk, nq, nq, nl};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(outs[i], outn[i], ins[j], inn[j])) return GQA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outn[i], outs[j], outn[j])) return GQA_ERR_ALIAS;
+  }
+  gqa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.Drow = static_cast<float*>(workspace);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.Tq = Tq;
+  a.Tkv = Tkv;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal ? 1 : 0;
+  return from_hip(gqa::launch_backward_bf16(a, stream));
 }
 
 gqa_status_t gqa_fold_kv(const void* src, void* dst, int B, int T, int H, int g, int d,

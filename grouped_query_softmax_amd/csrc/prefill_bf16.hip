@@ -474,7 +474,10 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
     __syncthreads();
     if (!grp_a) m_last(nkt);
 
-    const float inv = 1.f / pair_sum32(l_run);
+    const float l_tot = pair_sum32(l_run);
+    const float inv = 1.f / l_tot;
+    if (a.lse && valid && hh == 0)  // log-sum-exp of the scaled scores, natural log
+      a.lse[(q0 + pos) * a.Hq + hq] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     if (valid) {
       uint16_t* orow = Op + ((q0 + pos) * a.Hq + hq) * D;
 #pragma unroll

@@ -95,6 +95,9 @@ typedef struct {
   const float* rope_cos;
   const float* rope_sin;
   int rope_rows;
+  float* lse; /* optional OUTPUT (prefill only): DEVICE fp32 [B, Tq, Hq] ([1, total, Hq] when
+                 packed), the natural-log log-sum-exp of each row's scaled scores, as
+                 gqa_attn_backward needs it; NULL: not written */
 } gqa_attn_options_t;
 
 /* gqa_attn_prefill with options (window, sinks, rotary embedding). */
@@ -160,6 +163,24 @@ gqa_status_t gqa_attn_decode_ex(const void* q, const void* k_cache, const void* 
                                 const int32_t* cache_lens, const gqa_attn_options_t* options,
                                 void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
                                 hipStream_t stream);
+
+/*
+ * Backward of gqa_attn_prefill (dense batches): gradients of sum(out * dout).
+ *   q, out, dout [B, Tq, Hq, d]; k, v [B, Tkv, Hkv, d]; lse [B, Tq, Hq] fp32 from the forward
+ *   (gqa_attn_options_t.lse of gqa_attn_prefill_ex, same q, k, v, scale, causal);
+ *   outputs dq [B, Tq, Hq, d], dk, dv [B, Tkv, Hkv, d] in the input dtype, fully overwritten.
+ * The gradient of a key/value head is the SUM of the gradients of the G query heads that read it
+ * (K3 notes, section 4, backward: the backward of a replication sums over the copies).
+ * workspace: caller-owned device memory of at least gqa_attn_backward_workspace_bytes(B, Tq, Hq)
+ * bytes (per-row dout . out). bf16 only, d in {64, 128}. Outputs must not overlap the inputs,
+ * the workspace or each other (GQA_ERR_ALIAS). Errors as for gqa_attn_prefill.
+ */
+size_t gqa_attn_backward_workspace_bytes(int B, int Tq, int Hq);
+gqa_status_t gqa_attn_backward(const void* q, const void* k, const void* v, const void* out,
+                               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                               int B, int Tq, int Tkv, int Hq, int Hkv, int d, float scale,
+                               int causal, void* workspace, size_t workspace_bytes,
+                               gqa_dtype_t dtype, hipStream_t stream);
 
 /*
  * Fold key/value heads: src [B, T, H, d] -> dst [B, T, g, d] with

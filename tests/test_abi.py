@@ -100,19 +100,38 @@ def test_extended_options_validation(lib):
     def pex(opt, causal=1, dt=BF16, d=128, Tkv=8):
         return lib.gqa_attn_prefill_ex(Q, K, V, O, 1, 8, Tkv, 8, 2, d, 0.1, causal, None, 0,
                                        ctypes.byref(opt) if opt is not None else None, dt, None)
-    assert pex(Opt(0, 0, T, None, 8)) == B.GQA_ERR_NULL_PTR          # one table missing
-    assert pex(Opt(0, 0, T, T + 4096, 7)) == B.GQA_ERR_SHAPE         # fewer rows than keys
-    assert pex(Opt(0, 0, T + 4, T + 4096, 8)) == B.GQA_ERR_UNSUPPORTED  # misaligned table
-    assert pex(Opt(0, 0, T, T + 4096, 8), dt=F32, d=16) == B.GQA_ERR_UNSUPPORTED
-    assert pex(Opt(3, 0, None, None, 0), causal=0) == B.GQA_ERR_SHAPE  # windows are causal
-    assert pex(Opt(-1, 0, None, None, 0)) == B.GQA_ERR_SHAPE
+    assert pex(Opt(0, 0, T, None, 8, None)) == B.GQA_ERR_NULL_PTR    # one table missing
+    assert pex(Opt(0, 0, T, T + 4096, 7, None)) == B.GQA_ERR_SHAPE         # fewer rows than keys
+    assert pex(Opt(0, 0, T + 4, T + 4096, 8, None)) == B.GQA_ERR_UNSUPPORTED  # misaligned table
+    assert pex(Opt(0, 0, T, T + 4096, 8, None), dt=F32, d=16) == B.GQA_ERR_UNSUPPORTED
+    assert pex(Opt(3, 0, None, None, 0, None), causal=0) == B.GQA_ERR_SHAPE  # windows are causal
+    assert pex(Opt(-1, 0, None, None, 0, None)) == B.GQA_ERR_SHAPE
     need = lib.gqa_attn_decode_workspace_bytes(4, 1024, 32, 8, 128)
 
     def dex(opt, Tmax=1024):
         return lib.gqa_attn_decode_ex(Q, K, V, O, 4, Tmax, 32, 8, 128, 0.1, None,
                                       ctypes.byref(opt), W, need, BF16, None)
-    assert dex(Opt(0, 0, T, T + 4096, 1023)) == B.GQA_ERR_SHAPE      # rows must cover Tmax
-    assert dex(Opt(0, 0, None, T, 1024)) == B.GQA_ERR_NULL_PTR
+    assert dex(Opt(0, 0, T, T + 4096, 1023, None)) == B.GQA_ERR_SHAPE      # rows must cover Tmax
+    assert dex(Opt(0, 0, None, T, 1024, None)) == B.GQA_ERR_NULL_PTR
+
+
+def test_backward_validation(lib):
+    need = lib.gqa_attn_backward_workspace_bytes(2, 8, 8)
+    assert need >= 2 * 8 * 8 * 4 and need % 16 == 0
+    X = 0x100000000  # more fake, aligned, non-overlapping addresses
+    L, DQ, DK, DV, DO = (X + 0x10000000 * i for i in range(5))
+
+    def bwd(q=Q, lse=L, dq=DQ, ws=W, wsb=need, dt=BF16, d=128, causal=0, Tq=8, Tkv=8, Hkv=2):
+        return lib.gqa_attn_backward(q, K, V, O, DO, lse, dq, DK, DV, 2, Tq, Tkv, 8, Hkv, d, 0.1,
+                                     causal, ws, wsb, dt, None)
+    assert bwd(lse=None) == B.GQA_ERR_NULL_PTR
+    assert bwd(Hkv=3) == B.GQA_ERR_GROUPING
+    assert bwd(dt=F32, d=16) == B.GQA_ERR_UNSUPPORTED
+    assert bwd(Tq=9, causal=1) == B.GQA_ERR_SHAPE
+    assert bwd(ws=None) == B.GQA_ERR_WORKSPACE
+    assert bwd(wsb=need - 16) == B.GQA_ERR_WORKSPACE
+    assert bwd(dq=Q) == B.GQA_ERR_ALIAS             # gradient over its input
+    assert bwd(ws=DQ) == B.GQA_ERR_ALIAS            # workspace over a gradient
 
 
 def test_decode_validation(lib):
