@@ -9,15 +9,18 @@
 //
 // Three kernels:
 //   * bwd_rowdot: D = dout.out per query row (fp32).
-//   * bwd_dkdv: one workgroup of 4 waves per (sequence, key/value head, 128 keys); each wave owns
-//     32 keys and keeps their K^T, V^T operands and dK^T, dV^T accumulators in registers while
-//     32-row chunks of (q, dout, L, D) of every query head of the group stream through LDS.
+//   * bwd_dkdv: one workgroup of 4 waves per (sequence, key/value head, 32 keys); every wave keeps
+//     the keys' K^T, V^T operands and its own dK^T, dV^T accumulators in registers, while the
+//     32-row chunks of (q, dout, L, D) of all query heads of the group are shared out among the
+//     waves (every 4th chunk each, through a per-wave LDS buffer, the next chunk's loads in
+//     flight); the waves' partial sums are added in LDS at the end.
 //     Per chunk: S = Q K^T and dP = dO V^T with the keys as MFMA columns, P and dS in fp32,
 //     then dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T read transposed from LDS
 //     (ds_read_b64_tr_b16) in the key order of the accumulators.
-//   * bwd_dq: one workgroup of 4 waves per (sequence, key/value head, 32 positions x 4 heads of
-//     the group ... 128 query rows); 32-key chunks of K and V stream through LDS. Per chunk:
-//     S^T = K Q^T and dP^T = V dO^T with the queries as columns, dS^T, then dQ^T += K^T dS^T.
+//   * bwd_dq: one workgroup of 4 waves per (sequence, key/value head, 128 (position, head) query
+//     columns; causal: a pair of such tiles, heavy and light); 32-key chunks of K and V stream
+//     through two LDS buffers with the next chunk's loads in flight. Per chunk: S^T = K Q^T and
+//     dP^T = V dO^T with the queries as columns, dS^T, then dQ^T += K^T dS^T.
 // All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 #include <math.h>
 
@@ -96,15 +99,19 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restr
   if (row < rows && c == 0) Dr[row] = acc;
 }
 
+// Keeps the compiler from moving LDS accesses across this point. A wave's LDS region is written
+// and read back only by that wave, whose LDS instructions execute in program order.
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_tiles) {
   using C = BwdCfg<D>;
   constexpr int NS = C::kNS, NMT = C::kNMT;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kChunkBytes + 2 * kRows * 4];
-  char* sq = smem;                      // q chunk [32][D]
-  char* sg = smem + C::kChunkBytes;     // dout chunk [32][D]
-  float* sl = reinterpret_cast<float*>(smem + 2 * C::kChunkBytes);  // L of the rows (log2 units)
-  float* sd = sl + kRows;               // D of the rows
+  constexpr int kWaveBytes = 2 * C::kChunkBytes + 2 * kRows * 4;  // q, dout, L, D of a chunk
+  constexpr int kRedBytes = 2 * 2 * 32 * D * 4;                   // two waves' dK^T, dV^T
+  constexpr int kSmem = kWaves * kWaveBytes > kRedBytes ? kWaves * kWaveBytes : kRedBytes;
+  constexpr int kPieces = kRows * C::kLoadsPerRow / 64;           // 16-byte loads per lane
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
 
   const int lin = blockIdx.x;
   const int kt = lin % key_tiles;
@@ -116,16 +123,20 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_t
   const int n = lane & 31, hh = lane >> 5;
   const int off = a.Tkv - a.Tq;
   const float sl2 = a.scale * kLog2e;
-  const int kb0 = kt * kWaves * 32;
-  const int key = kb0 + 32 * wave + n;  // this lane's key column
+  const int kb0 = kt * 32;
+  const int key = kb0 + n;  // this lane's key column (the 4 waves share the 32 keys)
   const bool key_ok = key < a.Tkv;
+
+  char* sq = smem + wave * kWaveBytes;
+  char* sg = sq + C::kChunkBytes;
+  float* sl = reinterpret_cast<float*>(sg + C::kChunkBytes);
+  float* sd = sl + kRows;
 
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
   const uint16_t* V = static_cast<const uint16_t*>(a.v);
   const uint16_t* GO = static_cast<const uint16_t*>(a.dout);
 
-  // K^T and V^T operands of this lane's key: dims 16 s + 8 hh .. +7
   bf16x8 kop[NS], vop[NS];
   {
     const int64_t kr = ((static_cast<int64_t>(b) * a.Tkv + (key_ok ? key : 0)) * a.Hkv + kvh) * D;
@@ -145,72 +156,125 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_t
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[mt][i] = dv[mt][i] = 0.f;
 
-  // first query position that can see the tile's first key
+  // work items: (query head of the group, 32-row chunk from the first row that can see the
+  // tile's first key); the 4 waves take every 4th item
   const int qstart = a.causal ? max(0, kb0 - off) / kRows * kRows : 0;
-  const int nchunk = (a.Tq - qstart + kRows - 1) / kRows;
-  // staging: thread covers chunk row r = idx / LPR, piece c = idx % LPR for each of its loads
-  for (int h = 0; h < G; ++h) {
-    const int hq = kvh * G + h;
-    for (int ci = 0; ci < nchunk; ++ci) {
-      const int qc = qstart + ci * kRows;
-      __syncthreads();  // previous chunk fully consumed
-#pragma unroll
-      for (int i = 0; i < C::kChunkLoads; ++i) {
-        const int idx = i * kThreads + tid;
-        const int r = idx / C::kLoadsPerRow, c = idx % C::kLoadsPerRow;
-        const int p = qc + r;
-        u32x4 wq = {0, 0, 0, 0}, wg = {0, 0, 0, 0};
-        if (p < a.Tq) {
-          const int64_t src = ((static_cast<int64_t>(b) * a.Tq + p) * a.Hq + hq) * D + 8 * c;
-          wq = *reinterpret_cast<const u32x4*>(Q + src);
-          wg = *reinterpret_cast<const u32x4*>(GO + src);
-        }
-        *reinterpret_cast<u32x4*>(sq + r * C::kPitch + 16 * c) = wq;
-        *reinterpret_cast<u32x4*>(sg + r * C::kPitch + 16 * c) = wg;
-      }
-      if (tid < kRows) {
-        const int p = qc + tid;
-        const int64_t row = (static_cast<int64_t>(b) * a.Tq + p) * a.Hq + hq;
-        sl[tid] = p < a.Tq ? a.lse[row] * kLog2e : INFINITY;  // rows past the end get P = 0
-        sd[tid] = p < a.Tq ? a.Drow[row] : 0.f;
-      }
-      __syncthreads();
+  const int nchunk = qstart < a.Tq ? (a.Tq - qstart + kRows - 1) / kRows : 0;
+  const int nitems = G * nchunk;
 
-      // S = Q K^T and dP = dO V^T: rows are the chunk's queries, columns this wave's keys
-      f32x16 s_acc = {}, p_acc = {};
+  u32x4 pq[kPieces], pg[kPieces];
+  float pl = 0.f, pd = 0.f;
+  auto load = [&](int it) {  // chunk `it` into registers (rows past Tq: zeros)
+    const int h = it / max(nchunk, 1), ci = it - h * max(nchunk, 1);
+    const int hq = kvh * G + h;
+    const int qc = qstart + ci * kRows;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8 qa = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(sq + n * C::kPitch + 32 * s + 16 * hh));
-        const bf16x8 ga = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(sg + n * C::kPitch + 32 * s + 16 * hh));
-        s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[s], s_acc, 0, 0, 0);
-        p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vop[s], p_acc, 0, 0, 0);
-      }
-      float pr[16], ds[16];
+    for (int i = 0; i < kPieces; ++i) {
+      const int idx = i * 64 + lane;
+      const int r = idx / C::kLoadsPerRow, c = idx % C::kLoadsPerRow;
+      const int p = qc + r;
+      const bool ok = it < nitems && p < a.Tq;
+      const int64_t src = ((static_cast<int64_t>(b) * a.Tq + (ok ? p : 0)) * a.Hq + hq) * D + 8 * c;
+      pq[i] = ok ? *reinterpret_cast<const u32x4*>(Q + src) : u32x4{0, 0, 0, 0};
+      pg[i] = ok ? *reinterpret_cast<const u32x4*>(GO + src) : u32x4{0, 0, 0, 0};
+    }
+    const int p = qc + n;
+    const bool ok = it < nitems && p < a.Tq;
+    const int64_t row = (static_cast<int64_t>(b) * a.Tq + (ok ? p : 0)) * a.Hq + hq;
+    pl = ok ? a.lse[row] * kLog2e : INFINITY;  // rows past the end get P = 0
+    pd = ok ? a.Drow[row] : 0.f;
+  };
+  auto store = [&]() {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = (i >> 2) * 8 + 4 * hh + (i & 3);
-        const int p = qc + r;
-        const bool vis = key_ok && (!a.causal || key <= p + off);
-        const float pv = vis ? fast_exp2(fmaf(s_acc[i], sl2, -sl[r])) : 0.f;
-        pr[i] = pv;
-        ds[i] = pv * (p_acc[i] - sd[r]);
-      }
+    for (int i = 0; i < kPieces; ++i) {
+      const int idx = i * 64 + lane;
+      const int r = idx / C::kLoadsPerRow, c = idx % C::kLoadsPerRow;
+      *reinterpret_cast<u32x4*>(sq + r * C::kPitch + 16 * c) = pq[i];
+      *reinterpret_cast<u32x4*>(sg + r * C::kPitch + 16 * c) = pg[i];
+    }
+    if (hh == 0) {
+      sl[n] = pl;
+      sd[n] = pd;
+    }
+  };
+
+  int it = wave;
+  if (it < nitems) {
+    load(it);
+    store();
+  }
+  for (; it < nitems; it += kWaves) {
+    const int h = it / nchunk, ci = it - h * nchunk;
+    const int qc = qstart + ci * kRows;
+    load(it + kWaves);  // next item of this wave, in flight during this one
+    lds_order();
+    f32x16 s_acc = {}, p_acc = {};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 pb = pack_rows(pr, ks);
-        const bf16x8 db = pack_rows(ds, ks);
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 qa = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(sq + n * C::kPitch + 32 * s + 16 * hh));
+      const bf16x8 ga = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(sg + n * C::kPitch + 32 * s + 16 * hh));
+      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[s], s_acc, 0, 0, 0);
+      p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vop[s], p_acc, 0, 0, 0);
+    }
+    float pr[16], ds[16];
 #pragma unroll
-        for (int mt = 0; mt < NMT; ++mt) {
-          dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(sg, lane, 32 * mt, ks),
-                                                           pb, dv[mt], 0, 0, 0);
-          dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(sq, lane, 32 * mt, ks),
-                                                           db, dk[mt], 0, 0, 0);
-        }
+    for (int i = 0; i < 16; ++i) {
+      const int r = (i >> 2) * 8 + 4 * hh + (i & 3);
+      const int p = qc + r;
+      const bool vis = key_ok && (!a.causal || key <= p + off);
+      const float pv = vis ? fast_exp2(fmaf(s_acc[i], sl2, -sl[r])) : 0.f;
+      pr[i] = pv;
+      ds[i] = pv * (p_acc[i] - sd[r]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 pb = pack_rows(pr, ks);
+      const bf16x8 db = pack_rows(ds, ks);
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(sg, lane, 32 * mt, ks),
+                                                         pb, dv[mt], 0, 0, 0);
+        dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(sq, lane, 32 * mt, ks),
+                                                         db, dk[mt], 0, 0, 0);
       }
     }
+    lds_order();
+    if (it + kWaves < nitems) store();
   }
+
+  // sum the 4 waves' partial dK^T, dV^T: waves 2, 3 hand theirs to waves 0, 1, then wave 1 to 0
+  float* red = reinterpret_cast<float*>(smem);
+  auto put = [&](int slot) {
+    float* base = red + slot * 2 * 32 * D;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        base[(mt * 16 + i) * 64 + lane] = dk[mt][i];
+        base[32 * D + (mt * 16 + i) * 64 + lane] = dv[mt][i];
+      }
+  };
+  auto add = [&](int slot) {
+    const float* base = red + slot * 2 * 32 * D;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        dk[mt][i] += base[(mt * 16 + i) * 64 + lane];
+        dv[mt][i] += base[32 * D + (mt * 16 + i) * 64 + lane];
+      }
+  };
+  __syncthreads();  // every wave is done with its chunk buffers
+  if (wave >= 2) put(wave - 2);
+  __syncthreads();
+  if (wave < 2) add(wave);
+  __syncthreads();
+  if (wave == 1) put(0);
+  __syncthreads();
+  if (wave != 0) return;
+  add(0);
   if (key_ok) {
     uint16_t* DK = static_cast<uint16_t*>(a.dk);
     uint16_t* DV = static_cast<uint16_t*>(a.dv);
@@ -234,16 +298,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_t
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per_wg,
                                                           int heads_per_wg, int head_tiles,
-                                                          int pos_tiles) {
+                                                          int pos_tiles, int gz) {
   using C = BwdCfg<D>;
   constexpr int NS = C::kNS, NMT = C::kNMT;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kChunkBytes];
-  char* sk = smem;                   // k chunk [32][D]
-  char* sv = smem + C::kChunkBytes;  // v chunk [32][D]
+  __shared__ __attribute__((aligned(16))) char smem[4 * C::kChunkBytes];  // 2 x (K, V) chunks
 
   const int lin = blockIdx.x;
-  const int pt = lin % pos_tiles;
-  const int rest = lin / pos_tiles;
+  const int z = lin % gz;
+  const int rest = lin / gz;
   const int ht = rest % head_tiles;
   const int kvh = (rest / head_tiles) % a.Hkv;
   const int b = rest / (head_tiles * a.Hkv);
@@ -253,101 +315,136 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
   const int n = lane & 31, hh = lane >> 5;
   const int off = a.Tkv - a.Tq;
   const float sl2 = a.scale * kLog2e;
-
-  // this lane's query column: 128 (position, head) columns per workgroup, heads fastest
-  const int col = wave * 32 + n;
-  const int p0 = pt * pos_per_wg;
-  const int pl = col / heads_per_wg;
-  const int hi = ht * heads_per_wg + col % heads_per_wg;
-  const bool valid = pl < pos_per_wg && p0 + pl < a.Tq && hi < G;
-  const int pos = min(p0 + pl, a.Tq - 1);
-  const int hq = kvh * G + min(hi, G - 1);
-  const int64_t qrow = (static_cast<int64_t>(b) * a.Tq + pos) * a.Hq + hq;
+  // causal: each workgroup takes the query tile pair (pos_tiles-1-z, z), equal work per pair
+  int tiles[2];
+  int ntile_here;
+  if (a.causal) {
+    tiles[0] = pos_tiles - 1 - z;
+    tiles[1] = z;
+    ntile_here = tiles[1] != tiles[0] ? 2 : 1;
+  } else {
+    tiles[0] = z;
+    ntile_here = 1;
+  }
 
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
   const uint16_t* V = static_cast<const uint16_t*>(a.v);
   const uint16_t* GO = static_cast<const uint16_t*>(a.dout);
-  bf16x8 qop[NS], gop[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const u32x4 wq = valid ? *reinterpret_cast<const u32x4*>(Q + qrow * D + 16 * s + 8 * hh)
-                           : u32x4{0, 0, 0, 0};
-    const u32x4 wg = valid ? *reinterpret_cast<const u32x4*>(GO + qrow * D + 16 * s + 8 * hh)
-                           : u32x4{0, 0, 0, 0};
-    qop[s] = __builtin_bit_cast(bf16x8, wq);
-    gop[s] = __builtin_bit_cast(bf16x8, wg);
-  }
-  const float Lr = valid ? a.lse[qrow] * kLog2e : INFINITY;
-  const float Dq = valid ? a.Drow[qrow] : 0.f;
-  f32x16 dq[NMT];
-#pragma unroll
-  for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dq[mt][i] = 0.f;
 
-  const int last = min(p0 + pos_per_wg, a.Tq) - 1;
-  const int kend = a.causal ? min(a.Tkv, last + off + 1) : a.Tkv;
-  const int nchunk = (kend + kRows - 1) / kRows;
-  for (int ci = 0; ci < nchunk; ++ci) {
-    const int kc = ci * kRows;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < C::kChunkLoads; ++i) {
-      const int idx = i * kThreads + tid;
-      const int r = idx / C::kLoadsPerRow, c = idx % C::kLoadsPerRow;
-      const int kk = kc + r;
-      u32x4 wk = {0, 0, 0, 0}, wv = {0, 0, 0, 0};
-      if (kk < a.Tkv) {
-        const int64_t src = ((static_cast<int64_t>(b) * a.Tkv + kk) * a.Hkv + kvh) * D + 8 * c;
-        wk = *reinterpret_cast<const u32x4*>(K + src);
-        wv = *reinterpret_cast<const u32x4*>(V + src);
-      }
-      *reinterpret_cast<u32x4*>(sk + r * C::kPitch + 16 * c) = wk;
-      *reinterpret_cast<u32x4*>(sv + r * C::kPitch + 16 * c) = wv;
-    }
-    __syncthreads();
-    // S^T = K Q^T and dP^T = V dO^T: rows are the chunk's keys, columns the queries
-    f32x16 s_acc = {}, p_acc = {};
+  for (int tt = 0; tt < ntile_here; ++tt) {
+    // this lane's query column: 128 (position, head) columns per workgroup, heads fastest
+    const int col = wave * 32 + n;
+    const int p0 = tiles[tt] * pos_per_wg;
+    const int pl = col / heads_per_wg;
+    const int hi = ht * heads_per_wg + col % heads_per_wg;
+    const bool valid = pl < pos_per_wg && p0 + pl < a.Tq && hi < G;
+    const int pos = min(p0 + pl, a.Tq - 1);
+    const int hq = kvh * G + min(hi, G - 1);
+    const int64_t qrow = (static_cast<int64_t>(b) * a.Tq + pos) * a.Hq + hq;
+
+    bf16x8 qop[NS], gop[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const bf16x8 ka = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(sk + n * C::kPitch + 32 * s + 16 * hh));
-      const bf16x8 va = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(sv + n * C::kPitch + 32 * s + 16 * hh));
-      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[s], s_acc, 0, 0, 0);
-      p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gop[s], p_acc, 0, 0, 0);
+      const u32x4 wq = valid ? *reinterpret_cast<const u32x4*>(Q + qrow * D + 16 * s + 8 * hh)
+                             : u32x4{0, 0, 0, 0};
+      const u32x4 wg = valid ? *reinterpret_cast<const u32x4*>(GO + qrow * D + 16 * s + 8 * hh)
+                             : u32x4{0, 0, 0, 0};
+      qop[s] = __builtin_bit_cast(bf16x8, wq);
+      gop[s] = __builtin_bit_cast(bf16x8, wg);
     }
-    float ds[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kk = kc + (i >> 2) * 8 + 4 * hh + (i & 3);
-      const bool vis = kk < a.Tkv && (!a.causal || kk <= pos + off);
-      const float pv = vis ? fast_exp2(fmaf(s_acc[i], sl2, -Lr)) : 0.f;
-      ds[i] = pv * (p_acc[i] - Dq);
-    }
-    // dQ^T += K^T dS^T (K^T read transposed in the accumulator's key order)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 db = pack_rows(ds, ks);
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
-        dq[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(sk, lane, 32 * mt, ks), db,
-                                                         dq[mt], 0, 0, 0);
-    }
-  }
-  if (valid) {
-    uint16_t* DQ = static_cast<uint16_t*>(a.dq) + qrow * D;
+    const float Lr = valid ? a.lse[qrow] * kLog2e : INFINITY;
+    const float Dq = valid ? a.Drow[qrow] : 0.f;
+    f32x16 dq[NMT];
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int dd = mt * 32 + g4 * 8 + hh * 4;
-        u32x2 w;
-        w[0] = pack_bf16x2(dq[mt][4 * g4] * a.scale, dq[mt][4 * g4 + 1] * a.scale);
-        w[1] = pack_bf16x2(dq[mt][4 * g4 + 2] * a.scale, dq[mt][4 * g4 + 3] * a.scale);
-        *reinterpret_cast<u32x2*>(DQ + dd) = w;
+      for (int i = 0; i < 16; ++i) dq[mt][i] = 0.f;
+
+    const int last = min(p0 + pos_per_wg, a.Tq) - 1;
+    const int kend = a.causal ? min(a.Tkv, last + off + 1) : a.Tkv;
+    const int nchunk = (kend + kRows - 1) / kRows;
+
+    u32x4 pk[C::kChunkLoads], pv[C::kChunkLoads];
+    auto load = [&](int ci) {
+#pragma unroll
+      for (int i = 0; i < C::kChunkLoads; ++i) {
+        const int idx = i * kThreads + tid;
+        const int r = idx / C::kLoadsPerRow, c = idx % C::kLoadsPerRow;
+        const int kk = ci * kRows + r;
+        const bool ok = kk < a.Tkv;
+        const int64_t src =
+            ((static_cast<int64_t>(b) * a.Tkv + (ok ? kk : 0)) * a.Hkv + kvh) * D + 8 * c;
+        pk[i] = ok ? *reinterpret_cast<const u32x4*>(K + src) : u32x4{0, 0, 0, 0};
+        pv[i] = ok ? *reinterpret_cast<const u32x4*>(V + src) : u32x4{0, 0, 0, 0};
       }
+    };
+    auto store = [&](int buf) {
+      char* sk = smem + buf * 2 * C::kChunkBytes;
+      char* sv = sk + C::kChunkBytes;
+#pragma unroll
+      for (int i = 0; i < C::kChunkLoads; ++i) {
+        const int idx = i * kThreads + tid;
+        const int r = idx / C::kLoadsPerRow, c = idx % C::kLoadsPerRow;
+        *reinterpret_cast<u32x4*>(sk + r * C::kPitch + 16 * c) = pk[i];
+        *reinterpret_cast<u32x4*>(sv + r * C::kPitch + 16 * c) = pv[i];
+      }
+    };
+
+    __syncthreads();  // the previous query tile is done with both buffers
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int ci = 0; ci < nchunk; ++ci) {
+      const int kc = ci * kRows;
+      if (ci + 1 < nchunk) load(ci + 1);  // in flight during this chunk
+      char* sk = smem + (ci & 1) * 2 * C::kChunkBytes;
+      char* sv = sk + C::kChunkBytes;
+      // S^T = K Q^T and dP^T = V dO^T: rows are the chunk's keys, columns the queries
+      f32x16 s_acc = {}, p_acc = {};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 ka = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(sk + n * C::kPitch + 32 * s + 16 * hh));
+        const bf16x8 va = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(sv + n * C::kPitch + 32 * s + 16 * hh));
+        s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[s], s_acc, 0, 0, 0);
+        p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gop[s], p_acc, 0, 0, 0);
+      }
+      float ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kk = kc + (i >> 2) * 8 + 4 * hh + (i & 3);
+        const bool vis = kk < a.Tkv && (!a.causal || kk <= pos + off);
+        const float pv2 = vis ? fast_exp2(fmaf(s_acc[i], sl2, -Lr)) : 0.f;
+        ds[i] = pv2 * (p_acc[i] - Dq);
+      }
+      // dQ^T += K^T dS^T (K^T read transposed in the accumulator's key order)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 db = pack_rows(ds, ks);
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+          dq[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(sk, lane, 32 * mt, ks),
+                                                           db, dq[mt], 0, 0, 0);
+      }
+      // the other buffer was last read in chunk ci-1, before the previous barrier
+      if (ci + 1 < nchunk) store((ci + 1) & 1);
+      __syncthreads();
+    }
+    if (valid) {
+      uint16_t* DQ = static_cast<uint16_t*>(a.dq) + qrow * D;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int dd = mt * 32 + g4 * 8 + hh * 4;
+          u32x2 w;
+          w[0] = pack_bf16x2(dq[mt][4 * g4] * a.scale, dq[mt][4 * g4 + 1] * a.scale);
+          w[1] = pack_bf16x2(dq[mt][4 * g4 + 2] * a.scale, dq[mt][4 * g4 + 3] * a.scale);
+          *reinterpret_cast<u32x2*>(DQ + dd) = w;
+        }
+    }
   }
 }
 
@@ -360,7 +457,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
                      a.Drow, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int key_tiles = (a.Tkv + kWaves * 32 - 1) / (kWaves * 32);
+  const int key_tiles = (a.Tkv + 31) / 32;
   hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv * key_tiles), dim3(kThreads), 0, s, a,
                      key_tiles);
   e = hipGetLastError();
@@ -371,8 +468,9 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const int pos_per_wg = kCols / heads_per_wg;
   const int head_tiles = (G + heads_per_wg - 1) / heads_per_wg;
   const int pos_tiles = (a.Tq + pos_per_wg - 1) / pos_per_wg;
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.B * a.Hkv * head_tiles * pos_tiles), dim3(kThreads),
-                     0, s, a, pos_per_wg, heads_per_wg, head_tiles, pos_tiles);
+  const int gz = a.causal ? (pos_tiles + 1) / 2 : pos_tiles;
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.B * a.Hkv * head_tiles * gz), dim3(kThreads), 0, s,
+                     a, pos_per_wg, heads_per_wg, head_tiles, pos_tiles, gz);
   return hipGetLastError();
 }
 

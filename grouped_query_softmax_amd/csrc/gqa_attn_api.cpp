@@ -4,6 +4,7 @@
 // The error convention follows the GQA lab page ("Transformer -- attention by hand: reducing only
 // the key/value heads", steps 1-3 and 6-7): head counts that do not split evenly are an error
 // (GQA_ERR_GROUPING), never silently truncated.
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -327,9 +328,12 @@ gqa_status_t gqa_attn_backward(const void* q, const void* k, const void* v, cons
   const size_t need = gqa_attn_backward_workspace_bytes(B, Tq, Hq);
   if (!workspace || workspace_bytes < need) return GQA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return GQA_ERR_UNSUPPORTED;
-  const int64_t wgs = static_cast<int64_t>(B) * Hkv * ((Tkv + 127) / 128) +
-                      static_cast<int64_t>(B) * Tq * Hq / 128 + static_cast<int64_t>(B) * Hq;
-  if (wgs > kMaxFlatWorkgroups256 || static_cast<int64_t>(B) * Tq * Hq * d > INT32_MAX * 8LL)
+  // the largest of the three launches: rows / (256 / (d / 8)), key tiles of 32, query tiles
+  const int64_t rows = static_cast<int64_t>(B) * Tq * Hq;
+  const int64_t wgs = std::max({rows * (d / 8) / 256 + 1,
+                                static_cast<int64_t>(B) * Hkv * ((Tkv + 31) / 32),
+                                rows / 128 + static_cast<int64_t>(B) * Hkv + 1});
+  if (wgs > kMaxFlatWorkgroups256 || rows * d > INT32_MAX * 8LL)
     return GQA_ERR_UNSUPPORTED;
   const size_t nq = static_cast<size_t>(B) * Tq * Hq * d * 2;
   const size_t nk = static_cast<size_t>(B) * Tkv * Hkv * d * 2;
