@@ -9,11 +9,13 @@
 //
 // Three kernels:
 //   * bwd_rowdot: D = dout.out per query row (fp32).
-//   * bwd_dkdv: one workgroup of 4 waves per (sequence, key/value head, 32 keys); every wave keeps
-//     the keys' K^T, V^T operands and its own dK^T, dV^T accumulators in registers, while the
-//     32-row chunks of (q, dout, L, D) of all query heads of the group are shared out among the
-//     waves (every 4th chunk each, through a per-wave LDS buffer, the next chunk's loads in
-//     flight); the waves' partial sums are added in LDS at the end.
+//   * bwd_dkdv: one workgroup of 4 waves per (sequence, key/value head, 64-key tile; causal: a
+//     pair of tiles, heavy and light). Waves 0 and 2 own the tile's first 32 keys, waves 1 and 3
+//     the other 32, each with the keys' K^T, V^T operands and its own dK^T, dV^T accumulators in
+//     registers. The 32-row chunks of (q, dout, L, D) of all query heads of the group stream
+//     through two LDS stages two at a time (the next pair's loads in flight): waves 0, 1 take the
+//     first chunk of a pair, waves 2, 3 the second, so every chunk read from memory feeds 64
+//     keys. Waves 2, 3 hand their partial sums to waves 0, 1 through LDS at the end of a tile.
 //     Per chunk: S = Q K^T and dP = dO V^T with the keys as MFMA columns, P and dS in fp32,
 //     then dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T read transposed from LDS
 //     (ds_read_b64_tr_b16) in the key order of the accumulators.
@@ -32,6 +34,12 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32;  // rows of a streamed chunk
+// Raw buffer resource word 3: loads at or past num_records bytes return zeros. Only the VGPR
+// offset takes part in that check, so every offset goes there; kOutside is past any buffer here.
+constexpr int kBufWord3 = 0x00020000;
+constexpr unsigned kOutside = 0x80000000u;
+// s_waitcnt immediate for vmcnt(0) with the other counters left alone (expcnt 7, lgkmcnt 15)
+constexpr int kVmcnt0 = 0x0F70;
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -104,194 +112,254 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restr
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_tiles) {
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_tiles, int tile_wgs) {
   using C = BwdCfg<D>;
   constexpr int NS = C::kNS, NMT = C::kNMT;
-  constexpr int kWaveBytes = 2 * C::kChunkBytes + 2 * kRows * 4;  // q, dout, L, D of a chunk
+  constexpr int kSlotBytes = 2 * C::kChunkBytes + 2 * kRows * 4;  // q, dout, L, D of a chunk
+  constexpr int kStageBytes = 2 * kSlotBytes;                     // the two items of a step
   constexpr int kRedBytes = 2 * 2 * 32 * D * 4;                   // two waves' dK^T, dV^T
-  constexpr int kSmem = kWaves * kWaveBytes > kRedBytes ? kWaves * kWaveBytes : kRedBytes;
-  constexpr int kPieces = kRows * C::kLoadsPerRow / 64;           // 16-byte loads per lane
+  constexpr int kSmem = 2 * kStageBytes > kRedBytes ? 2 * kStageBytes : kRedBytes;
+  constexpr int kMatPieces = kRows * C::kLoadsPerRow;             // 16-byte pieces per matrix
+  constexpr int kPieces = 2 * 2 * kMatPieces / kThreads;          // per thread and step
+  static_assert(kMatPieces % kThreads == 0, "a piece index decides its matrix uniformly");
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
 
+  // key/value heads fastest: consecutive workgroups go round-robin to the XCDs, so with 8 heads
+  // each XCD's L2 serves one head, whose query chunks its workgroups read in the same order
   const int lin = blockIdx.x;
-  const int kt = lin % key_tiles;
-  const int kvh = (lin / key_tiles) % a.Hkv;
-  const int b = lin / (key_tiles * a.Hkv);
+  const int kvh = lin % a.Hkv;
+  const int z = (lin / a.Hkv) % tile_wgs;
+  const int b = lin / (tile_wgs * a.Hkv);
   const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = wave & 1;    // which 32 keys of the 64-key tile
+  const int slot = wave >> 1;  // which item of each step (waves 0, 1: the first; 2, 3: the second)
   const int n = lane & 31, hh = lane >> 5;
   const int off = a.Tkv - a.Tq;
   const float sl2 = a.scale * kLog2e;
-  const int kb0 = kt * 32;
-  const int key = kb0 + n;  // this lane's key column (the 4 waves share the 32 keys)
-  const bool key_ok = key < a.Tkv;
-
-  char* sq = smem + wave * kWaveBytes;
-  char* sg = sq + C::kChunkBytes;
-  float* sl = reinterpret_cast<float*>(sg + C::kChunkBytes);
-  float* sd = sl + kRows;
 
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
   const uint16_t* V = static_cast<const uint16_t*>(a.v);
   const uint16_t* GO = static_cast<const uint16_t*>(a.dout);
+  // this sequence's q, dout, L and D (each below 2 GiB: checked by the entry point)
+  const int64_t qe0 = static_cast<int64_t>(b) * a.Tq * a.Hq;
+  const int qbytes = a.Tq * a.Hq * D * 2, lbytes = a.Tq * a.Hq * 4;
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(Q + qe0 * D), 0, qbytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(GO + qe0 * D), 0, qbytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.lse + qe0), 0, lbytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc(a.Drow + qe0, 0, lbytes,
+                                                                       kBufWord3);
 
-  bf16x8 kop[NS], vop[NS];
-  {
-    const int64_t kr = ((static_cast<int64_t>(b) * a.Tkv + (key_ok ? key : 0)) * a.Hkv + kvh) * D;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const u32x4 wk = key_ok ? *reinterpret_cast<const u32x4*>(K + kr + 16 * s + 8 * hh)
-                              : u32x4{0, 0, 0, 0};
-      const u32x4 wv = key_ok ? *reinterpret_cast<const u32x4*>(V + kr + 16 * s + 8 * hh)
-                              : u32x4{0, 0, 0, 0};
-      kop[s] = __builtin_bit_cast(bf16x8, wk);
-      vop[s] = __builtin_bit_cast(bf16x8, wv);
-    }
+  // causal: a workgroup takes the key tile pair (z, key_tiles-1-z), equal work per pair
+  int tiles[2];
+  int ntile_here = 1;
+  tiles[0] = z;
+  if (a.causal) {
+    tiles[1] = key_tiles - 1 - z;
+    ntile_here = tiles[1] != tiles[0] ? 2 : 1;
   }
-  f32x16 dk[NMT], dv[NMT];
-#pragma unroll
-  for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dk[mt][i] = dv[mt][i] = 0.f;
 
-  // work items: (query head of the group, 32-row chunk from the first row that can see the
-  // tile's first key); the 4 waves take every 4th item
-  const int qstart = a.causal ? max(0, kb0 - off) / kRows * kRows : 0;
-  const int nchunk = qstart < a.Tq ? (a.Tq - qstart + kRows - 1) / kRows : 0;
-  const int nitems = G * nchunk;
+  for (int tt = 0; tt < ntile_here; ++tt) {
+    const int kb0 = tiles[tt] * 64;
+    const int kfirst = kb0 + 32 * kh;  // first key of this wave
+    const int key = kfirst + n;        // this lane's key column
+    const bool key_ok = key < a.Tkv;
 
-  u32x4 pq[kPieces], pg[kPieces];
-  float pl = 0.f, pd = 0.f;
-  auto load = [&](int it) {  // chunk `it` into registers (rows past Tq: zeros)
-    const int h = it / max(nchunk, 1), ci = it - h * max(nchunk, 1);
-    const int hq = kvh * G + h;
-    const int qc = qstart + ci * kRows;
+    bf16x8 kop[NS], vop[NS];
+    {
+      const int64_t kr =
+          ((static_cast<int64_t>(b) * a.Tkv + (key_ok ? key : 0)) * a.Hkv + kvh) * D;
 #pragma unroll
-    for (int i = 0; i < kPieces; ++i) {
-      const int idx = i * 64 + lane;
-      const int r = idx / C::kLoadsPerRow, c = idx % C::kLoadsPerRow;
-      const int p = qc + r;
-      const bool ok = it < nitems && p < a.Tq;
-      const int64_t src = ((static_cast<int64_t>(b) * a.Tq + (ok ? p : 0)) * a.Hq + hq) * D + 8 * c;
-      pq[i] = ok ? *reinterpret_cast<const u32x4*>(Q + src) : u32x4{0, 0, 0, 0};
-      pg[i] = ok ? *reinterpret_cast<const u32x4*>(GO + src) : u32x4{0, 0, 0, 0};
-    }
-    const int p = qc + n;
-    const bool ok = it < nitems && p < a.Tq;
-    const int64_t row = (static_cast<int64_t>(b) * a.Tq + (ok ? p : 0)) * a.Hq + hq;
-    pl = ok ? a.lse[row] * kLog2e : INFINITY;  // rows past the end get P = 0
-    pd = ok ? a.Drow[row] : 0.f;
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int i = 0; i < kPieces; ++i) {
-      const int idx = i * 64 + lane;
-      const int r = idx / C::kLoadsPerRow, c = idx % C::kLoadsPerRow;
-      *reinterpret_cast<u32x4*>(sq + r * C::kPitch + 16 * c) = pq[i];
-      *reinterpret_cast<u32x4*>(sg + r * C::kPitch + 16 * c) = pg[i];
-    }
-    if (hh == 0) {
-      sl[n] = pl;
-      sd[n] = pd;
-    }
-  };
-
-  int it = wave;
-  if (it < nitems) {
-    load(it);
-    store();
-  }
-  for (; it < nitems; it += kWaves) {
-    const int h = it / nchunk, ci = it - h * nchunk;
-    const int qc = qstart + ci * kRows;
-    load(it + kWaves);  // next item of this wave, in flight during this one
-    lds_order();
-    f32x16 s_acc = {}, p_acc = {};
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const bf16x8 qa = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(sq + n * C::kPitch + 32 * s + 16 * hh));
-      const bf16x8 ga = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(sg + n * C::kPitch + 32 * s + 16 * hh));
-      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[s], s_acc, 0, 0, 0);
-      p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vop[s], p_acc, 0, 0, 0);
-    }
-    float pr[16], ds[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = (i >> 2) * 8 + 4 * hh + (i & 3);
-      const int p = qc + r;
-      const bool vis = key_ok && (!a.causal || key <= p + off);
-      const float pv = vis ? fast_exp2(fmaf(s_acc[i], sl2, -sl[r])) : 0.f;
-      pr[i] = pv;
-      ds[i] = pv * (p_acc[i] - sd[r]);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 pb = pack_rows(pr, ks);
-      const bf16x8 db = pack_rows(ds, ks);
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-        dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(sg, lane, 32 * mt, ks),
-                                                         pb, dv[mt], 0, 0, 0);
-        dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(sq, lane, 32 * mt, ks),
-                                                         db, dk[mt], 0, 0, 0);
+      for (int s = 0; s < NS; ++s) {
+        const u32x4 wk = key_ok ? *reinterpret_cast<const u32x4*>(K + kr + 16 * s + 8 * hh)
+                                : u32x4{0, 0, 0, 0};
+        const u32x4 wv = key_ok ? *reinterpret_cast<const u32x4*>(V + kr + 16 * s + 8 * hh)
+                                : u32x4{0, 0, 0, 0};
+        kop[s] = __builtin_bit_cast(bf16x8, wk);
+        vop[s] = __builtin_bit_cast(bf16x8, wv);
       }
     }
-    lds_order();
-    if (it + kWaves < nitems) store();
-  }
-
-  // sum the 4 waves' partial dK^T, dV^T: waves 2, 3 hand theirs to waves 0, 1, then wave 1 to 0
-  float* red = reinterpret_cast<float*>(smem);
-  auto put = [&](int slot) {
-    float* base = red + slot * 2 * 32 * D;
+    f32x16 dk[NMT], dv[NMT];
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        base[(mt * 16 + i) * 64 + lane] = dk[mt][i];
-        base[32 * D + (mt * 16 + i) * 64 + lane] = dv[mt][i];
+      for (int i = 0; i < 16; ++i) dk[mt][i] = dv[mt][i] = 0.f;
+
+    // items: (32-row chunk from the first row that can see the tile's first key, query head of
+    // the group), chunks from the last one down and heads inner, so that every workgroup walks
+    // the rows in the same order; step s holds items 2s (waves 0, 1) and 2s+1 (waves 2, 3)
+    const int qstart = a.causal ? max(0, kb0 - off) / kRows * kRows : 0;
+    const int nchunk = qstart < a.Tq ? (a.Tq - qstart + kRows - 1) / kRows : 0;
+    const int nitems = G * nchunk;
+    const int nsteps = (nitems + 1) / 2;
+
+    // the next step's loads: two chunks of q and dout (kPieces 16-byte pieces per thread), and
+    // L and D of their rows (threads 0..63). Buffer loads with the range check doing the
+    // padding: rows past the end get an offset past the buffer and read zeros.
+    u32x4 pr_[kPieces];
+    float pL = 0.f, pD = 0.f;
+    bool pvalid = false;
+    auto load = [&](int st) {
+      int soff[2], srow[2], nrows[2];  // per slot: element offset / row index of the chunk's
+                                       // first row (head h), rows present
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const int it = 2 * st + sl;
+        const int h = it % G, ci = nchunk - 1 - it / G;
+        const int p0 = qstart + ci * kRows;
+        const bool ok = it < nitems;
+        srow[sl] = ok ? p0 * a.Hq + kvh * G + h : 0;
+        soff[sl] = srow[sl] * D;
+        nrows[sl] = ok ? min(kRows, a.Tq - p0) : 0;
       }
-  };
-  auto add = [&](int slot) {
-    const float* base = red + slot * 2 * 32 * D;
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        dk[mt][i] += base[(mt * 16 + i) * 64 + lane];
-        dv[mt][i] += base[32 * D + (mt * 16 + i) * 64 + lane];
+      for (int i = 0; i < kPieces; ++i) {
+        constexpr int kSlotPieces = 2 * kMatPieces;
+        const int sl = (i * kThreads) / kSlotPieces;           // the same for the whole workgroup
+        const int mat = ((i * kThreads) / kMatPieces) & 1;     // 0: q, 1: dout
+        const int pc = (i * kThreads) % kMatPieces + tid;
+        const int r = pc / C::kLoadsPerRow, c = pc % C::kLoadsPerRow;
+        const unsigned vo =
+            r < nrows[sl] ? static_cast<unsigned>(soff[sl] + r * a.Hq * D + 8 * c) * 2u : kOutside;
+        pr_[i] = __builtin_amdgcn_raw_buffer_load_b128(mat ? grs : qrs, vo, 0, 0);
       }
-  };
-  __syncthreads();  // every wave is done with its chunk buffers
-  if (wave >= 2) put(wave - 2);
-  __syncthreads();
-  if (wave < 2) add(wave);
-  __syncthreads();
-  if (wave == 1) put(0);
-  __syncthreads();
-  if (wave != 0) return;
-  add(0);
-  if (key_ok) {
-    uint16_t* DK = static_cast<uint16_t*>(a.dk);
-    uint16_t* DV = static_cast<uint16_t*>(a.dv);
-    const int64_t orow = ((static_cast<int64_t>(b) * a.Tkv + key) * a.Hkv + kvh) * D;
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int dd = mt * 32 + g4 * 8 + hh * 4;
-        u32x2 wk, wv;
-        wk[0] = pack_bf16x2(dk[mt][4 * g4] * a.scale, dk[mt][4 * g4 + 1] * a.scale);
-        wk[1] = pack_bf16x2(dk[mt][4 * g4 + 2] * a.scale, dk[mt][4 * g4 + 3] * a.scale);
-        wv[0] = pack_bf16x2(dv[mt][4 * g4], dv[mt][4 * g4 + 1]);
-        wv[1] = pack_bf16x2(dv[mt][4 * g4 + 2], dv[mt][4 * g4 + 3]);
-        *reinterpret_cast<u32x2*>(DK + orow + dd) = wk;
-        *reinterpret_cast<u32x2*>(DV + orow + dd) = wv;
+      if (tid < 2 * kRows) {
+        const int sl = tid / kRows, r = tid % kRows;
+        pvalid = r < nrows[sl];
+        const unsigned vo = pvalid ? static_cast<unsigned>(srow[sl] + r * a.Hq) * 4u : kOutside;
+        pL = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, vo, 0, 0));
+        pD = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(drs, vo, 0, 0));
       }
+    };
+    auto store = [&](int stage) {
+      char* base = smem + stage * kStageBytes;
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) {
+        const int sl = (i * kThreads) / (2 * kMatPieces);
+        const int mat = ((i * kThreads) / kMatPieces) & 1;
+        const int pc = (i * kThreads) % kMatPieces + tid;
+        const int r = pc / C::kLoadsPerRow, c = pc % C::kLoadsPerRow;
+        *reinterpret_cast<u32x4*>(base + sl * kSlotBytes + mat * C::kChunkBytes + r * C::kPitch +
+                                  16 * c) = pr_[i];
+      }
+      if (tid < 2 * kRows) {
+        const int sl = tid / kRows, r = tid % kRows;
+        float* ld = reinterpret_cast<float*>(base + sl * kSlotBytes + 2 * C::kChunkBytes);
+        ld[r] = pvalid ? pL * kLog2e : INFINITY;  // rows past the end: P = 0
+        ld[kRows + r] = pD;
+      }
+    };
+
+    __syncthreads();  // the previous tile's reduction is done with the LDS
+    if (nsteps > 0) {
+      load(0);
+      store(0);
+    }
+    // nothing in flight from here on (the K/V operands included), so that the loop below waits
+    // only for its own loads
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+    for (int st = 0; st < nsteps; ++st) {
+      if (st + 1 < nsteps) load(st + 1);  // in flight during this step
+      const int it = 2 * st + slot;
+      const int ci = nchunk - 1 - it / G;
+      const int qc = qstart + ci * kRows;
+      // a chunk whose last row cannot see this wave's first key contributes nothing
+      const bool work = it < nitems && (!a.causal || qc + kRows - 1 + off >= kfirst);
+      if (work) {
+        char* sq = smem + (st & 1) * kStageBytes + slot * kSlotBytes;
+        char* sg = sq + C::kChunkBytes;
+        const float* sl = reinterpret_cast<const float*>(sg + C::kChunkBytes);
+        const float* sd = sl + kRows;
+        f32x16 s_acc = {}, p_acc = {};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const bf16x8 qa = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(sq + n * C::kPitch + 32 * s + 16 * hh));
+          const bf16x8 ga = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(sg + n * C::kPitch + 32 * s + 16 * hh));
+          s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[s], s_acc, 0, 0, 0);
+          p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vop[s], p_acc, 0, 0, 0);
+        }
+        float lrow[16], drow[16], pr[16], ds[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = (i >> 2) * 8 + 4 * hh + (i & 3);
+          lrow[i] = sl[r];
+          drow[i] = sd[r];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int p = qc + (i >> 2) * 8 + 4 * hh + (i & 3);
+          const bool vis = key_ok && (!a.causal || key <= p + off);
+          const float e = fast_exp2(fmaf(s_acc[i], sl2, -lrow[i]));
+          pr[i] = vis ? e : 0.f;
+          ds[i] = pr[i] * (p_acc[i] - drow[i]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 pb = pack_rows(pr, ks);
+          const bf16x8 db = pack_rows(ds, ks);
+#pragma unroll
+          for (int mt = 0; mt < NMT; ++mt) {
+            dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(sg, lane, 32 * mt, ks),
+                                                             pb, dv[mt], 0, 0, 0);
+            dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(sq, lane, 32 * mt, ks),
+                                                             db, dk[mt], 0, 0, 0);
+          }
+        }
+      }
+      // the other stage was last read in step st-1, before the previous barrier
+      if (st + 1 < nsteps) store((st + 1) & 1);
+      __syncthreads();
+    }
+
+    // waves 2, 3 hand their partial dK^T, dV^T to waves 0, 1 (same keys), which write them
+    float* red = reinterpret_cast<float*>(smem);
+    if (slot == 1) {
+      float* base = red + kh * 2 * 32 * D;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          base[(mt * 16 + i) * 64 + lane] = dk[mt][i];
+          base[32 * D + (mt * 16 + i) * 64 + lane] = dv[mt][i];
+        }
+    }
+    __syncthreads();
+    if (slot == 0) {
+      const float* base = red + kh * 2 * 32 * D;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          dk[mt][i] += base[(mt * 16 + i) * 64 + lane];
+          dv[mt][i] += base[32 * D + (mt * 16 + i) * 64 + lane];
+        }
+      if (key_ok) {
+        uint16_t* DK = static_cast<uint16_t*>(a.dk);
+        uint16_t* DV = static_cast<uint16_t*>(a.dv);
+        const int64_t orow = ((static_cast<int64_t>(b) * a.Tkv + key) * a.Hkv + kvh) * D;
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int dd = mt * 32 + g4 * 8 + hh * 4;
+            u32x2 wk, wv;
+            wk[0] = pack_bf16x2(dk[mt][4 * g4] * a.scale, dk[mt][4 * g4 + 1] * a.scale);
+            wk[1] = pack_bf16x2(dk[mt][4 * g4 + 2] * a.scale, dk[mt][4 * g4 + 3] * a.scale);
+            wv[0] = pack_bf16x2(dv[mt][4 * g4], dv[mt][4 * g4 + 1]);
+            wv[1] = pack_bf16x2(dv[mt][4 * g4 + 2], dv[mt][4 * g4 + 3]);
+            *reinterpret_cast<u32x2*>(DK + orow + dd) = wk;
+            *reinterpret_cast<u32x2*>(DV + orow + dd) = wv;
+          }
+      }
+    }
   }
 }
 
@@ -303,12 +371,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
   constexpr int NS = C::kNS, NMT = C::kNMT;
   __shared__ __attribute__((aligned(16))) char smem[4 * C::kChunkBytes];  // 2 x (K, V) chunks
 
+  // key/value heads fastest (one head per XCD L2 with 8 heads: its K/V chunks are shared there)
   const int lin = blockIdx.x;
-  const int z = lin % gz;
-  const int rest = lin / gz;
-  const int ht = rest % head_tiles;
-  const int kvh = (rest / head_tiles) % a.Hkv;
-  const int b = rest / (head_tiles * a.Hkv);
+  const int kvh = lin % a.Hkv;
+  const int rest = lin / a.Hkv;
+  const int z = rest % gz;
+  const int ht = (rest / gz) % head_tiles;
+  const int b = rest / (gz * head_tiles);
   const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -331,6 +400,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
   const uint16_t* V = static_cast<const uint16_t*>(a.v);
   const uint16_t* GO = static_cast<const uint16_t*>(a.dout);
+  // this sequence's K and V (below 2 GiB each: checked by the entry point)
+  const int64_t ke0 = static_cast<int64_t>(b) * a.Tkv * a.Hkv * D;
+  const int kbytes = a.Tkv * a.Hkv * D * 2;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(K + ke0), 0, kbytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(V + ke0), 0, kbytes, kBufWord3);
 
   for (int tt = 0; tt < ntile_here; ++tt) {
     // this lane's query column: 128 (position, head) columns per workgroup, heads fastest
@@ -366,17 +442,16 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
     const int nchunk = (kend + kRows - 1) / kRows;
 
     u32x4 pk[C::kChunkLoads], pv[C::kChunkLoads];
-    auto load = [&](int ci) {
+    auto load = [&](int ci) {  // keys past the end read zeros (offset past the buffer)
 #pragma unroll
       for (int i = 0; i < C::kChunkLoads; ++i) {
         const int idx = i * kThreads + tid;
         const int r = idx / C::kLoadsPerRow, c = idx % C::kLoadsPerRow;
         const int kk = ci * kRows + r;
-        const bool ok = kk < a.Tkv;
-        const int64_t src =
-            ((static_cast<int64_t>(b) * a.Tkv + (ok ? kk : 0)) * a.Hkv + kvh) * D + 8 * c;
-        pk[i] = ok ? *reinterpret_cast<const u32x4*>(K + src) : u32x4{0, 0, 0, 0};
-        pv[i] = ok ? *reinterpret_cast<const u32x4*>(V + src) : u32x4{0, 0, 0, 0};
+        const unsigned vo =
+            kk < a.Tkv ? static_cast<unsigned>((kk * a.Hkv + kvh) * D + 8 * c) * 2u : kOutside;
+        pk[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, vo, 0, 0);
+        pv[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, vo, 0, 0);
       }
     };
     auto store = [&](int buf) {
@@ -394,6 +469,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
     __syncthreads();  // the previous query tile is done with both buffers
     load(0);
     store(0);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);  // nothing in flight: the loop waits only for its loads
     __syncthreads();
     for (int ci = 0; ci < nchunk; ++ci) {
       const int kc = ci * kRows;
@@ -457,9 +533,10 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
                      a.Drow, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int key_tiles = (a.Tkv + 31) / 32;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv * key_tiles), dim3(kThreads), 0, s, a,
-                     key_tiles);
+  const int key_tiles = (a.Tkv + 63) / 64;
+  const int tile_wgs = a.causal ? (key_tiles + 1) / 2 : key_tiles;
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv * tile_wgs), dim3(kThreads), 0, s, a,
+                     key_tiles, tile_wgs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;

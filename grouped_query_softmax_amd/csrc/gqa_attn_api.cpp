@@ -333,7 +333,10 @@ gqa_status_t gqa_attn_backward(const void* q, const void* k, const void* v, cons
   const int64_t wgs = std::max({rows * (d / 8) / 256 + 1,
                                 static_cast<int64_t>(B) * Hkv * ((Tkv + 31) / 32),
                                 rows / 128 + static_cast<int64_t>(B) * Hkv + 1});
-  if (wgs > kMaxFlatWorkgroups256 || rows * d > INT32_MAX * 8LL)
+  // one sequence's q / dout and k / v rows are addressed with 32-bit byte offsets
+  const bool seq_fits = static_cast<int64_t>(Tq) * Hq * d * 2 < (1LL << 31) &&
+                        static_cast<int64_t>(Tkv) * Hkv * d * 2 < (1LL << 31);
+  if (wgs > kMaxFlatWorkgroups256 || rows * d > INT32_MAX * 8LL || !seq_fits)
     return GQA_ERR_UNSUPPORTED;
   const size_t nq = static_cast<size_t>(B) * Tq * Hq * d * 2;
   const size_t nk = static_cast<size_t>(B) * Tkv * Hkv * d * 2;
