@@ -77,6 +77,9 @@ def _bind(lib):
     lib.oracle_gqa_attention_bwd.argtypes = [P, P, P, P, I, P, P, P, I64, I64, I64, I, I, I, D,
                                              I, I64, I64]
     lib.oracle_gqa_attention_bwd.restype = I
+    lib.oracle_gva_attention.argtypes = [P, P, P, I, P, I64, I64, I64, I, I, I, D, I, P, I, I64,
+                                         I64]
+    lib.oracle_gva_attention.restype = I
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = I
     return lib
@@ -243,6 +246,42 @@ class Oracle:
                                                int(bool(causal)), int(window), int(n_sink))
         self._check(rc)
         return dq, dk, dv
+
+    def attention_gva(self, q, k, v, scale: Optional[float] = None, causal: bool = False,
+                      cu_seqlens=None, window: int = 0, n_sink: int = 0) -> np.ndarray:
+        """Grouped value attention (K3 notes, section 4): q, k [B,T,H,d] shared by the
+        HV = G*H value heads of v [B,Tkv,HV,d]; value head j uses query/key head j // G.
+        Returns float64 out[B,Tq,HV,d]."""
+        q, dq = self._prep(q)
+        k, dk = self._prep(k)
+        v, dv = self._prep(v)
+        if not (dq == dk == dv):
+            raise TypeError("q, k and v must share a dtype")
+        if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+            raise ValueError("expected q[B,Tq,H,d], k[B,Tkv,H,d], v[B,Tkv,HV,d]")
+        B, Tq, H, d = q.shape
+        if k.shape[0] != B or k.shape[2] != H or k.shape[3] != d or v.shape[:2] != k.shape[:2] \
+                or v.shape[3] != d:
+            raise ValueError("q, k and v disagree on batch, length, heads or head dim")
+        Tkv, HV = k.shape[1], v.shape[2]
+        if HV % H != 0:
+            raise ValueError(f"{HV} value heads do not group evenly over {H} query/key heads")
+        if scale is None:
+            scale = 1.0 / np.sqrt(d)
+        cu, nseq = None, 0
+        if cu_seqlens is not None:
+            cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+            nseq = len(cu) - 1
+            if B != 1 or Tq != Tkv or cu[-1] != Tq:
+                raise ValueError("packed batch needs [1,total,H,d] inputs with total == cu[-1]")
+        out = np.empty((B, Tq, HV, d), dtype=np.float64)
+        rc = self.lib.oracle_gva_attention(q.ctypes.data, k.ctypes.data, v.ctypes.data, dq,
+                                           out.ctypes.data, B, Tq, Tkv, H, HV, d, float(scale),
+                                           int(bool(causal)),
+                                           cu.ctypes.data if cu is not None else None, nseq,
+                                           int(window), int(n_sink))
+        self._check(rc)
+        return out
 
     def heads_out(self, q, k, v, g: int, causal: bool = False) -> np.ndarray:
         """The lab's three-way protocol: fold K and V to g heads, then attend with all query heads."""

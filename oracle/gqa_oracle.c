@@ -408,6 +408,85 @@ int oracle_gqa_attention_rows(const void* q, const void* k, const void* v, int d
   return err;
 }
 
+/* Grouped value attention (K3 notes, section 4, GVA: the inverse sharing). H query/key heads
+ * serve HV = G*H value heads; before attending, q and k are repeated from H to HV heads with
+ * adjacent copies (the notes' forward: repeat_interleave over the head axis), so value head j
+ * is attended with query/key head j / G, and every value head keeps its own values.
+ *   q [B, Tq, H, d], k [B, Tkv, H, d], v [B, Tkv, HV, d] (dtype_in)   (or packed, cu_seqlens)
+ *   out [B, Tq, HV, d] fp64
+ * Steps: widen; expand q and k to HV heads (materialised copies, oracle_expand); for every
+ * item, value head j and query row, attend the expanded query row over the expanded keys of
+ * head j and the values of head j. Mask, window and sinks as for oracle_gqa_attention. */
+int oracle_gva_attention(const void* q, const void* k, const void* v, int dtype_in, double* out,
+                         int64_t B, int64_t Tq, int64_t Tkv, int H, int HV, int d, double scale,
+                         int causal, const int32_t* cu_seqlens, int nseq, int64_t window,
+                         int64_t n_sink) {
+  if (H <= 0 || HV <= 0 || d <= 0) return ORACLE_ERR_SHAPE;
+  if ((window > 0 || n_sink > 0) && !causal) return ORACLE_ERR_SHAPE;
+  if (HV % H != 0) return ORACLE_ERR_GROUPING;
+  item_t* items = NULL;
+  int nitems = 0;
+  int rc = make_items(B, Tq, Tkv, cu_seqlens, nseq, &items, &nitems);
+  if (rc) return rc;
+  const int64_t qrows = cu_seqlens ? cu_seqlens[nseq] : B * Tq;
+  const int64_t krows = cu_seqlens ? cu_seqlens[nseq] : B * Tkv;
+
+  double* qw = (double*)malloc(sizeof(double) * (size_t)(qrows * H * d));
+  double* kw = (double*)malloc(sizeof(double) * (size_t)(krows * H * d));
+  double* qe = (double*)malloc(sizeof(double) * (size_t)(qrows * HV * d));
+  double* ke = (double*)malloc(sizeof(double) * (size_t)(krows * HV * d));
+  double* vw = (double*)malloc(sizeof(double) * (size_t)(krows * HV * d));
+  int* row_item = (int*)malloc(sizeof(int) * (size_t)(qrows > 0 ? qrows : 1));
+  if (!qw || !kw || !qe || !ke || !vw || !row_item) {
+    free(qw); free(kw); free(qe); free(ke); free(vw); free(row_item); free(items);
+    return ORACLE_ERR_ALLOC;
+  }
+  for (int64_t i = 0; i < qrows * H * d; ++i) qw[i] = widen(q, dtype_in, i);
+  for (int64_t i = 0; i < krows * H * d; ++i) kw[i] = widen(k, dtype_in, i);
+  for (int64_t i = 0; i < krows * HV * d; ++i) vw[i] = widen(v, dtype_in, i);
+  oracle_expand(qw, qe, 1, qrows, H, HV, d);
+  oracle_expand(kw, ke, 1, krows, H, HV, d);
+  free(qw);
+  free(kw);
+
+  int64_t max_tkv = 0;
+  for (int it = 0; it < nitems; ++it)
+    if (items[it].Tkv > max_tkv) max_tkv = items[it].Tkv;
+  for (int it = 0; it < nitems; ++it)
+    for (int64_t t = 0; t < items[it].Tq; ++t) row_item[items[it].q_row0 + t] = it;
+
+  int err = ORACLE_OK;
+#pragma omp parallel
+  {
+    double* sc = (double*)malloc(sizeof(double) * (size_t)(max_tkv + 1));
+    if (!sc) {
+#pragma omp atomic write
+      err = ORACLE_ERR_ALLOC;
+    } else {
+#pragma omp for schedule(dynamic, 8)
+      for (int64_t r = 0; r < qrows * HV; ++r) {
+        const int64_t row = r / HV;
+        const int j = (int)(r % HV);
+        const item_t I = items[row_item[row]];
+        const int64_t t = row - I.q_row0;
+        const double* qh = &qe[(row * HV + j) * (int64_t)d];
+        const double* kh = &ke[(I.k_row0 * HV + j) * (int64_t)d];
+        const double* vh = &vw[(I.k_row0 * HV + j) * (int64_t)d];
+        attend_row(qh, kh, vh, (int64_t)HV * d, visible_keys(t, I.Tq, I.Tkv, causal),
+                   window_lo(t, I.Tq, I.Tkv, window), n_sink, d, scale, sc,
+                   &out[(row * HV + j) * (int64_t)d]);
+      }
+    }
+    free(sc);
+  }
+  free(row_item);
+  free(qe);
+  free(ke);
+  free(vw);
+  free(items);
+  return err;
+}
+
 /* Backward of grouped-query attention, written out from the chain rule in fp64.
  *   q, dout [B, Tq, Hq, d]; k, v [B, Tkv, Hkv, d] (dtype_in); dq [B, Tq, Hq, d] and
  *   dk, dv [B, Tkv, Hkv, d] fp64 outputs (dense batches).

@@ -20,6 +20,8 @@ Sources of the facts (page, section):
     sinks: the window bounds what a query sees, the first tokens stay visible; rotary position
     embedding: pairs of coordinates turned by pos * theta_i, theta_i = base^(-2i/d), the pair
     being one complex number, so scores depend only on position differences).
+  * K3 notes, section 4 (GVA): q and k repeated to the value heads with repeat_interleave
+    (forward); the backward of a replication sums over the copies.
 """
 from __future__ import annotations
 
@@ -476,6 +478,58 @@ def check_rope_relative_positions(orc):
 
 
 # ------------------------------------------------------------------------------------------------
+# K3 notes, section 4, GVA: H query/key heads shared by HV = G*H value heads
+# ------------------------------------------------------------------------------------------------
+
+def check_gva_matches_repeat_interleave_sdpa(orc):
+    """Library cross-check of the notes' forward: repeat q and k from H to HV heads with
+    torch's repeat_interleave (adjacent copies), then torch fp64 SDPA per value head."""
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(25)
+    for (Tq, Tkv, H, HV, causal, W, S) in [(6, 6, 2, 4, True, 0, 0), (5, 5, 1, 3, False, 0, 0),
+                                           (4, 9, 3, 6, True, 0, 0), (8, 8, 2, 8, True, 3, 1),
+                                           (7, 7, 4, 4, True, 0, 0)]:
+        d = 8
+        q = rng.standard_normal((2, Tq, H, d)); k = rng.standard_normal((2, Tkv, H, d))
+        v = rng.standard_normal((2, Tkv, HV, d))
+        got = orc.attention_gva(q, k, v, causal=causal, window=W, n_sink=S)
+        G = HV // H
+        qt = torch.from_numpy(q).repeat_interleave(G, dim=2).permute(0, 2, 1, 3).contiguous()
+        kt = torch.from_numpy(k).repeat_interleave(G, dim=2).permute(0, 2, 1, 3).contiguous()
+        vt = torch.from_numpy(v).permute(0, 2, 1, 3).contiguous()
+        mask = torch.from_numpy(_window_mask(Tq, Tkv, W if W > 0 else Tkv + 1, S)) if causal \
+            else None
+        ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+        err = np.max(np.abs(got - ref.permute(0, 2, 1, 3).numpy()))
+        assert err <= 1e-12, (Tq, Tkv, H, HV, causal, W, S, err)
+
+
+def check_gva_shares_weights_within_a_group(orc):
+    """The G value heads of a group use one softmax (the scores of their shared query/key
+    head): value heads built as multiples of one base head give the same multiples of its
+    output, while the groups differ; G = 1 is multi-head attention, bit for bit."""
+    rng = _rng(26)
+    H, G, d = 3, 4, 8
+    q = rng.standard_normal((1, 7, H, d)); k = rng.standard_normal((1, 7, H, d))
+    base = rng.standard_normal((1, 7, H, d))
+    v = np.concatenate([base[:, :, h:h + 1] * (m + 1) for h in range(H) for m in range(G)],
+                       axis=2)
+    out = orc.attention_gva(q, k, v, causal=True)
+    for h in range(H):
+        for m in range(G):
+            err = np.max(np.abs(out[:, :, h * G + m] - (m + 1) * out[:, :, h * G]))
+            assert err <= 1e-13 * (m + 1), (h, m, err)
+    assert np.max(np.abs(out[:, :, 0] - out[:, :, G])) > 1e-3
+    mha = orc.attention(q, k, base, causal=True)
+    assert np.array_equal(orc.attention_gva(q, k, base, causal=True), mha)
+    # constant values per head: every output row is that constant
+    vc = np.broadcast_to(rng.standard_normal((1, 1, H * G, d)), (1, 7, H * G, d)).copy()
+    outc = orc.attention_gva(q, k, vc, causal=False)
+    assert np.max(np.abs(outc - vc)) <= 1e-14
+
+
+# ------------------------------------------------------------------------------------------------
 # backward (K3 notes, section 4: the gradient of a replicated head is the sum over its copies)
 # ------------------------------------------------------------------------------------------------
 
@@ -568,6 +622,8 @@ ALL_CHECKS = [
     check_rope_worked_example,
     check_rope_matches_complex_torch,
     check_rope_relative_positions,
+    check_gva_matches_repeat_interleave_sdpa,
+    check_gva_shares_weights_within_a_group,
     check_bwd_matches_torch_autograd,
     check_bwd_finite_differences,
     check_bwd_invariants,

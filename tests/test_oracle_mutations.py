@@ -45,6 +45,10 @@ MUTANTS = {
     # backward: query gradient without the scale
     "bwd_dq_no_scale": ("dqr[c] += scale * ds * kh[j * kstride + c];",
                         "dqr[c] += ds * kh[j * kstride + c];"),
+    # GVA: every value head of a group reads the group's first value head
+    "gva_value_head_of_group": ("const double* vh = &vw[(I.k_row0 * HV + j) * (int64_t)d];",
+                                "const double* vh = &vw[(I.k_row0 * HV + j - j % (HV / H)) * "
+                                "(int64_t)d];"),
     # value rows weighted by the wrong key
     "value_index_shift": ("out[c] += s[j] * v[j * kstride + c];",
                           "out[c] += s[j] * v[((j + 1) % nvis) * kstride + c];"),
