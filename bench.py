@@ -169,6 +169,29 @@ def bench_backward(gqa, w, steps, warmup, torch, seed):
             "frac_mfma": flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "wall_s": wall}
 
 
+def bench_gva(gqa, w, steps, warmup, torch, seed):
+    """Grouped value attention prefill (H = w.Hkv query/key heads, HV = w.Hq value heads):
+    algorithmic work per unmasked (query, key, query/key head) pair is 2*d for the score and
+    2*d per value head for the weighted sum, 2*d*(1 + G)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    H, HV = w.Hkv, w.Hq
+    q = torch.randn(w.B, w.Tq, H, w.d, generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn(w.B, w.Tkv, H, w.d, generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn(w.B, w.Tkv, HV, w.d, generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty(w.B, w.Tq, HV, w.d, dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        gqa.gqa_attn_prefill_gva(q, k, v, causal=w.causal, out=out)
+
+    ms, wall = time_launches(step, steps, warmup, torch)
+    flops = 2 * w.d * (H + HV) * w.B * visible_pairs(w.Tq, w.Tkv, w.causal)
+    avg = sum(ms) / len(ms)
+    return {"workload": w.name, "flops_per_launch": flops, "avg_ms": avg, "min_ms": min(ms),
+            "tflops": flops / (avg * 1e-3) / 1e12,
+            "frac_mfma": flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "wall_s": wall}
+
+
 def bench_decode(gqa, w, steps, warmup, torch, seed):
     """Alternates two distinct caches (4 GiB together) so no run rides the previous one's
     last-level cache."""
@@ -271,7 +294,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "mqa", "varlen", "window",
-                                       "ragged", "rope", "backward", "copy"],
+                                       "ragged", "rope", "backward", "gva", "copy"],
                     default=None,
                     help="time a single workload (for profiling); still prints one JSON line. "
                          "'copy' times a plain 1 GiB device copy, the calibration kernel for "
@@ -333,6 +356,10 @@ def main():
         bw = bench_backward(gqa, workloads.LLAMA_PREFILL, args.steps, args.warmup, torch, 2000)
         extra["backward"] = bw
         log(f"backward: {bw['avg_ms'] * 1e3:.1f} us, {bw['tflops']:.1f} TFLOP/s")
+    if args.only == "gva" or args.all:
+        gv = bench_gva(gqa, workloads.GVA_PREFILL, args.steps, args.warmup, torch, 8000)
+        extra["gva_prefill"] = gv
+        log(f"gva prefill: {gv['avg_ms'] * 1e3:.1f} us, {gv['tflops']:.1f} TFLOP/s")
     if args.only == "ragged" or args.all:
         rd = bench_decode(gqa, workloads.RAGGED_DECODE, args.steps, args.warmup, torch, 7000)
         extra["ragged_decode"] = rd
@@ -343,8 +370,9 @@ def main():
         log(f"decode: {dec['avg_ms'] * 1e3:.1f} us, {dec['gbs']:.0f} GB/s")
     sha = kernel_source_sha("prefill")
     metric = "GQA prefill TFLOPS (% MFMA peak); decode KV GB/s (% HBM peak)"
-    if pre is None and args.only in ("mqa", "varlen", "window", "rope", "backward"):
-        key, w = {"mqa": ("mqa_prefill", workloads.MQA_PREFILL),
+    if pre is None and args.only in ("mqa", "varlen", "window", "rope", "backward", "gva"):
+        key, w = {"gva": ("gva_prefill", workloads.GVA_PREFILL),
+                  "mqa": ("mqa_prefill", workloads.MQA_PREFILL),
                   "varlen": ("varlen_prefill", workloads.VARLEN_PREFILL),
                   "window": ("window_prefill", workloads.WINDOW_PREFILL),
                   "rope": ("rope_prefill", workloads.LLAMA_PREFILL),
@@ -358,8 +386,9 @@ def main():
                     "unit": "TFLOP/s", "frac": pre["tflops"] / PEAK_BF16_TFLOPS,
                     "traffic": traffic,
                     "kernel": {"backward": "bwd_rowdot + bwd_dkdv_kernel<128> + bwd_dq_kernel<128>",
-                               "rope": "prefill_pp_kernel<128, true>"}.get(
-                                   args.only, "prefill_pp_kernel<128, false>"),
+                               "rope": "prefill_pp_kernel<128, 128, true>",
+                               "gva": "prefill_pp_kernel<64, 128, false>"}.get(
+                                   args.only, "prefill_pp_kernel<128, 128, false>"),
                     "flops_per_launch": pre["flops_per_launch"],
                     "avg_launch_ms": pre["avg_ms"], "kernel_source_sha": sha}
         config = {"workload": w.name, "B": w.B, "T": w.Tq, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
@@ -369,6 +398,9 @@ def main():
             config["seqlens"] = list(w.seqlens)
         if w.window > 0:
             config["window"], config["n_sink"] = w.window, w.n_sink
+        if args.only == "gva":
+            config.update({"H": w.Hkv, "HV": w.Hq})
+            del config["Hq"], config["Hkv"]
     else:
         dw = workloads.RAGGED_DECODE if args.only == "ragged" else workloads.DECODE
         dec = extra.pop("ragged_decode" if args.only == "ragged" else "decode")

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     gqa_attn_decode_workspace_bytes,
     gqa_attn_prefill,
     gqa_attn_prefill_ex,
+    gqa_attn_prefill_gva,
     gqa_attn_prefill_window,
     gqa_fold_kv,
     gqa_status_string,

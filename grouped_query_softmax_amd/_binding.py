@@ -66,7 +66,7 @@ def _options(window: int, n_sink: int, rope, d: int, lse=None) -> AttnOptions:
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
-        raise ImportError(f"{path} is missing: build it with `python -m grouped_query_softmax_amd.build`")
+        raise ImportError(f"{path} is missing: build it with `python grouped_query_softmax_amd/build.py`")
     lib = ctypes.CDLL(path)
     P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.gqa_attn_prefill.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P, I, I, P]
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     OP = ctypes.POINTER(AttnOptions)
     lib.gqa_attn_prefill_ex.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P, I, OP, I, P]
     lib.gqa_attn_prefill_ex.restype = I
+    lib.gqa_attn_prefill_gva.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P, I, OP, I, P]
+    lib.gqa_attn_prefill_gva.restype = I
     lib.gqa_attn_decode_ex.argtypes = [P, P, P, P, I, I, I, I, I, F, P, OP, P, SZ, I, P]
     lib.gqa_attn_decode_ex.restype = I
     lib.gqa_attn_backward_workspace_bytes.argtypes = [I, I, I]
@@ -226,6 +228,51 @@ def gqa_attn_prefill_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causa
                                   *dims, int(bool(causal)), cu_ptr, msl, ctypes.byref(opt),
                                   _dtype_code(q), _stream(stream))
     _check(rc, "gqa_attn_prefill_ex")
+    return out
+
+
+def gqa_attn_prefill_gva(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                         window: int = 0, n_sink: int = 0, scale: Optional[float] = None,
+                         cu_seqlens: Optional[torch.Tensor] = None,
+                         max_seqlen: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Grouped value attention: q, k [B,Tq|Tkv,H,d] shared by the HV = G*H value heads of
+    v [B,Tkv,HV,d]; value head j uses query/key head j // G. Returns out [B,Tq,HV,d]. bf16."""
+    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected q[B,Tq,H,d], k[B,Tkv,H,d], v[B,Tkv,HV,d]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    B, Tq, H, d = q.shape
+    Tkv, HV = k.shape[1], v.shape[2]
+    if k.shape[0] != B or k.shape[2] != H or k.shape[3] != d or v.shape[:2] != k.shape[:2] \
+            or v.shape[3] != d:
+        raise ValueError("q, k and v disagree on batch, length, heads or head dim")
+    if scale is None:
+        scale = d ** -0.5
+    cu_ptr, nseq, msl = None, B, 0
+    if cu_seqlens is not None:
+        cu = _dev(cu_seqlens, "cu_seqlens")
+        if cu.dtype != torch.int32 or cu.dim() != 1 or cu.numel() < 2 or B != 1:
+            raise ValueError("packed batches: int32 cu_seqlens and [1, total, ., d] tensors")
+        nseq = cu.numel() - 1
+        if max_seqlen is None:
+            max_seqlen = int((cu[1:] - cu[:-1]).max().item())
+        cu_ptr, msl = cu.data_ptr(), int(max_seqlen)
+    oshape = (B, Tq, HV, d)
+    if out is None:
+        out = torch.empty(oshape, dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != oshape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor [B, Tq, HV, d] of q's dtype")
+    if lse is not None:
+        lse = _dev(lse, "lse")
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Tq, H) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 device tensor [B, Tq, H]")
+    opt = _options(window, n_sink, None, d, lse)
+    rc = _lib.gqa_attn_prefill_gva(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   nseq, Tq, Tkv, H, HV, d, float(scale), int(bool(causal)),
+                                   cu_ptr, msl, ctypes.byref(opt), _dtype_code(q), _stream(stream))
+    _check(rc, "gqa_attn_prefill_gva")
     return out
 
 

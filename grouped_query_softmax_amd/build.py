@@ -1,6 +1,7 @@
 """Build ``libgqa_attn.so`` in-tree with hipcc for gfx950.
 
-Usage: ``python -m grouped_query_softmax_amd.build`` (or ``build()`` from Python). Each source is
+Usage: ``python grouped_query_softmax_amd/build.py`` (run as a file: importing it through the
+package would first load the library it builds), or ``build()`` from Python. Each source is
 compiled to an object under ``_build/`` (parallel), then linked into the package directory.
 Always recompiles: this is the "does it build" check as well as the build.
 """

@@ -104,6 +104,13 @@ struct PrefillArgs {
   const float* rope_sin;
   int rope_rows;
   float* lse;  // optional output: natural-log log-sum-exp of each row's scaled scores
+  // Value and output geometry, in elements. Grouped-query attention: dv = d, vslices = 1,
+  // v_row = Hkv*d, v_head = d, o_row = Hq*d, o_head = d. Grouped value attention hands in the
+  // G value heads of a query/key head as one value row of G*d columns, produced in vslices
+  // slices of dv columns each.
+  int dv, vslices;
+  int v_row, v_head;  // between value rows of consecutive positions / key-value heads
+  int o_row, o_head;  // between output rows of consecutive positions / query heads
 };
 
 struct DecodeArgs {

@@ -52,6 +52,17 @@ int64_t head_tiles(gqa_dtype_t t, int G) {
 
 gqa_status_t from_hip(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
 
+// Value/output geometry of grouped-query attention: one value row of d columns per key/value
+// head, one output row per query head.
+void set_gqa_geometry(gqa::PrefillArgs& a) {
+  a.dv = a.d;
+  a.vslices = 1;
+  a.v_row = a.Hkv * a.d;
+  a.v_head = a.d;
+  a.o_row = a.Hq * a.d;
+  a.o_head = a.d;
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,6 +166,7 @@ static gqa_status_t prefill_impl(const void* q, const void* k, const void* v, vo
   a.rope_sin = opt ? opt->rope_sin : nullptr;
   a.rope_rows = opt ? opt->rope_rows : 0;
   a.lse = opt ? opt->lse : nullptr;
+  set_gqa_geometry(a);
   if (a.lse && overlap(a.lse, rows_q * Hq * sizeof(float), q, nq)) return GQA_ERR_ALIAS;
   return from_hip(dtype == GQA_DTYPE_BF16 ? gqa::launch_prefill_bf16(a, stream)
                                           : gqa::launch_prefill_f32(a, stream));
@@ -184,6 +196,79 @@ gqa_status_t gqa_attn_prefill_ex(const void* q, const void* k, const void* v, vo
                                  hipStream_t stream) {
   return prefill_impl(q, k, v, out, B, Tq, Tkv, Hq, Hkv, d, scale, causal, options, cu_seqlens,
                       max_seqlen, dtype, stream);
+}
+
+gqa_status_t gqa_attn_prefill_gva(const void* q, const void* k, const void* v, void* out, int B,
+                                  int Tq, int Tkv, int H, int HV, int d, float scale, int causal,
+                                  const int32_t* cu_seqlens, int max_seqlen,
+                                  const gqa_attn_options_t* opt, gqa_dtype_t dtype,
+                                  hipStream_t stream) {
+  if (!q || !k || !v || !out) return GQA_ERR_NULL_PTR;
+  if (B <= 0 || Tq <= 0 || Tkv <= 0 || H <= 0 || HV <= 0 || d <= 0) return GQA_ERR_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.f)) return GQA_ERR_SHAPE;
+  if (HV % H != 0) return GQA_ERR_GROUPING;
+  if (dtype != GQA_DTYPE_BF16 || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
+  if (const gqa_status_t st = check_options(opt, dtype, cu_seqlens ? max_seqlen : Tkv)) return st;
+  if (opt && (opt->rope_cos || opt->rope_sin)) return GQA_ERR_UNSUPPORTED;
+  const int window = opt ? opt->window : 0;
+  const int n_sink = opt ? opt->n_sink : 0;
+  if ((window > 0 || n_sink > 0) && !causal) return GQA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return GQA_ERR_UNSUPPORTED;
+  int max_tq;
+  if (cu_seqlens) {
+    if (Tq != Tkv || max_seqlen <= 0 || max_seqlen > Tq) return GQA_ERR_SHAPE;
+    max_tq = max_seqlen;
+  } else {
+    if (causal && Tq > Tkv) return GQA_ERR_SHAPE;
+    max_tq = Tq;
+  }
+  const int G = HV / H;
+  // a workgroup produces dv value columns of one query/key head: 128 when the head's value row
+  // (G*d columns) splits into 128-column slices, else d (then one slice per value head)
+  const int dv = (G * d) % 128 == 0 ? 128 : d;
+  const int vslices = G * d / dv;
+  const int64_t tiles = prefill_tiles(dtype, 1, max_tq);
+  const int64_t wgs = static_cast<int64_t>(H) * vslices * B * (causal ? (tiles + 1) / 2 : tiles);
+  const int64_t item_v_bytes = static_cast<int64_t>(cu_seqlens ? max_tq : Tkv) * HV * d * 2;
+  if (wgs > kMaxFlatWorkgroups512 || item_v_bytes > INT32_MAX) return GQA_ERR_UNSUPPORTED;
+  const size_t rows_q = cu_seqlens ? static_cast<size_t>(Tq) : static_cast<size_t>(B) * Tq;
+  const size_t rows_k = cu_seqlens ? static_cast<size_t>(Tkv) : static_cast<size_t>(B) * Tkv;
+  const size_t nq = rows_q * H * d * 2, nk = rows_k * H * d * 2, nv = rows_k * HV * d * 2;
+  const size_t no = rows_q * HV * d * 2;
+  if (overlap(out, no, q, nq) || overlap(out, no, k, nk) || overlap(out, no, v, nv))
+    return GQA_ERR_ALIAS;
+
+  gqa::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.nitems = B;
+  a.max_tq = max_tq;
+  a.items.cu = cu_seqlens;
+  a.items.Tq = Tq;
+  a.items.Tkv = Tkv;
+  a.Hq = H;  // one query per query/key head: the kernel's grouped-query view with G = 1
+  a.Hkv = H;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal ? 1 : 0;
+  a.window = window;
+  a.n_sink = window > 0 ? n_sink : 0;
+  a.rope_cos = a.rope_sin = nullptr;
+  a.rope_rows = 0;
+  a.lse = opt ? opt->lse : nullptr;
+  a.dv = dv;
+  a.vslices = vslices;
+  a.v_row = HV * d;
+  a.v_head = G * d;
+  a.o_row = HV * d;
+  a.o_head = G * d;
+  if (a.lse && (overlap(a.lse, rows_q * H * sizeof(float), q, nq) ||
+                overlap(a.lse, rows_q * H * sizeof(float), out, no)))
+    return GQA_ERR_ALIAS;
+  return from_hip(gqa::launch_prefill_bf16(a, stream));
 }
 
 size_t gqa_attn_decode_workspace_bytes(int B, int Tkv, int Hq, int Hkv, int d) {
@@ -247,6 +332,7 @@ static gqa_status_t decode_impl(const void* q, const void* k_cache, const void* 
     a.rope_cos = a.rope_sin = nullptr;
     a.rope_rows = 0;
     a.lse = nullptr;
+    set_gqa_geometry(a);
     return from_hip(gqa::launch_prefill_f32(a, stream));
   }
   const size_t need = gqa::decode_workspace_bytes(B, Tkv, Hq, Hkv, d);

@@ -75,40 +75,44 @@ __device__ __forceinline__ void lds_write(char* base, int byte_off, T v) {
   *reinterpret_cast<T*>(base + byte_off) = v;
 }
 
-template <int D>
+// DQ: query/key head dim; DV: value columns a workgroup produces (DQ for grouped-query
+// attention; a slice of the wider value row for grouped value attention).
+template <int DQ, int DV>
 struct PPCfg {
   static constexpr int kGroupThreads = 256;
-  static constexpr int kChunks = D / 8;
+  static constexpr int kChunks = DQ / 8;
   static constexpr int kKLoads = kKT * kChunks / kGroupThreads;  // 16-byte K loads per thread
-  static constexpr int kVD = (kKT / 4) * D / kGroupThreads;      // d values per V item
-  static constexpr int kKPitch = D * 2 + 16;
+  static constexpr int kVD = (kKT / 4) * DV / kGroupThreads;     // value columns per V item
+  static constexpr int kKPitch = DQ * 2 + 16;
   static constexpr int kVPitch = kKT * 2 + 16;
   static constexpr int kKBytes = kKT * kKPitch;
-  static constexpr int kVBytes = D * kVPitch;
+  static constexpr int kVBytes = DV * kVPitch;
   static constexpr int kVBase = 3 * kKBytes;  // LDS: [K stage 0..2][V^T stage 0..2]
   static constexpr int kSmemBytes = 3 * (kKBytes + kVBytes);
   static_assert(kVD == 8 || kVD == 4, "V staging split");
   static_assert(kVBase < 65536 && 3 * kVBytes < 65536, "stage offsets fit LDS immediates");
 };
 
-template <int D, bool ROPE>
+template <int DQ, int DV, bool ROPE>
 __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int heads_per_wg,
                                                          int pos_per_wg, int head_tiles, int gz) {
-  using C = PPCfg<D>;
-  constexpr int NS = D / 16;   // MFMA k-steps over d for the scores
-  constexpr int NMT = D / 32;  // 32-row d tiles of O^T
+  using C = PPCfg<DQ, DV>;
+  constexpr int D = DQ;
+  constexpr int NS = DQ / 16;   // MFMA k-steps over the head dim for the scores
+  constexpr int NMT = DV / 32;  // 32-row value-column tiles of O^T
   constexpr int VD = C::kVD;
   constexpr int VW = VD / 2;
   __shared__ __attribute__((aligned(16))) char smem[C::kSmemBytes];
 
-  const int gx = a.Hkv * head_tiles;
+  const int gx = a.Hkv * head_tiles * a.vslices;
   const int lin = blockIdx.x;
   const int xi = lin % gx;
   const int rest = lin / gx;
   const int z = rest % gz;  // query tiles, then items
   const int item = rest / gz;
-  const int kvh = xi / head_tiles;
-  const int ht = xi % head_tiles;
+  const int vsl = xi % a.vslices;  // value slice
+  const int kvh = xi / (head_tiles * a.vslices);
+  const int ht = (xi / a.vslices) % head_tiles;
   int64_t q0, k0;
   int tq, tkv;
   a.items.get(item, q0, k0, tq, tkv);
@@ -139,9 +143,11 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
 
   const uint16_t* __restrict__ Qp = static_cast<const uint16_t*>(a.q);
   uint16_t* __restrict__ Op = static_cast<uint16_t*>(a.out);
-  const int row_bytes = a.Hkv * D * 2;
+  const int row_bytes = a.Hkv * D * 2;  // between K rows
+  const int vrow_bytes = a.v_row * 2;   // between V rows
   const uint16_t* kbase_ptr = static_cast<const uint16_t*>(a.k) + (k0 * a.Hkv + kvh) * D;
-  const uint16_t* vbase_ptr = static_cast<const uint16_t*>(a.v) + (k0 * a.Hkv + kvh) * D;
+  const uint16_t* vbase_ptr = static_cast<const uint16_t*>(a.v) + k0 * a.v_row +
+                              static_cast<int64_t>(kvh) * a.v_head + vsl * DV;
 
   // staging geometry of this thread inside its group (loop invariant)
   int k_src[C::kKLoads], k_dst[C::kKLoads];
@@ -155,7 +161,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
   // V items: 4 keys x VD dims; the key group runs fastest across lanes so 16 lanes write one
   // V^T row (128 contiguous bytes) at once
   const int v_kg = gtid % 16, v_c = gtid / 16;
-  const int v_src = 4 * v_kg * row_bytes + 2 * VD * v_c;
+  const int v_src = 4 * v_kg * vrow_bytes + 2 * VD * v_c;
   const int v_dst = (VD * v_c) * C::kVPitch + 8 * vt_slot(v_kg);
   const int k_rd = n * C::kKPitch + 16 * hh;
   const int v_rd = n * C::kVPitch + 16 * hh;
@@ -207,10 +213,11 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
     const int nkt = nst + (kt_end - wt0);
     auto ktile = [&](int t) { return t < nst ? t : t - nst + wt0; };
     const int nrec = (kend - 1) * row_bytes + D * 2;
+    const int vnrec = (kend - 1) * vrow_bytes + DV * 2;
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kbase_ptr), 0, nrec, kBufWord3);
     const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vbase_ptr), 0, nrec, kBufWord3);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vbase_ptr), 0, vnrec, kBufWord3);
 
     // one staging register file per thread: group B stages K tiles, group A stages V tiles
     constexpr int kStageRegs = (4 * C::kKLoads > 4 * VW) ? 4 * C::kKLoads : 4 * VW;
@@ -260,17 +267,17 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
       }
     };
     auto load_v = [&](int t) {
-      const int soff = ktile(t) * kKT * row_bytes;
+      const int soff = ktile(t) * kKT * vrow_bytes;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if constexpr (VD == 8) {
           const u32x4 w =
-              __builtin_amdgcn_raw_buffer_load_b128(vrs, v_src + r * row_bytes + soff, 0, 0);
+              __builtin_amdgcn_raw_buffer_load_b128(vrs, v_src + r * vrow_bytes + soff, 0, 0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) stg[VW * r + e] = w[e];
         } else {
           const u32x2 w =
-              __builtin_amdgcn_raw_buffer_load_b64(vrs, v_src + r * row_bytes + soff, 0, 0);
+              __builtin_amdgcn_raw_buffer_load_b64(vrs, v_src + r * vrow_bytes + soff, 0, 0);
           stg[VW * r] = w[0];
           stg[VW * r + 1] = w[1];
         }
@@ -476,10 +483,11 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
 
     const float l_tot = pair_sum32(l_run);
     const float inv = 1.f / l_tot;
-    if (a.lse && valid && hh == 0)  // log-sum-exp of the scaled scores, natural log
+    if (a.lse && valid && hh == 0 && vsl == 0)  // log-sum-exp of the scaled scores, natural log
       a.lse[(q0 + pos) * a.Hq + hq] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     if (valid) {
-      uint16_t* orow = Op + ((q0 + pos) * a.Hq + hq) * D;
+      uint16_t* orow =
+          Op + (q0 + pos) * a.o_row + static_cast<int64_t>(hq) * a.o_head + vsl * DV;
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
@@ -494,7 +502,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
   }
 }
 
-template <int D, bool ROPE>
+template <int DQ, int DV, bool ROPE>
 hipError_t launch_pp(const PrefillArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int heads_per_wg = G < kCols ? G : kCols;
@@ -502,9 +510,9 @@ hipError_t launch_pp(const PrefillArgs& a, hipStream_t s) {
   const int head_tiles = (G + heads_per_wg - 1) / heads_per_wg;
   const int ntiles = (a.max_tq + pos_per_wg - 1) / pos_per_wg;
   const int gz = a.causal ? (ntiles + 1) / 2 : ntiles;
-  const dim3 grid(a.Hkv * head_tiles * a.nitems * gz);
-  hipLaunchKernelGGL((prefill_pp_kernel<D, ROPE>), grid, dim3(512), 0, s, a, heads_per_wg, pos_per_wg,
-                     head_tiles, gz);
+  const dim3 grid(a.Hkv * head_tiles * a.vslices * a.nitems * gz);
+  hipLaunchKernelGGL((prefill_pp_kernel<DQ, DV, ROPE>), grid, dim3(512), 0, s, a, heads_per_wg,
+                     pos_per_wg, head_tiles, gz);
   return hipGetLastError();
 }
 
@@ -513,11 +521,13 @@ hipError_t launch_pp(const PrefillArgs& a, hipStream_t s) {
 int prefill_bf16_cols() { return kCols; }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
-  switch (a.d) {
-    case 64: return a.rope_cos ? launch_pp<64, true>(a, s) : launch_pp<64, false>(a, s);
-    case 128: return a.rope_cos ? launch_pp<128, true>(a, s) : launch_pp<128, false>(a, s);
-    default: return hipErrorInvalidValue;
-  }
+  const bool rope = a.rope_cos != nullptr;
+  if (a.d == 64 && a.dv == 64)
+    return rope ? launch_pp<64, 64, true>(a, s) : launch_pp<64, 64, false>(a, s);
+  if (a.d == 128 && a.dv == 128)
+    return rope ? launch_pp<128, 128, true>(a, s) : launch_pp<128, 128, false>(a, s);
+  if (a.d == 64 && a.dv == 128 && !rope) return launch_pp<64, 128, false>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace gqa

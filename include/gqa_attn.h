@@ -122,6 +122,26 @@ gqa_status_t gqa_attn_prefill_window(const void* q, const void* k, const void* v
                                      int max_seqlen, gqa_dtype_t dtype, hipStream_t stream);
 
 /*
+ * Grouped value attention, prefill (K3 notes, section 4, GVA: the inverse of grouped-query
+ * sharing). H query/key heads serve HV = G*H value heads; value head j is attended with
+ * query/key head j / G (contiguous groups: the notes repeat q and k with repeat_interleave)
+ * and keeps its own values:
+ *   out[b,t,j,:] = softmax_keys(scale * q[b,t,j/G,:] . k[b,:,j/G,:]) v[b,:,j,:]
+ *   q [B, Tq, H, d]   k [B, Tkv, H, d]   v [B, Tkv, HV, d]   out [B, Tq, HV, d]
+ * (packed batches: [1, total, ., d] with cu_seqlens, as for gqa_attn_prefill.) The scores of a
+ * query/key head are computed once for each 128 value columns of its G value heads (G*d a
+ * multiple of 128), otherwise once per value head. Options: window, n_sink and lse ([B, Tq, H]:
+ * one log-sum-exp per query/key head) as for gqa_attn_prefill_ex; rotary tables are not
+ * supported here (GQA_ERR_UNSUPPORTED). bf16 only, d in {64, 128} (else GQA_ERR_UNSUPPORTED).
+ * HV not a multiple of H is GQA_ERR_GROUPING; other errors as for gqa_attn_prefill.
+ */
+gqa_status_t gqa_attn_prefill_gva(const void* q, const void* k, const void* v, void* out, int B,
+                                  int Tq, int Tkv, int H, int HV, int d, float scale, int causal,
+                                  const int32_t* cu_seqlens, int max_seqlen,
+                                  const gqa_attn_options_t* options, gqa_dtype_t dtype,
+                                  hipStream_t stream);
+
+/*
  * Decode: one query token per sequence against a key/value cache, split along the cache length.
  *   q [B, 1, Hq, d]     k_cache, v_cache [B, Tkv, Hkv, d]     out [B, 1, Hq, d]
  * Each split writes an fp32 partial result (running max, sum and unnormalised output) to

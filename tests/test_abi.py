@@ -115,6 +115,24 @@ def test_extended_options_validation(lib):
     assert dex(Opt(0, 0, None, T, 1024, None)) == B.GQA_ERR_NULL_PTR
 
 
+def test_gva_validation(lib):
+    Opt = B.AttnOptions
+    T = W + 8192
+
+    def gva(q=Q, o=O, H=2, HV=8, d=128, dt=BF16, causal=1, Tq=8, Tkv=8, opt=None):
+        return lib.gqa_attn_prefill_gva(q, K, V, o, 1, Tq, Tkv, H, HV, d, 0.1, causal, None, 0,
+                                        ctypes.byref(opt) if opt is not None else None, dt, None)
+    assert gva(q=None) == B.GQA_ERR_NULL_PTR
+    assert gva(HV=7) == B.GQA_ERR_GROUPING             # value heads do not group evenly
+    assert gva(H=0) == B.GQA_ERR_SHAPE
+    assert gva(dt=F32, d=16) == B.GQA_ERR_UNSUPPORTED  # bf16 only
+    assert gva(d=96) == B.GQA_ERR_UNSUPPORTED
+    assert gva(Tq=9) == B.GQA_ERR_SHAPE                # causal needs Tq <= Tkv
+    assert gva(opt=Opt(0, 0, T, T + 4096, 8, None)) == B.GQA_ERR_UNSUPPORTED  # no rotary here
+    assert gva(causal=0, opt=Opt(4, 0, None, None, 0, None)) == B.GQA_ERR_SHAPE  # window: causal
+    assert gva(o=V + 64) == B.GQA_ERR_ALIAS            # output over the values
+
+
 def test_backward_validation(lib):
     need = lib.gqa_attn_backward_workspace_bytes(2, 8, 8)
     assert need >= 2 * 8 * 8 * 4 and need % 16 == 0

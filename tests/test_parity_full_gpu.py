@@ -134,3 +134,27 @@ def test_full_rope_prefill_sampled_rows(gqa):
     got = np.stack([to_f64(o[b, t, h]) for b, t, h in rows])
     err, rel = assert_bf16_close(got, ref, what="rope prefill")
     say(f"full-size rope prefill: max-abs {err:.3e} rel {rel:.3e}")
+
+
+def test_full_gva_prefill_sampled_heads(gqa):
+    """Grouped value attention at the benchmark size: the first and last query/key head of every
+    sequence, with all of their value heads and every position, against the fp64 oracle."""
+    w = workloads.GVA_PREFILL
+    H, HV = w.Hkv, w.Hq
+    G = HV // H
+    say(f"full-size gva {w.name}: generating inputs")
+    q, k, v = workloads.gva_inputs(w)
+    say(f"full-size gva {w.name}: launching")
+    out = gqa.gqa_attn_prefill_gva(to_dev(q), to_dev(k), to_dev(v), causal=w.causal)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    o = out.cpu()
+    orc = oracle.default()
+    qh, kh, vh = host_view(q), host_view(k), host_view(v)
+    for b in range(w.B):
+        for h in (0, H - 1):
+            say(f"full-size gva {w.name}: oracle on sequence {b}, query/key head {h}")
+            ref = orc.attention_gva(qh[b:b + 1, :, h:h + 1], kh[b:b + 1, :, h:h + 1],
+                                    vh[b:b + 1, :, h * G:(h + 1) * G], causal=w.causal)
+            assert_bf16_close(to_f64(o[b:b + 1, :, h * G:(h + 1) * G]), ref,
+                              what=f"{w.name} b={b} h={h}")

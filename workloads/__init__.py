@@ -174,9 +174,15 @@ RAGGED_DECODE = Workload("ragged_decode_B64_max8192", B=64, Tq=1, Tkv=8192, Hq=3
                          dtype="bf16", causal=False, seeds=(7000, 7001, 7002),
                          cache_lens=ragged_lengths(64, 8192, 7003))
 
+# Grouped value attention (K3 notes, section 4): 16 query/key heads shared by 32 value heads
+# (G = 2) of 64 dims, so one query/key head's values form one 128-column row; two 4096-token
+# sequences. Hq here counts the value heads (the output heads) and Hkv the query/key heads.
+GVA_PREFILL = Workload("gva_prefill_B2_T4096_H16_HV32_d64", B=2, Tq=4096, Tkv=4096, Hq=32, Hkv=16,
+                       d=64, dtype="bf16", causal=True, seeds=(8000, 8001, 8002))
+
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in
                                   (TINY, LLAMA_PREFILL, DECODE, MQA_PREFILL, VARLEN_PREFILL,
-                                   WINDOW_PREFILL, RAGGED_DECODE)}
+                                   WINDOW_PREFILL, RAGGED_DECODE, GVA_PREFILL)}
 
 
 def tiny_lab_inputs(x1000: bool = False) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
@@ -240,6 +246,16 @@ def peaked_rows(w: Workload) -> np.ndarray:
     g = torch.Generator(device="cpu")
     g.manual_seed(w.peaked_seed)
     return torch.randperm(nrows, generator=g)[:nsel].numpy().astype(np.int64)
+
+
+def gva_inputs(w: Workload):
+    """q, k [B, T, H, d] and v [B, T, HV, d] as CPU bf16 tensors for a grouped value attention
+    workload (H = w.Hkv query/key heads, HV = w.Hq value heads), N(0,1) with the workload seeds."""
+    H, HV = w.Hkv, w.Hq
+    q = randn_bf16((w.B, w.Tq, H, w.d), w.seeds[0])
+    k = randn_bf16((w.B, w.Tkv, H, w.d), w.seeds[1])
+    v = randn_bf16((w.B, w.Tkv, HV, w.d), w.seeds[2])
+    return q, k, v
 
 
 def sample_rows(w: Workload, n: int, seed: int) -> np.ndarray:
