@@ -52,6 +52,10 @@ FILE_FLAGS = {
     # decode also keeps its matrix-core accumulators in ordinary VGPRs, so the occasional softmax
     # rescale of the output accumulators needs no accumulator-register copies
     "decode.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # the backward's gradient accumulators are read by vector code between products (the
+    # cross-wave sums); in accumulator registers the compiler copied them in and out around
+    # every product
+    "backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

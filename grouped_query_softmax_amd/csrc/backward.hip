@@ -52,9 +52,19 @@ __device__ __forceinline__ u32x2 lds_read_tr(char* base, int byte_off) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// LDS layout of a [rows][D] chunk: rows of 2*D bytes, the 16-byte pieces of row r stored at
+// piece index c ^ swz(r). The two readers of a chunk -- 16-byte reads down a column of rows (an
+// MFMA operand with the rows as its M index) and transposing 8-byte reads of 4 rows x 64 bytes --
+// then both hit 64 distinct banks per pass, which no plain row padding achieves for both.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
+}
+
 template <int D>
 struct BwdCfg {
-  static constexpr int kPitch = 2 * D + 16;        // bytes per LDS row of a [rows][D] chunk
+  static constexpr int kPitch = 2 * D;             // bytes per LDS row of a [rows][D] chunk
   static constexpr int kChunkBytes = kRows * kPitch;
   static constexpr int kNS = D / 16;               // MFMA k-steps over d
   static constexpr int kNMT = D / 32;              // 32-row d tiles
@@ -66,12 +76,17 @@ struct BwdCfg {
 // values are the 16 chunk rows 16 ks .. 16 ks + 15 in the accumulator order
 // (rows 16ks+4hh+0..3, then 16ks+8+4hh+0..3), read transposed from a [rows][D] LDS chunk.
 template <int D>
+__device__ __forceinline__ int chunk_off(int r, int c) {  // byte offset of piece c of row r
+  return r * BwdCfg<D>::kPitch + 16 * (c ^ swz<D>(r));
+}
+
+template <int D>
 __device__ __forceinline__ bf16x8 tr_operand(char* chunk, int lane, int base, int ks) {
   const int hh = lane >> 5, sub = (lane >> 4) & 1, j = lane & 15;
   const int row = 16 * ks + 4 * hh + (j >> 2);
-  const int off = row * BwdCfg<D>::kPitch + 2 * (base + 16 * sub + 4 * (j & 3));
-  const u32x2 lo = lds_read_tr(chunk, off);
-  const u32x2 hi = lds_read_tr(chunk, off + 8 * BwdCfg<D>::kPitch);
+  const int c = base / 8 + 2 * sub + ((j & 3) >> 1);  // 16-byte piece; 8-byte half (j & 1)
+  const u32x2 lo = lds_read_tr(chunk, chunk_off<D>(row, c) + 8 * (j & 1));
+  const u32x2 hi = lds_read_tr(chunk, chunk_off<D>(row + 8, c) + 8 * (j & 1));
   return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
@@ -244,8 +259,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_t
         const int mat = ((i * kThreads) / kMatPieces) & 1;
         const int pc = (i * kThreads) % kMatPieces + tid;
         const int r = pc / C::kLoadsPerRow, c = pc % C::kLoadsPerRow;
-        *reinterpret_cast<u32x4*>(base + sl * kSlotBytes + mat * C::kChunkBytes + r * C::kPitch +
-                                  16 * c) = pr_[i];
+        *reinterpret_cast<u32x4*>(base + sl * kSlotBytes + mat * C::kChunkBytes +
+                                  chunk_off<D>(r, c)) = pr_[i];
       }
       if (tid < 2 * kRows) {
         const int sl = tid / kRows, r = tid % kRows;
@@ -280,9 +295,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_t
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const bf16x8 qa = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(sq + n * C::kPitch + 32 * s + 16 * hh));
+              bf16x8, *reinterpret_cast<const u32x4*>(sq + chunk_off<D>(n, 2 * s + hh)));
           const bf16x8 ga = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(sg + n * C::kPitch + 32 * s + 16 * hh));
+              bf16x8, *reinterpret_cast<const u32x4*>(sg + chunk_off<D>(n, 2 * s + hh)));
           s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[s], s_acc, 0, 0, 0);
           p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vop[s], p_acc, 0, 0, 0);
         }
@@ -461,8 +476,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
       for (int i = 0; i < C::kChunkLoads; ++i) {
         const int idx = i * kThreads + tid;
         const int r = idx / C::kLoadsPerRow, c = idx % C::kLoadsPerRow;
-        *reinterpret_cast<u32x4*>(sk + r * C::kPitch + 16 * c) = pk[i];
-        *reinterpret_cast<u32x4*>(sv + r * C::kPitch + 16 * c) = pv[i];
+        *reinterpret_cast<u32x4*>(sk + chunk_off<D>(r, c)) = pk[i];
+        *reinterpret_cast<u32x4*>(sv + chunk_off<D>(r, c)) = pv[i];
       }
     };
 
@@ -481,9 +496,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const bf16x8 ka = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(sk + n * C::kPitch + 32 * s + 16 * hh));
+            bf16x8, *reinterpret_cast<const u32x4*>(sk + chunk_off<D>(n, 2 * s + hh)));
         const bf16x8 va = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(sv + n * C::kPitch + 32 * s + 16 * hh));
+            bf16x8, *reinterpret_cast<const u32x4*>(sv + chunk_off<D>(n, 2 * s + hh)));
         s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[s], s_acc, 0, 0, 0);
         p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gop[s], p_acc, 0, 0, 0);
       }
