@@ -69,10 +69,10 @@ def _bind(lib):
     lib.oracle_expand.argtypes = [P, P, I64, I64, I, I, I]
     lib.oracle_expand.restype = I
     lib.oracle_gqa_attention.argtypes = [P, P, P, I, P, I64, I64, I64, I, I, I, D, I, P, I, I64,
-                                         I64, P, P, I64, I]
+                                         I64, P, P, I64, I, P, P, D]
     lib.oracle_gqa_attention.restype = I
     lib.oracle_gqa_attention_rows.argtypes = [P, P, P, I, I64, I64, I64, I, I, I, D, I, P, I, P,
-                                              I64, P, I64, I64, P, P, I64, I]
+                                              I64, P, I64, I64, P, P, I64, I, P, P, D]
     lib.oracle_gqa_attention_rows.restype = I
     lib.oracle_gqa_attention_bwd.argtypes = [P, P, P, P, I, P, P, P, I64, I64, I64, I, I, I, D,
                                              I, I64, I64]
@@ -189,43 +189,62 @@ class Oracle:
         mode = {"qk": 3, "q": 1}[rope_mode]
         return cos_t.ctypes.data, sin_t.ctypes.data, cos_t.shape[0], mode, (cos_t, sin_t)
 
+    @staticmethod
+    def _norm(qk_norm, qk_norm_mode, d):
+        """qk_norm: None or (w_q, w_k, eps) with float32 weights [d]; qk_norm_mode "qk" normalises
+        queries and keys, "q" only the queries (keys already normalised, as in a cache)."""
+        if qk_norm is None:
+            return None, None, 0.0, ()
+        wq = np.ascontiguousarray(qk_norm[0], dtype=np.float32)
+        wk = np.ascontiguousarray(qk_norm[1], dtype=np.float32)
+        if wq.shape != (d,) or wk.shape != (d,):
+            raise ValueError("qk-norm weights must be float32 [d]")
+        kp = wk.ctypes.data if qk_norm_mode == "qk" else None
+        return wq.ctypes.data, kp, float(qk_norm[2]), (wq, wk)
+
     def attention(self, q, k, v, scale: Optional[float] = None, causal: bool = False,
                   cu_seqlens=None, window: int = 0, n_sink: int = 0, rope=None,
-                  rope_mode: str = "qk") -> np.ndarray:
+                  rope_mode: str = "qk", qk_norm=None, qk_norm_mode: str = "qk") -> np.ndarray:
         """Grouped-query attention forward (``heads_out``): float64 out[B,Tq,Hq,d].
 
         ``window`` > 0 (causal only) limits each query at position p to keys p-window+1 .. p,
         plus the ``n_sink`` first keys; ``rope`` = (cos, sin) tables rotates query t at position
         t + Tkv - Tq and key j at position j before the scores (course page "Week 7. Attention",
-        step 3)."""
+        step 3). ``qk_norm`` = (w_q, w_k, eps) applies RMSNorm with those weights to every query
+        and key head row before the rotation (course page, step 3: QK-norm)."""
         q, k, v, dt, B, Tq, Tkv, Hq, Hkv, d, scale, cu, nseq = self._common(q, k, v, scale,
                                                                             cu_seqlens)
         cp, sp, npos, mode, keep = self._rope(rope, rope_mode, d)
+        qn, kn, eps, keep2 = self._norm(qk_norm, qk_norm_mode, d)
         out = np.empty((B, Tq, Hq, d), dtype=np.float64)
         rc = self.lib.oracle_gqa_attention(q.ctypes.data, k.ctypes.data, v.ctypes.data, dt,
                                            out.ctypes.data, B, Tq, Tkv, Hq, Hkv, d, scale,
                                            int(bool(causal)),
                                            cu.ctypes.data if cu is not None else None, nseq,
-                                           int(window), int(n_sink), cp, sp, npos, mode)
-        del keep
+                                           int(window), int(n_sink), cp, sp, npos, mode, qn, kn,
+                                           eps)
+        del keep, keep2
         self._check(rc)
         return out
 
     def attention_rows(self, q, k, v, rows: np.ndarray, scale: Optional[float] = None,
                        causal: bool = False, cu_seqlens=None, window: int = 0,
-                       n_sink: int = 0, rope=None, rope_mode: str = "qk") -> np.ndarray:
+                       n_sink: int = 0, rope=None, rope_mode: str = "qk", qk_norm=None,
+                       qk_norm_mode: str = "qk") -> np.ndarray:
         """Selected output rows only. rows: int64 [n, 3] of (b, t, head); returns float64 [n, d]."""
         q, k, v, dt, B, Tq, Tkv, Hq, Hkv, d, scale, cu, nseq = self._common(q, k, v, scale,
                                                                             cu_seqlens)
         r = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
         cp, sp, npos, mode, keep = self._rope(rope, rope_mode, d)
+        qn, kn, eps, keep2 = self._norm(qk_norm, qk_norm_mode, d)
         out = np.empty((r.shape[0], d), dtype=np.float64)
         rc = self.lib.oracle_gqa_attention_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, dt,
                                                 B, Tq, Tkv, Hq, Hkv, d, scale, int(bool(causal)),
                                                 cu.ctypes.data if cu is not None else None, nseq,
                                                 r.ctypes.data, r.shape[0], out.ctypes.data,
-                                                int(window), int(n_sink), cp, sp, npos, mode)
-        del keep
+                                                int(window), int(n_sink), cp, sp, npos, mode, qn,
+                                                kn, eps)
+        del keep, keep2
         self._check(rc)
         return out
 

@@ -178,6 +178,16 @@ static void rope_row(double* x, int d, const float* cos_t, const float* sin_t, i
   }
 }
 
+/* QK-norm of one head row in place (course page "Week 7. Attention", step 3: RMSNorm applied to
+ * q and k before the dot product): x * w / sqrt(mean(x^2) + eps), the mean over the d
+ * coordinates of the row, w the caller's per-coordinate weights (fp32 [d]). */
+static void rms_row(double* x, int d, const float* w, double eps) {
+  double ss = 0.0;
+  for (int c = 0; c < d; ++c) ss += x[c] * x[c];
+  const double inv = 1.0 / sqrt(ss / d + eps);
+  for (int c = 0; c < d; ++c) x[c] = x[c] * inv * (double)w[c];
+}
+
 /* Item table: a dense batch has B items of (Tq, Tkv); a packed batch (cu_seqlens) has nseq items
  * of equal query and key length, laid out back to back in a single [1, total, H, d] tensor. */
 typedef struct {
@@ -225,7 +235,8 @@ int oracle_gqa_attention(const void* q, const void* k, const void* v, int dtype_
                          int64_t B, int64_t Tq, int64_t Tkv, int Hq, int Hkv, int d, double scale,
                          int causal, const int32_t* cu_seqlens, int nseq, int64_t window,
                          int64_t n_sink, const float* rope_cos, const float* rope_sin,
-                         int64_t rope_npos, int rope_mode) {
+                         int64_t rope_npos, int rope_mode, const float* qn_w, const float* kn_w,
+                         double norm_eps) {
   if (Hq <= 0 || Hkv <= 0 || d <= 0) return ORACLE_ERR_SHAPE;
   if ((window > 0 || n_sink > 0) && !causal) return ORACLE_ERR_SHAPE;  /* windows are causal */
   if (rope_mode && (!rope_cos || !rope_sin || d % 2 != 0)) return ORACLE_ERR_SHAPE;
@@ -249,6 +260,9 @@ int oracle_gqa_attention(const void* q, const void* k, const void* v, int dtype_
     kw[i] = widen(k, dtype_in, i);
     vw[i] = widen(v, dtype_in, i);
   }
+  /* QK-norm of the keys first, then their rotation (the norm acts on the raw head row) */
+  if (kn_w)
+    for (int64_t r = 0; r < krows * Hkv; ++r) rms_row(&kw[r * (int64_t)d], d, kn_w, norm_eps);
   if (rope_mode & ROPE_K) {
     /* key j of an item sits at position j */
     for (int it = 0; it < nitems; ++it)
@@ -294,6 +308,7 @@ int oracle_gqa_attention(const void* q, const void* k, const void* v, int dtype_
         const item_t I = items[row_item[row]];
         const int64_t t = row - I.q_row0;
         for (int c = 0; c < d; ++c) qh[c] = widen(q, dtype_in, (row * Hq + h) * (int64_t)d + c);
+        if (qn_w) rms_row(qh, d, qn_w, norm_eps);
         if (rope_mode & ROPE_Q) {
           /* query t sits at position t + (Tkv - Tq), the same alignment as the causal mask */
           const int64_t qpos = t + (I.Tkv - I.Tq);
@@ -331,7 +346,8 @@ int oracle_gqa_attention_rows(const void* q, const void* k, const void* v, int d
                               double scale, int causal, const int32_t* cu_seqlens, int nseq,
                               const int64_t* rows, int64_t nrows, double* out, int64_t window,
                               int64_t n_sink, const float* rope_cos, const float* rope_sin,
-                              int64_t rope_npos, int rope_mode) {
+                              int64_t rope_npos, int rope_mode, const float* qn_w,
+                              const float* kn_w, double norm_eps) {
   if (Hq <= 0 || Hkv <= 0 || d <= 0) return ORACLE_ERR_SHAPE;
   if ((window > 0 || n_sink > 0) && !causal) return ORACLE_ERR_SHAPE;  /* windows are causal */
   if (rope_mode && (!rope_cos || !rope_sin || d % 2 != 0)) return ORACLE_ERR_SHAPE;
@@ -393,10 +409,12 @@ int oracle_gqa_attention_rows(const void* q, const void* k, const void* v, int d
             kh[j * d + c] = widen(k, dtype_in, src);
             vh[j * d + c] = widen(v, dtype_in, src);
           }
+          if (kn_w) rms_row(&kh[j * d], d, kn_w, norm_eps);
           if (rope_mode & ROPE_K) rope_row(&kh[j * d], d, rope_cos, rope_sin, j);
         }
         const int64_t row = I.q_row0 + t;
         for (int c = 0; c < d; ++c) qh[c] = widen(q, dtype_in, (row * Hq + h) * (int64_t)d + c);
+        if (qn_w) rms_row(qh, d, qn_w, norm_eps);
         if (rope_mode & ROPE_Q) rope_row(qh, d, rope_cos, rope_sin, qpos);
         attend_row(qh, kh, vh, d, visible_keys(t, I.Tq, I.Tkv, causal),
                    window_lo(t, I.Tq, I.Tkv, window), n_sink, d, scale, sc, &out[r * d]);

@@ -19,7 +19,8 @@ Sources of the facts (page, section):
     check against torch's scaled_dot_product_attention; step 3 (sliding window and attention
     sinks: the window bounds what a query sees, the first tokens stay visible; rotary position
     embedding: pairs of coordinates turned by pos * theta_i, theta_i = base^(-2i/d), the pair
-    being one complex number, so scores depend only on position differences).
+    being one complex number, so scores depend only on position differences; QK-norm: RMSNorm
+    on q and k before the dot product).
   * K3 notes, section 4 (GVA): q and k repeated to the value heads with repeat_interleave
     (forward); the backward of a replication sums over the copies.
 """
@@ -477,6 +478,77 @@ def check_rope_relative_positions(orc):
                           orc.attention(q, k, v, causal=True))
 
 
+def check_qk_norm_matches_torch_rms_norm(orc):
+    """Library cross-check of QK-norm (course page, step 3: RMSNorm on q and k before the dot
+    product): torch's rms_norm over the head dim with the same weights and eps, then the rotation
+    (complex multiplication), then fp64 SDPA; and the queries-only form against pre-processed
+    keys (a cache)."""
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(27)
+    for (Tq, Tkv, Hq, Hkv, d, causal, rope) in [(6, 6, 4, 2, 8, True, False),
+                                                (4, 9, 3, 1, 16, True, True),
+                                                (5, 5, 2, 2, 8, False, True)]:
+        q = rng.standard_normal((2, Tq, Hq, d)) * 3.0
+        k = rng.standard_normal((2, Tkv, Hkv, d)) * 0.5
+        v = rng.standard_normal((2, Tkv, Hkv, d))
+        wq = (rng.random(d) + 0.5).astype(np.float32)
+        wk = (rng.random(d) + 0.5).astype(np.float32)
+        eps = 1e-6
+        tabs = rope_tables(Tkv + 1, d) if rope else None
+        got = orc.attention(q, k, v, causal=causal, rope=tabs, qk_norm=(wq, wk, eps))
+
+        def norm(x, w):
+            return F.rms_norm(torch.from_numpy(x), (d,), torch.from_numpy(w.astype(np.float64)),
+                              eps)
+
+        def turn(x, pos0):
+            if not rope:
+                return x
+            rot = torch.complex(torch.from_numpy(tabs[0].astype(np.float64)),
+                                torch.from_numpy(tabs[1].astype(np.float64)))
+            z = torch.view_as_complex(x.reshape(*x.shape[:-1], d // 2, 2).contiguous())
+            z = z * rot[pos0:pos0 + x.shape[1]][None, :, None, :]
+            return torch.view_as_real(z).reshape(x.shape)
+        G = Hq // Hkv
+        qt = turn(norm(q, wq), Tkv - Tq).permute(0, 2, 1, 3).contiguous()
+        kp = turn(norm(k, wk), 0)
+        kt = kp.repeat_interleave(G, dim=2).permute(0, 2, 1, 3).contiguous()
+        vt = torch.from_numpy(v).repeat_interleave(G, dim=2).permute(0, 2, 1, 3).contiguous()
+        mask = torch.from_numpy(_window_mask(Tq, Tkv, Tkv + 1, 0)) if causal else None
+        ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+        err = np.max(np.abs(got - ref.permute(0, 2, 1, 3).numpy()))
+        assert err <= 1e-12, (Tq, Tkv, d, causal, rope, err)
+        got_q = orc.attention(q, kp.numpy(), v, causal=causal, rope=tabs, rope_mode="q",
+                              qk_norm=(wq, wk, eps), qk_norm_mode="q")
+        assert np.max(np.abs(got_q - got)) <= 1e-12
+
+
+def check_qk_norm_worked_example_and_scale_invariance(orc):
+    """d = 2, unit weights, eps = 0: q = (3, 4) normalises to (3, 4) / sqrt(12.5); keys (1, 0) and
+    (0, 2) to (sqrt 2, 0) and (0, sqrt 2); the two scores and the output follow in closed form.
+    And with eps = 0 the output does not change when q or k is scaled by a positive factor (the
+    point of the norm: it fixes the scale of the logits)."""
+    q = np.array([3.0, 4.0]).reshape(1, 1, 1, 2)
+    k = np.array([[1.0, 0.0], [0.0, 2.0]]).reshape(1, 2, 1, 2)
+    v = np.array([[1.0, 0.0], [0.0, 1.0]]).reshape(1, 2, 1, 2)
+    one = np.ones(2, dtype=np.float32)
+    got = orc.attention(q, k, v, qk_norm=(one, one, 0.0))
+    r = math.sqrt(12.5)
+    s0 = (3.0 / r) * math.sqrt(2.0) / math.sqrt(2.0)
+    s1 = (4.0 / r) * math.sqrt(2.0) / math.sqrt(2.0)
+    p0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    assert abs(got[0, 0, 0, 0] - p0) <= 1e-14 and abs(got[0, 0, 0, 1] - (1 - p0)) <= 1e-14, got
+    rng = _rng(28)
+    q = rng.standard_normal((1, 7, 4, 8)); k = rng.standard_normal((1, 7, 2, 8))
+    v = rng.standard_normal((1, 7, 2, 8))
+    w = (rng.random(8) + 0.5).astype(np.float32)
+    a = orc.attention(q, k, v, causal=True, qk_norm=(w, w, 0.0))
+    b = orc.attention(q * 37.0, k * 0.01, v, causal=True, qk_norm=(w, w, 0.0))
+    assert np.max(np.abs(a - b)) <= 1e-13, np.max(np.abs(a - b))
+    assert np.max(np.abs(a - orc.attention(q, k, v, causal=True))) > 1e-3
+
+
 # ------------------------------------------------------------------------------------------------
 # K3 notes, section 4, GVA: H query/key heads shared by HV = G*H value heads
 # ------------------------------------------------------------------------------------------------
@@ -622,6 +694,8 @@ ALL_CHECKS = [
     check_rope_worked_example,
     check_rope_matches_complex_torch,
     check_rope_relative_positions,
+    check_qk_norm_matches_torch_rms_norm,
+    check_qk_norm_worked_example_and_scale_invariance,
     check_gva_matches_repeat_interleave_sdpa,
     check_gva_shares_weights_within_a_group,
     check_bwd_matches_torch_autograd,

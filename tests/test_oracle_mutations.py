@@ -45,6 +45,11 @@ MUTANTS = {
     # backward: query gradient without the scale
     "bwd_dq_no_scale": ("dqr[c] += scale * ds * kh[j * kstride + c];",
                         "dqr[c] += ds * kh[j * kstride + c];"),
+    # course step 3: QK-norm with the sum of squares instead of their mean
+    "qk_norm_sum_not_mean": ("const double inv = 1.0 / sqrt(ss / d + eps);",
+                             "const double inv = 1.0 / sqrt(ss + eps);"),
+    # course step 3: QK-norm without its weights
+    "qk_norm_no_weights": ("x[c] = x[c] * inv * (double)w[c];", "x[c] = x[c] * inv;"),
     # GVA: every value head of a group reads the group's first value head
     "gva_value_head_of_group": ("const double* vh = &vw[(I.k_row0 * HV + j) * (int64_t)d];",
                                 "const double* vh = &vw[(I.k_row0 * HV + j - j % (HV / H)) * "
