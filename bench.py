@@ -118,8 +118,9 @@ def time_launches(fn, steps, warmup, torch):
     return ms, wall
 
 
-def bench_prefill(gqa, w, steps, warmup, torch, seed, rope=False):
-    """rope: turn q and k inside the kernel with (cos, sin) tables (rotary embedding)."""
+def bench_prefill(gqa, w, steps, warmup, torch, seed, rope=False, qk_norm=False):
+    """rope: turn q and k inside the kernel with (cos, sin) tables (rotary embedding); qk_norm:
+    RMSNorm of q and k (weights 1 + N(0, 0.1^2), eps 1e-6) before the rotation."""
     q, k, v, cu = device_inputs(w, torch, seed)
     out = torch.empty_like(q)
     msl = max(w.seqlens) if w.seqlens else None
@@ -127,11 +128,18 @@ def bench_prefill(gqa, w, steps, warmup, torch, seed, rope=False):
     if rope:
         import workloads
         tables = tuple(torch.from_numpy(t).cuda() for t in workloads.rope_tables(w.Tkv, w.d))
+    norm = None
+    if qk_norm:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed + 11)
+        wq = 1 + 0.1 * torch.randn(w.d, generator=g, device="cuda")
+        wk = 1 + 0.1 * torch.randn(w.d, generator=g, device="cuda")
+        norm = (wq, wk, 1e-6)
 
     def step():
-        if tables is not None:
+        if tables is not None or norm is not None:
             gqa.gqa_attn_prefill_ex(q, k, v, causal=w.causal, window=w.window, n_sink=w.n_sink,
-                                    rope=tables, out=out)
+                                    rope=tables, qk_norm=norm, out=out)
         elif w.window > 0:
             gqa.gqa_attn_prefill_window(q, k, v, window=w.window, n_sink=w.n_sink, out=out)
         else:
@@ -294,7 +302,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "mqa", "varlen", "window",
-                                       "ragged", "rope", "backward", "gva", "copy"],
+                                       "ragged", "rope", "qknorm", "backward", "gva",
+                                       "copy"],
                     default=None,
                     help="time a single workload (for profiling); still prints one JSON line. "
                          "'copy' times a plain 1 GiB device copy, the calibration kernel for "
@@ -352,6 +361,13 @@ def main():
         rp["workload"] = workloads.LLAMA_PREFILL.name + "+rope"
         extra["rope_prefill"] = rp
         log(f"rope prefill: {rp['avg_ms'] * 1e3:.1f} us, {rp['tflops']:.1f} TFLOP/s")
+    if args.only == "qknorm" or args.all:
+        qn, _ = bench_prefill(gqa, workloads.LLAMA_PREFILL, args.steps, args.warmup, torch, 2000,
+                              rope=True, qk_norm=True)
+        qn["frac_mfma"] = qn["tflops"] / PEAK_BF16_TFLOPS
+        qn["workload"] = workloads.LLAMA_PREFILL.name + "+qknorm+rope"
+        extra["qknorm_rope_prefill"] = qn
+        log(f"qk-norm + rope prefill: {qn['avg_ms'] * 1e3:.1f} us, {qn['tflops']:.1f} TFLOP/s")
     if args.only == "backward" or args.all:
         bw = bench_backward(gqa, workloads.LLAMA_PREFILL, args.steps, args.warmup, torch, 2000)
         extra["backward"] = bw
@@ -370,8 +386,10 @@ def main():
         log(f"decode: {dec['avg_ms'] * 1e3:.1f} us, {dec['gbs']:.0f} GB/s")
     sha = kernel_source_sha("prefill")
     metric = "GQA prefill TFLOPS (% MFMA peak); decode KV GB/s (% HBM peak)"
-    if pre is None and args.only in ("mqa", "varlen", "window", "rope", "backward", "gva"):
+    if pre is None and args.only in ("mqa", "varlen", "window", "rope", "qknorm", "backward",
+                                     "gva"):
         key, w = {"gva": ("gva_prefill", workloads.GVA_PREFILL),
+                  "qknorm": ("qknorm_rope_prefill", workloads.LLAMA_PREFILL),
                   "mqa": ("mqa_prefill", workloads.MQA_PREFILL),
                   "varlen": ("varlen_prefill", workloads.VARLEN_PREFILL),
                   "window": ("window_prefill", workloads.WINDOW_PREFILL),
@@ -386,9 +404,10 @@ def main():
                     "unit": "TFLOP/s", "frac": pre["tflops"] / PEAK_BF16_TFLOPS,
                     "traffic": traffic,
                     "kernel": {"backward": "bwd_rowdot + bwd_dkdv_kernel<128> + bwd_dq_kernel<128>",
-                               "rope": "prefill_pp_kernel<128, 128, true>",
-                               "gva": "prefill_pp_kernel<64, 128, false>"}.get(
-                                   args.only, "prefill_pp_kernel<128, 128, false>"),
+                               "rope": "prefill_pp_kernel<128, 128, true, false>",
+                               "qknorm": "prefill_pp_kernel<128, 128, true, true>",
+                               "gva": "prefill_pp_kernel<64, 128, false, false>"}.get(
+                                   args.only, "prefill_pp_kernel<128, 128, false, false>"),
                     "flops_per_launch": pre["flops_per_launch"],
                     "avg_launch_ms": pre["avg_ms"], "kernel_source_sha": sha}
         config = {"workload": w.name, "B": w.B, "T": w.Tq, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,

@@ -45,14 +45,20 @@ def _hip_runtimes_mapped():
 
 
 class AttnOptions(ctypes.Structure):
-    """``gqa_attn_options_t``: sliding window, sinks and rotary tables of the extended calls."""
+    """``gqa_attn_options_t``: sliding window, sinks, rotary tables, log-sum-exp output and
+    QK-norm weights of the extended calls."""
     _fields_ = [("window", ctypes.c_int), ("n_sink", ctypes.c_int),
                 ("rope_cos", ctypes.c_void_p), ("rope_sin", ctypes.c_void_p),
-                ("rope_rows", ctypes.c_int), ("lse", ctypes.c_void_p)]
+                ("rope_rows", ctypes.c_int), ("lse", ctypes.c_void_p),
+                ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float)]
 
 
-def _options(window: int, n_sink: int, rope, d: int, lse=None) -> AttnOptions:
-    o = AttnOptions(int(window), int(n_sink), None, None, 0, None)
+def _options(window: int, n_sink: int, rope, d: int, lse=None, qk_norm=None) -> AttnOptions:
+    """qk_norm: None or (w_q, w_k, eps), float32 device weights [d]. The returned struct keeps
+    the tensors it points to alive (``_keep``) until the call has been enqueued."""
+    o = AttnOptions(int(window), int(n_sink), None, None, 0, None, None, None, 0.0)
+    keep = []
     if lse is not None:
         o.lse = lse.data_ptr()
     if rope is not None:
@@ -61,6 +67,16 @@ def _options(window: int, n_sink: int, rope, d: int, lse=None) -> AttnOptions:
                 or cos_t.shape != sin_t.shape or cos_t.shape[1] * 2 != d):
             raise ValueError("rope tables must be float32 device tensors [rows, d/2]")
         o.rope_cos, o.rope_sin, o.rope_rows = cos_t.data_ptr(), sin_t.data_ptr(), cos_t.shape[0]
+        keep += [cos_t, sin_t]
+    if qk_norm is not None:
+        wq, wk = (_dev(t, name) for t, name in zip(qk_norm[:2], ("q norm weights",
+                                                               "k norm weights")))
+        if wq.dtype != torch.float32 or wk.dtype != torch.float32 or \
+                tuple(wq.shape) != (d,) or tuple(wk.shape) != (d,):
+            raise ValueError("qk-norm weights must be float32 device tensors [d]")
+        o.q_norm_w, o.k_norm_w, o.norm_eps = wq.data_ptr(), wk.data_ptr(), float(qk_norm[2])
+        keep += [wq, wk]
+    o._keep = keep
     return o
 
 
@@ -213,17 +229,19 @@ def gqa_attn_prefill_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causa
                         window: int = 0, n_sink: int = 0, rope=None,
                         scale: Optional[float] = None, cu_seqlens: Optional[torch.Tensor] = None,
                         max_seqlen: Optional[int] = None, out: Optional[torch.Tensor] = None,
-                        lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                        lse: Optional[torch.Tensor] = None, qk_norm=None,
+                        stream=None) -> torch.Tensor:
     """:func:`gqa_attn_prefill` with a sliding window / sinks and rotary embedding of q and k
     inside the kernel; rope = (cos, sin) float32 device tables [rows, d/2]; lse: optional float32
-    device output [B, Tq, Hq] receiving each row's log-sum-exp (for the backward). bf16 only."""
+    device output [B, Tq, Hq] receiving each row's log-sum-exp (for the backward); qk_norm =
+    (w_q, w_k, eps): RMSNorm of every q and k head row before the rotation. bf16 only."""
     q, k, v, out, dims, cu_ptr, msl = _prefill_args(q, k, v, scale, cu_seqlens, max_seqlen, out)
     if lse is not None:
         lse = _dev(lse, "lse")
         if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]) \
                 or not lse.is_contiguous():
             raise ValueError("lse must be a contiguous float32 device tensor [B, Tq, Hq]")
-    opt = _options(window, n_sink, rope, q.shape[-1], lse)
+    opt = _options(window, n_sink, rope, q.shape[-1], lse, qk_norm)
     rc = _lib.gqa_attn_prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                   *dims, int(bool(causal)), cu_ptr, msl, ctypes.byref(opt),
                                   _dtype_code(q), _stream(stream))
@@ -345,9 +363,11 @@ def gqa_attn_decode_ex(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                        cache_lens: Optional[torch.Tensor] = None, window: int = 0,
                        n_sink: int = 0, rope=None, scale: Optional[float] = None,
                        workspace: Optional[torch.Tensor] = None,
-                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """:func:`gqa_attn_decode_ragged` plus rotary embedding of the query (the cache holds
-    turned keys); rope = (cos, sin) float32 device tables [rows >= Tmax, d/2]. bf16 only."""
+                       out: Optional[torch.Tensor] = None, qk_norm=None,
+                       stream=None) -> torch.Tensor:
+    """:func:`gqa_attn_decode_ragged` plus rotary embedding and QK-norm of the query (the cache
+    holds processed keys); rope = (cos, sin) float32 device tables [rows >= Tmax, d/2];
+    qk_norm = (w_q, w_k, eps). bf16 only."""
     q, k, v, out, dims, ws_ptr, ws_bytes, _ = _decode_args(q, k_cache, v_cache, scale, workspace,
                                                            out)
     lens_ptr = None
@@ -357,7 +377,7 @@ def gqa_attn_decode_ex(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
             raise ValueError("cache_lens must be a 1-D int32 device tensor with one entry per "
                              "sequence")
         lens_ptr = lens.data_ptr()
-    opt = _options(window, n_sink, rope, q.shape[-1])
+    opt = _options(window, n_sink, rope, q.shape[-1], None, qk_norm)
     rc = _lib.gqa_attn_decode_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), *dims,
                                  lens_ptr, ctypes.byref(opt), ws_ptr, ws_bytes, _dtype_code(q),
                                  _stream(stream))

@@ -104,6 +104,9 @@ struct PrefillArgs {
   const float* rope_sin;
   int rope_rows;
   float* lse;  // optional output: natural-log log-sum-exp of each row's scaled scores
+  const float* qn_w;  // QK-norm weights [d] of queries and keys (device), or nullptr
+  const float* kn_w;
+  float norm_eps;
   // Value and output geometry, in elements. Grouped-query attention: dv = d, vslices = 1,
   // v_row = Hkv*d, v_head = d, o_row = Hq*d, o_head = d. Grouped value attention hands in the
   // G value heads of a query/key head as one value row of G*d columns, produced in vslices
@@ -129,6 +132,8 @@ struct DecodeArgs {
   const float* rope_cos;  // rotary tables for the query [rope_rows][d/2] (device), or nullptr
   const float* rope_sin;
   int rope_rows;
+  const float* qn_w;  // QK-norm weights [d] of the query (device), or nullptr
+  float norm_eps;
 };
 // Rotary embedding of one 16-byte chunk of a head row in place: 4 pairs (2i, 2i+1), each turned
 // by the angle whose cos / sin are given (the pair is one complex number times e^{i angle}).
@@ -139,6 +144,62 @@ __device__ __forceinline__ u32x4 rope_chunk(u32x4 w, f32x4 c, f32x4 s) {
     w[e] = pack_bf16x2(fmaf(re, c[e], -im * s[e]), fmaf(re, s[e], im * c[e]));
   }
   return w;
+}
+
+// The same arithmetic on 8 fp32 values (one 16-byte chunk of a head row, 4 pairs).
+__device__ __forceinline__ void rope8(float* x, f32x4 c, f32x4 s) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float re = x[2 * e], im = x[2 * e + 1];
+    x[2 * e] = fmaf(re, c[e], -im * s[e]);
+    x[2 * e + 1] = fmaf(re, s[e], im * c[e]);
+  }
+}
+__device__ __forceinline__ void unpack8(u32x4 w, float* x) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = bf16_lo(w[e]);
+    x[2 * e + 1] = bf16_hi(w[e]);
+  }
+}
+__device__ __forceinline__ u32x4 pack8(const float* x) {
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+  return w;
+}
+__device__ __forceinline__ float sumsq8(u32x4 w) {
+  float x[8], s = 0.f;
+  unpack8(w, x);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s = fmaf(x[e], x[e], s);
+  return s;
+}
+// QK-norm of one 16-byte chunk: x * inv * w, with inv = 1/sqrt(mean(x^2) + eps) of the whole
+// head row and w the chunk's 8 weights (two fp32 vectors).
+__device__ __forceinline__ void norm8(float* x, float inv, f32x4 w0, f32x4 w1) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] *= inv * w0[e];
+    x[4 + e] *= inv * w1[e];
+  }
+}
+// Sum over aligned groups of N = 8 or 16 consecutive lanes, left in every lane of the group, with
+// DPP moves inside a 16-lane row (no LDS crossbar): swap neighbours, swap pairs, mirror the
+// 8-lane halves (quad sums meet), and for 16 also mirror the row. DPP controls: quad_perm
+// [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140.
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  static_assert(N == 8 || N == 16, "DPP row reductions over 8 or 16 lanes");
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+  if constexpr (N == 16)
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+__device__ __forceinline__ float rms_inv(float sumsq, int d, float eps) {
+  return __builtin_amdgcn_rsqf(sumsq / static_cast<float>(d) + eps);
 }
 
 struct BwdArgs {

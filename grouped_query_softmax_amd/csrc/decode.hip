@@ -127,13 +127,37 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                            (static_cast<int64_t>(b) * a.Hq + kvh * G + (col_ok ? col : 0)) * D +
                            8 * g;
+    u32x4 wq[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      wq[s] = col_ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * s) : u32x4{0, 0, 0, 0};
+    float inv = 0.f;
+    if (a.qn_w) {
+      // QK-norm of the query (the cache holds normalised keys): the row is spread over the
+      // lanes r16 + 16 g, g = 0..3
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) ss += sumsq8(wq[s]);
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      inv = rms_inv(ss, D, a.norm_eps);
+    }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      u32x4 w = col_ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * s) : u32x4{0, 0, 0, 0};
-      if (a.rope_cos) {
-        // rotary embedding of the query at its position L - 1 (the cache holds turned keys);
-        // this lane's dimensions 32s + 8g .. +7 are the pairs 16s + 4g .. +3
-        const int ti = (L - 1) * (D / 2) + 16 * s + 4 * g;
+      u32x4 w = wq[s];
+      // rotary embedding of the query at its position L - 1 (the cache holds turned keys);
+      // this lane's dimensions 32s + 8g .. +7 are the pairs 16s + 4g .. +3
+      const int ti = (L - 1) * (D / 2) + 16 * s + 4 * g;
+      if (a.qn_w) {
+        float x[8];
+        unpack8(w, x);
+        norm8(x, inv, *reinterpret_cast<const f32x4*>(a.qn_w + 32 * s + 8 * g),
+              *reinterpret_cast<const f32x4*>(a.qn_w + 32 * s + 8 * g + 4));
+        if (a.rope_cos)
+          rope8(x, *reinterpret_cast<const f32x4*>(a.rope_cos + ti),
+                *reinterpret_cast<const f32x4*>(a.rope_sin + ti));
+        w = pack8(x);
+      } else if (a.rope_cos) {
         w = rope_chunk(w, *reinterpret_cast<const f32x4*>(a.rope_cos + ti),
                        *reinterpret_cast<const f32x4*>(a.rope_sin + ti));
       }

@@ -96,6 +96,13 @@ static gqa_status_t check_options(const gqa_attn_options_t* o, gqa_dtype_t dtype
     if (o->rope_rows < rows_needed) return GQA_ERR_SHAPE;
   }
   if (o->lse && dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+  const bool norm = o->q_norm_w || o->k_norm_w;
+  if (norm) {
+    if (!o->q_norm_w || !o->k_norm_w) return GQA_ERR_NULL_PTR;
+    if (dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+    if (!aligned16(o->q_norm_w) || !aligned16(o->k_norm_w)) return GQA_ERR_UNSUPPORTED;
+    if (!isfinite(o->norm_eps) || !(o->norm_eps > 0.f)) return GQA_ERR_SHAPE;
+  }
   return GQA_OK;
 }
 
@@ -166,6 +173,9 @@ static gqa_status_t prefill_impl(const void* q, const void* k, const void* v, vo
   a.rope_sin = opt ? opt->rope_sin : nullptr;
   a.rope_rows = opt ? opt->rope_rows : 0;
   a.lse = opt ? opt->lse : nullptr;
+  a.qn_w = opt ? opt->q_norm_w : nullptr;
+  a.kn_w = opt ? opt->k_norm_w : nullptr;
+  a.norm_eps = opt ? opt->norm_eps : 0.f;
   set_gqa_geometry(a);
   if (a.lse && overlap(a.lse, rows_q * Hq * sizeof(float), q, nq)) return GQA_ERR_ALIAS;
   return from_hip(dtype == GQA_DTYPE_BF16 ? gqa::launch_prefill_bf16(a, stream)
@@ -209,7 +219,8 @@ gqa_status_t gqa_attn_prefill_gva(const void* q, const void* k, const void* v, v
   if (HV % H != 0) return GQA_ERR_GROUPING;
   if (dtype != GQA_DTYPE_BF16 || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
   if (const gqa_status_t st = check_options(opt, dtype, cu_seqlens ? max_seqlen : Tkv)) return st;
-  if (opt && (opt->rope_cos || opt->rope_sin)) return GQA_ERR_UNSUPPORTED;
+  if (opt && (opt->rope_cos || opt->rope_sin || opt->q_norm_w || opt->k_norm_w))
+    return GQA_ERR_UNSUPPORTED;
   const int window = opt ? opt->window : 0;
   const int n_sink = opt ? opt->n_sink : 0;
   if ((window > 0 || n_sink > 0) && !causal) return GQA_ERR_SHAPE;
@@ -259,6 +270,8 @@ gqa_status_t gqa_attn_prefill_gva(const void* q, const void* k, const void* v, v
   a.rope_cos = a.rope_sin = nullptr;
   a.rope_rows = 0;
   a.lse = opt ? opt->lse : nullptr;
+  a.qn_w = a.kn_w = nullptr;
+  a.norm_eps = 0.f;
   a.dv = dv;
   a.vslices = vslices;
   a.v_row = HV * d;
@@ -332,6 +345,8 @@ static gqa_status_t decode_impl(const void* q, const void* k_cache, const void* 
     a.rope_cos = a.rope_sin = nullptr;
     a.rope_rows = 0;
     a.lse = nullptr;
+    a.qn_w = a.kn_w = nullptr;
+    a.norm_eps = 0.f;
     set_gqa_geometry(a);
     return from_hip(gqa::launch_prefill_f32(a, stream));
   }
@@ -361,6 +376,8 @@ static gqa_status_t decode_impl(const void* q, const void* k_cache, const void* 
   a.rope_cos = opt ? opt->rope_cos : nullptr;
   a.rope_sin = opt ? opt->rope_sin : nullptr;
   a.rope_rows = opt ? opt->rope_rows : 0;
+  a.qn_w = opt ? opt->q_norm_w : nullptr;  // the cache holds normalised keys
+  a.norm_eps = opt ? opt->norm_eps : 0.f;
   return from_hip(gqa::launch_decode_bf16(a, stream));
 }
 

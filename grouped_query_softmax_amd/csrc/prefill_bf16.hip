@@ -93,7 +93,7 @@ struct PPCfg {
   static_assert(kVBase < 65536 && 3 * kVBytes < 65536, "stage offsets fit LDS immediates");
 };
 
-template <int DQ, int DV, bool ROPE>
+template <int DQ, int DV, bool ROPE, bool NORM>
 __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int heads_per_wg,
                                                          int pos_per_wg, int head_tiles, int gz) {
   using C = PPCfg<DQ, DV>;
@@ -102,7 +102,9 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
   constexpr int NMT = DV / 32;  // 32-row value-column tiles of O^T
   constexpr int VD = C::kVD;
   constexpr int VW = VD / 2;
-  __shared__ __attribute__((aligned(16))) char smem[C::kSmemBytes];
+  // with QK-norm the key weights follow the stages in LDS (read while staging K)
+  constexpr int kNormOff = C::kSmemBytes;
+  __shared__ __attribute__((aligned(16))) char smem[C::kSmemBytes + (NORM ? DQ * 4 : 0)];
 
   const int gx = a.Hkv * head_tiles * a.vslices;
   const int lin = blockIdx.x;
@@ -165,6 +167,11 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
   const int v_dst = (VD * v_c) * C::kVPitch + 8 * vt_slot(v_kg);
   const int k_rd = n * C::kKPitch + 16 * hh;
   const int v_rd = n * C::kVPitch + 16 * hh;
+  // QK-norm weights of the keys into LDS (made visible by the barrier opening each query tile)
+  if constexpr (NORM) {
+    if (tid < DQ / 4)
+      lds_write<f32x4>(smem, kNormOff + 16 * tid, *reinterpret_cast<const f32x4*>(a.kn_w + 4 * tid));
+  }
 
   for (int tt = 0; tt < ntile_here; ++tt) {
     const int tile = tiles[tt];
@@ -180,12 +187,34 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
     bf16x8 qf[NS];
     {
       const uint16_t* qrow = Qp + ((q0 + pos) * a.Hq + hq) * D + 8 * hh;
+      u32x4 wq[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        wq[s] = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * s) : u32x4{0, 0, 0, 0};
+      [[maybe_unused]] float inv = 0.f;
+      if constexpr (NORM) {
+        // the row's sum of squares: this lane's half plus its partner's (lane ^ 32)
+        float ss = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) ss += sumsq8(wq[s]);
+        ss += __shfl_xor(ss, 32);
+        inv = rms_inv(ss, D, a.norm_eps);
+      }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        u32x4 w = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * s) : u32x4{0, 0, 0, 0};
-        if constexpr (ROPE) {
-          // query at position pos + off (the causal mask's alignment); pairs 8s + 4hh .. +3
-          const int ti = (pos + off) * (D / 2) + 8 * s + 4 * hh;
+        u32x4 w = wq[s];
+        // query at position pos + off (the causal mask's alignment); pairs 8s + 4hh .. +3
+        [[maybe_unused]] const int ti = (pos + off) * (D / 2) + 8 * s + 4 * hh;
+        if constexpr (NORM) {
+          float x[8];
+          unpack8(w, x);
+          norm8(x, inv, *reinterpret_cast<const f32x4*>(a.qn_w + 16 * s + 8 * hh),
+                *reinterpret_cast<const f32x4*>(a.qn_w + 16 * s + 8 * hh + 4));
+          if constexpr (ROPE)
+            rope8(x, *reinterpret_cast<const f32x4*>(a.rope_cos + ti),
+                  *reinterpret_cast<const f32x4*>(a.rope_sin + ti));
+          w = pack8(x);
+        } else if constexpr (ROPE) {
           w = rope_chunk(w, *reinterpret_cast<const f32x4*>(a.rope_cos + ti),
                          *reinterpret_cast<const f32x4*>(a.rope_sin + ti));
         }
@@ -259,10 +288,30 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
     };
     auto store_k = [&](int stage) {
       char* base = smem + stage * C::kKBytes;
+      [[maybe_unused]] float inv_k[C::kKLoads];
+      if constexpr (NORM) {
+        // each key row is spread over kChunks consecutive lanes: sum their squares
+#pragma unroll
+        for (int i = 0; i < C::kKLoads; ++i) {
+          const float ss = lane_group_sum<C::kChunks>(
+              sumsq8(u32x4{stg[4 * i], stg[4 * i + 1], stg[4 * i + 2], stg[4 * i + 3]}));
+          inv_k[i] = rms_inv(ss, D, a.norm_eps);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < C::kKLoads; ++i) {
         u32x4 w = {stg[4 * i], stg[4 * i + 1], stg[4 * i + 2], stg[4 * i + 3]};
-        if constexpr (ROPE) w = rope_chunk(w, rc[i], rs[i]);
+        if constexpr (NORM) {
+          float x[8];
+          unpack8(w, x);
+          // weights of this thread's pieces (piece gtid % kChunks of each row)
+          const int woff = kNormOff + 32 * (gtid % C::kChunks);
+          norm8(x, inv_k[i], lds_read<f32x4>(smem, woff), lds_read<f32x4>(smem, woff + 16));
+          if constexpr (ROPE) rope8(x, rc[i], rs[i]);
+          w = pack8(x);
+        } else if constexpr (ROPE) {
+          w = rope_chunk(w, rc[i], rs[i]);
+        }
         lds_write<u32x4>(base, k_dst[i], w);
       }
     };
@@ -502,7 +551,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
   }
 }
 
-template <int DQ, int DV, bool ROPE>
+template <int DQ, int DV, bool ROPE, bool NORM>
 hipError_t launch_pp(const PrefillArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int heads_per_wg = G < kCols ? G : kCols;
@@ -511,9 +560,17 @@ hipError_t launch_pp(const PrefillArgs& a, hipStream_t s) {
   const int ntiles = (a.max_tq + pos_per_wg - 1) / pos_per_wg;
   const int gz = a.causal ? (ntiles + 1) / 2 : ntiles;
   const dim3 grid(a.Hkv * head_tiles * a.vslices * a.nitems * gz);
-  hipLaunchKernelGGL((prefill_pp_kernel<DQ, DV, ROPE>), grid, dim3(512), 0, s, a, heads_per_wg,
-                     pos_per_wg, head_tiles, gz);
+  hipLaunchKernelGGL((prefill_pp_kernel<DQ, DV, ROPE, NORM>), grid, dim3(512), 0, s, a,
+                     heads_per_wg, pos_per_wg, head_tiles, gz);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_same_width(const PrefillArgs& a, hipStream_t s) {
+  const bool rope = a.rope_cos != nullptr, norm = a.qn_w != nullptr;
+  if (norm)
+    return rope ? launch_pp<D, D, true, true>(a, s) : launch_pp<D, D, false, true>(a, s);
+  return rope ? launch_pp<D, D, true, false>(a, s) : launch_pp<D, D, false, false>(a, s);
 }
 
 }  // namespace
@@ -521,12 +578,10 @@ hipError_t launch_pp(const PrefillArgs& a, hipStream_t s) {
 int prefill_bf16_cols() { return kCols; }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
-  const bool rope = a.rope_cos != nullptr;
-  if (a.d == 64 && a.dv == 64)
-    return rope ? launch_pp<64, 64, true>(a, s) : launch_pp<64, 64, false>(a, s);
-  if (a.d == 128 && a.dv == 128)
-    return rope ? launch_pp<128, 128, true>(a, s) : launch_pp<128, 128, false>(a, s);
-  if (a.d == 64 && a.dv == 128 && !rope) return launch_pp<64, 128, false>(a, s);
+  if (a.d == 64 && a.dv == 64) return launch_same_width<64>(a, s);
+  if (a.d == 128 && a.dv == 128) return launch_same_width<128>(a, s);
+  if (a.d == 64 && a.dv == 128 && !a.rope_cos && !a.qn_w)
+    return launch_pp<64, 128, false, false>(a, s);
   return hipErrorInvalidValue;
 }
 

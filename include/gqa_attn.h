@@ -87,7 +87,15 @@ gqa_status_t gqa_attn_prefill(const void* q, const void* k, const void* v, void*
  *                   keys already turned at their positions.
  *   rope_rows:      rows of the tables; must cover every position used (>= Tkv, >= max_seqlen
  *                   for packed batches, >= Tmax for decode), else GQA_ERR_SHAPE.
- * Windows and rotation are bf16 only (GQA_ERR_UNSUPPORTED for f32).
+ *   q_norm_w, k_norm_w, norm_eps: QK-norm (course page, step 3: RMSNorm of q and k before the
+ *                   dot product). Every query and key head row x becomes
+ *                   x * w / sqrt(mean(x^2) + norm_eps), w the DEVICE fp32 weights [d] (16-byte
+ *                   aligned), applied before the rotation. Both NULL: no norm; exactly one
+ *                   NULL: GQA_ERR_NULL_PTR; norm_eps must be finite and > 0 (else GQA_ERR_SHAPE).
+ *                   Prefill normalises queries at load and keys as they are staged; decode
+ *                   normalises the query and expects the cache to hold normalised keys
+ *                   (k_norm_w is then only validated).
+ * Windows, rotation and QK-norm are bf16 only (GQA_ERR_UNSUPPORTED for f32).
  */
 typedef struct {
   int window;
@@ -98,6 +106,9 @@ typedef struct {
   float* lse; /* optional OUTPUT (prefill only): DEVICE fp32 [B, Tq, Hq] ([1, total, Hq] when
                  packed), the natural-log log-sum-exp of each row's scaled scores, as
                  gqa_attn_backward needs it; NULL: not written */
+  const float* q_norm_w;
+  const float* k_norm_w;
+  float norm_eps;
 } gqa_attn_options_t;
 
 /* gqa_attn_prefill with options (window, sinks, rotary embedding). */
@@ -215,7 +226,7 @@ gqa_status_t gqa_fold_kv(const void* src, void* dst, int B, int T, int H, int g,
 const char* gqa_status_string(gqa_status_t s);
 
 /* Interface version of this header: bumped on any incompatible change. */
-#define GQA_ATTN_ABI_VERSION 1
+#define GQA_ATTN_ABI_VERSION 2
 int gqa_attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -23,7 +23,7 @@ def test_library_exports_every_header_function(lib):
                           "gqa_fold_kv", "gqa_status_string", "gqa_attn_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gqa_attn_abi_version() == 1
+    assert lib.gqa_attn_abi_version() == 2
 
 
 def test_single_hip_runtime_in_process():
@@ -113,6 +113,21 @@ def test_extended_options_validation(lib):
                                       ctypes.byref(opt), W, need, BF16, None)
     assert dex(Opt(0, 0, T, T + 4096, 1023, None)) == B.GQA_ERR_SHAPE      # rows must cover Tmax
     assert dex(Opt(0, 0, None, T, 1024, None)) == B.GQA_ERR_NULL_PTR
+
+
+def test_qk_norm_options_validation(lib):
+    Opt = B.AttnOptions
+    N = W + 65536   # fake aligned weight addresses
+
+    def pex(opt, dt=BF16, d=128):
+        return lib.gqa_attn_prefill_ex(Q, K, V, O, 1, 8, 8, 8, 2, d, 0.1, 1, None, 0,
+                                       ctypes.byref(opt), dt, None)
+    assert pex(Opt(0, 0, None, None, 0, None, N, None, 1e-6)) == B.GQA_ERR_NULL_PTR
+    assert pex(Opt(0, 0, None, None, 0, None, N, N + 4096, 0.0)) == B.GQA_ERR_SHAPE
+    assert pex(Opt(0, 0, None, None, 0, None, N, N + 4096, float("nan"))) == B.GQA_ERR_SHAPE
+    assert pex(Opt(0, 0, None, None, 0, None, N + 4, N + 4096, 1e-6)) == B.GQA_ERR_UNSUPPORTED
+    assert pex(Opt(0, 0, None, None, 0, None, N, N + 4096, 1e-6), dt=F32, d=16) == \
+        B.GQA_ERR_UNSUPPORTED
 
 
 def test_gva_validation(lib):
