@@ -118,9 +118,12 @@ def time_launches(fn, steps, warmup, torch):
     return ms, wall
 
 
-def bench_prefill(gqa, w, steps, warmup, torch, seed, rope=False, qk_norm=False):
+def bench_prefill(gqa, w, steps, warmup, torch, seed, rope=False, qk_norm=False,
+                  prepared=False):
     """rope: turn q and k inside the kernel with (cos, sin) tables (rotary embedding); qk_norm:
-    RMSNorm of q and k (weights 1 + N(0, 0.1^2), eps 1e-6) before the rotation."""
+    RMSNorm of q and k (weights 1 + N(0, 0.1^2), eps 1e-6) before the rotation; prepared: each
+    step runs gqa_prepare_keys (keys normalised / turned once) and then the attention with
+    keys_prepared, both timed."""
     q, k, v, cu = device_inputs(w, torch, seed)
     out = torch.empty_like(q)
     msl = max(w.seqlens) if w.seqlens else None
@@ -136,8 +139,14 @@ def bench_prefill(gqa, w, steps, warmup, torch, seed, rope=False, qk_norm=False)
         wk = 1 + 0.1 * torch.randn(w.d, generator=g, device="cuda")
         norm = (wq, wk, 1e-6)
 
+    kbuf = torch.empty_like(k) if prepared else None
+
     def step():
-        if tables is not None or norm is not None:
+        if prepared:
+            gqa.gqa_prepare_keys(k, rope=tables, qk_norm=norm, out=kbuf)
+            gqa.gqa_attn_prefill_ex(q, kbuf, v, causal=w.causal, rope=tables, qk_norm=norm,
+                                    keys_prepared=True, out=out)
+        elif tables is not None or norm is not None:
             gqa.gqa_attn_prefill_ex(q, k, v, causal=w.causal, window=w.window, n_sink=w.n_sink,
                                     rope=tables, qk_norm=norm, out=out)
         elif w.window > 0:
@@ -361,6 +370,13 @@ def main():
         rp["workload"] = workloads.LLAMA_PREFILL.name + "+rope"
         extra["rope_prefill"] = rp
         log(f"rope prefill: {rp['avg_ms'] * 1e3:.1f} us, {rp['tflops']:.1f} TFLOP/s")
+        pp, _ = bench_prefill(gqa, workloads.LLAMA_PREFILL, args.steps, args.warmup, torch, 2000,
+                              rope=True, prepared=True)
+        pp["frac_mfma"] = pp["tflops"] / PEAK_BF16_TFLOPS
+        pp["workload"] = workloads.LLAMA_PREFILL.name + "+rope, keys prepared"
+        extra["rope_prefill_keys_prepared"] = pp
+        log(f"rope prefill, keys prepared: {pp['avg_ms'] * 1e3:.1f} us, "
+            f"{pp['tflops']:.1f} TFLOP/s")
     if args.only == "qknorm" or args.all:
         qn, _ = bench_prefill(gqa, workloads.LLAMA_PREFILL, args.steps, args.warmup, torch, 2000,
                               rope=True, qk_norm=True)
@@ -368,6 +384,13 @@ def main():
         qn["workload"] = workloads.LLAMA_PREFILL.name + "+qknorm+rope"
         extra["qknorm_rope_prefill"] = qn
         log(f"qk-norm + rope prefill: {qn['avg_ms'] * 1e3:.1f} us, {qn['tflops']:.1f} TFLOP/s")
+        qp, _ = bench_prefill(gqa, workloads.LLAMA_PREFILL, args.steps, args.warmup, torch, 2000,
+                              rope=True, qk_norm=True, prepared=True)
+        qp["frac_mfma"] = qp["tflops"] / PEAK_BF16_TFLOPS
+        qp["workload"] = workloads.LLAMA_PREFILL.name + "+qknorm+rope, keys prepared"
+        extra["qknorm_rope_prefill_keys_prepared"] = qp
+        log(f"qk-norm + rope prefill, keys prepared: {qp['avg_ms'] * 1e3:.1f} us, "
+            f"{qp['tflops']:.1f} TFLOP/s")
     if args.only == "backward" or args.all:
         bw = bench_backward(gqa, workloads.LLAMA_PREFILL, args.steps, args.warmup, torch, 2000)
         extra["backward"] = bw

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     gqa_attn_prefill_gva,
     gqa_attn_prefill_window,
     gqa_fold_kv,
+    gqa_prepare_keys,
     gqa_status_string,
     header_functions,
     load_library,

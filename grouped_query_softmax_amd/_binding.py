@@ -51,13 +51,15 @@ class AttnOptions(ctypes.Structure):
                 ("rope_cos", ctypes.c_void_p), ("rope_sin", ctypes.c_void_p),
                 ("rope_rows", ctypes.c_int), ("lse", ctypes.c_void_p),
                 ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p),
-                ("norm_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("keys_prepared", ctypes.c_int)]
 
 
-def _options(window: int, n_sink: int, rope, d: int, lse=None, qk_norm=None) -> AttnOptions:
+def _options(window: int, n_sink: int, rope, d: int, lse=None, qk_norm=None,
+             keys_prepared: bool = False) -> AttnOptions:
     """qk_norm: None or (w_q, w_k, eps), float32 device weights [d]. The returned struct keeps
     the tensors it points to alive (``_keep``) until the call has been enqueued."""
-    o = AttnOptions(int(window), int(n_sink), None, None, 0, None, None, None, 0.0)
+    o = AttnOptions(int(window), int(n_sink), None, None, 0, None, None, None, 0.0,
+                    int(bool(keys_prepared)))
     keep = []
     if lse is not None:
         o.lse = lse.data_ptr()
@@ -69,13 +71,15 @@ def _options(window: int, n_sink: int, rope, d: int, lse=None, qk_norm=None) -> 
         o.rope_cos, o.rope_sin, o.rope_rows = cos_t.data_ptr(), sin_t.data_ptr(), cos_t.shape[0]
         keep += [cos_t, sin_t]
     if qk_norm is not None:
-        wq, wk = (_dev(t, name) for t, name in zip(qk_norm[:2], ("q norm weights",
-                                                               "k norm weights")))
-        if wq.dtype != torch.float32 or wk.dtype != torch.float32 or \
-                tuple(wq.shape) != (d,) or tuple(wk.shape) != (d,):
-            raise ValueError("qk-norm weights must be float32 device tensors [d]")
-        o.q_norm_w, o.k_norm_w, o.norm_eps = wq.data_ptr(), wk.data_ptr(), float(qk_norm[2])
-        keep += [wq, wk]
+        ws = [None if t is None else _dev(t, name)
+              for t, name in zip(qk_norm[:2], ("q norm weights", "k norm weights"))]
+        for t in ws:
+            if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (d,)):
+                raise ValueError("qk-norm weights must be float32 device tensors [d]")
+        o.q_norm_w = ws[0].data_ptr() if ws[0] is not None else None
+        o.k_norm_w = ws[1].data_ptr() if ws[1] is not None else None
+        o.norm_eps = float(qk_norm[2])
+        keep += [t for t in ws if t is not None]
     o._keep = keep
     return o
 
@@ -100,6 +104,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_attn_prefill_ex.restype = I
     lib.gqa_attn_prefill_gva.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P, I, OP, I, P]
     lib.gqa_attn_prefill_gva.restype = I
+    lib.gqa_prepare_keys.argtypes = [P, P, I, I, I, I, P, I, I, OP, I, P]
+    lib.gqa_prepare_keys.restype = I
     lib.gqa_attn_decode_ex.argtypes = [P, P, P, P, I, I, I, I, I, F, P, OP, P, SZ, I, P]
     lib.gqa_attn_decode_ex.restype = I
     lib.gqa_attn_backward_workspace_bytes.argtypes = [I, I, I]
@@ -230,18 +236,19 @@ def gqa_attn_prefill_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causa
                         scale: Optional[float] = None, cu_seqlens: Optional[torch.Tensor] = None,
                         max_seqlen: Optional[int] = None, out: Optional[torch.Tensor] = None,
                         lse: Optional[torch.Tensor] = None, qk_norm=None,
-                        stream=None) -> torch.Tensor:
+                        keys_prepared: bool = False, stream=None) -> torch.Tensor:
     """:func:`gqa_attn_prefill` with a sliding window / sinks and rotary embedding of q and k
     inside the kernel; rope = (cos, sin) float32 device tables [rows, d/2]; lse: optional float32
     device output [B, Tq, Hq] receiving each row's log-sum-exp (for the backward); qk_norm =
-    (w_q, w_k, eps): RMSNorm of every q and k head row before the rotation. bf16 only."""
+    (w_q, w_k, eps): RMSNorm of every q and k head row before the rotation; keys_prepared: k
+    already normalised / turned (:func:`gqa_prepare_keys`), only q is processed. bf16 only."""
     q, k, v, out, dims, cu_ptr, msl = _prefill_args(q, k, v, scale, cu_seqlens, max_seqlen, out)
     if lse is not None:
         lse = _dev(lse, "lse")
         if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]) \
                 or not lse.is_contiguous():
             raise ValueError("lse must be a contiguous float32 device tensor [B, Tq, Hq]")
-    opt = _options(window, n_sink, rope, q.shape[-1], lse, qk_norm)
+    opt = _options(window, n_sink, rope, q.shape[-1], lse, qk_norm, keys_prepared)
     rc = _lib.gqa_attn_prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                   *dims, int(bool(causal)), cu_ptr, msl, ctypes.byref(opt),
                                   _dtype_code(q), _stream(stream))
@@ -291,6 +298,36 @@ def gqa_attn_prefill_gva(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, caus
                                    nseq, Tq, Tkv, H, HV, d, float(scale), int(bool(causal)),
                                    cu_ptr, msl, ctypes.byref(opt), _dtype_code(q), _stream(stream))
     _check(rc, "gqa_attn_prefill_gva")
+    return out
+
+
+def gqa_prepare_keys(k: torch.Tensor, rope=None, qk_norm=None, pos0: int = 0,
+                     cu_seqlens: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
+                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """QK-norm (qk_norm = (w_q or None, w_k, eps); only w_k is used) then the rotary turn of
+    every key row of k [B, T, Hkv, d] (packed: [1, total, Hkv, d] with cu_seqlens); key j of a
+    sequence at position pos0 + j. out may be k itself. bf16."""
+    k = _dev(k, "k")
+    if k.dim() != 4:
+        raise ValueError("expected k[B, T, Hkv, d]")
+    B, T, H, d = k.shape
+    nseq, cu_ptr, msl = B, None, 0
+    if cu_seqlens is not None:
+        cu = _dev(cu_seqlens, "cu_seqlens")
+        if cu.dtype != torch.int32 or cu.dim() != 1 or cu.numel() < 2 or B != 1:
+            raise ValueError("packed keys: int32 cu_seqlens and k of shape [1, total, Hkv, d]")
+        nseq = cu.numel() - 1
+        if max_seqlen is None:
+            max_seqlen = int((cu[1:] - cu[:-1]).max().item())
+        cu_ptr, msl = cu.data_ptr(), int(max_seqlen)
+    if out is None:
+        out = torch.empty_like(k)
+    elif out.shape != k.shape or out.dtype != k.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like k")
+    opt = _options(0, 0, rope, d, None, qk_norm)
+    rc = _lib.gqa_prepare_keys(k.data_ptr(), out.data_ptr(), nseq, T, H, d, cu_ptr, msl,
+                               int(pos0), ctypes.byref(opt), _dtype_code(k), _stream(stream))
+    _check(rc, "gqa_prepare_keys")
     return out
 
 

@@ -22,7 +22,7 @@ LIB_NAME = "libgqa_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["gqa_attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "fold.hip",
-           "backward.hip"]
+           "backward.hip", "keys.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

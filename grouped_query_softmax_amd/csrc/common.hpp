@@ -107,6 +107,7 @@ struct PrefillArgs {
   const float* qn_w;  // QK-norm weights [d] of queries and keys (device), or nullptr
   const float* kn_w;
   float norm_eps;
+  int keys_prepared;  // keys already normalised / turned: process the queries only
   // Value and output geometry, in elements. Grouped-query attention: dv = d, vslices = 1,
   // v_row = Hkv*d, v_head = d, o_row = Hq*d, o_head = d. Grouped value attention hands in the
   // G value heads of a query/key head as one value row of G*d columns, produced in vslices
@@ -224,6 +225,22 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 int prefill_bf16_cols();  // (position, head) columns per bf16 prefill workgroup
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_backward_bf16(const BwdArgs& a, hipStream_t s);
+// Key preparation (QK-norm and rotary embedding of key rows, once per key).
+struct KeyPrepArgs {
+  const void* k;
+  void* out;
+  int64_t rows;       // B*T*H key rows (dense) or total*H (packed)
+  int T, H, d;        // dense sequence length, heads, head dim
+  const int32_t* cu;  // packed sequence offsets (device) or nullptr
+  int nseq;
+  int pos0;           // position of each sequence's first key
+  const float* w;     // QK-norm weights [d] or nullptr
+  float eps;
+  const float* rope_cos;  // rotary tables [rows][d/2] or nullptr
+  const float* rope_sin;
+};
+hipError_t launch_prepare_keys(const KeyPrepArgs& a, hipStream_t s);
+
 hipError_t launch_fold(const void* src, void* dst, int64_t BT, int H, int g, int d, int is_bf16,
                        hipStream_t s);
 

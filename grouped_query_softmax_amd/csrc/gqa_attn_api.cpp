@@ -84,7 +84,10 @@ const char* gqa_status_string(gqa_status_t s) {
 }
 
 // Options shared by the extended entry points; a null pointer means none of them.
-static gqa_status_t check_options(const gqa_attn_options_t* o, gqa_dtype_t dtype, int rows_needed) {
+// keys_ready: the call reads keys that were normalised / turned beforehand (decode caches, or
+// prefill with keys_prepared), so only the query weights are needed.
+static gqa_status_t check_options(const gqa_attn_options_t* o, gqa_dtype_t dtype, int rows_needed,
+                                  bool keys_ready = false) {
   if (!o) return GQA_OK;
   if (o->window < 0 || o->n_sink < 0) return GQA_ERR_SHAPE;
   const bool rope = o->rope_cos || o->rope_sin;
@@ -96,11 +99,13 @@ static gqa_status_t check_options(const gqa_attn_options_t* o, gqa_dtype_t dtype
     if (o->rope_rows < rows_needed) return GQA_ERR_SHAPE;
   }
   if (o->lse && dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+  keys_ready = keys_ready || o->keys_prepared;
   const bool norm = o->q_norm_w || o->k_norm_w;
   if (norm) {
-    if (!o->q_norm_w || !o->k_norm_w) return GQA_ERR_NULL_PTR;
+    if (!o->q_norm_w || (!keys_ready && !o->k_norm_w)) return GQA_ERR_NULL_PTR;
     if (dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
-    if (!aligned16(o->q_norm_w) || !aligned16(o->k_norm_w)) return GQA_ERR_UNSUPPORTED;
+    if (!aligned16(o->q_norm_w) || (o->k_norm_w && !aligned16(o->k_norm_w)))
+      return GQA_ERR_UNSUPPORTED;
     if (!isfinite(o->norm_eps) || !(o->norm_eps > 0.f)) return GQA_ERR_SHAPE;
   }
   return GQA_OK;
@@ -176,6 +181,7 @@ static gqa_status_t prefill_impl(const void* q, const void* k, const void* v, vo
   a.qn_w = opt ? opt->q_norm_w : nullptr;
   a.kn_w = opt ? opt->k_norm_w : nullptr;
   a.norm_eps = opt ? opt->norm_eps : 0.f;
+  a.keys_prepared = opt ? opt->keys_prepared : 0;
   set_gqa_geometry(a);
   if (a.lse && overlap(a.lse, rows_q * Hq * sizeof(float), q, nq)) return GQA_ERR_ALIAS;
   return from_hip(dtype == GQA_DTYPE_BF16 ? gqa::launch_prefill_bf16(a, stream)
@@ -272,6 +278,7 @@ gqa_status_t gqa_attn_prefill_gva(const void* q, const void* k, const void* v, v
   a.lse = opt ? opt->lse : nullptr;
   a.qn_w = a.kn_w = nullptr;
   a.norm_eps = 0.f;
+  a.keys_prepared = 0;
   a.dv = dv;
   a.vslices = vslices;
   a.v_row = HV * d;
@@ -299,7 +306,7 @@ static gqa_status_t decode_impl(const void* q, const void* k_cache, const void* 
   if (!isfinite(scale) || !(scale > 0.f)) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0) return GQA_ERR_GROUPING;
   if (!dtype_ok(dtype) || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
-  if (const gqa_status_t st = check_options(opt, dtype, Tkv)) return st;
+  if (const gqa_status_t st = check_options(opt, dtype, Tkv, true)) return st;
   if (cache_lens && dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
   const int window = opt ? opt->window : 0;
   const int n_sink = opt ? opt->n_sink : 0;
@@ -347,6 +354,7 @@ static gqa_status_t decode_impl(const void* q, const void* k_cache, const void* 
     a.lse = nullptr;
     a.qn_w = a.kn_w = nullptr;
     a.norm_eps = 0.f;
+    a.keys_prepared = 0;
     set_gqa_geometry(a);
     return from_hip(gqa::launch_prefill_f32(a, stream));
   }
@@ -475,6 +483,50 @@ gqa_status_t gqa_attn_backward(const void* q, const void* k, const void* v, cons
   a.scale = scale;
   a.causal = causal ? 1 : 0;
   return from_hip(gqa::launch_backward_bf16(a, stream));
+}
+
+gqa_status_t gqa_prepare_keys(const void* k, void* k_out, int B, int T, int Hkv, int d,
+                              const int32_t* cu_seqlens, int max_seqlen, int pos0,
+                              const gqa_attn_options_t* opt, gqa_dtype_t dtype,
+                              hipStream_t stream) {
+  if (!k || !k_out || !opt) return GQA_ERR_NULL_PTR;
+  if (B <= 0 || T <= 0 || Hkv <= 0 || d <= 0 || pos0 < 0) return GQA_ERR_SHAPE;
+  if (dtype != GQA_DTYPE_BF16 || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
+  const bool rope = opt->rope_cos || opt->rope_sin;
+  if (rope && (!opt->rope_cos || !opt->rope_sin)) return GQA_ERR_NULL_PTR;
+  if (!rope && !opt->k_norm_w) return GQA_ERR_SHAPE;  // nothing to apply
+  const int longest = cu_seqlens ? max_seqlen : T;
+  if (cu_seqlens && (max_seqlen <= 0 || max_seqlen > T)) return GQA_ERR_SHAPE;
+  if (rope) {
+    if (!aligned16(opt->rope_cos) || !aligned16(opt->rope_sin)) return GQA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(opt->rope_rows) < static_cast<int64_t>(pos0) + longest)
+      return GQA_ERR_SHAPE;
+  }
+  if (opt->k_norm_w) {
+    if (!aligned16(opt->k_norm_w)) return GQA_ERR_UNSUPPORTED;
+    if (!isfinite(opt->norm_eps) || !(opt->norm_eps > 0.f)) return GQA_ERR_SHAPE;
+  }
+  if (!aligned16(k) || !aligned16(k_out)) return GQA_ERR_UNSUPPORTED;
+  // packed: [1, T = total, Hkv, d] with B + 1 offsets; dense: [B, T, Hkv, d]
+  const int64_t rows = static_cast<int64_t>(cu_seqlens ? 1 : B) * T * Hkv;
+  const size_t bytes = static_cast<size_t>(rows) * d * 2;
+  if (k_out != k && overlap(k_out, bytes, k, bytes)) return GQA_ERR_ALIAS;
+  if ((rows * (d / 8) + 255) / 256 > kMaxFlatWorkgroups256) return GQA_ERR_UNSUPPORTED;
+  gqa::KeyPrepArgs a;
+  a.k = k;
+  a.out = k_out;
+  a.rows = rows;
+  a.T = T;
+  a.H = Hkv;
+  a.d = d;
+  a.cu = cu_seqlens;
+  a.nseq = cu_seqlens ? B : 0;
+  a.pos0 = pos0;
+  a.w = opt->k_norm_w;
+  a.eps = opt->norm_eps;
+  a.rope_cos = rope ? opt->rope_cos : nullptr;
+  a.rope_sin = rope ? opt->rope_sin : nullptr;
+  return from_hip(gqa::launch_prepare_keys(a, stream));
 }
 
 gqa_status_t gqa_fold_kv(const void* src, void* dst, int B, int T, int H, int g, int d,

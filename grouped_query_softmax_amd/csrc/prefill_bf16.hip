@@ -93,7 +93,7 @@ struct PPCfg {
   static_assert(kVBase < 65536 && 3 * kVBytes < 65536, "stage offsets fit LDS immediates");
 };
 
-template <int DQ, int DV, bool ROPE, bool NORM>
+template <int DQ, int DV, bool ROPE, bool NORM, bool KPROC>
 __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int heads_per_wg,
                                                          int pos_per_wg, int head_tiles, int gz) {
   using C = PPCfg<DQ, DV>;
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
   constexpr int VW = VD / 2;
   // with QK-norm the key weights follow the stages in LDS (read while staging K)
   constexpr int kNormOff = C::kSmemBytes;
-  __shared__ __attribute__((aligned(16))) char smem[C::kSmemBytes + (NORM ? DQ * 4 : 0)];
+  __shared__ __attribute__((aligned(16))) char smem[C::kSmemBytes + (NORM && KPROC ? 4 * DQ : 0)];
 
   const int gx = a.Hkv * head_tiles * a.vslices;
   const int lin = blockIdx.x;
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
   const int k_rd = n * C::kKPitch + 16 * hh;
   const int v_rd = n * C::kVPitch + 16 * hh;
   // QK-norm weights of the keys into LDS (made visible by the barrier opening each query tile)
-  if constexpr (NORM) {
+  if constexpr (NORM && KPROC) {
     if (tid < DQ / 4)
       lds_write<f32x4>(smem, kNormOff + 16 * tid, *reinterpret_cast<const f32x4*>(a.kn_w + 4 * tid));
   }
@@ -220,6 +220,9 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
         }
         qf[s] = __builtin_bit_cast(bf16x8, w);
       }
+      // finish the query operands before anything of the tile loop is scheduled in between:
+      // the norm's and rotation's temporaries then never overlap the loop's registers
+      if constexpr (ROPE || NORM) __builtin_amdgcn_sched_barrier(0);
     }
     f32x16 acc_o[NMT];
 #pragma unroll
@@ -254,9 +257,10 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
     // rotary embedding of the staged keys: key j of the item sits at position j; the tables are
     // read through a range-checked resource (rows past the table read as 0: those keys are the
     // zero padding of the last tile)
-    [[maybe_unused]] f32x4 rc[ROPE ? C::kKLoads : 1], rs[ROPE ? C::kKLoads : 1];
+    constexpr int kRopeRegs = ROPE && KPROC ? C::kKLoads : 1;
+    [[maybe_unused]] f32x4 rc[kRopeRegs], rs[kRopeRegs];
     [[maybe_unused]] __amdgpu_buffer_rsrc_t crs, srs;
-    if constexpr (ROPE) {
+    if constexpr (ROPE && KPROC) {
       const int tbytes = a.rope_rows * (D / 2) * 4;
       crs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.rope_cos), 0, tbytes,
                                               kBufWord3);
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
     // the table rows of the keys staged next; issued at the start of a matrix phase so they
     // arrive by its end, where the keys are turned and written to LDS
     auto load_rope = [&](int t) {
-      if constexpr (ROPE) {
+      if constexpr (ROPE && KPROC) {
 #pragma unroll
         for (int i = 0; i < C::kKLoads; ++i) {
           const int idx = i * C::kGroupThreads + gtid;
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
     auto store_k = [&](int stage) {
       char* base = smem + stage * C::kKBytes;
       [[maybe_unused]] float inv_k[C::kKLoads];
-      if constexpr (NORM) {
+      if constexpr (NORM && KPROC) {
         // each key row is spread over kChunks consecutive lanes: sum their squares
 #pragma unroll
         for (int i = 0; i < C::kKLoads; ++i) {
@@ -301,7 +305,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
 #pragma unroll
       for (int i = 0; i < C::kKLoads; ++i) {
         u32x4 w = {stg[4 * i], stg[4 * i + 1], stg[4 * i + 2], stg[4 * i + 3]};
-        if constexpr (NORM) {
+        if constexpr (NORM && KPROC) {
           float x[8];
           unpack8(w, x);
           // weights of this thread's pieces (piece gtid % kChunks of each row)
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
           norm8(x, inv_k[i], lds_read<f32x4>(smem, woff), lds_read<f32x4>(smem, woff + 16));
           if constexpr (ROPE) rope8(x, rc[i], rs[i]);
           w = pack8(x);
-        } else if constexpr (ROPE) {
+        } else if constexpr (ROPE && KPROC) {
           w = rope_chunk(w, rc[i], rs[i]);
         }
         lds_write<u32x4>(base, k_dst[i], w);
@@ -551,7 +555,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
   }
 }
 
-template <int DQ, int DV, bool ROPE, bool NORM>
+template <int DQ, int DV, bool ROPE, bool NORM, bool KPROC>
 hipError_t launch_pp(const PrefillArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int heads_per_wg = G < kCols ? G : kCols;
@@ -560,17 +564,24 @@ hipError_t launch_pp(const PrefillArgs& a, hipStream_t s) {
   const int ntiles = (a.max_tq + pos_per_wg - 1) / pos_per_wg;
   const int gz = a.causal ? (ntiles + 1) / 2 : ntiles;
   const dim3 grid(a.Hkv * head_tiles * a.vslices * a.nitems * gz);
-  hipLaunchKernelGGL((prefill_pp_kernel<DQ, DV, ROPE, NORM>), grid, dim3(512), 0, s, a,
+  hipLaunchKernelGGL((prefill_pp_kernel<DQ, DV, ROPE, NORM, KPROC>), grid, dim3(512), 0, s, a,
                      heads_per_wg, pos_per_wg, head_tiles, gz);
   return hipGetLastError();
 }
 
+template <int D, bool KPROC>
+hipError_t launch_processed(const PrefillArgs& a, hipStream_t s) {
+  const bool rope = a.rope_cos != nullptr, norm = a.qn_w != nullptr;
+  if (norm && rope) return launch_pp<D, D, true, true, KPROC>(a, s);
+  if (norm) return launch_pp<D, D, false, true, KPROC>(a, s);
+  return launch_pp<D, D, true, false, KPROC>(a, s);
+}
+
 template <int D>
 hipError_t launch_same_width(const PrefillArgs& a, hipStream_t s) {
-  const bool rope = a.rope_cos != nullptr, norm = a.qn_w != nullptr;
-  if (norm)
-    return rope ? launch_pp<D, D, true, true>(a, s) : launch_pp<D, D, false, true>(a, s);
-  return rope ? launch_pp<D, D, true, false>(a, s) : launch_pp<D, D, false, false>(a, s);
+  if (!a.rope_cos && !a.qn_w) return launch_pp<D, D, false, false, false>(a, s);
+  // keys_prepared: the keys were normalised / turned beforehand; only the queries are here
+  return a.keys_prepared ? launch_processed<D, false>(a, s) : launch_processed<D, true>(a, s);
 }
 
 }  // namespace
@@ -581,7 +592,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   if (a.d == 64 && a.dv == 64) return launch_same_width<64>(a, s);
   if (a.d == 128 && a.dv == 128) return launch_same_width<128>(a, s);
   if (a.d == 64 && a.dv == 128 && !a.rope_cos && !a.qn_w)
-    return launch_pp<64, 128, false, false>(a, s);
+    return launch_pp<64, 128, false, false, false>(a, s);
   return hipErrorInvalidValue;
 }
 

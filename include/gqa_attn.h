@@ -94,7 +94,12 @@ gqa_status_t gqa_attn_prefill(const void* q, const void* k, const void* v, void*
  *                   NULL: GQA_ERR_NULL_PTR; norm_eps must be finite and > 0 (else GQA_ERR_SHAPE).
  *                   Prefill normalises queries at load and keys as they are staged; decode
  *                   normalises the query and expects the cache to hold normalised keys
- *                   (k_norm_w is then only validated).
+ *                   (k_norm_w may then be NULL).
+ *   keys_prepared:  nonzero: the keys were already normalised and turned (gqa_prepare_keys, or
+ *                   a cache written that way); prefill then applies QK-norm and rotation to the
+ *                   queries only and k_norm_w may be NULL. Every workgroup stages every key tile
+ *                   of its head, so preparing the keys once and passing keys_prepared is faster
+ *                   than turning them inside the attention kernel.
  * Windows, rotation and QK-norm are bf16 only (GQA_ERR_UNSUPPORTED for f32).
  */
 typedef struct {
@@ -109,6 +114,7 @@ typedef struct {
   const float* q_norm_w;
   const float* k_norm_w;
   float norm_eps;
+  int keys_prepared;
 } gqa_attn_options_t;
 
 /* gqa_attn_prefill with options (window, sinks, rotary embedding). */
@@ -131,6 +137,21 @@ gqa_status_t gqa_attn_prefill_window(const void* q, const void* k, const void* v
                                      int B, int Tq, int Tkv, int Hq, int Hkv, int d, float scale,
                                      int window, int n_sink, const int32_t* cu_seqlens,
                                      int max_seqlen, gqa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Key preparation (course page "Week 7. Attention", step 3): QK-norm (opt->k_norm_w, norm_eps)
+ * and then the rotary turn (opt->rope_cos / rope_sin / rope_rows) of every key row, once, as a
+ * model writes its key cache. k, k_out [B, T, Hkv, d] bf16 (packed: [1, T = total, Hkv, d] with
+ * B + 1 offsets in cu_seqlens and the longest sequence in max_seqlen); key j of a sequence sits
+ * at position pos0 + j (rope_rows must cover pos0 + the longest length). k_out == k (in place)
+ * is allowed, any other overlap is GQA_ERR_ALIAS. At least one of the norm and the turn must be
+ * requested (else GQA_ERR_SHAPE); the other options fields are ignored. bf16, d in {64, 128}.
+ * Feeds gqa_attn_prefill_ex / gqa_attn_decode_ex with opt->keys_prepared set.
+ */
+gqa_status_t gqa_prepare_keys(const void* k, void* k_out, int B, int T, int Hkv, int d,
+                              const int32_t* cu_seqlens, int max_seqlen, int pos0,
+                              const gqa_attn_options_t* options, gqa_dtype_t dtype,
+                              hipStream_t stream);
 
 /*
  * Grouped value attention, prefill (K3 notes, section 4, GVA: the inverse of grouped-query

@@ -130,6 +130,23 @@ def test_qk_norm_options_validation(lib):
         B.GQA_ERR_UNSUPPORTED
 
 
+def test_prepare_keys_validation(lib):
+    Opt = B.AttnOptions
+    N, T = W + 65536, W + 8192
+
+    def prep(opt, k=K, out=O, dt=BF16, d=128, pos0=0, Tn=8):
+        return lib.gqa_prepare_keys(k, out, 2, Tn, 2, d, None, 0, pos0,
+                                    ctypes.byref(opt) if opt is not None else None, dt, None)
+    ok_norm = Opt(0, 0, None, None, 0, None, None, N, 1e-6)
+    assert prep(None) == B.GQA_ERR_NULL_PTR
+    assert prep(Opt()) == B.GQA_ERR_SHAPE                       # nothing to apply
+    assert prep(ok_norm, dt=F32, d=16) == B.GQA_ERR_UNSUPPORTED
+    assert prep(Opt(0, 0, T, T + 4096, 8, None), pos0=1) == B.GQA_ERR_SHAPE  # table too short
+    assert prep(ok_norm, pos0=-1) == B.GQA_ERR_SHAPE
+    assert prep(ok_norm, out=K + 64) == B.GQA_ERR_ALIAS         # partial overlap
+    assert prep(Opt(0, 0, None, None, 0, None, None, N, 0.0)) == B.GQA_ERR_SHAPE
+
+
 def test_gva_validation(lib):
     Opt = B.AttnOptions
     T = W + 8192

@@ -140,3 +140,111 @@ def test_bf16_decode_qknorm_vs_oracle(gqa, orc, case):
                             np.ascontiguousarray(vh[b:b + 1, :L]), causal=True, rope=tabs,
                             rope_mode="q", qk_norm=(wq, wk, EPS), qk_norm_mode="q")
         assert_bf16_close(got[b:b + 1], ref, what=f"{case[:5]} seq {b} len {L}")
+
+
+def _ref_prepared(k_bf16, tabs, wk, pos0=0, lens=None):
+    """Keys normalised (wk not None) and turned (tabs not None) in float64 (per sequence
+    positions pos0 + j), as float64 numpy."""
+    x = k_bf16.double()
+    if wk is not None:
+        x = x * torch.rsqrt((x * x).mean(-1, keepdim=True) + EPS) * torch.from_numpy(wk).double()
+    if tabs is not None:
+        B, T, H, d = x.shape
+        if lens is None:
+            pos = torch.arange(T) + pos0
+        else:
+            pos = torch.cat([torch.arange(n) for n in lens]) + pos0
+        z = torch.view_as_complex(x.reshape(B, T, H, d // 2, 2).contiguous())
+        rot = torch.complex(torch.from_numpy(tabs[0]).double(), torch.from_numpy(tabs[1]).double())
+        x = torch.view_as_real(z * rot[pos][None, :, None, :]).reshape(B, T, H, d)
+    return x.numpy()
+
+
+PREP_CASES = [
+    # B, T, H, d, norm, rope, pos0, packed lens
+    (2, 300, 8, 128, True, True, 0, None),
+    (2, 300, 8, 128, False, True, 5, None),
+    (1, 77, 2, 64, True, False, 0, None),
+    (1, 494, 4, 128, True, True, 3, (300, 1, 129, 64)),
+]
+
+
+@pytest.mark.parametrize("case", PREP_CASES,
+                         ids=lambda c: "B{}_T{}_H{}_d{}_norm{}_rope{}_p{}_packed{}".format(
+                             *c[:7], c[7] is not None))
+def test_bf16_prepare_keys_vs_float64(gqa, case):
+    B, T, H, d, norm, rope, pos0, lens = case
+    say(f"bf16 prepare keys {case}")
+    k = workloads.randn_bf16((B, T, H, d), 177)
+    wq, wk = _weights(d, 178)
+    tabs = workloads.rope_tables(T + pos0 + 1, d) if rope else None
+    cu = None
+    if lens is not None:
+        cu = to_dev(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+    got = gqa.gqa_prepare_keys(to_dev(k), rope=tuple(to_dev(t) for t in tabs) if rope else None,
+                               qk_norm=(None, to_dev(wk), EPS) if norm else None, pos0=pos0,
+                               cu_seqlens=cu)
+    torch.cuda.synchronize()
+    ref = _ref_prepared(k, tabs, wk if norm else None, pos0, lens)
+    # one rounding to bf16 of an fp32 computation: within 2^-8 of each value (+ tiny absolute)
+    err = np.abs(to_f64(got) - ref) - (2.0 ** -8 * np.abs(ref) + 1e-6)
+    assert np.max(err) <= 0, np.max(err)
+
+
+PREPARED_PREFILL_CASES = [
+    # B, Tq, Tkv, Hq, Hkv, d, rope, norm
+    (1, 300, 300, 8, 2, 128, True, True),
+    (2, 200, 200, 32, 1, 128, True, False),
+    (1, 77, 333, 4, 4, 64, True, True),
+    (1, 150, 150, 6, 2, 128, False, True),
+]
+
+
+@pytest.mark.parametrize("case", PREPARED_PREFILL_CASES,
+                         ids=lambda c: "B{}_Tq{}_Tkv{}_Hq{}_Hkv{}_d{}_rope{}_norm{}".format(*c))
+def test_bf16_prefill_keys_prepared_vs_oracle(gqa, orc, case):
+    """gqa_prepare_keys then the attention with keys_prepared equals the oracle's full
+    processing of the raw q, k."""
+    B, Tq, Tkv, Hq, Hkv, d, rope, norm = case
+    say(f"bf16 prefill keys prepared {case}")
+    q = workloads.randn_bf16((B, Tq, Hq, d), 179)
+    k = workloads.randn_bf16((B, Tkv, Hkv, d), 180)
+    v = workloads.randn_bf16((B, Tkv, Hkv, d), 181)
+    wq, wk = _weights(d, 182)
+    tabs = workloads.rope_tables(Tkv, d) if rope else None
+    dt = tuple(to_dev(t) for t in tabs) if rope else None
+    qn = (to_dev(wq), to_dev(wk), EPS) if norm else None
+    kp = gqa.gqa_prepare_keys(to_dev(k), rope=dt, qk_norm=qn)
+    out = gqa.gqa_attn_prefill_ex(to_dev(q), kp, to_dev(v), causal=True, rope=dt,
+                                  qk_norm=(qn[0], None, EPS) if norm else None,
+                                  keys_prepared=True)
+    torch.cuda.synchronize()
+    ref = orc.attention(host_view(q), host_view(k), host_view(v), causal=True, rope=tabs,
+                        qk_norm=(wq, wk, EPS) if norm else None)
+    assert_bf16_close(to_f64(out), ref, what=str(case))
+
+
+def test_bf16_decode_with_prepared_cache_vs_oracle(gqa, orc):
+    """A cache written by gqa_prepare_keys (QK-norm and RoPE) serves decode."""
+    B, Tmax, Hq, Hkv, d = 3, 1500, 32, 8, 128
+    lens = (1500, 700, 1)
+    say("bf16 decode with a prepared cache")
+    wq, wk = _weights(d, 183)
+    tabs = workloads.rope_tables(Tmax, d)
+    q = workloads.randn_bf16((B, 1, Hq, d), 184)
+    k = workloads.randn_bf16((B, Tmax, Hkv, d), 185)
+    v = workloads.randn_bf16((B, Tmax, Hkv, d), 186)
+    dt = tuple(to_dev(t) for t in tabs)
+    kc = gqa.gqa_prepare_keys(to_dev(k), rope=dt, qk_norm=(None, to_dev(wk), EPS))
+    out = gqa.gqa_attn_decode_ex(to_dev(q), kc, to_dev(v),
+                                 cache_lens=to_dev(np.asarray(lens, dtype=np.int32)), rope=dt,
+                                 qk_norm=(to_dev(wq), None, EPS))
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    qh, kh, vh = host_view(q), host_view(k), host_view(v)
+    for b in range(B):
+        L = lens[b]
+        ref = orc.attention(qh[b:b + 1], np.ascontiguousarray(kh[b:b + 1, :L]),
+                            np.ascontiguousarray(vh[b:b + 1, :L]), causal=True, rope=tabs,
+                            qk_norm=(wq, wk, EPS))
+        assert_bf16_close(got[b:b + 1], ref, what=f"seq {b} len {L}")
