@@ -33,6 +33,8 @@ TRAFFIC = {
                 ("prefill_bf16.hip", "common.hpp")),
     "decode": (os.path.join(ROOT, "profiles", "decode_bf16_B64_kv8192_traffic.json"),
                ("decode.hip", "common.hpp")),
+    "gva": (os.path.join(ROOT, "profiles", "gva_prefill_B2_T4096_H16_HV32_d64_traffic.json"),
+            ("prefill_bf16.hip", "common.hpp")),
 }
 
 
@@ -422,7 +424,11 @@ def main():
     if pre is not None:
         value, unit = pre["tflops"], "TFLOP/s"
         ms_per_step = pre["avg_ms"]
-        traffic = traffic_for("prefill") if w is workloads.LLAMA_PREFILL else None
+        traffic = None
+        if args.only in (None, "prefill"):
+            traffic = traffic_for("prefill")
+        elif args.only == "gva":
+            traffic = traffic_for("gva")
         roofline = {"bound": "mfma", "achieved": pre["tflops"], "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": pre["tflops"] / PEAK_BF16_TFLOPS,
                     "traffic": traffic,
