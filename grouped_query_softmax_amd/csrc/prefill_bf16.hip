@@ -390,7 +390,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
     auto m_full = [&](int t) {  // 1 <= t < nkt
       pv(t);
       qk(t);
-      sched_stream(std::integral_constant<int, 2 * NMT * 4>{});
+      sched_stream(std::integral_constant<int, NMT * 4 + 2 * NS>{});
     };
     auto m_first = [&]() {
       qk(0);
