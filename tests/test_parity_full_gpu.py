@@ -158,3 +158,32 @@ def test_full_gva_prefill_sampled_heads(gqa):
                                     vh[b:b + 1, :, h * G:(h + 1) * G], causal=w.causal)
             assert_bf16_close(to_f64(o[b:b + 1, :, h * G:(h + 1) * G]), ref,
                               what=f"{w.name} b={b} h={h}")
+
+
+def test_full_backward_sampled_groups(gqa):
+    """Backward at the benchmark size (T = 4096, 32/8, causal): the gradients of the first and
+    last key/value-head group (its 4 query heads, every position) against the fp64 oracle run
+    on that group alone (a group's dq, dk, dv depend only on its own heads)."""
+    w = workloads.LLAMA_PREFILL
+    G = w.Hq // w.Hkv
+    say("full-size backward: generating inputs")
+    q, k, v, _ = workloads.make_inputs(w)
+    g = workloads.randn_bf16((w.B, w.Tq, w.Hq, w.d), 2099)
+    qd, kd, vd, gd = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
+    lse = torch.empty(w.B, w.Tq, w.Hq, dtype=torch.float32, device="cuda")
+    say("full-size backward: forward + backward")
+    out = gqa.gqa_attn_prefill_ex(qd, kd, vd, causal=True, lse=lse)
+    dq, dk, dv = gqa.gqa_attn_backward(qd, kd, vd, out, gd, lse, causal=True)
+    torch.cuda.synchronize()
+    orc = oracle.default()
+    qh, kh, vh, gh = host_view(q), host_view(k), host_view(v), host_view(g)
+    for j in (0, w.Hkv - 1):
+        say(f"full-size backward: oracle on key/value head {j}")
+        hs = slice(j * G, (j + 1) * G)
+        rq, rk, rv = orc.attention_bwd(qh[:, :, hs], kh[:, :, j:j + 1], vh[:, :, j:j + 1],
+                                       gh[:, :, hs], causal=True)
+        for name, got, ref in (("dq", dq[:, :, hs], rq), ("dk", dk[:, :, j:j + 1], rk),
+                               ("dv", dv[:, :, j:j + 1], rv)):
+            e = float(np.max(np.abs(to_f64(got) - ref)) / np.max(np.abs(ref)))
+            say(f"full-size backward head {j} {name}: rel-to-max {e:.3e}")
+            assert np.all(np.isfinite(to_f64(got))) and e <= 1e-2, (j, name, e)
