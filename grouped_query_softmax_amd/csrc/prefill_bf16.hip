@@ -104,6 +104,13 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
   constexpr int VW = VD / 2;
   // with QK-norm the key weights follow the stages in LDS (read while staging K)
   constexpr int kNormOff = C::kSmemBytes;
+  // epilogue: one region of 32 rows x 64 values (bf16) per wave; the 16-byte pad puts the 32
+  // rows' 8-byte pieces in distinct bank pairs
+  constexpr int kEpiPitch = 128 + 16;
+  constexpr int kEpiBytes = 32 * kEpiPitch;
+  constexpr bool kEpiBarrier = 8 * kEpiBytes > 3 * C::kKBytes;
+  static_assert(4 * kEpiBytes <= 3 * C::kKBytes && 8 * kEpiBytes <= C::kSmemBytes,
+                "epilogue regions must fit the K stages (group A) and the stages (both groups)");
   __shared__ __attribute__((aligned(16))) char smem[C::kSmemBytes + (NORM && KPROC ? 4 * DQ : 0)];
 
   const int gx = a.Hkv * head_tiles * a.vslices;
@@ -525,33 +532,69 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
       }
       __syncthreads();
     }
-    // t = nkt: only O += V(nkt-1) P(nkt-1)
+    // Epilogue: O / l rounded to bf16. A lane holds 4 consecutive values of its column per
+    // accumulator group, so a direct store would put 16 bytes into each of 32 rows per
+    // instruction. Instead each wave passes its 32 columns through its own LDS region, 64 values
+    // at a time, and reads them back as 16-byte pieces of rows: every store instruction then
+    // writes 8 whole 128-byte row segments.
+    auto epilogue = [&]() __attribute__((always_inline)) {
+      const float l_tot = pair_sum32(l_run);
+      const float inv = 1.f / l_tot;
+      if (a.lse && valid && hh == 0 && vsl == 0)  // log-sum-exp of the scaled scores, natural log
+        a.lse[(q0 + pos) * a.Hq + hq] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      char* tb = smem + wave * kEpiBytes;
+      // position (-1: no output) and head of the columns whose row pieces this lane moves, from
+      // the lanes that own those columns
+      int rpos[4], rhq[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 8 * j + (lane >> 3);
+        rpos[j] = __shfl(valid ? pos : -1, r);
+        rhq[j] = __shfl(hq, r);
+      }
+#pragma unroll
+      for (int h = 0; h < DV / 64; ++h) {
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int mt = 2 * h + m2;
+            u32x2 w;
+            w[0] = pack_bf16x2(acc_o[mt][4 * g4 + 0] * inv, acc_o[mt][4 * g4 + 1] * inv);
+            w[1] = pack_bf16x2(acc_o[mt][4 * g4 + 2] * inv, acc_o[mt][4 * g4 + 3] * inv);
+            lds_write<u32x2>(tb, n * kEpiPitch + 2 * (32 * m2 + 8 * g4 + 4 * hh), w);
+          }
+        asm volatile("" ::: "memory");  // one wave's LDS accesses run in program order
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 8 * j + (lane >> 3);  // the wave's column whose row piece this lane moves
+          const u32x4 x = lds_read<u32x4>(tb, r * kEpiPitch + 16 * (lane & 7));
+          if (rpos[j] >= 0) {
+            uint16_t* orow = Op + (q0 + rpos[j]) * a.o_row +
+                             static_cast<int64_t>(rhq[j]) * a.o_head + vsl * DV;
+            *reinterpret_cast<u32x4*>(orow + 64 * h + 8 * (lane & 7)) = x;
+          }
+        }
+        asm volatile("" ::: "memory");
+      }
+    };
+    // t = nkt: only O += V(nkt-1) P(nkt-1). Group A's epilogue regions lie in the K stages, which
+    // nobody reads any more; group B's follow them and, when the K stages are too small for
+    // eight regions, reach into the V stages, so B then waits until all of its waves are done
+    // with them.
     if (grp_a) {
       m_last(nkt);
     } else {
       v_phase(nkt - 1);
     }
     __syncthreads();
-    if (!grp_a) m_last(nkt);
-
-    const float l_tot = pair_sum32(l_run);
-    const float inv = 1.f / l_tot;
-    if (a.lse && valid && hh == 0 && vsl == 0)  // log-sum-exp of the scaled scores, natural log
-      a.lse[(q0 + pos) * a.Hq + hq] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-    if (valid) {
-      uint16_t* orow =
-          Op + (q0 + pos) * a.o_row + static_cast<int64_t>(hq) * a.o_head + vsl * DV;
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int dd = mt * 32 + g4 * 8 + hh * 4;
-          u32x2 w;
-          w[0] = pack_bf16x2(acc_o[mt][4 * g4 + 0] * inv, acc_o[mt][4 * g4 + 1] * inv);
-          w[1] = pack_bf16x2(acc_o[mt][4 * g4 + 2] * inv, acc_o[mt][4 * g4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + dd) = w;
-        }
+    if (!grp_a) {
+      m_last(nkt);
+    } else {
+      epilogue();
     }
+    if constexpr (kEpiBarrier) __syncthreads();
+    if (!grp_a) epilogue();
   }
 }
 

@@ -117,6 +117,7 @@ VARLEN_CASES = [
     ((1, 65, 200, 7, 128), 16, 2, True),
     ((130, 3, 64, 257), 8, 8, True),
     ((33, 100), 32, 1, False),
+    ((5, 0, 70, 1, 0), 8, 2, True),   # empty sequences (repeated offsets) and a single token
 ]
 
 
