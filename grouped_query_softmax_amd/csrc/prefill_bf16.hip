@@ -48,7 +48,7 @@ namespace {
 
 constexpr int kKT = 64;                // keys per tile
 constexpr float kRescaleSlack = 8.0f;  // log2 units
-constexpr int kLdsAhead = 4;           // MFMA operand reads kept in flight
+constexpr int kLdsAhead = 6;           // MFMA operand reads kept in flight
 constexpr int kCols = 256;             // (position, head) columns per workgroup
 
 // Buffer resource word 3 for raw (unformatted) buffer loads on CDNA; loads at or beyond
