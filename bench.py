@@ -433,10 +433,12 @@ def main():
                     "unit": "TFLOP/s", "frac": pre["tflops"] / PEAK_BF16_TFLOPS,
                     "traffic": traffic,
                     "kernel": {"backward": "bwd_rowdot + bwd_dkdv_kernel<128> + bwd_dq_kernel<128>",
-                               "rope": "prefill_pp_kernel<128, 128, true, false>",
-                               "qknorm": "prefill_pp_kernel<128, 128, true, true>",
-                               "gva": "prefill_pp_kernel<64, 128, false, false>"}.get(
-                                   args.only, "prefill_pp_kernel<128, 128, false, false>"),
+                               # <DQ, DV, ROPE, NORM, KPROC>: the fused variants process
+                               # the keys in the kernel
+                               "rope": "prefill_pp_kernel<128, 128, true, false, true>",
+                               "qknorm": "prefill_pp_kernel<128, 128, true, true, true>",
+                               "gva": "prefill_pp_kernel<64, 128, false, false, false>"}.get(
+                                   args.only, "prefill_pp_kernel<128, 128, false, false, false>"),
                     "flops_per_launch": pre["flops_per_launch"],
                     "avg_launch_ms": pre["avg_ms"], "kernel_source_sha": sha}
         config = {"workload": w.name, "B": w.B, "T": w.Tq, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
