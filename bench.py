@@ -102,22 +102,24 @@ def device_inputs(w, torch, seed_base):
 
 
 def time_launches(fn, steps, warmup, torch):
-    """Per-step HIP event pairs on the stream the kernels are launched on (torch's current
-    stream, which the binding passes to the library), plus wall clock."""
+    """Times `steps` launches on the stream the kernels are launched on (torch's current stream,
+    which the binding passes to the library): after `warmup` untimed launches, exactly `steps`
+    back-to-back launches between two synchronizations, bracketed by one pair of HIP events on
+    that stream. Returns (average ms per launch, wall-clock s of the timed region). Back to back
+    the chip runs at its sustained (lower) clock; a kernel trace of the same command averages
+    the same duration per launch."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record()
+    start.record()
+    for _ in range(steps):
         fn()
-        ends[i].record()
+    end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return ms, wall
+    return start.elapsed_time(end) / steps, wall
 
 
 def bench_prefill(gqa, w, steps, warmup, torch, seed, rope=False, qk_norm=False,
@@ -156,11 +158,9 @@ def bench_prefill(gqa, w, steps, warmup, torch, seed, rope=False, qk_norm=False,
         else:
             gqa.gqa_attn_prefill(q, k, v, causal=w.causal, cu_seqlens=cu, max_seqlen=msl, out=out)
 
-    ms, wall = time_launches(step, steps, warmup, torch)
+    avg, wall = time_launches(step, steps, warmup, torch)
     flops = prefill_flops(w)
-    avg = sum(ms) / len(ms)
     res = {"workload": w.name, "flops_per_launch": flops, "avg_ms": avg,
-           "min_ms": min(ms), "median_ms": sorted(ms)[len(ms) // 2],
            "tflops": flops / (avg * 1e-3) / 1e12, "wall_s": wall}
     return res, (q, k, v, cu)
 
@@ -180,11 +180,10 @@ def bench_backward(gqa, w, steps, warmup, torch, seed):
     def step():
         gqa.gqa_attn_backward(q, k, v, out, dout, lse, causal=w.causal, workspace=ws)
 
-    ms, wall = time_launches(step, steps, warmup, torch)
+    avg, wall = time_launches(step, steps, warmup, torch)
     flops = prefill_flops(w) * 10 // 4
-    avg = sum(ms) / len(ms)
     return {"workload": w.name + "+backward", "flops_per_launch": flops, "avg_ms": avg,
-            "min_ms": min(ms), "tflops": flops / (avg * 1e-3) / 1e12,
+            "tflops": flops / (avg * 1e-3) / 1e12,
             "frac_mfma": flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "wall_s": wall}
 
 
@@ -203,10 +202,9 @@ def bench_gva(gqa, w, steps, warmup, torch, seed):
     def step():
         gqa.gqa_attn_prefill_gva(q, k, v, causal=w.causal, out=out)
 
-    ms, wall = time_launches(step, steps, warmup, torch)
+    avg, wall = time_launches(step, steps, warmup, torch)
     flops = 2 * w.d * (H + HV) * w.B * visible_pairs(w.Tq, w.Tkv, w.causal)
-    avg = sum(ms) / len(ms)
-    return {"workload": w.name, "flops_per_launch": flops, "avg_ms": avg, "min_ms": min(ms),
+    return {"workload": w.name, "flops_per_launch": flops, "avg_ms": avg,
             "tflops": flops / (avg * 1e-3) / 1e12,
             "frac_mfma": flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "wall_s": wall}
 
@@ -234,14 +232,13 @@ def bench_decode(gqa, w, steps, warmup, torch, seed):
         else:
             gqa.gqa_attn_decode(q, k, v, workspace=ws, out=out)
 
-    ms, wall = time_launches(step, steps, warmup, torch)
+    avg, wall = time_launches(step, steps, warmup, torch)
     entries = sum(w.cache_lens) if w.cache_lens is not None else w.B * w.Tkv
     kv_bytes = 2 * entries * w.Hkv * w.d * 2
     qo_bytes = 2 * w.B * w.Hq * w.d * 2
-    avg = sum(ms) / len(ms)
     gbs = (kv_bytes + qo_bytes) / (avg * 1e-3) / 1e9
     return {"workload": w.name, "bytes_per_launch": kv_bytes + qo_bytes, "avg_ms": avg,
-            "min_ms": min(ms), "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "wall_s": wall,
+            "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "wall_s": wall,
             "traffic": traffic_for("decode") if w.cache_lens is None else None}
 
 
@@ -253,8 +250,7 @@ def bench_copy(steps, warmup, torch):
     so the HBM byte counters it reports calibrate those of the attention kernels."""
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    ms, wall = time_launches(lambda: dst.copy_(src), steps, warmup, torch)
-    avg = sum(ms) / len(ms)
+    avg, wall = time_launches(lambda: dst.copy_(src), steps, warmup, torch)
     gbs = 2 * COPY_BYTES / (avg * 1e-3) / 1e9
     return {"metric": "device copy GB/s (read + write)", "value": gbs, "unit": "GB/s",
             "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": avg,
