@@ -242,6 +242,34 @@ def bench_decode(gqa, w, steps, warmup, torch, seed):
             "traffic": traffic_for("decode") if w.cache_lens is None else None}
 
 
+FOLD_SHAPE = (8, 4096, 32, 128, 8)  # B, T, H, d, g: a 32-head K (or V) folded to 8 heads
+
+
+def bench_fold(gqa, steps, warmup, torch):
+    """gqa_fold_kv on a multi-head key tensor [B, T, H, d] folded to g heads (the step that
+    turns a multi-head checkpoint or cache into a grouped one): reads B*T*H*d and writes B*T*g*d
+    bf16 values once each; HBM-bound."""
+    B, T, H, d, g = FOLD_SHAPE
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9000)
+    src = torch.randn(B, T, H, d, generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.empty(B, T, g, d, dtype=torch.bfloat16, device="cuda")
+    avg, wall = time_launches(lambda: gqa.gqa_fold_kv(src, g, out=out), steps, warmup, torch)
+    nbytes = (B * T * H * d + B * T * g * d) * 2
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    return {"metric": "fold_kv GB/s (read + write, % HBM peak)", "value": gbs, "unit": "GB/s",
+            "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": avg,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) on device)",
+            "config": {"workload": f"fold_B{B}_T{T}_H{H}_g{g}_d{d}", "B": B, "T": T, "H": H,
+                       "g": g, "d": d},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                         "kernel": "fold_kernel<BF16>", "bytes_per_launch": nbytes,
+                         "avg_launch_ms": avg},
+            "cpu_baseline": None, "wall_s": wall}
+
+
 COPY_BYTES = 1 << 30
 
 
@@ -310,11 +338,11 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "mqa", "varlen", "window",
                                        "ragged", "rope", "qknorm", "backward", "gva",
-                                       "copy"],
+                                       "fold", "copy"],
                     default=None,
                     help="time a single workload (for profiling); still prints one JSON line. "
                          "'copy' times a plain 1 GiB device copy, the calibration kernel for "
-                         "the HBM byte counters")
+                         "the HBM byte counters; 'fold' times gqa_fold_kv")
     ap.add_argument("--all", action="store_true", help="also time the MQA and varlen prefills")
     args = ap.parse_args()
 
@@ -335,6 +363,11 @@ def main():
 
     if args.only == "copy":
         print(json.dumps(bench_copy(args.steps, args.warmup, torch)), flush=True)
+        return
+    if args.only == "fold":
+        res = bench_fold(gqa, args.steps, args.warmup, torch)
+        log(f"fold: {res['ms_per_step'] * 1e3:.1f} us, {res['value']:.0f} GB/s")
+        print(json.dumps(res), flush=True)
         return
 
     w = workloads.LLAMA_PREFILL
