@@ -36,6 +36,7 @@ GVA_CASES = [
     (1, 77, 333, 2, 6, 64, True, 0, 0),       # G = 3, G*d = 192: one slice per value head
     (1, 257, 257, 8, 8, 128, True, 0, 0),     # G = 1: multi-head attention
     (1, 500, 500, 4, 8, 64, True, 130, 5),    # sliding window with sinks
+    (3, 1, 700, 4, 8, 64, True, 0, 0),        # one query row per sequence (a decode step)
 ]
 
 
