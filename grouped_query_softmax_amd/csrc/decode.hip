@@ -8,7 +8,7 @@
 // query-head term).
 //
 // Kernel 1 (split): one workgroup of 4 waves per (sequence, key/value head, chunk of up to 16
-// query heads, split of the cache). Each wave streams its own 32-key tiles of the split and keeps
+// query heads -- 32 when the group has more than 16 -- split of the cache). Each wave streams its own 32-key tiles of the split and keeps
 // the next tile's loads in flight while it computes the current one, so the vector and matrix
 // work hides under the HBM stream. Per tile, on the matrix cores (v_mfma_f32_16x16x32_bf16):
 //   * the tile's K and V rows are loaded whole (each load instruction covers complete 128-byte
@@ -86,7 +86,10 @@ __device__ __forceinline__ u32x2 lds_read_tr(char* base, int byte_off) {
 // workgroup barrier is needed; only the compiler must not reorder them.
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
-template <int D>
+// NCH: 16-head chunks of query heads per workgroup (1, or 2 when a group has more than 16 heads:
+// every K/V operand read from LDS then feeds both chunks' MFMAs, and the cache is read once for
+// up to 32 heads)
+template <int D, int NCH>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, int head_chunks) {
   using C = DecCfg<D>;
   constexpr int NS = C::kSteps;
@@ -119,11 +122,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   const int row_bytes = a.Hkv * D * 2;
   const float sl2 = a.scale * kLog2e;
 
-  // this lane's query head (accumulator column) and its B operand, loaded once
-  const int col = hc * kHeadCols + r16;
-  const bool col_ok = col < G;
-  bf16x8 qop[NS];
-  {
+  // this lane's query head (accumulator column) of each chunk and its B operand, loaded once
+  bf16x8 qop[NCH][NS];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int col = (hc * NCH + c) * kHeadCols + r16;
+    const bool col_ok = col < G;
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                            (static_cast<int64_t>(b) * a.Hq + kvh * G + (col_ok ? col : 0)) * D +
                            8 * g;
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
         w = rope_chunk(w, *reinterpret_cast<const f32x4*>(a.rope_cos + ti),
                        *reinterpret_cast<const f32x4*>(a.rope_sin + ti));
       }
-      qop[s] = __builtin_bit_cast(bf16x8, w);
+      qop[c][s] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
@@ -186,10 +190,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   const int k_rd = r16 * C::kKPitch + 16 * g;
   const int v_rd = (4 * g + (r16 >> 2)) * C::kPitch + 8 * (r16 & 3);
 
-  f32x4 acc_o[NDT];
+  f32x4 acc_o[NCH][NDT];
+  float m_run[NCH], l_run[NCH];
 #pragma unroll
-  for (int nt = 0; nt < NDT; ++nt) acc_o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+    for (int nt = 0; nt < NDT; ++nt) acc_o[c][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[c] = -INFINITY;
+    l_run[c] = 0.f;
+  }
 
   // Rows past the split's list positions are pointed past num_records and read as zeros; tiles
   // at or past ntile are never processed.
@@ -219,63 +228,75 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
         *reinterpret_cast<u32x4*>(vt + v_wr + row * C::kPitch) = vr[blk][s];
       }
     lds_order();
-    // S^T for the 2 blocks of 16 keys: lane (g, r16) gets keys 16 blk + 4g + i of head r16
-    f32x4 sc[2];
+    // S^T for the 2 blocks of 16 keys: lane (g, r16) gets keys 16 blk + 4g + i of head r16 of
+    // each chunk; every K operand read feeds the MFMAs of all chunks
+    f32x4 sc[NCH][2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      sc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) sc[c][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const u32x4 kw =
             *reinterpret_cast<const u32x4*>(kt + k_rd + blk * 16 * C::kKPitch + 64 * s);
-        sc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw),
-                                                          qop[s], sc[blk], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          sc[c][blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw),
+                                                               qop[c][s], sc[c][blk], 0, 0, 0);
       }
     }
     const int k0 = t * kTK;
-    if (k0 + kTK > nkeys) {
-      const int rem = nkeys - 1 - k0 - 4 * g;
+    bf16x8 pop[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (k0 + kTK > nkeys) {
+        const int rem = nkeys - 1 - k0 - 4 * g;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sc[c][blk][i] = (16 * blk + i <= rem) ? sc[c][blk][i] : -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(sc[c][0][0], sc[c][0][1]), fmaxf(sc[c][0][2], sc[c][0][3])),
+                       fmaxf(fmaxf(sc[c][1][0], sc[c][1][1]), fmaxf(sc[c][1][2], sc[c][1][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = pair_max32(mx) * sl2;
+      const bool move = mx > m_run[c] + kRescaleSlack;
+      if (__any(move)) {
+        const float m_new = move ? mx : m_run[c];
+        const float alpha = move ? fast_exp2(m_run[c] - m_new) : 1.f;
+        l_run[c] *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < NDT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc_o[c][nt][i] *= alpha;
+        m_run[c] = m_new;
+      }
+      uint32_t pw[4];
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[blk][i] = (16 * blk + i <= rem) ? sc[blk][i] : -INFINITY;
+        for (int e = 0; e < 2; ++e)
+          pw[2 * blk + e] = pack_bf16x2(fast_exp2(fmaf(sc[c][blk][2 * e], sl2, -m_run[c])),
+                                        fast_exp2(fmaf(sc[c][blk][2 * e + 1], sl2, -m_run[c])));
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]),
+                                               __builtin_bit_cast(bf16x2, 0x3f803f80u), psum,
+                                               false);
+      l_run[c] += psum;
+      pop[c] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
     }
-    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = pair_max32(mx) * sl2;
-    const bool move = mx > m_run + kRescaleSlack;
-    if (__any(move)) {
-      const float m_new = move ? mx : m_run;
-      const float alpha = move ? fast_exp2(m_run - m_new) : 1.f;
-      l_run *= alpha;
-#pragma unroll
-      for (int nt = 0; nt < NDT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc_o[nt][i] *= alpha;
-      m_run = m_new;
-    }
-    uint32_t pw[4];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        pw[2 * blk + e] = pack_bf16x2(fast_exp2(fmaf(sc[blk][2 * e], sl2, -m_run)),
-                                      fast_exp2(fmaf(sc[blk][2 * e + 1], sl2, -m_run)));
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]),
-                                             __builtin_bit_cast(bf16x2, 0x3f803f80u), psum, false);
-    l_run += psum;
-    const bf16x8 pop = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
     lds_order();
 #pragma unroll
     for (int nt = 0; nt < NDT; ++nt) {
       const u32x2 lo = lds_read_tr(vt, v_rd + 32 * nt);                  // keys 4g .. 4g+3
       const u32x2 hi = lds_read_tr(vt, v_rd + 16 * C::kPitch + 32 * nt);  // keys 16+4g ..
       const bf16x8 vop = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-      acc_o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, acc_o[nt], 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        acc_o[c][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[c], acc_o[c][nt], 0, 0, 0);
     }
     lds_order();
   };
@@ -298,63 +319,70 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
     if (mine & 1) process(ka, va, t);
   }
 
-  // this wave's running sum: the 4 lane groups hold different keys of the same head
-  l_run += __shfl_xor(l_run, 16);
-  l_run = pair_sum32(l_run);
+  // this wave's running sums: the 4 lane groups hold different keys of the same head
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    l_run[c] += __shfl_xor(l_run[c], 16);
+    l_run[c] = pair_sum32(l_run[c]);
+  }
 
-  // merge the 4 waves in LDS: m, l per head, then o[head][dim]
-  __syncthreads();  // every wave is done with its V tile
+  // merge the 4 waves in LDS, one chunk at a time: m, l per head, then o[head][dim]
   float* mm = reinterpret_cast<float*>(smem);
   float* ll = mm + kWaves * kHeadCols;
   float* oo = ll + kWaves * kHeadCols;
-  if (g == 0) {
-    mm[wave * kHeadCols + r16] = m_run;
-    ll[wave * kHeadCols + r16] = l_run;
-  }
-#pragma unroll
-  for (int nt = 0; nt < NDT; ++nt)
-    *reinterpret_cast<f32x4*>(oo + (wave * kHeadCols + r16) * D + 16 * nt + 4 * g) = acc_o[nt];
-  __syncthreads();
   constexpr int kDimsPerThread = kHeadCols * D / kThreads;  // 8 at d = 128, 4 at d = 64
   const int h = tid / (D / kDimsPerThread);
   const int d0 = (tid % (D / kDimsPerThread)) * kDimsPerThread;
-  const int hq_in = hc * kHeadCols + h;
-  if (hq_in < G) {
-    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mm[w * kHeadCols + h]);
-    float L = 0.f, o[kDimsPerThread];
-#pragma unroll
-    for (int e = 0; e < kDimsPerThread; ++e) o[e] = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = mm[w * kHeadCols + h];
-      const float aw = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-      L = fmaf(aw, ll[w * kHeadCols + h], L);
-#pragma unroll
-      for (int e = 0; e < kDimsPerThread; ++e)
-        o[e] = fmaf(aw, oo[(w * kHeadCols + h) * D + d0 + e], o[e]);
+  for (int c = 0; c < NCH; ++c) {
+    __syncthreads();  // every wave is done with its V tile (c = 0) or the previous chunk's merge
+    if (g == 0) {
+      mm[wave * kHeadCols + r16] = m_run[c];
+      ll[wave * kHeadCols + r16] = l_run[c];
     }
-    const int64_t idx = (static_cast<int64_t>(b) * a.Hq + kvh * G + hq_in) * S + split;
-    if (S == 1) {  // the whole cache in one split: finish here, no combine pass
-      uint16_t* orow = static_cast<uint16_t*>(a.out) + idx * D + d0;
 #pragma unroll
-      for (int e = 0; e < kDimsPerThread; e += 4) {
-        u32x2 w;
-        w[0] = pack_bf16x2(o[e] / L, o[e + 1] / L);
-        w[1] = pack_bf16x2(o[e + 2] / L, o[e + 3] / L);
-        *reinterpret_cast<u32x2*>(orow + e) = w;
+    for (int nt = 0; nt < NDT; ++nt)
+      *reinterpret_cast<f32x4*>(oo + (wave * kHeadCols + r16) * D + 16 * nt + 4 * g) =
+          acc_o[c][nt];
+    __syncthreads();
+    const int hq_in = (hc * NCH + c) * kHeadCols + h;
+    if (hq_in < G) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mm[w * kHeadCols + h]);
+      float L = 0.f, o[kDimsPerThread];
+#pragma unroll
+      for (int e = 0; e < kDimsPerThread; ++e) o[e] = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = mm[w * kHeadCols + h];
+        const float aw = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+        L = fmaf(aw, ll[w * kHeadCols + h], L);
+#pragma unroll
+        for (int e = 0; e < kDimsPerThread; ++e)
+          o[e] = fmaf(aw, oo[(w * kHeadCols + h) * D + d0 + e], o[e]);
       }
-      return;
-    }
-    float* wo = a.ws + idx * D + d0;
+      const int64_t idx = (static_cast<int64_t>(b) * a.Hq + kvh * G + hq_in) * S + split;
+      if (S == 1) {  // the whole cache in one split: finish here, no combine pass
+        uint16_t* orow = static_cast<uint16_t*>(a.out) + idx * D + d0;
 #pragma unroll
-    for (int e = 0; e < kDimsPerThread; e += 4)
-      *reinterpret_cast<f32x4*>(wo + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
-    if (d0 == 0) {
-      const int64_t nbh = static_cast<int64_t>(a.B) * a.Hq * S;
-      a.ws[nbh * D + idx] = M;
-      a.ws[nbh * D + nbh + idx] = L;
+        for (int e = 0; e < kDimsPerThread; e += 4) {
+          u32x2 w;
+          w[0] = pack_bf16x2(o[e] / L, o[e + 1] / L);
+          w[1] = pack_bf16x2(o[e + 2] / L, o[e + 3] / L);
+          *reinterpret_cast<u32x2*>(orow + e) = w;
+        }
+      } else {
+        float* wo = a.ws + idx * D + d0;
+#pragma unroll
+        for (int e = 0; e < kDimsPerThread; e += 4)
+          *reinterpret_cast<f32x4*>(wo + e) = f32x4{o[e], o[e + 1], o[e + 2], o[e + 3]};
+        if (d0 == 0) {
+          const int64_t nbh = static_cast<int64_t>(a.B) * a.Hq * S;
+          a.ws[nbh * D + idx] = M;
+          a.ws[nbh * D + nbh + idx] = L;
+        }
+      }
     }
   }
 }
@@ -379,13 +407,22 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
   out[static_cast<int64_t>(bh) * D + d] = f32_to_bf16(num / den);
 }
 
-int head_chunks_of(int G) { return (G + kHeadCols - 1) / kHeadCols; }
+// 16-head chunks per workgroup: two when a group has more than 16 query heads
+int chunks_per_wg(int G) { return G > kHeadCols ? 2 : 1; }
+int head_chunks_of(int G) {
+  const int per = kHeadCols * chunks_per_wg(G);
+  return (G + per - 1) / per;
+}
 
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
-  const int hcs = head_chunks_of(a.Hq / a.Hkv);
+  const int G = a.Hq / a.Hkv;
+  const int hcs = head_chunks_of(G);
   const dim3 grid(a.nsplit * a.Hkv * hcs * a.B);
-  hipLaunchKernelGGL(decode_split_kernel<D>, grid, dim3(kThreads), 0, s, a, hcs);
+  if (chunks_per_wg(G) == 2)
+    hipLaunchKernelGGL((decode_split_kernel<D, 2>), grid, dim3(kThreads), 0, s, a, hcs);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, dim3(kThreads), 0, s, a, hcs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.B * a.Hq), dim3(D), 0, s, a.ws,

@@ -196,6 +196,7 @@ DECODE_CASES = [
     (1, 5000, 40, 2, 128),  # G = 20: a second, partial chunk of query heads
     (3, 31, 4, 1, 64),      # shorter than one key tile
     (2, 8192, 8, 8, 64),    # G = 1 (multi-head)
+    (2, 300, 64, 1, 128),   # G = 64: two workgroups of two 16-head chunks per sequence
 ]
 
 
