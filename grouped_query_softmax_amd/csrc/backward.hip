@@ -34,24 +34,6 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32;  // rows of a streamed chunk
-// Raw buffer resource word 3: loads at or past num_records bytes return zeros. Only the VGPR
-// offset takes part in that check, so every offset goes there; kOutside is past any buffer here.
-constexpr int kBufWord3 = 0x00020000;
-constexpr unsigned kOutside = 0x80000000u;
-// s_waitcnt immediate for vmcnt(0) with the other counters left alone (expcnt 7, lgkmcnt 15)
-constexpr int kVmcnt0 = 0x0F70;
-
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// Transposing LDS read: lane 4r + t of a 16-lane group points at 4 consecutive bf16 of row r;
-// lane j of the group receives column j of rows 0..3.
-__device__ __forceinline__ u32x2 lds_read_tr(char* base, int byte_off) {
-  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)((__attribute__((address_space(3))) char*)base + byte_off));
-  return __builtin_bit_cast(u32x2, r);
-}
-
 // LDS layout of a [rows][D] chunk: rows of 2*D bytes, the 16-byte pieces of row r stored at
 // piece index c ^ swz(r). The two readers of a chunk -- 16-byte reads down a column of rows (an
 // MFMA operand with the rows as its M index) and transposing 8-byte reads of 4 rows x 64 bytes --
@@ -122,9 +104,6 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restr
   if (row < rows && c == 0) Dr[row] = acc;
 }
 
-// Keeps the compiler from moving LDS accesses across this point. A wave's LDS region is written
-// and read back only by that wave, whose LDS instructions execute in program order.
-__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_tiles, int tile_wgs) {

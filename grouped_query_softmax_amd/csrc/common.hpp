@@ -49,6 +49,31 @@ __device__ __forceinline__ float pair_sum32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Raw buffer resource word 3 for unformatted buffer loads: loads at or past num_records bytes
+// return zeros. Only the VGPR offset takes part in that range check (the SGPR offset does not),
+// so every offset goes in the VGPR operand; kOutside is past any buffer used here.
+constexpr int kBufWord3 = 0x00020000;
+constexpr unsigned kOutside = 0x80000000u;
+// s_waitcnt immediate for vmcnt(0) with the other counters left alone (expcnt 7, lgkmcnt 15)
+constexpr int kVmcnt0 = 0x0F70;
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposing LDS read (ds_read_b64_tr_b16): with lane 4r + t of a 16-lane group pointing at 4
+// consecutive bf16 of row r (columns 4t .. 4t+3), lane j of the group receives column j of rows
+// 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr(const char* base, int byte_off) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)((__attribute__((address_space(3))) const char*)base + byte_off));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Keeps the compiler from moving LDS accesses across this point. For an LDS region written and
+// read back only by one wave, whose LDS instructions execute in program order, this is all the
+// ordering needed (no wait, no workgroup barrier).
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
 // Element type traits for the kernels that take either dtype.
 struct F32 {
   typedef float T;

@@ -50,12 +50,6 @@ constexpr int kTargetBlocks = 512;
 constexpr int kStreamLoad = 2;
 constexpr int kMinSplitKeys = 256;
 constexpr float kRescaleSlack = 8.0f;
-// Raw buffer resource word 3: loads at or past num_records bytes return zeros. Only the VGPR
-// offset is range checked (not the SGPR offset), so every offset goes in the VGPR operand.
-constexpr int kBufWord3 = 0x00020000;
-
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int D>
 struct DecCfg {
@@ -73,18 +67,6 @@ struct DecCfg {
   static constexpr int kSmemBytes = kVBytes > kMergeBytes ? kVBytes : kMergeBytes;
 };
 
-// Transposing LDS read: with lane 4r + t of a 16-lane group pointing at 4 consecutive bf16 of
-// row r (columns 4t .. 4t+3), lane j of the group receives column j of rows 0..3.
-__device__ __forceinline__ u32x2 lds_read_tr(char* base, int byte_off) {
-  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)((__attribute__((address_space(3))) char*)base + byte_off));
-  return __builtin_bit_cast(u32x2, r);
-}
-
-// Keeps the compiler from moving LDS accesses across this point. The tile in LDS is written and
-// read back by the same wave, whose LDS instructions execute in program order, so no wait or
-// workgroup barrier is needed; only the compiler must not reorder them.
-__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
 // NCH: 16-head chunks of query heads per workgroup (1, or 2 when a group has more than 16 heads:
 // every K/V operand read from LDS then feeds both chunks' MFMAs, and the cache is read once for

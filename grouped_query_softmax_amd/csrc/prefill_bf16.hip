@@ -51,11 +51,9 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units
 constexpr int kLdsAhead = 6;           // MFMA operand reads kept in flight
 constexpr int kCols = 256;             // (position, head) columns per workgroup
 
-// Buffer resource word 3 for raw (unformatted) buffer loads on CDNA; loads at or beyond
-// num_records bytes return zeros, which pads the last key tile without branches. Only the
-// VGPR offset takes part in that range check (the SGPR offset does not), so tile offsets are
-// added to the VGPR offset.
-constexpr int kBufWord3 = 0x00020000;
+// K/V tiles are read with raw buffer loads (kBufWord3): loads past the end of an item return
+// zeros, which pads the last key tile without branches; tile offsets go in the range-checked
+// VGPR offset.
 
 // V^T rows hold the 64 keys of a tile permuted inside each group of 16: key 8a + 4h + r
 // (a, h in {0,1}, r < 4) sits at position 8h + 4a + r. The 8 keys one lane feeds into one MFMA
