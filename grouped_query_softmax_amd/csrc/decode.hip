@@ -43,10 +43,12 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTK = 32;              // keys per tile
 constexpr int kHeadCols = 16;        // query heads per workgroup (MFMA columns)
-// Splits are added only until the grid has this many workgroups: one full round with no tail,
-// at 2 resident per CU (the one-chunk kernel's registers and LDS allow 2) x 256 CUs; the
-// two-chunk kernel at d = 128 (288 registers) holds one per CU and targets half as many.
-constexpr int kTargetBlocks = 512;
+// Splits are added only until the grid has this many workgroups: one per CU. Fewer, longer
+// splits stream faster than two resident per CU with half the keys each (measured: one
+// 131072-entry sequence 106 -> 98 us, 8 x 32768 entries 175 -> 170 us): a workgroup's fixed
+// cost (query load, merge, partial write) is spread over more keys, and 4 waves with two tiles
+// in flight each already cover the memory latency.
+constexpr int kTargetBlocks = 256;
 // Cache policy of the key/value loads: non-temporal (each cache line is read exactly once).
 constexpr int kStreamLoad = 2;
 constexpr int kMinSplitKeys = 256;
@@ -421,10 +423,9 @@ int decode_split_len(int Tkv, int nsplit) {
 }
 
 int decode_num_splits(int B, int Tkv, int Hq, int Hkv, int d) {
+  (void)d;
   const int64_t units = static_cast<int64_t>(B) * Hkv * head_chunks_of(Hq / Hkv);
-  const int target =
-      (d == 128 && chunks_per_wg(Hq / Hkv) == 2) ? kTargetBlocks / 2 : kTargetBlocks;
-  int64_t s = (target + units - 1) / units;
+  int64_t s = (kTargetBlocks + units - 1) / units;
   const int64_t max_s = Tkv / kMinSplitKeys > 1 ? Tkv / kMinSplitKeys : 1;
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
