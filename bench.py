@@ -347,8 +347,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(the kernels shard by key/value head; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (a multi-GPU "
+              f"run would shard the key/value heads, one process per GPU)", file=sys.stderr)
         sys.exit(2)
 
     import torch
