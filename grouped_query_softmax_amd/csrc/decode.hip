@@ -103,6 +103,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   const int nvis = a_end + (L - w_start);
   const int kb = split * a.per;
   const int nkeys = min(nvis, kb + a.per) - kb;  // <= 0: nothing of this sequence in the split
+  // a split past the sequence's visible entries has nothing to contribute: the combine reads
+  // only the splits a sequence has (with a single split the output must still be written)
+  if (S > 1 && nkeys <= 0) return;
   const int ntile = nkeys > 0 ? (nkeys + kTK - 1) / kTK : 0;
   const int row_bytes = a.Hkv * D * 2;
   const float sl2 = a.scale * kLog2e;
@@ -373,23 +376,30 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
 }
 
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ ws,
-                                                           uint16_t* __restrict__ out, int nbh,
-                                                           int nsplit) {
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+  const float* __restrict__ ws = a.ws;
+  const int nsplit = a.nsplit;
+  const int nbh = a.B * a.Hq;
   const int bh = blockIdx.x;
   const int d = threadIdx.x;
+  // the splits this sequence has: its visible entries (as in the split kernel) over a.per
+  const int b = bh / a.Hq;
+  const int L = a.lens ? min(max(a.lens[b], 1), a.Tkv) : a.Tkv;
+  const int w_start = a.window > 0 ? max(0, L - a.window) : 0;
+  const int nvis = min(a.n_sink, w_start) + (L - w_start);
+  const int nvalid = min(nsplit, (nvis + a.per - 1) / a.per);
   const int64_t ntot = static_cast<int64_t>(nbh) * nsplit;
   const float* wm = ws + ntot * D + static_cast<int64_t>(bh) * nsplit;
   const float* wl = ws + ntot * D + ntot + static_cast<int64_t>(bh) * nsplit;
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, wm[s]);
+  for (int s = 0; s < nvalid; ++s) M = fmaxf(M, wm[s]);
   float num = 0.f, den = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
+  for (int s = 0; s < nvalid; ++s) {
     const float w = (wm[s] == -INFINITY) ? 0.f : fast_exp2(wm[s] - M);
     num = fmaf(w, ws[(static_cast<int64_t>(bh) * nsplit + s) * D + d], num);
     den = fmaf(w, wl[s], den);
   }
-  out[static_cast<int64_t>(bh) * D + d] = f32_to_bf16(num / den);
+  static_cast<uint16_t*>(a.out)[static_cast<int64_t>(bh) * D + d] = f32_to_bf16(num / den);
 }
 
 // 16-head chunks per workgroup: two when a group has more than 16 query heads
@@ -410,8 +420,7 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, dim3(kThreads), 0, s, a, hcs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.B * a.Hq), dim3(D), 0, s, a.ws,
-                     static_cast<uint16_t*>(a.out), a.B * a.Hq, a.nsplit);
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.B * a.Hq), dim3(D), 0, s, a);
   return hipGetLastError();
 }
 
