@@ -1,0 +1,143 @@
+"""Seeded random shapes against the oracle, through the C ABI: dense, packed and sliding-window
+prefill, plain, ragged and windowed decode, and grouped value attention, over head counts, group
+sizes, lengths and head dims that the hand-picked cases do not name. The seed fixes the list, so
+a failure names a reproducible case (its id carries every size). Inputs are N(0, 1) rounded to
+bf16; the bf16 criterion is the one of every other parity test."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import assert_bf16_close, host_view, say, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ("prefill", "packed", "window", "decode", "ragged", "gva")
+
+
+def _cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = KINDS[i % len(KINDS)]
+        d = int(rng.choice([64, 128]))
+        hkv = int(rng.choice([1, 2, 3, 4, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 5, 8, 16, 24, 40]))
+        while hkv * g > 64:
+            g = max(1, g // 2)
+        c = {"kind": kind, "d": d, "Hkv": hkv, "G": g, "seed": 7000 + 10 * i}
+        if kind == "prefill":
+            c["B"] = int(rng.integers(1, 3))
+            c["Tkv"] = int(rng.integers(1, 301))
+            c["causal"] = bool(rng.integers(0, 2))
+            c["Tq"] = int(rng.integers(1, c["Tkv"] + 1)) if rng.integers(0, 2) else c["Tkv"]
+        elif kind == "packed":
+            lens = [int(x) for x in rng.integers(0, 200, size=int(rng.integers(1, 5)))]
+            lens[int(rng.integers(0, len(lens)))] += 1  # at least one token
+            c["lens"] = tuple(lens)
+            c["causal"] = bool(rng.integers(0, 2))
+        elif kind == "window":
+            c["T"] = int(rng.integers(1, 301))
+            c["window"] = int(rng.integers(1, c["T"] + 20))
+            c["n_sink"] = int(rng.integers(0, 9))
+        elif kind == "decode":
+            c["B"] = int(rng.integers(1, 5))
+            c["Tkv"] = int(rng.integers(1, 3001))
+        elif kind == "ragged":
+            c["B"] = int(rng.integers(2, 6))
+            tmax = int(rng.integers(1, 3001))
+            c["lens"] = tuple(int(x) for x in rng.integers(1, tmax + 1, size=c["B"]))
+            c["Tmax"] = max(c["lens"])
+            c["window"] = int(rng.integers(1, tmax + 1)) if rng.integers(0, 2) else 0
+            c["n_sink"] = int(rng.integers(0, 9)) if c["window"] else 0
+        else:  # gva: H query/key heads, HV = G*H value heads
+            c["Hkv"] = int(rng.choice([1, 2, 4]))
+            c["G"] = int(rng.choice([1, 2, 3, 4]))
+            c["T"] = int(rng.integers(1, 301))
+            c["causal"] = bool(rng.integers(0, 2))
+        out.append(c)
+    return out
+
+
+CASES = _cases(36, 20261203)
+
+
+def _id(c):
+    return "-".join(f"{k}{v}" for k, v in c.items() if k not in ("seed",)).replace(" ", "")
+
+
+@pytest.fixture(scope="module")
+def gqa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import grouped_query_softmax_amd as g
+    return g
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+@pytest.mark.parametrize("c", CASES, ids=_id)
+def test_random_shape_vs_oracle(gqa, orc, c):
+    say(f"random shape {_id(c)}")
+    d, hkv, s = c["d"], c["Hkv"], c["seed"]
+    hq = hkv * c["G"]
+    kind = c["kind"]
+    if kind == "prefill":
+        B, Tq, Tkv = c["B"], c["Tq"], c["Tkv"]
+        q = workloads.randn_bf16((B, Tq, hq, d), s)
+        k = workloads.randn_bf16((B, Tkv, hkv, d), s + 1)
+        v = workloads.randn_bf16((B, Tkv, hkv, d), s + 2)
+        got = gqa.gqa_attn_prefill(to_dev(q), to_dev(k), to_dev(v), causal=c["causal"])
+        ref = orc.attention(host_view(q), host_view(k), host_view(v), causal=c["causal"])
+    elif kind == "packed":
+        lens = c["lens"]
+        tot = sum(lens)
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        q = workloads.randn_bf16((1, tot, hq, d), s)
+        k = workloads.randn_bf16((1, tot, hkv, d), s + 1)
+        v = workloads.randn_bf16((1, tot, hkv, d), s + 2)
+        got = gqa.gqa_attn_prefill(to_dev(q), to_dev(k), to_dev(v), causal=c["causal"],
+                                   cu_seqlens=to_dev(cu), max_seqlen=max(lens))
+        ref = orc.attention(host_view(q), host_view(k), host_view(v), causal=c["causal"],
+                            cu_seqlens=cu)
+    elif kind == "window":
+        T, W, S = c["T"], c["window"], c["n_sink"]
+        q = workloads.randn_bf16((1, T, hq, d), s)
+        k = workloads.randn_bf16((1, T, hkv, d), s + 1)
+        v = workloads.randn_bf16((1, T, hkv, d), s + 2)
+        got = gqa.gqa_attn_prefill_window(to_dev(q), to_dev(k), to_dev(v), window=W, n_sink=S)
+        ref = orc.attention(host_view(q), host_view(k), host_view(v), causal=True, window=W,
+                            n_sink=S)
+    elif kind == "decode":
+        B, Tkv = c["B"], c["Tkv"]
+        q = workloads.randn_bf16((B, 1, hq, d), s)
+        k = workloads.randn_bf16((B, Tkv, hkv, d), s + 1)
+        v = workloads.randn_bf16((B, Tkv, hkv, d), s + 2)
+        got = gqa.gqa_attn_decode(to_dev(q), to_dev(k), to_dev(v))
+        ref = orc.attention(host_view(q), host_view(k), host_view(v), causal=True)
+    elif kind == "ragged":
+        B, lens, W, S = c["B"], c["lens"], c["window"], c["n_sink"]
+        q = workloads.randn_bf16((B, 1, hq, d), s)
+        k = workloads.randn_bf16((B, c["Tmax"], hkv, d), s + 1)
+        v = workloads.randn_bf16((B, c["Tmax"], hkv, d), s + 2)
+        got = gqa.gqa_attn_decode_ragged(to_dev(q), to_dev(k), to_dev(v),
+                                         cache_lens=to_dev(np.asarray(lens, dtype=np.int32)),
+                                         window=W, n_sink=S)
+        qh, kh, vh = host_view(q), host_view(k), host_view(v)
+        ref = np.concatenate([
+            orc.attention(qh[b:b + 1], np.ascontiguousarray(kh[b:b + 1, :L]),
+                          np.ascontiguousarray(vh[b:b + 1, :L]), causal=True, window=W, n_sink=S)
+            for b, L in enumerate(lens)])
+    else:
+        T, H, HV = c["T"], hkv, hkv * c["G"]
+        q = workloads.randn_bf16((1, T, H, d), s)
+        k = workloads.randn_bf16((1, T, H, d), s + 1)
+        v = workloads.randn_bf16((1, T, HV, d), s + 2)
+        got = gqa.gqa_attn_prefill_gva(to_dev(q), to_dev(k), to_dev(v), causal=c["causal"])
+        ref = orc.attention_gva(host_view(q), host_view(k), host_view(v), causal=c["causal"])
+    torch.cuda.synchronize()
+    assert_bf16_close(to_f64(got), ref, what=_id(c))
