@@ -141,3 +141,51 @@ def test_random_shape_vs_oracle(gqa, orc, c):
         ref = orc.attention_gva(host_view(q), host_view(k), host_view(v), causal=c["causal"])
     torch.cuda.synchronize()
     assert_bf16_close(to_f64(got), ref, what=_id(c))
+
+
+def _bwd_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 6, 8]))
+        tkv = int(rng.integers(1, 257))
+        causal = bool(rng.integers(0, 2))
+        tq = int(rng.integers(1, tkv + 1)) if rng.integers(0, 2) else tkv
+        out.append({"B": int(rng.integers(1, 3)), "Tq": tq, "Tkv": tkv, "Hkv": hkv, "G": g,
+                    "d": int(rng.choice([64, 128])), "causal": causal, "seed": 7500 + 10 * i})
+    return out
+
+
+BWD_CASES = _bwd_cases(12, 20261204)
+GRAD_REL = 1e-2  # rel-to-max per gradient, as for the hand-picked backward cases
+
+
+@pytest.mark.parametrize("c", BWD_CASES, ids=_id)
+def test_random_backward_vs_oracle(gqa, orc, c):
+    """dq, dk, dv of sum(out * dout) for random dense shapes; the GPU backward reads the GPU
+    forward's output and row log-sum-exp, as a training step does."""
+    say(f"random backward {_id(c)}")
+    B, Tq, Tkv, hkv, d, s = c["B"], c["Tq"], c["Tkv"], c["Hkv"], c["d"], c["seed"]
+    hq = hkv * c["G"]
+    q = workloads.randn_bf16((B, Tq, hq, d), s)
+    k = workloads.randn_bf16((B, Tkv, hkv, d), s + 1)
+    v = workloads.randn_bf16((B, Tkv, hkv, d), s + 2)
+    g = workloads.randn_bf16((B, Tq, hq, d), s + 3)
+    qd, kd, vd, gd = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
+    lse = torch.empty(B, Tq, hq, dtype=torch.float32, device="cuda")
+    out = gqa.gqa_attn_prefill_ex(qd, kd, vd, causal=c["causal"], lse=lse)
+    dq, dk, dv = gqa.gqa_attn_backward(qd, kd, vd, out, gd, lse, causal=c["causal"])
+    torch.cuda.synchronize()
+    refs = orc.attention_bwd(host_view(q), host_view(k), host_view(v), host_view(g),
+                             causal=c["causal"])
+    # Each gradient's error is taken relative to the larger of its own largest value and dv's:
+    # where every row sees a single key, P is 1, dS = P (dP - D) is 0 and dq, dk vanish exactly,
+    # so only rounding noise remains there and dv (the weighted dout) sets the gradient scale.
+    scale_dv = float(np.max(np.abs(refs[2])))
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        got = to_f64(got)
+        assert np.all(np.isfinite(got)), name
+        denom = max(float(np.max(np.abs(ref))), scale_dv, 1e-30)
+        err = float(np.max(np.abs(got - ref)) / denom)
+        assert err <= GRAD_REL, f"{_id(c)} {name}: rel-to-max {err:.3g}"
