@@ -1,5 +1,6 @@
 """Seeded random shapes against the oracle, through the C ABI: dense, packed and sliding-window
-prefill, plain, ragged and windowed decode, and grouped value attention, over head counts, group
+prefill, plain, ragged and windowed decode, grouped value attention, RoPE and QK-norm (fused or
+applied to the keys ahead) and the backward, over head counts, group
 sizes, lengths and head dims that the hand-picked cases do not name. The seed fixes the list, so
 a failure names a reproducible case (its id carries every size). Inputs are N(0, 1) rounded to
 bf16; the bf16 criterion is the one of every other parity test."""
@@ -189,3 +190,69 @@ def test_random_backward_vs_oracle(gqa, orc, c):
         denom = max(float(np.max(np.abs(ref))), scale_dv, 1e-30)
         err = float(np.max(np.abs(got - ref)) / denom)
         assert err <= GRAD_REL, f"{_id(c)} {name}: rel-to-max {err:.3g}"
+
+
+def _proc_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = ("fused", "prepared", "decode")[i % 3]
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 8]))
+        rope = bool(rng.integers(0, 2))
+        norm = bool(rng.integers(0, 2)) or not rope  # at least one of the two
+        c = {"kind": kind, "d": int(rng.choice([64, 128])), "Hkv": hkv, "G": g, "rope": rope,
+             "norm": norm, "seed": 7800 + 10 * i}
+        if kind == "decode":
+            c["B"] = int(rng.integers(1, 4))
+            c["Tkv"] = int(rng.integers(1, 2001))
+        else:
+            c["B"] = int(rng.integers(1, 3))
+            c["Tkv"] = int(rng.integers(1, 301))
+            c["Tq"] = int(rng.integers(1, c["Tkv"] + 1)) if rng.integers(0, 2) else c["Tkv"]
+            c["causal"] = bool(rng.integers(0, 2)) if kind == "fused" else True
+        out.append(c)
+    return out
+
+
+PROC_CASES = _proc_cases(12, 20261205)
+EPS = 1e-6
+
+
+@pytest.mark.parametrize("c", PROC_CASES, ids=_id)
+def test_random_rope_qknorm_vs_oracle(gqa, orc, c):
+    """RoPE and/or QK-norm: fused into prefill, applied to the keys once by gqa_prepare_keys
+    before a keys_prepared prefill, or applied to a decode cache before decode. The oracle
+    processes the raw q and k itself in every case."""
+    say(f"random rope/qk-norm {_id(c)}")
+    d, hkv, s, kind = c["d"], c["Hkv"], c["seed"], c["kind"]
+    hq, B, Tkv = hkv * c["G"], c["B"], c["Tkv"]
+    Tq = 1 if kind == "decode" else c["Tq"]
+    rng = np.random.default_rng(s + 3)
+    wq = (rng.random(d) * 1.5 + 0.25).astype(np.float32)
+    wk = (rng.random(d) * 1.5 + 0.25).astype(np.float32)
+    tabs = workloads.rope_tables(Tkv, d) if c["rope"] else None
+    dt = tuple(to_dev(t) for t in tabs) if c["rope"] else None
+    q = workloads.randn_bf16((B, Tq, hq, d), s)
+    k = workloads.randn_bf16((B, Tkv, hkv, d), s + 1)
+    v = workloads.randn_bf16((B, Tkv, hkv, d), s + 2)
+    dwq, dwk = to_dev(wq), to_dev(wk)
+    norm = c["norm"]
+    causal = c.get("causal", True)
+    if kind == "fused":
+        got = gqa.gqa_attn_prefill_ex(to_dev(q), to_dev(k), to_dev(v), causal=causal, rope=dt,
+                                      qk_norm=(dwq, dwk, EPS) if norm else None)
+    elif kind == "prepared":
+        kp = gqa.gqa_prepare_keys(to_dev(k), rope=dt, qk_norm=(None, dwk, EPS) if norm else None)
+        got = gqa.gqa_attn_prefill_ex(to_dev(q), kp, to_dev(v), causal=True, rope=dt,
+                                      qk_norm=(dwq, None, EPS) if norm else None,
+                                      keys_prepared=True)
+    else:
+        kc = gqa.gqa_prepare_keys(to_dev(k), rope=dt, qk_norm=(None, dwk, EPS) if norm else None)
+        lens = np.full(B, Tkv, dtype=np.int32)
+        got = gqa.gqa_attn_decode_ex(to_dev(q), kc, to_dev(v), cache_lens=to_dev(lens), rope=dt,
+                                     qk_norm=(dwq, None, EPS) if norm else None)
+    torch.cuda.synchronize()
+    ref = orc.attention(host_view(q), host_view(k), host_view(v), causal=causal, rope=tabs,
+                        qk_norm=(wq, wk, EPS) if norm else None)
+    assert_bf16_close(to_f64(got), ref, what=_id(c))
