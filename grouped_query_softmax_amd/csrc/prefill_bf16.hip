@@ -100,8 +100,10 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
   constexpr int NMT = DV / 32;  // 32-row value-column tiles of O^T
   constexpr int VD = C::kVD;
   constexpr int VW = VD / 2;
-  // with QK-norm the key weights follow the stages in LDS (read while staging K)
+  // with QK-norm the key weights (read while staging K) and then the query weights (read in
+  // each query tile's prologue) follow the stages in LDS
   constexpr int kNormOff = C::kSmemBytes;
+  constexpr int kQNormOff = kNormOff + (KPROC ? 4 * DQ : 0);
   // epilogue: one region of 32 rows x 64 values (bf16) per wave; the 16-byte pad puts the 32
   // rows' 8-byte pieces in distinct bank pairs
   constexpr int kEpiPitch = 128 + 16;
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
   constexpr bool kEpiBarrier = 8 * kEpiBytes > 3 * C::kKBytes;
   static_assert(4 * kEpiBytes <= 3 * C::kKBytes && 8 * kEpiBytes <= C::kSmemBytes,
                 "epilogue regions must fit the K stages (group A) and the stages (both groups)");
-  __shared__ __attribute__((aligned(16))) char smem[C::kSmemBytes + (NORM && KPROC ? 4 * DQ : 0)];
+  __shared__ __attribute__((aligned(16))) char smem[C::kSmemBytes + (NORM ? (KPROC ? 8 : 4) * DQ : 0)];
 
   const int gx = a.Hkv * head_tiles * a.vslices;
   const int lin = blockIdx.x;
@@ -172,10 +174,18 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
   const int v_dst = (VD * v_c) * C::kVPitch + 8 * vt_slot(v_kg);
   const int k_rd = n * C::kKPitch + 16 * hh;
   const int v_rd = n * C::kVPitch + 16 * hh;
-  // QK-norm weights of the keys into LDS (made visible by the barrier opening each query tile)
-  if constexpr (NORM && KPROC) {
-    if (tid < DQ / 4)
-      lds_write<f32x4>(smem, kNormOff + 16 * tid, *reinterpret_cast<const f32x4*>(a.kn_w + 4 * tid));
+  // QK-norm weights into LDS. Read from there, the query weights take no registers across the
+  // prologue's table loads; 64 more live registers per lane would spill at this tile size.
+  if constexpr (NORM) {
+    if constexpr (KPROC) {
+      if (tid < DQ / 4)
+        lds_write<f32x4>(smem, kNormOff + 16 * tid,
+                         *reinterpret_cast<const f32x4*>(a.kn_w + 4 * tid));
+    }
+    if (tid >= 64 && tid < 64 + DQ / 4)
+      lds_write<f32x4>(smem, kQNormOff + 16 * (tid - 64),
+                       *reinterpret_cast<const f32x4*>(a.qn_w + 4 * (tid - 64)));
+    __syncthreads();
   }
 
   for (int tt = 0; tt < ntile_here; ++tt) {
@@ -196,12 +206,42 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
 #pragma unroll
       for (int s = 0; s < NS; ++s)
         wq[s] = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * s) : u32x4{0, 0, 0, 0};
+      // with QK-norm the table rows are loaded up front (in flight with the query), the chunks
+      // below are then processed one at a time
+      constexpr int kQTabs = NORM && ROPE ? NS : 1;
+      [[maybe_unused]] f32x4 qc[kQTabs], qs[kQTabs];
+      if constexpr (NORM && ROPE) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const int ti = (pos + off) * (D / 2) + 8 * s + 4 * hh;
+          qc[s] = *reinterpret_cast<const f32x4*>(a.rope_cos + ti);
+          qs[s] = *reinterpret_cast<const f32x4*>(a.rope_sin + ti);
+        }
+      }
       [[maybe_unused]] float inv = 0.f;
+      // this lane's query weights in LDS: a base computed here from the lane id (an opaque
+      // instruction pair the compiler cannot move out of the loop), so that neither it nor the
+      // per-chunk addresses (its constant offsets) occupy registers across the key loop
+      [[maybe_unused]] int wbase = 0;
       if constexpr (NORM) {
-        // the row's sum of squares: this lane's half plus its partner's (lane ^ 32)
+        int l;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+        wbase = kQNormOff + 32 * (l >> 5);
+      }
+      if constexpr (NORM) {
+        // the row's sum of squares: this lane's half plus its partner's (lane ^ 32), taken on the
+        // packed words (bf16 squares are exact in fp32) so that no unpacked copy of the row
+        // stays live until the per-chunk pass below
         float ss = 0.f;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) ss += sumsq8(wq[s]);
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // through a scalar: a bit cast of the vector element itself reads element 0 here
+            const uint32_t x = wq[s][e];
+            ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),
+                                                 __builtin_bit_cast(bf16x2, x), ss, false);
+          }
         ss += __shfl_xor(ss, 32);
         inv = rms_inv(ss, D, a.norm_eps);
       }
@@ -213,12 +253,12 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
         if constexpr (NORM) {
           float x[8];
           unpack8(w, x);
-          norm8(x, inv, *reinterpret_cast<const f32x4*>(a.qn_w + 16 * s + 8 * hh),
-                *reinterpret_cast<const f32x4*>(a.qn_w + 16 * s + 8 * hh + 4));
-          if constexpr (ROPE)
-            rope8(x, *reinterpret_cast<const f32x4*>(a.rope_cos + ti),
-                  *reinterpret_cast<const f32x4*>(a.rope_sin + ti));
+          norm8(x, inv, lds_read<f32x4>(smem, wbase + 64 * s),
+                lds_read<f32x4>(smem, wbase + 64 * s + 16));
+          if constexpr (ROPE) rope8(x, qc[s], qs[s]);
           w = pack8(x);
+          // one chunk's weights in registers at a time
+          __builtin_amdgcn_sched_barrier(0);
         } else if constexpr (ROPE) {
           w = rope_chunk(w, *reinterpret_cast<const f32x4*>(a.rope_cos + ti),
                          *reinterpret_cast<const f32x4*>(a.rope_sin + ti));
