@@ -242,7 +242,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
             ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),
                                                  __builtin_bit_cast(bf16x2, x), ss, false);
           }
-        ss += __shfl_xor(ss, 32);
+        ss = pair_sum32(ss);
         inv = rms_inv(ss, D, a.norm_eps);
       }
 #pragma unroll
