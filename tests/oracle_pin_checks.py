@@ -307,7 +307,6 @@ def check_rows_equal_full(orc):
     got = orc.attention_rows(q, k, v, rows, causal=True)
     for r, (b, t, h) in enumerate(rows):
         assert np.array_equal(got[r], full[b, t, h]), (b, t, h)
-    lens = (3, 6)
     cu = np.array([0, 3, 9], dtype=np.int32)
     qp, kp, vp = q[:1], k[:1], v[:1]
     fullp = orc.attention(qp, kp, vp, causal=True, cu_seqlens=cu)
@@ -315,7 +314,113 @@ def check_rows_equal_full(orc):
     got = orc.attention_rows(qp, kp, vp, rows, causal=True, cu_seqlens=cu)
     for r, (b, t, h) in enumerate(rows):
         assert np.array_equal(got[r], fullp[b, t, h]), (b, t, h)
-    del lens
+
+
+def _torch_prepared_sdpa(q, k, v, causal, tabs=None, norm=None, keys_done=False):
+    """torch fp64 reference of attention with QK-norm (torch rms_norm) and then the rotary turn
+    (complex multiplication) applied to q and, unless ``keys_done``, to k; query t at position
+    t + Tkv - Tq, key j at position j (course page, step 3). Dense batch; numpy out."""
+    import torch
+    import torch.nn.functional as F
+    d = q.shape[3]
+    Tq, Tkv = q.shape[1], k.shape[1]
+
+    def norm_rows(x, w):
+        return F.rms_norm(torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64)), (d,),
+                          torch.from_numpy(w.astype(np.float64)), norm[2])
+
+    def turn(x, pos0):
+        if tabs is None:
+            return x
+        rot = torch.complex(torch.from_numpy(tabs[0].astype(np.float64)),
+                            torch.from_numpy(tabs[1].astype(np.float64)))
+        z = torch.view_as_complex(x.reshape(*x.shape[:-1], d // 2, 2).contiguous())
+        z = z * rot[pos0:pos0 + x.shape[1]][None, :, None, :]
+        return torch.view_as_real(z).reshape(x.shape)
+    qq = norm_rows(q, norm[0]) if norm is not None else torch.from_numpy(np.float64(q))
+    kk = torch.from_numpy(np.float64(k))
+    if not keys_done:
+        kk = norm_rows(k, norm[1]) if norm is not None else kk
+        kk = turn(kk, 0)
+    G = q.shape[2] // k.shape[2]
+    qt = turn(qq, Tkv - Tq).permute(0, 2, 1, 3).contiguous()
+    kt = kk.repeat_interleave(G, dim=2).permute(0, 2, 1, 3).contiguous()
+    vt = torch.from_numpy(np.float64(v)).repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    mask = torch.from_numpy(_window_mask(Tq, Tkv, Tkv + 1, 0)) if causal else None
+    ref = F.scaled_dot_product_attention(qt, kt, vt.contiguous(), attn_mask=mask)
+    return ref.permute(0, 2, 1, 3).numpy()
+
+
+def check_rows_with_rope_and_norm(orc):
+    """The selected-rows form with the course page's step-3 prologues (rotary turn from
+    position tables, QK-norm with caller weights, both together), with fewer queries than keys
+    (query t at position t + Tkv - Tq) and in packed batches (positions per sequence): each row
+    equals the whole-output oracle exactly and torch's rms_norm + complex rotation + fp64 SDPA
+    to 1e-12."""
+    rng = _rng(29)
+    d, Hq, Hkv = 8, 6, 2
+    cases = [(5, 9, True, "qk", False), (7, 7, True, "qk", True), (4, 9, True, None, True),
+             (3, 10, False, "qk", True), (6, 6, True, "q", False), (4, 8, True, "q", True)]
+    for Tq, Tkv, causal, rope_mode, use_norm in cases:
+        q = rng.standard_normal((2, Tq, Hq, d)) * 2.0
+        k = rng.standard_normal((2, Tkv, Hkv, d))
+        v = rng.standard_normal((2, Tkv, Hkv, d))
+        tabs = rope_tables(Tkv + 3, d) if rope_mode else None
+        norm = None
+        if use_norm:
+            norm = ((rng.random(d) + 0.5).astype(np.float32),
+                    (rng.random(d) + 0.5).astype(np.float32), 1e-6)
+        keys_done = rope_mode == "q"
+        kin = k
+        if keys_done:
+            # a cache: keys normalised and turned beforehand, by torch
+            kin = _torch_prepared_sdpa_keys(k, tabs, norm)
+        kw = dict(causal=causal, rope=tabs, rope_mode=rope_mode or "qk", qk_norm=norm,
+                  qk_norm_mode="q" if keys_done else "qk")
+        full = orc.attention(q, kin, v, **kw)
+        rows = np.array([(0, 0, 0), (1, Tq - 1, Hq - 1), (1, Tq // 2, 2), (0, Tq - 1, 3),
+                         (1, 0, 5)], dtype=np.int64)
+        got = orc.attention_rows(q, kin, v, rows, **kw)
+        ref = _torch_prepared_sdpa(q, kin, v, causal, tabs, norm, keys_done)
+        for r, (b, t, h) in enumerate(rows):
+            assert np.array_equal(got[r], full[b, t, h]), (Tq, Tkv, rope_mode, use_norm, b, t, h)
+            err = np.max(np.abs(got[r] - ref[b, t, h]))
+            assert err <= 1e-12, (Tq, Tkv, rope_mode, use_norm, b, t, h, err)
+    # packed: two sequences of 4 and 7 tokens, each turned from its own position 0
+    cu = np.array([0, 4, 11], dtype=np.int32)
+    q = rng.standard_normal((1, 11, Hq, d)); k = rng.standard_normal((1, 11, Hkv, d))
+    v = rng.standard_normal((1, 11, Hkv, d))
+    tabs = rope_tables(8, d)
+    norm = ((rng.random(d) + 0.5).astype(np.float32), (rng.random(d) + 0.5).astype(np.float32),
+            1e-5)
+    kw = dict(causal=True, cu_seqlens=cu, rope=tabs, qk_norm=norm)
+    full = orc.attention(q, k, v, **kw)
+    rows = np.array([(0, 0, 0), (0, 3, 5), (0, 4, 1), (0, 10, 4), (0, 7, 2)], dtype=np.int64)
+    got = orc.attention_rows(q, k, v, rows, **kw)
+    for s in range(2):
+        a, b = int(cu[s]), int(cu[s + 1])
+        ref = _torch_prepared_sdpa(q[:, a:b], k[:, a:b], v[:, a:b], True, tabs, norm)
+        for r, (_, t, h) in enumerate(rows):
+            if a <= t < b:
+                assert np.array_equal(got[r], full[0, t, h]), (t, h)
+                assert np.max(np.abs(got[r] - ref[0, t - a, h])) <= 1e-12, (t, h)
+
+
+def _torch_prepared_sdpa_keys(k, tabs, norm):
+    """Keys normalised (torch rms_norm) and turned (complex multiplication) at positions 0.."""
+    import torch
+    import torch.nn.functional as F
+    d = k.shape[3]
+    kk = torch.from_numpy(np.float64(k))
+    if norm is not None:
+        kk = F.rms_norm(kk, (d,), torch.from_numpy(norm[1].astype(np.float64)), norm[2])
+    if tabs is not None:
+        rot = torch.complex(torch.from_numpy(tabs[0].astype(np.float64)),
+                            torch.from_numpy(tabs[1].astype(np.float64)))
+        z = torch.view_as_complex(kk.reshape(*kk.shape[:-1], d // 2, 2).contiguous())
+        z = z * rot[0:kk.shape[1]][None, :, None, :]
+        kk = torch.view_as_real(z).reshape(kk.shape)
+    return kk.numpy()
 
 
 def check_bf16_widening_is_exact(orc):
@@ -676,6 +781,70 @@ def check_bwd_invariants(orc):
     assert np.max(np.abs(dvm.reshape(2, 7, 2, 3, 8).sum(axis=3) - dv)) <= 1e-12
 
 
+# ------------------------------------------------------------------------------------------------
+# lab steps 6-8: exact integer counts (these take the counts module, not the bound oracle)
+# ------------------------------------------------------------------------------------------------
+
+def check_counts_lab_scale_exact(counts):
+    """Lab step 8's model scale (layers 32, seq_len 4096, head_dim 128, h 8, d_model 1024,
+    n_tokens 4096) put through step 6's element count and step 7's per-term multiply count.
+    All sizes are powers of two, so the page's formulas reduce to closed forms:
+      cache elements 2 * 32 * g * 2^12 * 2^7 = g * 2^25;
+      proj_q = proj_out = 2^12 * 2^10 * (8 * 2^7) = 2^32; proj_k = proj_v = g * 2^29;
+      scores = weighted = 8 * 2^24 * 2^7 = 2^34; total = 2^30 * (40 + g);
+    so kv_ratio = 8 / g and mult_ratio = 48 / (40 + g) (1, 12/11, 8/7, 48/41)."""
+    from fractions import Fraction
+    table = counts.kv_table(32, 8, [8, 4, 2, 1], 4096, 128)
+    assert table == [(8, 268435456), (4, 134217728), (2, 67108864), (1, 33554432)], table
+    assert [g * 2 ** 25 for g, _ in table] == [e for _, e in table]
+    assert [table[0][1] // e for _, e in table] == [1, 2, 4, 8]
+    totals = []
+    for g in (8, 4, 2, 1):
+        m = counts.mults(4096, 1024, 8, g, 128)
+        assert m["proj_q"] == m["proj_out"] == 2 ** 32 == 4294967296, (g, m)
+        assert m["proj_k"] == m["proj_v"] == g * 2 ** 29 == 536870912 * g, (g, m)
+        assert m["scores"] == m["weighted"] == 2 ** 34 == 17179869184, (g, m)
+        assert m["total"] == 2 ** 30 * (40 + g), (g, m)
+        assert counts.core_mults(4096, 1024, 8, g, 128) == 2 ** 35
+        totals.append(m["total"])
+    assert totals == [51539607552, 47244640256, 45097156608, 44023414784]
+    assert [Fraction(totals[0], t) for t in totals] == [Fraction(1), Fraction(12, 11),
+                                                         Fraction(8, 7), Fraction(48, 41)]
+
+
+def check_counts_when_heads_times_dim_differs_from_width(counts):
+    """Step 7's projection term is tokens x model width x (that projection's heads x head dim);
+    at the lab scale h * head_dim equals d_model, so a width-squared projection would go unseen.
+    Hand-worked at n = 3, d_model = 5, h = 6, g = 2, head_dim = 7:
+      proj_q = proj_out = 3 * 5 * 42 = 630; proj_k = proj_v = 3 * 5 * 14 = 210;
+      scores = weighted = 6 * 3 * 3 * 7 = 378; total = 2436.
+    And step 6 at layers 3, kv heads 5, length 7, head dim 11: 2 * 3 * 5 * 7 * 11 = 2310."""
+    m = counts.mults(3, 5, 6, 2, 7)
+    want = {"proj_q": 630, "proj_k": 210, "proj_v": 210, "scores": 378, "weighted": 378,
+            "proj_out": 630, "total": 2436}
+    assert m == want, m
+    assert counts.core_mults(3, 5, 6, 2, 7) == 756
+    assert counts.kv_cache_elems(3, 5, 7, 11) == 2310
+    assert counts.kv_table(3, 10, [5, 1], 7, 11) == [(5, 2310), (1, 462)]
+
+
+def check_counts_reject_uneven(counts):
+    for bad in (lambda: counts.kv_table(32, 8, [3], 4096, 128),
+                lambda: counts.mults(4096, 1024, 8, 3, 128)):
+        try:
+            bad()
+        except ValueError:
+            continue
+        raise AssertionError("uneven grouping accepted")
+
+
+COUNT_CHECKS = [
+    check_counts_lab_scale_exact,
+    check_counts_when_heads_times_dim_differs_from_width,
+    check_counts_reject_uneven,
+]
+
+
 ALL_CHECKS = [
     check_group_of_worked_example,
     check_group_of_rejects_uneven,
@@ -705,5 +874,6 @@ ALL_CHECKS = [
     check_g_equals_h_is_mha,
     check_packed_equals_separate,
     check_rows_equal_full,
+    check_rows_with_rope_and_norm,
     check_bf16_widening_is_exact,
 ]

@@ -54,6 +54,14 @@ MUTANTS = {
     "gva_value_head_of_group": ("const double* vh = &vw[(I.k_row0 * HV + j) * (int64_t)d];",
                                 "const double* vh = &vw[(I.k_row0 * HV + j - j % (HV / H)) * "
                                 "(int64_t)d];"),
+    # selected-rows form: keys left unturned
+    "rows_key_rotation_dropped": ("if (rope_mode & ROPE_K) rope_row(&kh[j * d], d, rope_cos, "
+                                  "rope_sin, j);", "(void)0;"),
+    # selected-rows form: keys turned one position late
+    "rows_key_position_shifted": ("rope_row(&kh[j * d], d, rope_cos, rope_sin, j);",
+                                  "rope_row(&kh[j * d], d, rope_cos, rope_sin, j + 1);"),
+    # selected-rows form: keys not normalised
+    "rows_key_norm_dropped": ("if (kn_w) rms_row(&kh[j * d], d, kn_w, norm_eps);", "(void)0;"),
     # value rows weighted by the wrong key
     "value_index_shift": ("out[c] += s[j] * v[j * kstride + c];",
                           "out[c] += s[j] * v[((j + 1) % nvis) * kstride + c];"),
@@ -79,3 +87,42 @@ def test_mutant_is_caught(name, tmp_path):
         except (AssertionError, ValueError, FloatingPointError):
             failed.append(check.__name__)
     assert failed, f"no pin caught mutant {name}"
+
+
+COUNT_SRC = os.path.join(os.path.dirname(oracle.__file__), "counts.py")
+
+COUNT_MUTANTS = {
+    # step 7: projections priced as width x width instead of width x (heads x head dim)
+    "proj_width_squared": ('"proj_q": n * d_model * (h * head_dim),',
+                           '"proj_q": n * d_model * d_model,'),
+    "proj_out_width_squared": ('"proj_out": n * d_model * (h * head_dim),',
+                               '"proj_out": n * d_model * d_model,'),
+    # step 7: the score term with the group count instead of the query heads
+    "scores_use_groups": ('"scores": h * n * n * head_dim,', '"scores": g * n * n * head_dim,'),
+    # step 7: value projection with all query heads
+    "proj_v_query_heads": ('"proj_v": n * d_model * (g * head_dim),',
+                           '"proj_v": n * d_model * (h * head_dim),'),
+    # step 6: one tensor instead of K and V
+    "cache_one_tensor": ("return 2 * layers * kv_heads * seq_len * head_dim",
+                         "return layers * kv_heads * seq_len * head_dim"),
+    # step 6: the table indexed by query heads
+    "table_query_heads": ("out.append((g, kv_cache_elems(layers, g, seq_len, head_dim)))",
+                          "out.append((g, kv_cache_elems(layers, h, seq_len, head_dim)))"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(COUNT_MUTANTS))
+def test_count_mutant_is_caught(name):
+    import types
+    old, new = COUNT_MUTANTS[name]
+    src = open(COUNT_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} no longer in counts.py"
+    mod = types.ModuleType("counts_mutant")
+    exec(compile(src.replace(old, new), "counts_mutant.py", "exec"), mod.__dict__)
+    failed = []
+    for check in pins.COUNT_CHECKS:
+        try:
+            check(mod)
+        except (AssertionError, ValueError):
+            failed.append(check.__name__)
+    assert failed, f"no count pin caught mutant {name}"

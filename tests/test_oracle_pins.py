@@ -24,6 +24,11 @@ def test_pin(orc, check):
     check(orc)
 
 
+@pytest.mark.parametrize("check", pins.COUNT_CHECKS, ids=lambda c: c.__name__)
+def test_count_pin(check):
+    check(counts)
+
+
 def test_fold_and_expand_reject_uneven(orc):
     x = np.zeros((1, 2, 8, 4))
     with pytest.raises(ValueError):
