@@ -216,7 +216,7 @@ def bench_decode(gqa, w, steps, warmup, torch, seed):
     for i in range(2):
         q, k, v, _ = device_inputs(w, torch, seed + 10 * i)
         sets.append((q, k, v))
-    ws = torch.empty(gqa.gqa_attn_decode_workspace_bytes(w.B, w.Tkv, w.Hq, w.Hkv, w.d),
+    ws = torch.empty(gqa.gqa_attn_decode_workspace_bytes(w.B, w.Tkv, w.Hq, w.d),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty_like(sets[0][0])
     lens = None

@@ -20,8 +20,10 @@ LIB_PATH = os.path.join(PKG, "libgqa_attn.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "gqa_attn.h")
 
 GQA_OK, GQA_ERR_NULL_PTR, GQA_ERR_SHAPE, GQA_ERR_GROUPING = 0, 1, 2, 3
-GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_ALIAS, GQA_ERR_HIP = 4, 5, 6, 7
+GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP, GQA_ERR_ALIAS = 4, 5, 6, 7
 GQA_DTYPE_F32, GQA_DTYPE_BF16 = 0, 1
+# scale argument that makes the library use 1/sqrt(d)
+GQA_SCALE_DEFAULT = 0.0
 
 
 class GQAError(RuntimeError):
@@ -91,8 +93,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.gqa_attn_prefill.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P, I, I, P]
     lib.gqa_attn_prefill.restype = I
-    lib.gqa_attn_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.gqa_attn_decode_workspace_bytes.argtypes = [I, I, I, I]
     lib.gqa_attn_decode_workspace_bytes.restype = SZ
+    lib.gqa_attn_decode_workspace_bytes_hkv.argtypes = [I, I, I, I, I]
+    lib.gqa_attn_decode_workspace_bytes_hkv.restype = SZ
     lib.gqa_attn_decode.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, SZ, I, P]
     lib.gqa_attn_decode.restype = I
     lib.gqa_attn_prefill_window.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, P, I, I, P]
@@ -174,6 +178,14 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
+def _max_seqlen(max_seqlen) -> int:
+    """The longest packed sequence, from the caller: reading it from the device offsets would
+    synchronise the stream."""
+    if max_seqlen is None:
+        raise ValueError("packed batches need max_seqlen (the longest sequence, a host int)")
+    return int(max_seqlen)
+
+
 def _prefill_args(q, k, v, scale, cu_seqlens, max_seqlen, out):
     q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
@@ -185,7 +197,7 @@ def _prefill_args(q, k, v, scale, cu_seqlens, max_seqlen, out):
     if Bk != B or dk != d:
         raise ValueError("q and k/v disagree on batch or head dim")
     if scale is None:
-        scale = d ** -0.5
+        scale = GQA_SCALE_DEFAULT
     cu_ptr, nseq, msl = None, B, 0
     if cu_seqlens is not None:
         cu = _dev(cu_seqlens, "cu_seqlens")
@@ -194,9 +206,7 @@ def _prefill_args(q, k, v, scale, cu_seqlens, max_seqlen, out):
         if B != 1:
             raise ValueError("packed batches use q/k/v of shape [1, total, H, d]")
         nseq = cu.numel() - 1
-        if max_seqlen is None:
-            max_seqlen = int((cu[1:] - cu[:-1]).max().item())
-        cu_ptr, msl = cu.data_ptr(), int(max_seqlen)
+        cu_ptr, msl = cu.data_ptr(), _max_seqlen(max_seqlen)
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
@@ -274,16 +284,14 @@ def gqa_attn_prefill_gva(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, caus
             or v.shape[3] != d:
         raise ValueError("q, k and v disagree on batch, length, heads or head dim")
     if scale is None:
-        scale = d ** -0.5
+        scale = GQA_SCALE_DEFAULT
     cu_ptr, nseq, msl = None, B, 0
     if cu_seqlens is not None:
         cu = _dev(cu_seqlens, "cu_seqlens")
         if cu.dtype != torch.int32 or cu.dim() != 1 or cu.numel() < 2 or B != 1:
             raise ValueError("packed batches: int32 cu_seqlens and [1, total, ., d] tensors")
         nseq = cu.numel() - 1
-        if max_seqlen is None:
-            max_seqlen = int((cu[1:] - cu[:-1]).max().item())
-        cu_ptr, msl = cu.data_ptr(), int(max_seqlen)
+        cu_ptr, msl = cu.data_ptr(), _max_seqlen(max_seqlen)
     oshape = (B, Tq, HV, d)
     if out is None:
         out = torch.empty(oshape, dtype=q.dtype, device=q.device)
@@ -317,9 +325,7 @@ def gqa_prepare_keys(k: torch.Tensor, rope=None, qk_norm=None, pos0: int = 0,
         if cu.dtype != torch.int32 or cu.dim() != 1 or cu.numel() < 2 or B != 1:
             raise ValueError("packed keys: int32 cu_seqlens and k of shape [1, total, Hkv, d]")
         nseq = cu.numel() - 1
-        if max_seqlen is None:
-            max_seqlen = int((cu[1:] - cu[:-1]).max().item())
-        cu_ptr, msl = cu.data_ptr(), int(max_seqlen)
+        cu_ptr, msl = cu.data_ptr(), _max_seqlen(max_seqlen)
     if out is None:
         out = torch.empty_like(k)
     elif out.shape != k.shape or out.dtype != k.dtype or not out.is_contiguous():
@@ -331,8 +337,14 @@ def gqa_prepare_keys(k: torch.Tensor, rope=None, qk_norm=None, pos0: int = 0,
     return out
 
 
-def gqa_attn_decode_workspace_bytes(B: int, Tkv: int, Hq: int, Hkv: int, d: int) -> int:
-    return int(_lib.gqa_attn_decode_workspace_bytes(B, Tkv, Hq, Hkv, d))
+def gqa_attn_decode_workspace_bytes(B: int, Tkv: int, Hq: int, d: int) -> int:
+    """Workspace bytes enough for a decode of these sizes with any Hkv that divides Hq."""
+    return int(_lib.gqa_attn_decode_workspace_bytes(B, Tkv, Hq, d))
+
+
+def gqa_attn_decode_workspace_bytes_hkv(B: int, Tkv: int, Hq: int, Hkv: int, d: int) -> int:
+    """The exact workspace bytes a decode with Hkv key/value heads needs."""
+    return int(_lib.gqa_attn_decode_workspace_bytes_hkv(B, Tkv, Hq, Hkv, d))
 
 
 def _decode_args(q, k_cache, v_cache, scale, workspace, out):
@@ -346,15 +358,20 @@ def _decode_args(q, k_cache, v_cache, scale, workspace, out):
     if Bk != B or dk != d:
         raise ValueError("q and the caches disagree on batch or head dim")
     if scale is None:
-        scale = d ** -0.5
+        scale = GQA_SCALE_DEFAULT
     ws_ptr, ws_bytes = None, 0
     if q.dtype == torch.bfloat16:
-        need = gqa_attn_decode_workspace_bytes(B, Tkv, Hq, Hkv, d)
+        need = gqa_attn_decode_workspace_bytes_hkv(B, Tkv, Hq, Hkv, d)
         if workspace is None:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        elif workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     if out is None:
         out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous device tensor shaped and typed like q")
     return q, k, v, out, (B, Tkv, Hq, Hkv, d, float(scale)), ws_ptr, ws_bytes, workspace
 
 
@@ -434,13 +451,19 @@ def gqa_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: to
         raise ValueError("expected q, out, dout [B,Tq,Hq,d] and k, v [B,Tkv,Hkv,d]")
     if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]):
         raise ValueError("lse must be float32 [B, Tq, Hq]")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise TypeError("q, k, v, out and dout must share a dtype")
     B, Tq, Hq, d = q.shape
+    if k.dim() != 4 or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must be [B, Tkv, Hkv, d] with q's batch and head dim")
     Tkv, Hkv = k.shape[1], k.shape[2]
     if scale is None:
-        scale = d ** -0.5
+        scale = GQA_SCALE_DEFAULT
     need = int(_lib.gqa_attn_backward_workspace_bytes(B, Tq, Hq))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     rc = _lib.gqa_attn_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                 dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
@@ -463,6 +486,9 @@ def gqa_fold_kv(src: torch.Tensor, g: int, out: Optional[torch.Tensor] = None,
     src = _dev(src, "src")
     if out is None:
         out = torch.empty((B, T, g, d), dtype=src.dtype, device=src.device)
+    elif tuple(out.shape) != (B, T, g, d) or out.dtype != src.dtype or not out.is_contiguous() \
+            or out.device != src.device:
+        raise ValueError("out must be a contiguous device tensor [B, T, g, d] of src's dtype")
     rc = _lib.gqa_fold_kv(src.data_ptr(), out.data_ptr(), B, T, H, g, d, _dtype_code(src),
                           _stream(stream))
     _check(rc, "gqa_fold_kv")

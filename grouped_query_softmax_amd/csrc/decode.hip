@@ -97,7 +97,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   const int g = lane >> 4;
   // The visible cache entries of this sequence, as one list: the sink entries below the window
   // [0, a_end) followed by the window [w_start, L). Splits and tiles run over list positions.
-  const int L = a.lens ? min(max(a.lens[b], 1), a.Tkv) : a.Tkv;
+  // L = 0 (an empty cache) leaves nothing visible: the output row is zero
+  const int L = a.lens ? min(max(a.lens[b], 0), a.Tkv) : a.Tkv;
   const int w_start = a.window > 0 ? max(0, L - a.window) : 0;
   const int a_end = min(a.n_sink, w_start);
   const int nvis = a_end + (L - w_start);
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
       u32x4 w = wq[s];
       // rotary embedding of the query at its position L - 1 (the cache holds turned keys);
       // this lane's dimensions 32s + 8g .. +7 are the pairs 16s + 4g .. +3
-      const int ti = (L - 1) * (D / 2) + 16 * s + 4 * g;
+      const int ti = max(L - 1, 0) * (D / 2) + 16 * s + 4 * g;
       if (a.qn_w) {
         float x[8];
         unpack8(w, x);
@@ -158,7 +159,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   }
 
   const int64_t seq_elem = (static_cast<int64_t>(b) * a.Tkv * a.Hkv + kvh) * D;
-  const int nrec = (L - 1) * row_bytes + D * 2;
+  // bytes from the head's first entry to the end of its last visible one (0 for an empty cache,
+  // so every load of that sequence is out of range and reads zeros)
+  const int nrec = L > 0 ? (L - 1) * row_bytes + D * 2 : 0;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k) + seq_elem), 0, nrec, kBufWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -356,8 +359,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
 #pragma unroll
         for (int e = 0; e < kDimsPerThread; e += 4) {
           u32x2 w;
-          w[0] = pack_bf16x2(o[e] / L, o[e + 1] / L);
-          w[1] = pack_bf16x2(o[e + 2] / L, o[e + 3] / L);
+          // an empty cache (L = 0, o = 0) gives the zero row
+          const float r = L > 0.f ? L : 1.f;
+          w[0] = pack_bf16x2(o[e] / r, o[e + 1] / r);
+          w[1] = pack_bf16x2(o[e + 2] / r, o[e + 3] / r);
           *reinterpret_cast<u32x2*>(orow + e) = w;
         }
       } else {
@@ -384,10 +389,14 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const int d = threadIdx.x;
   // the splits this sequence has: its visible entries (as in the split kernel) over a.per
   const int b = bh / a.Hq;
-  const int L = a.lens ? min(max(a.lens[b], 1), a.Tkv) : a.Tkv;
+  const int L = a.lens ? min(max(a.lens[b], 0), a.Tkv) : a.Tkv;
   const int w_start = a.window > 0 ? max(0, L - a.window) : 0;
   const int nvis = min(a.n_sink, w_start) + (L - w_start);
   const int nvalid = min(nsplit, (nvis + a.per - 1) / a.per);
+  if (nvalid == 0) {  // an empty cache: no split wrote a partial, the row is zero
+    static_cast<uint16_t*>(a.out)[static_cast<int64_t>(bh) * D + d] = 0;
+    return;
+  }
   const int64_t ntot = static_cast<int64_t>(nbh) * nsplit;
   const float* wm = ws + ntot * D + static_cast<int64_t>(bh) * nsplit;
   const float* wl = ws + ntot * D + ntot + static_cast<int64_t>(bh) * nsplit;

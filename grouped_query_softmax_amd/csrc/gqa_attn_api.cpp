@@ -52,6 +52,14 @@ int64_t head_tiles(gqa_dtype_t t, int G) {
 
 gqa_status_t from_hip(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
 
+// The score factor: the caller's, or 1/sqrt(d) for GQA_SCALE_DEFAULT (GQA lab page, step 4:
+// scores are divided by the square root of the head dimension). False for a negative or
+// non-finite scale.
+bool resolve_scale(float& scale, int d) {
+  if (scale == GQA_SCALE_DEFAULT) scale = static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
+  return isfinite(scale) && scale > 0.f;
+}
+
 // Value/output geometry of grouped-query attention: one value row of d columns per key/value
 // head, one output row per query head.
 void set_gqa_geometry(gqa::PrefillArgs& a) {
@@ -117,7 +125,7 @@ static gqa_status_t prefill_impl(const void* q, const void* k, const void* v, vo
                                  int max_seqlen, gqa_dtype_t dtype, hipStream_t stream) {
   if (!q || !k || !v || !out) return GQA_ERR_NULL_PTR;
   if (B <= 0 || Tq <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_SHAPE;
-  if (!isfinite(scale) || !(scale > 0.f)) return GQA_ERR_SHAPE;
+  if (!resolve_scale(scale, d)) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0) return GQA_ERR_GROUPING;
   if (!dtype_ok(dtype) || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
   if (const gqa_status_t st = check_options(opt, dtype, cu_seqlens ? max_seqlen : Tkv))
@@ -221,7 +229,7 @@ gqa_status_t gqa_attn_prefill_gva(const void* q, const void* k, const void* v, v
                                   hipStream_t stream) {
   if (!q || !k || !v || !out) return GQA_ERR_NULL_PTR;
   if (B <= 0 || Tq <= 0 || Tkv <= 0 || H <= 0 || HV <= 0 || d <= 0) return GQA_ERR_SHAPE;
-  if (!isfinite(scale) || !(scale > 0.f)) return GQA_ERR_SHAPE;
+  if (!resolve_scale(scale, d)) return GQA_ERR_SHAPE;
   if (HV % H != 0) return GQA_ERR_GROUPING;
   if (dtype != GQA_DTYPE_BF16 || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
   if (const gqa_status_t st = check_options(opt, dtype, cu_seqlens ? max_seqlen : Tkv)) return st;
@@ -291,9 +299,18 @@ gqa_status_t gqa_attn_prefill_gva(const void* q, const void* k, const void* v, v
   return from_hip(gqa::launch_prefill_bf16(a, stream));
 }
 
-size_t gqa_attn_decode_workspace_bytes(int B, int Tkv, int Hq, int Hkv, int d) {
+size_t gqa_attn_decode_workspace_bytes_hkv(int B, int Tkv, int Hq, int Hkv, int d) {
   if (B <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0) return 0;
   return gqa::decode_workspace_bytes(B, Tkv, Hq, Hkv, d);
+}
+
+size_t gqa_attn_decode_workspace_bytes(int B, int Tkv, int Hq, int d) {
+  if (B <= 0 || Tkv <= 0 || Hq <= 0 || d <= 0) return 0;
+  // the largest requirement over every key/value head count that divides Hq
+  size_t most = 0;
+  for (int hkv = 1; hkv <= Hq; ++hkv)
+    if (Hq % hkv == 0) most = std::max(most, gqa::decode_workspace_bytes(B, Tkv, Hq, hkv, d));
+  return most;
 }
 
 static gqa_status_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
@@ -303,7 +320,7 @@ static gqa_status_t decode_impl(const void* q, const void* k_cache, const void* 
                                 hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !out) return GQA_ERR_NULL_PTR;
   if (B <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_SHAPE;
-  if (!isfinite(scale) || !(scale > 0.f)) return GQA_ERR_SHAPE;
+  if (!resolve_scale(scale, d)) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0) return GQA_ERR_GROUPING;
   if (!dtype_ok(dtype) || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
   if (const gqa_status_t st = check_options(opt, dtype, Tkv, true)) return st;
@@ -429,7 +446,7 @@ gqa_status_t gqa_attn_backward(const void* q, const void* k, const void* v, cons
                                gqa_dtype_t dtype, hipStream_t stream) {
   if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return GQA_ERR_NULL_PTR;
   if (B <= 0 || Tq <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_SHAPE;
-  if (!isfinite(scale) || !(scale > 0.f)) return GQA_ERR_SHAPE;
+  if (!resolve_scale(scale, d)) return GQA_ERR_SHAPE;
   if (causal && Tq > Tkv) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0) return GQA_ERR_GROUPING;
   if (dtype != GQA_DTYPE_BF16 || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;

@@ -26,7 +26,10 @@
  *   - Arguments are validated before anything is enqueued; on an error status nothing has been
  *     written. Outputs must not overlap inputs. No C++ exception crosses this interface.
  *   - Thread-safe: the library holds no mutable global state.
- *   - `scale` must be finite and positive (normally 1/sqrt(d)); anything else is GQA_ERR_SHAPE.
+ *   - `scale` multiplies every score. Pass a finite positive value, or GQA_SCALE_DEFAULT (0) for
+ *     1/sqrt(d), the factor both the GQA lab page (step 4: scores divided by the square root of
+ *     the head dimension) and the course page (step 1) use; the library then computes it as
+ *     (float)(1 / sqrt((double)d)). A negative or non-finite scale is GQA_ERR_SHAPE.
  *   - Internal arithmetic is fp32 (bf16 inputs are widened exactly; products accumulate in fp32);
  *     outputs are rounded to nearest-even in the input dtype.
  */
@@ -49,9 +52,12 @@ typedef enum {
   GQA_ERR_GROUPING = 3,    /* Hq is not divisible by Hkv (or H by g): heads do not split evenly */
   GQA_ERR_UNSUPPORTED = 4, /* (dtype, d) combination not built, or a pointer not 16-byte aligned */
   GQA_ERR_WORKSPACE = 5,   /* decode workspace missing or smaller than required */
-  GQA_ERR_ALIAS = 6,       /* an output buffer overlaps an input buffer */
-  GQA_ERR_HIP = 7          /* the HIP runtime reported an error when enqueueing */
+  GQA_ERR_HIP = 6,         /* the HIP runtime reported an error when enqueueing */
+  GQA_ERR_ALIAS = 7        /* an output buffer overlaps an input buffer */
 } gqa_status_t;
+
+/* `scale` value that selects 1/sqrt(d) (GQA lab page, step 4; course page, step 1). */
+#define GQA_SCALE_DEFAULT 0.0f
 
 typedef enum { GQA_DTYPE_F32 = 0, GQA_DTYPE_BF16 = 1 } gqa_dtype_t;
 
@@ -178,13 +184,20 @@ gqa_status_t gqa_attn_prefill_gva(const void* q, const void* k, const void* v, v
  *   q [B, 1, Hq, d]     k_cache, v_cache [B, Tkv, Hkv, d]     out [B, 1, Hq, d]
  * Each split writes an fp32 partial result (running max, sum and unnormalised output) to
  * `workspace`, and a second kernel merges the splits. `workspace` is caller-owned device memory
- * of at least gqa_attn_decode_workspace_bytes(...) bytes (16-byte aligned); its contents on
+ * of at least gqa_attn_decode_workspace_bytes(B, Tkv, Hq, d) bytes (or the exact figure
+ * gqa_attn_decode_workspace_bytes_hkv(B, Tkv, Hq, Hkv, d)), 16-byte aligned; its contents on
  * entry do not matter and are overwritten. Concurrent calls must use distinct workspaces.
  * `causal` is accepted for symmetry with prefill: a single query at the last position sees the
  * whole cache, so it changes nothing. bf16 uses the split-KV kernels; f32 runs the prefill
  * kernel with Tq = 1 and needs no workspace (workspace may then be NULL).
+ *
+ * gqa_attn_decode_workspace_bytes: an upper bound valid for every Hkv that divides Hq (the
+ * split count, and so the fp32 partials [B, Hq, splits, d + 2], depends on Hkv); 0 for
+ * non-positive sizes. gqa_attn_decode_workspace_bytes_hkv: the exact requirement for one Hkv
+ * (0 for non-positive sizes or Hq not divisible by Hkv); never above the bound.
  */
-size_t gqa_attn_decode_workspace_bytes(int B, int Tkv, int Hq, int Hkv, int d);
+size_t gqa_attn_decode_workspace_bytes(int B, int Tkv, int Hq, int d);
+size_t gqa_attn_decode_workspace_bytes_hkv(int B, int Tkv, int Hq, int Hkv, int d);
 gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
                              int B, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
                              void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
@@ -196,11 +209,13 @@ gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_c
  *   q [B, 1, Hq, d]     k_cache, v_cache [B, Tmax, Hkv, d] (Tmax = allocated entries per
  *   sequence)     out [B, 1, Hq, d]
  * cache_lens: DEVICE int32[B] (or NULL: every sequence uses all Tmax entries); sequence b uses its
- * entries 0 .. cache_lens[b]-1 and its query sits at position cache_lens[b]-1. Lengths outside
- * [1, Tmax] are clamped into it. With window > 0 the query sees only its last `window` entries
- * plus entries 0 .. n_sink-1; window = 0 means the whole (ragged) cache. Only visible entries
- * are read. Workspace as for gqa_attn_decode, sized by
- * gqa_attn_decode_workspace_bytes(B, Tmax, Hq, Hkv, d). bf16 only (else GQA_ERR_UNSUPPORTED);
+ * entries 0 .. cache_lens[b]-1 and its query sits at position cache_lens[b]-1. A length of 0
+ * (an empty cache) gives a zero output row: the query sees no key, and a softmax over an empty
+ * set is taken as zero weight everywhere. The lengths live on the device, so the host cannot
+ * validate them: a negative length counts as 0 and one above Tmax as Tmax. With window > 0 the
+ * query sees only its last `window` entries plus entries 0 .. n_sink-1; window = 0 means the
+ * whole (ragged) cache. Only visible entries are read. Workspace as for gqa_attn_decode, sized
+ * by gqa_attn_decode_workspace_bytes(B, Tmax, Hq, d). bf16 only (else GQA_ERR_UNSUPPORTED);
  * negative window or n_sink is GQA_ERR_SHAPE.
  */
 gqa_status_t gqa_attn_decode_ragged(const void* q, const void* k_cache, const void* v_cache,
@@ -247,7 +262,7 @@ gqa_status_t gqa_fold_kv(const void* src, void* dst, int B, int T, int H, int g,
 const char* gqa_status_string(gqa_status_t s);
 
 /* Interface version of this header: bumped on any incompatible change. */
-#define GQA_ATTN_ABI_VERSION 2
+#define GQA_ATTN_ABI_VERSION 3
 int gqa_attn_abi_version(void);
 
 #ifdef __cplusplus

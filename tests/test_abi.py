@@ -23,7 +23,60 @@ def test_library_exports_every_header_function(lib):
                           "gqa_fold_kv", "gqa_status_string", "gqa_attn_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gqa_attn_abi_version() == 2
+    assert lib.gqa_attn_abi_version() == 3
+
+
+# The boundary's core calls as the interface specification writes them (whitespace aside).
+SPEC_PROTOTYPES = [
+    "gqa_status_t gqa_attn_prefill(const void* q, const void* k, const void* v, void* out, int B, "
+    "int Tq, int Tkv, int Hq, int Hkv, int d, float scale, int causal, "
+    "const int32_t* cu_seqlens, int max_seqlen, gqa_dtype_t dtype, hipStream_t stream);",
+    "size_t gqa_attn_decode_workspace_bytes(int B, int Tkv, int Hq, int d);",
+    "gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, "
+    "void* out, int B, int Tkv, int Hq, int Hkv, int d, float scale, int causal, "
+    "void* workspace, size_t workspace_bytes, gqa_dtype_t dtype, hipStream_t stream);",
+    "gqa_status_t gqa_fold_kv(const void* src, void* dst, int B, int T, int H, int g, int d, "
+    "gqa_dtype_t dtype, hipStream_t stream);",
+    "const char* gqa_status_string(gqa_status_t s);",
+]
+
+
+def _norm_ws(text):
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    return re.sub(r"\s+", " ", text).replace("( ", "(").replace(" )", ")")
+
+
+def test_header_declares_the_specified_signatures_and_codes():
+    text = _norm_ws(open(os.path.join(ROOT, "include", "gqa_attn.h")).read())
+    for proto in SPEC_PROTOTYPES:
+        assert _norm_ws(proto) in text, proto
+    codes = {"GQA_OK": 0, "GQA_ERR_NULL_PTR": 1, "GQA_ERR_SHAPE": 2, "GQA_ERR_GROUPING": 3,
+             "GQA_ERR_UNSUPPORTED": 4, "GQA_ERR_WORKSPACE": 5, "GQA_ERR_HIP": 6}
+    for name, value in codes.items():
+        assert f"{name} = {value}" in text, name
+        assert getattr(B, name) == value
+    assert "GQA_DTYPE_F32 = 0" in text and "GQA_DTYPE_BF16 = 1" in text
+    assert B.GQA_ERR_ALIAS == 7 and "GQA_ERR_ALIAS = 7" in text
+
+
+def test_decode_workspace_bound_covers_every_grouping(lib):
+    for (Bn, Tkv, Hq, d) in [(64, 8192, 32, 128), (1, 131072, 32, 128), (3, 1000, 40, 64),
+                             (5, 300, 7, 128)]:
+        bound = lib.gqa_attn_decode_workspace_bytes(Bn, Tkv, Hq, d)
+        exact = [lib.gqa_attn_decode_workspace_bytes_hkv(Bn, Tkv, Hq, h, d)
+                 for h in range(1, Hq + 1) if Hq % h == 0]
+        assert bound == max(exact) and all(e > 0 for e in exact)
+    assert lib.gqa_attn_decode_workspace_bytes(0, 8, 8, 128) == 0
+    assert lib.gqa_attn_decode_workspace_bytes(1, 8, 8, -1) == 0
+
+
+def test_scale_default_and_invalid(lib):
+    # GQA_SCALE_DEFAULT passes validation (a later check fails instead); a negative or infinite
+    # scale is a shape error
+    assert pre(lib, scale=B.GQA_SCALE_DEFAULT, o=Q + 64) == B.GQA_ERR_ALIAS
+    assert pre(lib, scale=-0.1) == B.GQA_ERR_SHAPE
+    assert pre(lib, scale=float("inf")) == B.GQA_ERR_SHAPE
 
 
 def test_single_hip_runtime_in_process():
@@ -81,7 +134,7 @@ def test_window_and_ragged_validation(lib):
     assert prew(dt=F32, d=16) == B.GQA_ERR_UNSUPPORTED     # windows are bf16 only
     assert lib.gqa_attn_prefill_window(Q, K, V, O, 1, 9, 8, 8, 2, 128, 0.1, 4, 0, None, 0, BF16,
                                        None) == B.GQA_ERR_SHAPE   # causal needs Tq <= Tkv
-    need = lib.gqa_attn_decode_workspace_bytes(4, 1024, 32, 8, 128)
+    need = lib.gqa_attn_decode_workspace_bytes_hkv(4, 1024, 32, 8, 128)
 
     def rag(window=0, n_sink=0, dt=BF16, d=128, lens=W + 4096, ws=W, wsb=need, Tmax=1024):
         return lib.gqa_attn_decode_ragged(Q, K, V, O, 4, Tmax, 32, 8, d, 0.1, lens, window,
@@ -106,7 +159,7 @@ def test_extended_options_validation(lib):
     assert pex(Opt(0, 0, T, T + 4096, 8, None), dt=F32, d=16) == B.GQA_ERR_UNSUPPORTED
     assert pex(Opt(3, 0, None, None, 0, None), causal=0) == B.GQA_ERR_SHAPE  # windows are causal
     assert pex(Opt(-1, 0, None, None, 0, None)) == B.GQA_ERR_SHAPE
-    need = lib.gqa_attn_decode_workspace_bytes(4, 1024, 32, 8, 128)
+    need = lib.gqa_attn_decode_workspace_bytes_hkv(4, 1024, 32, 8, 128)
 
     def dex(opt, Tmax=1024):
         return lib.gqa_attn_decode_ex(Q, K, V, O, 4, Tmax, 32, 8, 128, 0.1, None,
@@ -185,9 +238,9 @@ def test_backward_validation(lib):
 
 
 def test_decode_validation(lib):
-    need = lib.gqa_attn_decode_workspace_bytes(4, 1024, 32, 8, 128)
+    need = lib.gqa_attn_decode_workspace_bytes_hkv(4, 1024, 32, 8, 128)
     assert need > 0 and need % 16 == 0
-    assert lib.gqa_attn_decode_workspace_bytes(4, 1024, 32, 5, 128) == 0
+    assert lib.gqa_attn_decode_workspace_bytes_hkv(4, 1024, 32, 5, 128) == 0
 
     def dec(q=Q, k=K, v=V, o=O, Bn=4, Tkv=1024, Hq=32, Hkv=8, d=128, ws=W, wsb=need, dt=BF16):
         return lib.gqa_attn_decode(q, k, v, o, Bn, Tkv, Hq, Hkv, d, 0.1, 0, ws, wsb, dt, None)

@@ -66,7 +66,7 @@ def test_bf16_gva_packed_vs_oracle(gqa, orc):
     k = workloads.randn_bf16((1, tot, 4, 64), 145)
     v = workloads.randn_bf16((1, tot, 8, 64), 146)
     out = gqa.gqa_attn_prefill_gva(to_dev(q), to_dev(k), to_dev(v), causal=True,
-                                   cu_seqlens=to_dev(cu))
+                                   cu_seqlens=to_dev(cu), max_seqlen=max(lens))
     torch.cuda.synchronize()
     ref = orc.attention_gva(host_view(q), host_view(k), host_view(v), causal=True, cu_seqlens=cu)
     assert_bf16_close(to_f64(out), ref, what="packed gva")

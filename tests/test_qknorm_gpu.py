@@ -78,7 +78,8 @@ def test_bf16_prefill_qknorm_packed_window_vs_oracle(gqa, orc):
     tabs = workloads.rope_tables(max(lens), 128)
     out = gqa.gqa_attn_prefill_ex(to_dev(q), to_dev(k), to_dev(v), causal=True, window=W,
                                   n_sink=S, rope=tuple(to_dev(t) for t in tabs),
-                                  qk_norm=(to_dev(wq), to_dev(wk), EPS), cu_seqlens=to_dev(cu))
+                                  qk_norm=(to_dev(wq), to_dev(wk), EPS), cu_seqlens=to_dev(cu),
+                                  max_seqlen=max(lens))
     torch.cuda.synchronize()
     ref = orc.attention(host_view(q), host_view(k), host_view(v), causal=True, window=W,
                         n_sink=S, cu_seqlens=cu, rope=tabs, qk_norm=(wq, wk, EPS))
@@ -183,7 +184,7 @@ def test_bf16_prepare_keys_vs_float64(gqa, case):
         cu = to_dev(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
     got = gqa.gqa_prepare_keys(to_dev(k), rope=tuple(to_dev(t) for t in tabs) if rope else None,
                                qk_norm=(None, to_dev(wk), EPS) if norm else None, pos0=pos0,
-                               cu_seqlens=cu)
+                               cu_seqlens=cu, max_seqlen=max(lens) if lens is not None else None)
     torch.cuda.synchronize()
     ref = _ref_prepared(k, tabs, wk if norm else None, pos0, lens)
     # one rounding to bf16 of an fp32 computation: within 2^-8 of each value (+ tiny absolute)

@@ -68,7 +68,7 @@ def test_bf16_prefill_rope_packed_vs_oracle(gqa, orc):
     v = workloads.randn_bf16((1, tot, 4, 128), 116)
     host_t, dev_t = _tables(max(lens), 128)
     out = gqa.gqa_attn_prefill_ex(to_dev(q), to_dev(k), to_dev(v), causal=True, rope=dev_t,
-                                  cu_seqlens=to_dev(cu))
+                                  cu_seqlens=to_dev(cu), max_seqlen=max(lens))
     torch.cuda.synchronize()
     ref = orc.attention(host_view(q), host_view(k), host_view(v), causal=True, cu_seqlens=cu,
                         rope=host_t)

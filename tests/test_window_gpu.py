@@ -65,7 +65,7 @@ def test_bf16_prefill_window_packed_vs_oracle(gqa, orc):
     k = workloads.randn_bf16((1, tot, 2, 128), 85)
     v = workloads.randn_bf16((1, tot, 2, 128), 86)
     out = gqa.gqa_attn_prefill_window(to_dev(q), to_dev(k), to_dev(v), window=W, n_sink=S,
-                                      cu_seqlens=to_dev(cu))
+                                      cu_seqlens=to_dev(cu), max_seqlen=max(lens))
     torch.cuda.synchronize()
     ref = orc.attention(host_view(q), host_view(k), host_view(v), causal=True, window=W,
                         n_sink=S, cu_seqlens=cu)
@@ -94,6 +94,10 @@ DECODE_RAGGED_CASES = [
     (3, 700, 8, 2, 128, (700, 33, 400), 65, 70),
     (2, 8192, 16, 1, 64, (5000, 8192), 1000, 16),   # cache splits past the visible entries
     (2, 5000, 40, 2, 128, (4321, 77), 300, 2),       # two chunks of query heads
+    # empty caches (length 0: the zero row), with one split per sequence and with several
+    (4, 600, 32, 8, 128, (0, 1, 0, 600), 0, 0),
+    (2, 9000, 16, 2, 64, (0, 8999), 0, 0),
+    (3, 4000, 32, 8, 128, (0, 3000, 17), 512, 3),
 ]
 
 
