@@ -1,15 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark: grouped-query attention forward on one MI355X.
 
-One step = one causal prefill forward of the Llama-3-8B-shaped workload (B=1, T=4096, 32 query /
-8 key-value heads, d=128, bf16), inputs already resident in HBM. Prints ONE JSON line with the
-prefill throughput (TFLOP/s of algorithmic work: 4*d flops per unmasked (query, key, head)
-triple), its fraction of the bf16 matrix-core peak, the batched-decode KV-stream bandwidth
-(B=64, 8192-entry cache) as a secondary figure, and the fp64 CPU oracle timed on a bounded
-sample of the same prefill workload.
+One step = one causal prefill forward of the packed long-context workload (four sequences of
+16384 / 8192 / 4096 / 1024 tokens, 64 query / 8 key-value heads, d = 128, bf16), inputs already
+resident in HBM: the largest configuration that fits one GPU. Prints ONE JSON line with its
+throughput (TFLOP/s of algorithmic work: 4*d flops per unmasked (query, key, head) triple) and
+fraction of the bf16 matrix-core peak, the other benchmark workloads as secondary legs with
+their own roofline records (the 4096-token 32/8 prefill, the 8 x 2048-token multi-query prefill
+with 5 % of the query rows scaled x30, and the 64-sequence decode against 8192-entry caches,
+whose key/value stream is measured against the HBM peak), and the fp64 CPU oracle timed on a
+bounded sample of the packed workload.
 
-  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-decode]
-                  [--only prefill|decode|mqa|varlen] [--all]
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-secondary]
+                  [--only varlen|prefill|decode|mqa|...] [--all]
 """
 from __future__ import annotations
 
@@ -31,6 +34,10 @@ CSRC = os.path.join(ROOT, "grouped_query_softmax_amd", "csrc")
 TRAFFIC = {
     "prefill": (os.path.join(ROOT, "profiles", "prefill_bf16_llama3_8b_T4096_traffic.json"),
                 ("prefill_bf16.hip", "common.hpp")),
+    "varlen": (os.path.join(ROOT, "profiles", "prefill_bf16_varlen_16k_8k_4k_1k_traffic.json"),
+               ("prefill_bf16.hip", "common.hpp")),
+    "mqa": (os.path.join(ROOT, "profiles", "prefill_bf16_mqa_B8_T2048_traffic.json"),
+            ("prefill_bf16.hip", "common.hpp")),
     "decode": (os.path.join(ROOT, "profiles", "decode_bf16_B64_kv8192_traffic.json"),
                ("decode.hip", "common.hpp")),
     "gva": (os.path.join(ROOT, "profiles", "gva_prefill_B2_T4096_H16_HV32_d64_traffic.json"),
@@ -101,13 +108,13 @@ def device_inputs(w, torch, seed_base):
     return q, k, v, cu
 
 
-def time_launches(fn, steps, warmup, torch):
+def time_launches(fn, steps, warmup, torch, per_launch=50):
     """Times `steps` launches on the stream the kernels are launched on (torch's current stream,
     which the binding passes to the library): after `warmup` untimed launches, exactly `steps`
     back-to-back launches between two synchronizations, bracketed by one pair of HIP events on
-    that stream. Returns (average ms per launch, wall-clock s of the timed region). Back to back
-    the chip runs at its sustained (lower) clock; a kernel trace of the same command averages
-    the same duration per launch."""
+    that stream. Then, untimed for the average, `per_launch` more launches each bracketed by its
+    own event pair, for the median and minimum launch time. Returns (average ms per launch of
+    the timed region, wall-clock s of the timed region, median ms, min ms)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -119,7 +126,17 @@ def time_launches(fn, steps, warmup, torch):
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return start.elapsed_time(end) / steps, wall
+    avg = start.elapsed_time(end) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(per_launch)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    each = sorted(a.elapsed_time(b) for a, b in evs)
+    median = each[len(each) // 2] if each else avg
+    return avg, wall, median, (each[0] if each else avg)
 
 
 def bench_prefill(gqa, w, steps, warmup, torch, seed, rope=False, qk_norm=False,
@@ -158,9 +175,10 @@ def bench_prefill(gqa, w, steps, warmup, torch, seed, rope=False, qk_norm=False,
         else:
             gqa.gqa_attn_prefill(q, k, v, causal=w.causal, cu_seqlens=cu, max_seqlen=msl, out=out)
 
-    avg, wall = time_launches(step, steps, warmup, torch)
+    avg, wall, med, mn = time_launches(step, steps, warmup, torch)
     flops = prefill_flops(w)
     res = {"workload": w.name, "flops_per_launch": flops, "avg_ms": avg,
+           "median_ms": med, "min_ms": mn,
            "tflops": flops / (avg * 1e-3) / 1e12, "wall_s": wall}
     return res, (q, k, v, cu)
 
@@ -180,7 +198,7 @@ def bench_backward(gqa, w, steps, warmup, torch, seed):
     def step():
         gqa.gqa_attn_backward(q, k, v, out, dout, lse, causal=w.causal, workspace=ws)
 
-    avg, wall = time_launches(step, steps, warmup, torch)
+    avg, wall, _, _ = time_launches(step, steps, warmup, torch, per_launch=0)
     flops = prefill_flops(w) * 10 // 4
     return {"workload": w.name + "+backward", "flops_per_launch": flops, "avg_ms": avg,
             "tflops": flops / (avg * 1e-3) / 1e12,
@@ -202,7 +220,7 @@ def bench_gva(gqa, w, steps, warmup, torch, seed):
     def step():
         gqa.gqa_attn_prefill_gva(q, k, v, causal=w.causal, out=out)
 
-    avg, wall = time_launches(step, steps, warmup, torch)
+    avg, wall, _, _ = time_launches(step, steps, warmup, torch, per_launch=0)
     flops = 2 * w.d * (H + HV) * w.B * visible_pairs(w.Tq, w.Tkv, w.causal)
     return {"workload": w.name, "flops_per_launch": flops, "avg_ms": avg,
             "tflops": flops / (avg * 1e-3) / 1e12,
@@ -232,12 +250,15 @@ def bench_decode(gqa, w, steps, warmup, torch, seed):
         else:
             gqa.gqa_attn_decode(q, k, v, workspace=ws, out=out)
 
-    avg, wall = time_launches(step, steps, warmup, torch)
+    avg, wall, med, mn = time_launches(step, steps, warmup, torch)
     entries = sum(w.cache_lens) if w.cache_lens is not None else w.B * w.Tkv
     kv_bytes = 2 * entries * w.Hkv * w.d * 2
     qo_bytes = 2 * w.B * w.Hq * w.d * 2
     gbs = (kv_bytes + qo_bytes) / (avg * 1e-3) / 1e9
     return {"workload": w.name, "bytes_per_launch": kv_bytes + qo_bytes, "avg_ms": avg,
+            "median_ms": med, "min_ms": mn,
+            "splits": gqa.gqa_attn_decode_workspace_bytes_hkv(w.B, w.Tkv, w.Hq, w.Hkv, w.d)
+            // (w.B * w.Hq * (w.d + 2) * 4),
             "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "wall_s": wall,
             "traffic": traffic_for("decode") if w.cache_lens is None else None}
 
@@ -254,7 +275,8 @@ def bench_fold(gqa, steps, warmup, torch):
     gen.manual_seed(9000)
     src = torch.randn(B, T, H, d, generator=gen, device="cuda").to(torch.bfloat16)
     out = torch.empty(B, T, g, d, dtype=torch.bfloat16, device="cuda")
-    avg, wall = time_launches(lambda: gqa.gqa_fold_kv(src, g, out=out), steps, warmup, torch)
+    avg, wall, _, _ = time_launches(lambda: gqa.gqa_fold_kv(src, g, out=out), steps, warmup,
+                                    torch, per_launch=0)
     nbytes = (B * T * H * d + B * T * g * d) * 2
     gbs = nbytes / (avg * 1e-3) / 1e9
     return {"metric": "fold_kv GB/s (read + write, % HBM peak)", "value": gbs, "unit": "GB/s",
@@ -278,7 +300,7 @@ def bench_copy(steps, warmup, torch):
     so the HBM byte counters it reports calibrate those of the attention kernels."""
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    avg, wall = time_launches(lambda: dst.copy_(src), steps, warmup, torch)
+    avg, wall, _, _ = time_launches(lambda: dst.copy_(src), steps, warmup, torch, per_launch=0)
     gbs = 2 * COPY_BYTES / (avg * 1e-3) / 1e9
     return {"metric": "device copy GB/s (read + write)", "value": gbs, "unit": "GB/s",
             "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": avg,
@@ -288,19 +310,27 @@ def bench_copy(steps, warmup, torch):
 
 def cpu_baseline(w, tensors, torch, target_s=15.0):
     """fp64 oracle on a bounded sample of the prefill workload: the first `ng` key/value heads
-    with their G query heads each (the same grouping; every query position, every key)."""
-    import numpy as np
-
+    with their G query heads each (the same grouping; every query position, every key) of one
+    item -- for a packed workload its 4096-token sequence, whose causal rows span the same
+    lengths as the others' (oracle time, like the kernel's work, grows as T^2)."""
     import oracle
     import workloads
     orc = oracle.default()
     q, k, v, _ = tensors
     G = w.Hq // w.Hkv
+    if w.seqlens:
+        s = list(w.seqlens).index(4096) if 4096 in w.seqlens else 0
+        a = int(w.cu_seqlens[s])
+        T = w.seqlens[s]
+        rows, what = slice(a, a + T), f"sequence {s} ({T} tokens)"
+    else:
+        T = w.Tq
+        rows, what = slice(0, T), f"all {T} positions"
 
     def run(ng):
-        qs = workloads.bf16_bits(q[:, :, :G * ng].contiguous().cpu())
-        ks = workloads.bf16_bits(k[:, :, :ng].contiguous().cpu())
-        vs = workloads.bf16_bits(v[:, :, :ng].contiguous().cpu())
+        qs = workloads.bf16_bits(q[:1, rows, :G * ng].contiguous().cpu())
+        ks = workloads.bf16_bits(k[:1, rows, :ng].contiguous().cpu())
+        vs = workloads.bf16_bits(v[:1, rows, :ng].contiguous().cpu())
         t0 = time.perf_counter()
         orc.attention(qs, ks, vs, causal=w.causal)
         return time.perf_counter() - t0
@@ -309,11 +339,11 @@ def cpu_baseline(w, tensors, torch, target_s=15.0):
     t1 = run(1)
     ng = max(1, min(w.Hkv, int(target_s / max(t1, 1e-3))))
     t = t1 if ng == 1 else run(ng)
-    flops = 4 * w.d * (G * ng) * w.B * visible_pairs(w.Tq, w.Tkv, w.causal)
+    flops = 4 * w.d * (G * ng) * visible_pairs(T, T, w.causal)
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
             "kind": "oracle",
-            "sample": f"{w.name}: key/value heads 0..{ng - 1} with their {G * ng} query heads "
-                      f"(of {w.Hq}), all {w.Tq} positions, causal; {flops / 1e9:.1f} GFLOP in "
+            "sample": f"{w.name}: {what} of item 0, key/value heads 0..{ng - 1} with their "
+                      f"{G * ng} query heads (of {w.Hq}), causal; {flops / 1e9:.1f} GFLOP in "
                       f"{t:.1f} s, fp64"}
 
 
@@ -329,21 +359,61 @@ def traffic_for(which):
     return rec.get("hbm_bytes_per_launch")
 
 
+KERNEL_PLAIN = "prefill_pp_kernel<128, 128, false, false, false>"
+
+
+def mfma_roofline(res, kernel, traffic_key=None):
+    """Roofline record of an MFMA-bound leg: algorithmic flops per launch over the measured
+    average launch time, against the bf16 dense peak."""
+    sha_key = traffic_key if traffic_key in TRAFFIC else "prefill"
+    return {"bound": "mfma", "achieved": res["tflops"], "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": res["tflops"] / PEAK_BF16_TFLOPS,
+            "traffic": traffic_for(traffic_key) if traffic_key else None, "kernel": kernel,
+            "flops_per_launch": res["flops_per_launch"], "avg_launch_ms": res["avg_ms"],
+            "median_launch_ms": res.get("median_ms"), "min_launch_ms": res.get("min_ms"),
+            "kernel_source_sha": kernel_source_sha(sha_key)}
+
+
+def hbm_roofline(res, kernel):
+    return {"bound": "hbm", "achieved": res["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": res["frac_hbm"], "traffic": res.get("traffic"), "kernel": kernel,
+            "bytes_per_launch": res["bytes_per_launch"], "avg_launch_ms": res["avg_ms"],
+            "median_launch_ms": res.get("median_ms"), "min_launch_ms": res.get("min_ms"),
+            "kernel_source_sha": kernel_source_sha("decode")}
+
+
+def prefill_config(w):
+    config = {"workload": w.name, "B": w.B, "T": w.Tq, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
+              "causal": w.causal, "global_batch": w.B, "seq_len": w.Tq,
+              "parallelism": "single-gpu"}
+    if w.seqlens:
+        config.update({"seqlens": list(w.seqlens), "global_batch": len(w.seqlens),
+                       "seq_len": max(w.seqlens), "total_tokens": sum(w.seqlens)})
+    if w.peaked_frac > 0:
+        config.update({"peaked_rows": w.peaked_frac, "peaked_scale": w.peaked_scale})
+    if w.window > 0:
+        config["window"], config["n_sink"] = w.window, w.n_sink
+    return config
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "mqa", "varlen", "window",
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="time only the headline workload")
+    ap.add_argument("--only", choices=["varlen", "prefill", "decode", "mqa", "window",
                                        "ragged", "rope", "qknorm", "backward", "gva",
                                        "fold", "copy"],
                     default=None,
-                    help="time a single workload (for profiling); still prints one JSON line. "
-                         "'copy' times a plain 1 GiB device copy, the calibration kernel for "
-                         "the HBM byte counters; 'fold' times gqa_fold_kv")
-    ap.add_argument("--all", action="store_true", help="also time the MQA and varlen prefills")
+                    help="time a single workload as the line's headline (for profiling); "
+                         "'copy' times a plain 1 GiB device copy, the calibration kernel for the "
+                         "HBM byte counters; 'fold' times gqa_fold_kv")
+    ap.add_argument("--all", action="store_true",
+                    help="also time the variant legs (window, ragged decode, RoPE, QK-norm, "
+                         "backward, grouped values)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -370,140 +440,103 @@ def main():
         print(json.dumps(res), flush=True)
         return
 
-    w = workloads.LLAMA_PREFILL
-    extra = {}
-    pre = None
-    tensors = None
-    if args.only in (None, "prefill"):
-        log(f"prefill {w.name}: {args.warmup} warmup + {args.steps} timed launches")
-        pre, tensors = bench_prefill(gqa, w, args.steps, args.warmup, torch, 2000)
-        log(f"prefill: {pre['avg_ms'] * 1e3:.1f} us avg, {pre['tflops']:.1f} TFLOP/s")
-    if args.only == "mqa" or args.all:
-        m, _ = bench_prefill(gqa, workloads.MQA_PREFILL, args.steps, args.warmup, torch, 4000)
-        m["frac_mfma"] = m["tflops"] / PEAK_BF16_TFLOPS
-        extra["mqa_prefill"] = m
-        log(f"mqa: {m['avg_ms'] * 1e3:.1f} us, {m['tflops']:.1f} TFLOP/s")
-    if args.only == "varlen" or args.all:
-        vl, _ = bench_prefill(gqa, workloads.VARLEN_PREFILL, max(5, args.steps // 5),
-                              args.warmup, torch, 5000)
-        vl["frac_mfma"] = vl["tflops"] / PEAK_BF16_TFLOPS
-        extra["varlen_prefill"] = vl
-        log(f"varlen: {vl['avg_ms']:.3f} ms, {vl['tflops']:.1f} TFLOP/s")
-    if args.only == "window" or args.all:
-        wp, _ = bench_prefill(gqa, workloads.WINDOW_PREFILL, args.steps, args.warmup, torch, 6000)
-        wp["frac_mfma"] = wp["tflops"] / PEAK_BF16_TFLOPS
-        extra["window_prefill"] = wp
-        log(f"window prefill: {wp['avg_ms'] * 1e3:.1f} us, {wp['tflops']:.1f} TFLOP/s")
-    if args.only == "rope" or args.all:
-        rp, _ = bench_prefill(gqa, workloads.LLAMA_PREFILL, args.steps, args.warmup, torch, 2000,
-                              rope=True)
-        rp["frac_mfma"] = rp["tflops"] / PEAK_BF16_TFLOPS
-        rp["workload"] = workloads.LLAMA_PREFILL.name + "+rope"
-        extra["rope_prefill"] = rp
-        log(f"rope prefill: {rp['avg_ms'] * 1e3:.1f} us, {rp['tflops']:.1f} TFLOP/s")
-        pp, _ = bench_prefill(gqa, workloads.LLAMA_PREFILL, args.steps, args.warmup, torch, 2000,
-                              rope=True, prepared=True)
-        pp["frac_mfma"] = pp["tflops"] / PEAK_BF16_TFLOPS
-        pp["workload"] = workloads.LLAMA_PREFILL.name + "+rope, keys prepared"
-        extra["rope_prefill_keys_prepared"] = pp
-        log(f"rope prefill, keys prepared: {pp['avg_ms'] * 1e3:.1f} us, "
-            f"{pp['tflops']:.1f} TFLOP/s")
-    if args.only == "qknorm" or args.all:
-        qn, _ = bench_prefill(gqa, workloads.LLAMA_PREFILL, args.steps, args.warmup, torch, 2000,
-                              rope=True, qk_norm=True)
-        qn["frac_mfma"] = qn["tflops"] / PEAK_BF16_TFLOPS
-        qn["workload"] = workloads.LLAMA_PREFILL.name + "+qknorm+rope"
-        extra["qknorm_rope_prefill"] = qn
-        log(f"qk-norm + rope prefill: {qn['avg_ms'] * 1e3:.1f} us, {qn['tflops']:.1f} TFLOP/s")
-        qp, _ = bench_prefill(gqa, workloads.LLAMA_PREFILL, args.steps, args.warmup, torch, 2000,
-                              rope=True, qk_norm=True, prepared=True)
-        qp["frac_mfma"] = qp["tflops"] / PEAK_BF16_TFLOPS
-        qp["workload"] = workloads.LLAMA_PREFILL.name + "+qknorm+rope, keys prepared"
-        extra["qknorm_rope_prefill_keys_prepared"] = qp
-        log(f"qk-norm + rope prefill, keys prepared: {qp['avg_ms'] * 1e3:.1f} us, "
-            f"{qp['tflops']:.1f} TFLOP/s")
-    if args.only == "backward" or args.all:
-        bw = bench_backward(gqa, workloads.LLAMA_PREFILL, args.steps, args.warmup, torch, 2000)
-        extra["backward"] = bw
-        log(f"backward: {bw['avg_ms'] * 1e3:.1f} us, {bw['tflops']:.1f} TFLOP/s")
-    if args.only == "gva" or args.all:
-        gv = bench_gva(gqa, workloads.GVA_PREFILL, args.steps, args.warmup, torch, 8000)
-        extra["gva_prefill"] = gv
-        log(f"gva prefill: {gv['avg_ms'] * 1e3:.1f} us, {gv['tflops']:.1f} TFLOP/s")
-    if args.only == "ragged" or args.all:
-        rd = bench_decode(gqa, workloads.RAGGED_DECODE, args.steps, args.warmup, torch, 7000)
-        extra["ragged_decode"] = rd
-        log(f"ragged decode: {rd['avg_ms'] * 1e3:.1f} us, {rd['gbs']:.0f} GB/s")
-    if args.only == "decode" or (args.only is None and not args.no_decode):
-        dec = bench_decode(gqa, workloads.DECODE, args.steps, args.warmup, torch, 3000)
-        extra["decode"] = dec
-        log(f"decode: {dec['avg_ms'] * 1e3:.1f} us, {dec['gbs']:.0f} GB/s")
-    sha = kernel_source_sha("prefill")
-    metric = "GQA prefill TFLOPS (% MFMA peak); decode KV GB/s (% HBM peak)"
-    if pre is None and args.only in ("mqa", "varlen", "window", "rope", "qknorm", "backward",
-                                     "gva"):
-        key, w = {"gva": ("gva_prefill", workloads.GVA_PREFILL),
-                  "qknorm": ("qknorm_rope_prefill", workloads.LLAMA_PREFILL),
-                  "mqa": ("mqa_prefill", workloads.MQA_PREFILL),
-                  "varlen": ("varlen_prefill", workloads.VARLEN_PREFILL),
-                  "window": ("window_prefill", workloads.WINDOW_PREFILL),
-                  "rope": ("rope_prefill", workloads.LLAMA_PREFILL),
-                  "backward": ("backward", workloads.LLAMA_PREFILL)}[args.only]
-        pre = extra.pop(key)
-    if pre is not None:
-        value, unit = pre["tflops"], "TFLOP/s"
-        ms_per_step = pre["avg_ms"]
-        traffic = None
-        if args.only in (None, "prefill"):
-            traffic = traffic_for("prefill")
-        elif args.only == "gva":
-            traffic = traffic_for("gva")
-        roofline = {"bound": "mfma", "achieved": pre["tflops"], "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": pre["tflops"] / PEAK_BF16_TFLOPS,
-                    "traffic": traffic,
-                    "kernel": {"backward": "bwd_rowdot + bwd_dkdv_kernel<128> + bwd_dq_kernel<128>",
-                               # <DQ, DV, ROPE, NORM, KPROC>: the fused variants process
-                               # the keys in the kernel
-                               "rope": "prefill_pp_kernel<128, 128, true, false, true>",
-                               "qknorm": "prefill_pp_kernel<128, 128, true, true, true>",
-                               "gva": "prefill_pp_kernel<64, 128, false, false, false>"}.get(
-                                   args.only, "prefill_pp_kernel<128, 128, false, false, false>"),
-                    "flops_per_launch": pre["flops_per_launch"],
-                    "avg_launch_ms": pre["avg_ms"], "kernel_source_sha": sha}
-        config = {"workload": w.name, "B": w.B, "T": w.Tq, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
-                  "causal": w.causal, "global_batch": w.B, "seq_len": w.Tq,
-                  "parallelism": "single-gpu"}
-        if w.seqlens:
-            config["seqlens"] = list(w.seqlens)
-        if w.window > 0:
-            config["window"], config["n_sink"] = w.window, w.n_sink
-        if args.only == "gva":
-            config.update({"H": w.Hkv, "HV": w.Hq})
-            del config["Hq"], config["Hkv"]
+    S, Wu = args.steps, args.warmup
+    headline = args.only or "varlen"
+    legs = {}      # name -> (result, roofline, config)
+    tensors = {}
+
+    def run_prefill(name, w, seed, kernel=KERNEL_PLAIN, traffic_key=None, **kw):
+        log(f"{name} {w.name}: {Wu} warmup + {S} timed launches")
+        res, t = bench_prefill(gqa, w, S, Wu, torch, seed, **kw)
+        tensors[name] = (w, t)
+        log(f"{name}: {res['avg_ms'] * 1e3:.1f} us avg (median {res['median_ms'] * 1e3:.1f}, "
+            f"min {res['min_ms'] * 1e3:.1f}), {res['tflops']:.1f} TFLOP/s")
+        legs[name] = (res, mfma_roofline(res, kernel, traffic_key), prefill_config(w))
+
+    def run_decode(name, w, seed):
+        log(f"{name} {w.name}: {Wu} warmup + {S} timed launches")
+        res = bench_decode(gqa, w, S, Wu, torch, seed)
+        log(f"{name}: {res['avg_ms'] * 1e3:.1f} us, {res['gbs']:.0f} GB/s")
+        cfg = {"workload": w.name, "B": w.B, "Tkv": w.Tkv, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
+               "parallelism": "single-gpu"}
+        if w.cache_lens is not None:
+            cfg["cache_lens"] = "uniform 1..Tkv (seeded)"
+        kern = "decode_split_kernel<128, 1>"
+        if res["splits"] > 1:
+            kern += " + decode_combine_kernel<128>"
+        legs[name] = (res, hbm_roofline(res, kern), cfg)
+
+    plan = []
+    if headline == "varlen" or not args.no_secondary and args.only is None:
+        plan.append("varlen")
+    if args.only is None and not args.no_secondary:
+        plan += ["prefill", "mqa", "decode"]
+    elif args.only not in (None, "varlen"):
+        plan.append(args.only)
+    if args.all:
+        plan += [x for x in ("window", "ragged", "rope", "qknorm", "backward", "gva")
+                 if x not in plan]
+
+    for name in plan:
+        if name == "varlen":
+            run_prefill("varlen", workloads.VARLEN_PREFILL, 5000, traffic_key="varlen")
+        elif name == "prefill":
+            run_prefill("prefill", workloads.LLAMA_PREFILL, 2000, traffic_key="prefill")
+        elif name == "mqa":
+            run_prefill("mqa", workloads.MQA_PREFILL, 4000, traffic_key="mqa")
+        elif name == "window":
+            run_prefill("window", workloads.WINDOW_PREFILL, 6000)
+        elif name == "rope":
+            run_prefill("rope", workloads.LLAMA_PREFILL, 2000, rope=True,
+                        kernel="prefill_pp_kernel<128, 128, true, false, true>")
+            run_prefill("rope_keys_prepared", workloads.LLAMA_PREFILL, 2000, rope=True,
+                        prepared=True,
+                        kernel="prepare_keys_kernel + prefill_pp_kernel<128, 128, true, false, "
+                               "false>")
+        elif name == "qknorm":
+            run_prefill("qknorm", workloads.LLAMA_PREFILL, 2000, rope=True, qk_norm=True,
+                        kernel="prefill_pp_kernel<128, 128, true, true, true>")
+            run_prefill("qknorm_keys_prepared", workloads.LLAMA_PREFILL, 2000, rope=True,
+                        qk_norm=True, prepared=True,
+                        kernel="prepare_keys_kernel + prefill_pp_kernel<128, 128, true, true, "
+                               "false>")
+        elif name == "backward":
+            bw = bench_backward(gqa, workloads.LLAMA_PREFILL, S, Wu, torch, 2000)
+            log(f"backward: {bw['avg_ms'] * 1e3:.1f} us, {bw['tflops']:.1f} TFLOP/s")
+            legs["backward"] = (bw, mfma_roofline(
+                bw, "bwd_rowdot + bwd_dkdv_kernel<128> + bwd_dq_kernel<128>"),
+                prefill_config(workloads.LLAMA_PREFILL))
+        elif name == "gva":
+            gv = bench_gva(gqa, workloads.GVA_PREFILL, S, Wu, torch, 8000)
+            log(f"gva prefill: {gv['avg_ms'] * 1e3:.1f} us, {gv['tflops']:.1f} TFLOP/s")
+            cfg = prefill_config(workloads.GVA_PREFILL)
+            cfg.update({"H": cfg.pop("Hkv"), "HV": cfg.pop("Hq")})
+            legs["gva"] = (gv, mfma_roofline(gv, "prefill_pp_kernel<64, 128, false, false, "
+                                                 "false>", "gva"), cfg)
+        elif name == "decode":
+            run_decode("decode", workloads.DECODE, 3000)
+        elif name == "ragged":
+            run_decode("ragged", workloads.RAGGED_DECODE, 7000)
+
+    head_key = {"prefill": "prefill"}.get(headline, headline)
+    res, roofline, config = legs.pop(head_key)
+    if "tflops" in res:
+        value, unit = res["tflops"], "TFLOP/s"
     else:
-        dw = workloads.RAGGED_DECODE if args.only == "ragged" else workloads.DECODE
-        dec = extra.pop("ragged_decode" if args.only == "ragged" else "decode")
-        value, unit = dec["gbs"], "GB/s"
-        ms_per_step = dec["avg_ms"]
-        roofline = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": dec["frac_hbm"], "traffic": dec["traffic"],
-                    "kernel": "decode_split_kernel<128>", "bytes_per_launch":
-                    dec["bytes_per_launch"], "avg_launch_ms": dec["avg_ms"],
-                    "kernel_source_sha": kernel_source_sha("decode")}
-        config = {"workload": dw.name, "B": dw.B, "Tkv": dw.Tkv, "Hq": dw.Hq, "Hkv": dw.Hkv,
-                  "d": dw.d, "parallelism": "single-gpu"}
-    line = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-            "data": "synthetic (seeded N(0,1) on device)", "config": config,
-            "roofline": roofline}
-    if extra:
-        line["secondary"] = extra
-    if not args.no_cpu_baseline and tensors is not None:
+        value, unit = res["gbs"], "GB/s"
+    line = {"metric": "GQA prefill TFLOPS (% MFMA peak); decode KV GB/s (% HBM peak)",
+            "value": value, "unit": unit, "n_gpus": 1, "steps": S, "warmup": Wu,
+            "ms_per_step": res["avg_ms"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) on device)",
+            "config": config, "roofline": roofline}
+    if legs:
+        line["secondary"] = {name: dict(res, roofline=rf, config=cfg)
+                             for name, (res, rf, cfg) in legs.items()}
+    line["cpu_baseline"] = None
+    if not args.no_cpu_baseline and head_key in tensors:
         log("cpu baseline: fp64 oracle on a sample")
-        line["cpu_baseline"] = cpu_baseline(w, tensors, torch)
-    else:
-        line["cpu_baseline"] = None
+        w, t = tensors[head_key]
+        line["cpu_baseline"] = cpu_baseline(w, t, torch)
     print(json.dumps(line), flush=True)
 
 

@@ -24,7 +24,8 @@ def test_decode_rejects_bad_out(gqa):
     say("binding: decode out checks")
     q, k = _t(2, 1, 8, 128), _t(2, 64, 2, 128)
     for bad in (_t(2, 1, 4, 128), _t(2, 1, 8, 128, dtype=torch.float32),
-                _t(2, 8, 1, 128).transpose(1, 2)):
+                _t(2, 1, 8, 256)[..., :128]):
+        assert bad.shape != q.shape or bad.dtype != q.dtype or not bad.is_contiguous()
         with pytest.raises(ValueError):
             gqa.gqa_attn_decode(q, k, k, out=bad)
         with pytest.raises(ValueError):
@@ -38,6 +39,7 @@ def test_fold_rejects_bad_out(gqa):
     src = _t(1, 4, 8, 64)
     for bad in (_t(1, 4, 4, 64), _t(1, 4, 2, 64, dtype=torch.float32),
                 _t(1, 2, 4, 64).transpose(1, 2)):
+        assert bad.shape != (1, 4, 2, 64) or bad.dtype != src.dtype or not bad.is_contiguous()
         with pytest.raises(ValueError):
             gqa.gqa_fold_kv(src, 2, out=bad)
 
