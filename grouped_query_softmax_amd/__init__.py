@@ -11,10 +11,12 @@ from ._binding import (  # noqa: F401
     gqa_attn_backward,
     gqa_attn_decode,
     gqa_attn_decode_ex,
+    gqa_attn_decode_noalloc,
     gqa_attn_decode_ragged,
     gqa_attn_decode_workspace_bytes,
     gqa_attn_decode_workspace_bytes_hkv,
     GQA_SCALE_DEFAULT,
+    GQA_DECODE_SCRATCH_BYTES,
     gqa_attn_prefill,
     gqa_attn_prefill_ex,
     gqa_attn_prefill_gva,

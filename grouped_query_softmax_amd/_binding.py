@@ -24,6 +24,8 @@ GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP, GQA_ERR_ALIAS = 4, 5, 6, 7
 GQA_DTYPE_F32, GQA_DTYPE_BF16 = 0, 1
 # scale argument that makes the library use 1/sqrt(d)
 GQA_SCALE_DEFAULT = 0.0
+# size of the library's per-GPU decode scratch (gqa_attn_decode_noalloc)
+GQA_DECODE_SCRATCH_BYTES = 16 << 20
 
 
 class GQAError(RuntimeError):
@@ -99,6 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_attn_decode_workspace_bytes_hkv.restype = SZ
     lib.gqa_attn_decode.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, SZ, I, P]
     lib.gqa_attn_decode.restype = I
+    lib.gqa_attn_decode_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.gqa_attn_decode_noalloc.restype = I
     lib.gqa_attn_prefill_window.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, P, I, I, P]
     lib.gqa_attn_prefill_window.restype = I
     lib.gqa_attn_decode_ragged.argtypes = [P, P, P, P, I, I, I, I, I, F, P, I, I, P, SZ, I, P]
@@ -347,7 +351,7 @@ def gqa_attn_decode_workspace_bytes_hkv(B: int, Tkv: int, Hq: int, Hkv: int, d: 
     return int(_lib.gqa_attn_decode_workspace_bytes_hkv(B, Tkv, Hq, Hkv, d))
 
 
-def _decode_args(q, k_cache, v_cache, scale, workspace, out):
+def _decode_args(q, k_cache, v_cache, scale, workspace, out, workspace_needed=True):
     q, k, v = _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache")
     if q.dim() != 4 or q.shape[1] != 1 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("expected q[B,1,Hq,d] and k_cache, v_cache[B,Tkv,Hkv,d]")
@@ -360,7 +364,7 @@ def _decode_args(q, k_cache, v_cache, scale, workspace, out):
     if scale is None:
         scale = GQA_SCALE_DEFAULT
     ws_ptr, ws_bytes = None, 0
-    if q.dtype == torch.bfloat16:
+    if q.dtype == torch.bfloat16 and workspace_needed:
         need = gqa_attn_decode_workspace_bytes_hkv(B, Tkv, Hq, Hkv, d)
         if workspace is None:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -387,6 +391,20 @@ def gqa_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
                               int(bool(causal)), ws_ptr, ws_bytes, _dtype_code(q),
                               _stream(stream))
     _check(rc, "gqa_attn_decode")
+    return out
+
+
+def gqa_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            scale: Optional[float] = None, causal: bool = False,
+                            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """:func:`gqa_attn_decode` with the split partials in the library's fixed per-GPU scratch
+    (no workspace; the call allocates nothing when ``out`` is given). Calls that overlap on one
+    GPU share that scratch and race."""
+    q, k, v, out, dims, _, _, _ = _decode_args(q, k_cache, v_cache, scale, None, out,
+                                               workspace_needed=False)
+    rc = _lib.gqa_attn_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      *dims, int(bool(causal)), _dtype_code(q), _stream(stream))
+    _check(rc, "gqa_attn_decode_noalloc")
     return out
 
 

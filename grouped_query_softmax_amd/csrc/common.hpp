@@ -273,5 +273,9 @@ hipError_t launch_fold(const void* src, void* dst, int64_t BT, int H, int g, int
 int decode_num_splits(int B, int Tkv, int Hq, int Hkv, int d);
 int decode_split_len(int Tkv, int nsplit);
 size_t decode_workspace_bytes(int B, int Tkv, int Hq, int Hkv, int d);
+// The library's own decode scratch (for callers that cannot allocate): its size, and its device
+// address on the current device (taken once per device).
+constexpr size_t kDecodeScratchBytes = size_t{16} << 20;
+hipError_t decode_scratch(void** ptr);
 
 }  // namespace gqa

@@ -34,10 +34,26 @@
 //   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
+
+// Scratch for callers that cannot allocate: the fp32 split partials of gqa_attn_decode_noalloc
+// live in this fixed device array (one copy per GPU, for the life of the process) instead of a
+// caller workspace. Every call on a GPU shares that GPU's copy, so calls that overlap in time on
+// one GPU race. Nothing in it needs clearing between calls: each split writes every partial the
+// combine pass reads.
+static __device__ __align__(256) char scratch[gqa::kDecodeScratchBytes];
 
 namespace gqa {
 namespace {
+
+// The device address of `scratch` on each GPU, taken once per device with that device current
+// (host code must never pass the array's own name to a kernel: on the host it stands for a
+// host-side shadow, not device memory).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -455,6 +471,22 @@ int decode_num_splits(int B, int Tkv, int Hq, int Hkv, int d) {
 size_t decode_workspace_bytes(int B, int Tkv, int Hq, int Hkv, int d) {
   const int64_t S = decode_num_splits(B, Tkv, Hq, Hkv, d);
   return static_cast<size_t>(static_cast<int64_t>(B) * Hq * S * (d + 2)) * sizeof(float);
+}
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {

@@ -11,6 +11,9 @@
 #include "gqa_attn.h"
 #include "common.hpp"
 
+static_assert(GQA_DECODE_SCRATCH_BYTES == gqa::kDecodeScratchBytes,
+              "the header's scratch limit is the size of the library's array");
+
 namespace {
 
 constexpr int kMaxGridYZ = 65535;
@@ -413,6 +416,26 @@ gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_c
   (void)causal;  // a single query at the last position sees the whole cache
   return decode_impl(q, k_cache, v_cache, out, B, Tkv, Hq, Hkv, d, scale, nullptr, nullptr,
                      workspace, workspace_bytes, dtype, stream);
+}
+
+gqa_status_t gqa_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                     void* out, int B, int Tkv, int Hq, int Hkv, int d,
+                                     float scale, int causal, gqa_dtype_t dtype,
+                                     hipStream_t stream) {
+  (void)causal;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (dtype == GQA_DTYPE_BF16 && B > 0 && Tkv > 0 && Hq > 0 && Hkv > 0 && d > 0 &&
+      Hq % Hkv == 0) {
+    // the sizes decide the partials' footprint; past the fixed scratch the call is refused
+    // before the scratch is even looked up
+    if (gqa::decode_workspace_bytes(B, Tkv, Hq, Hkv, d) > GQA_DECODE_SCRATCH_BYTES)
+      return GQA_ERR_WORKSPACE;
+    if (gqa::decode_scratch(&ws) != hipSuccess) return GQA_ERR_HIP;
+    ws_bytes = GQA_DECODE_SCRATCH_BYTES;
+  }
+  return decode_impl(q, k_cache, v_cache, out, B, Tkv, Hq, Hkv, d, scale, nullptr, nullptr, ws,
+                     ws_bytes, dtype, stream);
 }
 
 gqa_status_t gqa_attn_decode_ragged(const void* q, const void* k_cache, const void* v_cache,

@@ -20,12 +20,14 @@
  * Conventions shared by every entry point:
  *   - Tensors are dense, row-major device buffers in the [batch, position, head, head_dim] layout
  *     with head_dim contiguous; all pointers must be 16-byte aligned.
- *   - The caller owns every buffer. The library allocates no device memory, keeps no pointer
- *     after returning, and never synchronises: all work is enqueued on `stream` (a HIP stream,
- *     NULL for the default stream) and completes asynchronously.
+ *   - The caller owns every buffer. The library allocates no device memory at run time (its one
+ *     fixed array, the decode scratch of gqa_attn_decode_noalloc, is part of the loaded code
+ *     object), keeps no pointer after returning, and never synchronises: all work is enqueued
+ *     on `stream` (a HIP stream, NULL for the default stream) and completes asynchronously.
  *   - Arguments are validated before anything is enqueued; on an error status nothing has been
  *     written. Outputs must not overlap inputs. No C++ exception crosses this interface.
- *   - Thread-safe: the library holds no mutable global state.
+ *   - Thread-safe: the only mutable global state is the table of per-GPU addresses of the
+ *     decode scratch array (gqa_attn_decode_noalloc), filled once per device under a mutex.
  *   - `scale` multiplies every score. Pass a finite positive value, or GQA_SCALE_DEFAULT (0) for
  *     1/sqrt(d), the factor both the GQA lab page (step 4: scores divided by the square root of
  *     the head dimension) and the course page (step 1) use; the library then computes it as
@@ -202,6 +204,24 @@ gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_c
                              int B, int Tkv, int Hq, int Hkv, int d, float scale, int causal,
                              void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
                              hipStream_t stream);
+
+/*
+ * Decode that allocates nothing, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation). Same arguments,
+ * layout, result and errors as gqa_attn_decode, without the workspace: the split partials go to
+ * a fixed scratch array of GQA_DECODE_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends (its address is taken once per device, on the first call there).
+ * A call whose partials would not fit (gqa_attn_decode_workspace_bytes_hkv(...) larger than
+ * GQA_DECODE_SCRATCH_BYTES) returns GQA_ERR_WORKSPACE and enqueues nothing. Every call on one
+ * GPU shares that GPU's scratch: calls that overlap in time on the same GPU (different streams
+ * or threads without ordering between them) race and must be serialised by the caller. The
+ * scratch needs no clearing between calls. f32 needs no scratch, as for gqa_attn_decode.
+ */
+#define GQA_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+gqa_status_t gqa_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                     void* out, int B, int Tkv, int Hq, int Hkv, int d,
+                                     float scale, int causal, gqa_dtype_t dtype,
+                                     hipStream_t stream);
 
 /*
  * Decode against a ragged cache, optionally with a sliding window and sinks (course page
