@@ -121,6 +121,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_attn_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, SZ, I,
                                       P]
     lib.gqa_attn_backward.restype = I
+    lib.gqa_attn_backward_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I,
+                                         OP, P, SZ, I, P]
+    lib.gqa_attn_backward_ex.restype = I
     lib.gqa_fold_kv.argtypes = [P, P, I, I, I, I, I, I, P]
     lib.gqa_fold_kv.restype = I
     lib.gqa_status_string.argtypes = [I]
@@ -460,9 +463,11 @@ def gqa_attn_decode_ex(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
 def gqa_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
                       dout: torch.Tensor, lse: torch.Tensor, causal: bool = False,
                       scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
-                      stream=None):
+                      window: int = 0, n_sink: int = 0, cu_seqlens: Optional[torch.Tensor] = None,
+                      max_seqlen: Optional[int] = None, stream=None):
     """Gradients (dq, dk, dv) of sum(out * dout) for a forward with the same arguments; lse from
-    :func:`gqa_attn_prefill_ex`. Dense bf16 batches."""
+    :func:`gqa_attn_prefill_ex`. bf16. A sliding window / sinks (causal) and packed batches
+    ([1, total, H, d] with int32 device cu_seqlens and the host max_seqlen) as in the forward."""
     q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
     out, dout, lse = _dev(out, "out"), _dev(dout, "dout"), _dev(lse, "lse")
     if q.dim() != 4 or k.shape != v.shape or out.shape != q.shape or dout.shape != q.shape:
@@ -477,19 +482,31 @@ def gqa_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: to
     Tkv, Hkv = k.shape[1], k.shape[2]
     if scale is None:
         scale = GQA_SCALE_DEFAULT
+    nseq, cu_ptr, msl = B, None, 0
+    if cu_seqlens is not None:
+        cu = _dev(cu_seqlens, "cu_seqlens")
+        if cu.dtype != torch.int32 or cu.dim() != 1 or cu.numel() < 2 or B != 1:
+            raise ValueError("packed batches: int32 cu_seqlens and [1, total, H, d] tensors")
+        nseq = cu.numel() - 1
+        cu_ptr, msl = cu.data_ptr(), _max_seqlen(max_seqlen)
     need = int(_lib.gqa_attn_backward_workspace_bytes(B, Tq, Hq))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     elif workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    rc = _lib.gqa_attn_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                                dv.data_ptr(), B, Tq, Tkv, Hq, Hkv, d, float(scale),
-                                int(bool(causal)), workspace.data_ptr(),
-                                workspace.numel() * workspace.element_size(), _dtype_code(q),
-                                _stream(stream))
-    _check(rc, "gqa_attn_backward")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), nseq, Tq, Tkv, Hq, Hkv,
+            d, float(scale), int(bool(causal)))
+    ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    if window or n_sink or cu_seqlens is not None:
+        opt = _options(window, n_sink, None, d)
+        rc = _lib.gqa_attn_backward_ex(*args, cu_ptr, msl, ctypes.byref(opt), *ws, _dtype_code(q),
+                                       _stream(stream))
+        _check(rc, "gqa_attn_backward_ex")
+    else:
+        rc = _lib.gqa_attn_backward(*args, *ws, _dtype_code(q), _stream(stream))
+        _check(rc, "gqa_attn_backward")
     return dq, dk, dv
 
 

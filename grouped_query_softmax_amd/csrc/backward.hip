@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restr
 
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_tiles, int tile_wgs) {
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int tile_wgs) {
   using C = BwdCfg<D>;
   constexpr int NS = C::kNS, NMT = C::kNMT;
   constexpr int kSlotBytes = 2 * C::kChunkBytes + 2 * kRows * 4;  // q, dout, L, D of a chunk
@@ -123,23 +123,29 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_t
   const int lin = blockIdx.x;
   const int kvh = lin % a.Hkv;
   const int z = (lin / a.Hkv) % tile_wgs;
-  const int b = lin / (tile_wgs * a.Hkv);
+  const int b = lin / (tile_wgs * a.Hkv);  // batch item or packed sequence
+  int64_t q0, k0;
+  int tq, tkv;
+  a.items.get(b, q0, k0, tq, tkv);
+  const int key_tiles = (tkv + 63) / 64;
+  if (z >= (a.causal ? (key_tiles + 1) / 2 : key_tiles)) return;  // past this item's keys
   const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kh = wave & 1;    // which 32 keys of the 64-key tile
   const int slot = wave >> 1;  // which item of each step (waves 0, 1: the first; 2, 3: the second)
   const int n = lane & 31, hh = lane >> 5;
-  const int off = a.Tkv - a.Tq;
+  const int off = tkv - tq;
   const float sl2 = a.scale * kLog2e;
+  const int W = a.window;
 
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
   const uint16_t* V = static_cast<const uint16_t*>(a.v);
   const uint16_t* GO = static_cast<const uint16_t*>(a.dout);
   // this sequence's q, dout, L and D (each below 2 GiB: checked by the entry point)
-  const int64_t qe0 = static_cast<int64_t>(b) * a.Tq * a.Hq;
-  const int qbytes = a.Tq * a.Hq * D * 2, lbytes = a.Tq * a.Hq * 4;
+  const int64_t qe0 = q0 * a.Hq;
+  const int qbytes = tq * a.Hq * D * 2, lbytes = tq * a.Hq * 4;
   const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Q + qe0 * D), 0, qbytes, kBufWord3);
   const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
@@ -162,12 +168,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_t
     const int kb0 = tiles[tt] * 64;
     const int kfirst = kb0 + 32 * kh;  // first key of this wave
     const int key = kfirst + n;        // this lane's key column
-    const bool key_ok = key < a.Tkv;
+    const bool key_ok = key < tkv;
 
     bf16x8 kop[NS], vop[NS];
     {
-      const int64_t kr =
-          ((static_cast<int64_t>(b) * a.Tkv + (key_ok ? key : 0)) * a.Hkv + kvh) * D;
+      const int64_t kr = ((k0 + (key_ok ? key : 0)) * a.Hkv + kvh) * D;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const u32x4 wk = key_ok ? *reinterpret_cast<const u32x4*>(K + kr + 16 * s + 8 * hh)
@@ -187,8 +192,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_t
     // items: (32-row chunk from the first row that can see the tile's first key, query head of
     // the group), chunks from the last one down and heads inner, so that every workgroup walks
     // the rows in the same order; step s holds items 2s (waves 0, 1) and 2s+1 (waves 2, 3)
+    // With a sliding window (course page "Week 7. Attention", step 3) the rows end at the last
+    // one whose window still reaches the tile's last key, unless the tile holds sink keys.
     const int qstart = a.causal ? max(0, kb0 - off) / kRows * kRows : 0;
-    const int nchunk = qstart < a.Tq ? (a.Tq - qstart + kRows - 1) / kRows : 0;
+    const int qlast = (W > 0 && kb0 >= a.n_sink) ? min(tq - 1, kb0 + 63 + W - 1 - off) : tq - 1;
+    const int nchunk = qstart <= qlast ? (qlast - qstart) / kRows + 1 : 0;
     const int nitems = G * nchunk;
     const int nsteps = (nitems + 1) / 2;
 
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_t
         const bool ok = it < nitems;
         srow[sl] = ok ? p0 * a.Hq + kvh * G + h : 0;
         soff[sl] = srow[sl] * D;
-        nrows[sl] = ok ? min(kRows, a.Tq - p0) : 0;
+        nrows[sl] = ok ? min(kRows, tq - p0) : 0;
       }
 #pragma unroll
       for (int i = 0; i < kPieces; ++i) {
@@ -263,8 +271,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_t
       const int it = 2 * st + slot;
       const int ci = nchunk - 1 - it / G;
       const int qc = qstart + ci * kRows;
-      // a chunk whose last row cannot see this wave's first key contributes nothing
-      const bool work = it < nitems && (!a.causal || qc + kRows - 1 + off >= kfirst);
+      // a chunk whose last row cannot see this wave's first key, or whose first row's window
+      // starts past this wave's keys (none of them a sink), contributes nothing
+      const bool work = it < nitems && (!a.causal || qc + kRows - 1 + off >= kfirst) &&
+                        (W == 0 || kfirst < a.n_sink || kfirst + 31 > qc + off - W);
       if (work) {
         char* sq = smem + (st & 1) * kStageBytes + slot * kSlotBytes;
         char* sg = sq + C::kChunkBytes;
@@ -290,7 +300,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_t
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int p = qc + (i >> 2) * 8 + 4 * hh + (i & 3);
-          const bool vis = key_ok && (!a.causal || key <= p + off);
+          const bool vis = key_ok && (!a.causal || key <= p + off) &&
+                           (W == 0 || key > p + off - W || key < a.n_sink);
           const float e = fast_exp2(fmaf(s_acc[i], sl2, -lrow[i]));
           pr[i] = vis ? e : 0.f;
           ds[i] = pr[i] * (p_acc[i] - drow[i]);
@@ -338,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_t
       if (key_ok) {
         uint16_t* DK = static_cast<uint16_t*>(a.dk);
         uint16_t* DV = static_cast<uint16_t*>(a.dv);
-        const int64_t orow = ((static_cast<int64_t>(b) * a.Tkv + key) * a.Hkv + kvh) * D;
+        const int64_t orow = ((k0 + key) * a.Hkv + kvh) * D;
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
@@ -360,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int key_t
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per_wg,
                                                           int heads_per_wg, int head_tiles,
-                                                          int pos_tiles, int gz) {
+                                                          int gz) {
   using C = BwdCfg<D>;
   constexpr int NS = C::kNS, NMT = C::kNMT;
   __shared__ __attribute__((aligned(16))) char smem[4 * C::kChunkBytes];  // 2 x (K, V) chunks
@@ -371,13 +382,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
   const int rest = lin / a.Hkv;
   const int z = rest % gz;
   const int ht = (rest / gz) % head_tiles;
-  const int b = rest / (gz * head_tiles);
+  const int b = rest / (gz * head_tiles);  // batch item or packed sequence
+  int64_t q0, k0;
+  int tq, tkv;
+  a.items.get(b, q0, k0, tq, tkv);
+  const int pos_tiles = (tq + pos_per_wg - 1) / pos_per_wg;
+  if (a.causal ? 2 * z >= pos_tiles : z >= pos_tiles) return;  // past this item's rows
   const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
-  const int off = a.Tkv - a.Tq;
+  const int off = tkv - tq;
   const float sl2 = a.scale * kLog2e;
+  const int W = a.window;
   // causal: each workgroup takes the query tile pair (pos_tiles-1-z, z), equal work per pair
   int tiles[2];
   int ntile_here;
@@ -395,8 +412,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
   const uint16_t* V = static_cast<const uint16_t*>(a.v);
   const uint16_t* GO = static_cast<const uint16_t*>(a.dout);
   // this sequence's K and V (below 2 GiB each: checked by the entry point)
-  const int64_t ke0 = static_cast<int64_t>(b) * a.Tkv * a.Hkv * D;
-  const int kbytes = a.Tkv * a.Hkv * D * 2;
+  const int64_t ke0 = k0 * a.Hkv * D;
+  const int kbytes = tkv * a.Hkv * D * 2;
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(K + ke0), 0, kbytes, kBufWord3);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -408,10 +425,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
     const int p0 = tiles[tt] * pos_per_wg;
     const int pl = col / heads_per_wg;
     const int hi = ht * heads_per_wg + col % heads_per_wg;
-    const bool valid = pl < pos_per_wg && p0 + pl < a.Tq && hi < G;
-    const int pos = min(p0 + pl, a.Tq - 1);
+    const bool valid = pl < pos_per_wg && p0 + pl < tq && hi < G;
+    const int pos = min(p0 + pl, tq - 1);
     const int hq = kvh * G + min(hi, G - 1);
-    const int64_t qrow = (static_cast<int64_t>(b) * a.Tq + pos) * a.Hq + hq;
+    const int64_t qrow = (q0 + pos) * a.Hq + hq;
 
     bf16x8 qop[NS], gop[NS];
 #pragma unroll
@@ -431,9 +448,18 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
 #pragma unroll
       for (int i = 0; i < 16; ++i) dq[mt][i] = 0.f;
 
-    const int last = min(p0 + pos_per_wg, a.Tq) - 1;
-    const int kend = a.causal ? min(a.Tkv, last + off + 1) : a.Tkv;
-    const int nchunk = (kend + kRows - 1) / kRows;
+    const int last = min(p0 + pos_per_wg, tq) - 1;
+    const int kend = a.causal ? min(tkv, last + off + 1) : tkv;
+    // key chunks: with a sliding window, the sink chunks [0, nsc) and then the chunks from the
+    // window start of the tile's first row up; step ci works on chunk kchunk(ci)
+    const int kc_end = (kend + kRows - 1) / kRows;
+    int nsc = 0, wc0 = 0;
+    if (W > 0) {
+      wc0 = max(0, p0 + off - W + 1) / kRows;
+      nsc = min((min(a.n_sink, kend) + kRows - 1) / kRows, wc0);
+    }
+    const int nchunk = nsc + (kc_end - wc0);
+    auto kchunk = [&](int ci) { return ci < nsc ? ci : ci - nsc + wc0; };
 
     u32x4 pk[C::kChunkLoads], pv[C::kChunkLoads];
     auto load = [&](int ci) {  // keys past the end read zeros (offset past the buffer)
@@ -441,9 +467,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
       for (int i = 0; i < C::kChunkLoads; ++i) {
         const int idx = i * kThreads + tid;
         const int r = idx / C::kLoadsPerRow, c = idx % C::kLoadsPerRow;
-        const int kk = ci * kRows + r;
+        const int kk = kchunk(ci) * kRows + r;
         const unsigned vo =
-            kk < a.Tkv ? static_cast<unsigned>((kk * a.Hkv + kvh) * D + 8 * c) * 2u : kOutside;
+            kk < tkv ? static_cast<unsigned>((kk * a.Hkv + kvh) * D + 8 * c) * 2u : kOutside;
         pk[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, vo, 0, 0);
         pv[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, vo, 0, 0);
       }
@@ -466,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
     __builtin_amdgcn_s_waitcnt(kVmcnt0);  // nothing in flight: the loop waits only for its loads
     __syncthreads();
     for (int ci = 0; ci < nchunk; ++ci) {
-      const int kc = ci * kRows;
+      const int kc = kchunk(ci) * kRows;
       if (ci + 1 < nchunk) load(ci + 1);  // in flight during this chunk
       char* sk = smem + (ci & 1) * 2 * C::kChunkBytes;
       char* sv = sk + C::kChunkBytes;
@@ -485,7 +511,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kk = kc + (i >> 2) * 8 + 4 * hh + (i & 3);
-        const bool vis = kk < a.Tkv && (!a.causal || kk <= pos + off);
+        const bool vis = kk < tkv && (!a.causal || kk <= pos + off) &&
+                         (W == 0 || kk > pos + off - W || kk < a.n_sink);
         const float pv2 = vis ? fast_exp2(fmaf(s_acc[i], sl2, -Lr)) : 0.f;
         ds[i] = pv2 * (p_acc[i] - Dq);
       }
@@ -520,17 +547,22 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
 
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
-  const int64_t rows = static_cast<int64_t>(a.B) * a.Tq * a.Hq;
+  // one row per (query position, head): all items back to back, dense or packed
+  const int64_t rows =
+      (a.items.cu ? static_cast<int64_t>(a.Tq) : static_cast<int64_t>(a.B) * a.Tq) * a.Hq;
   const int64_t rblocks = (rows * (D / 8) + 255) / 256;
   hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3(static_cast<unsigned>(rblocks)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(a.out), static_cast<const uint16_t*>(a.dout),
                      a.Drow, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int key_tiles = (a.Tkv + 63) / 64;
+  // the grid covers the longest item; workgroups past a shorter item's tiles return at once
+  const int max_tkv = a.items.cu ? a.max_len : a.Tkv;
+  const int max_tq = a.items.cu ? a.max_len : a.Tq;
+  const int key_tiles = (max_tkv + 63) / 64;
   const int tile_wgs = a.causal ? (key_tiles + 1) / 2 : key_tiles;
   hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv * tile_wgs), dim3(kThreads), 0, s, a,
-                     key_tiles, tile_wgs);
+                     tile_wgs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;
@@ -538,10 +570,10 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const int heads_per_wg = G < kCols ? G : kCols;
   const int pos_per_wg = kCols / heads_per_wg;
   const int head_tiles = (G + heads_per_wg - 1) / heads_per_wg;
-  const int pos_tiles = (a.Tq + pos_per_wg - 1) / pos_per_wg;
+  const int pos_tiles = (max_tq + pos_per_wg - 1) / pos_per_wg;
   const int gz = a.causal ? (pos_tiles + 1) / 2 : pos_tiles;
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.B * a.Hkv * head_tiles * gz), dim3(kThreads), 0, s,
-                     a, pos_per_wg, heads_per_wg, head_tiles, pos_tiles, gz);
+                     a, pos_per_wg, heads_per_wg, head_tiles, gz);
   return hipGetLastError();
 }
 

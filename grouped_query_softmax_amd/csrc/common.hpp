@@ -242,6 +242,12 @@ struct BwdArgs {
   int B, Tq, Tkv, Hq, Hkv, d;
   float scale;
   int causal;
+  // packed batch: B sequences at the device offsets items.cu (Tq == Tkv == total tokens), the
+  // longest max_len tokens; dense: items.cu == nullptr, items.Tq / items.Tkv == Tq / Tkv
+  Items items;
+  int max_len;
+  int window;  // > 0: causal sliding window of this many keys (0: none)
+  int n_sink;  // keys 0 .. n_sink-1 stay visible below the window
 };
 
 // Launchers (return hipSuccess or the launch error). Shapes have been validated by the caller.

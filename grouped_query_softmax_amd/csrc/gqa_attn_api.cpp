@@ -462,36 +462,57 @@ size_t gqa_attn_backward_workspace_bytes(int B, int Tq, int Hq) {
   return (static_cast<size_t>(B) * Tq * Hq * sizeof(float) + 15) / 16 * 16;
 }
 
-gqa_status_t gqa_attn_backward(const void* q, const void* k, const void* v, const void* out,
-                               const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                               int B, int Tq, int Tkv, int Hq, int Hkv, int d, float scale,
-                               int causal, void* workspace, size_t workspace_bytes,
-                               gqa_dtype_t dtype, hipStream_t stream) {
+static gqa_status_t backward_impl(const void* q, const void* k, const void* v, const void* out,
+                                  const void* dout, const float* lse, void* dq, void* dk,
+                                  void* dv, int B, int Tq, int Tkv, int Hq, int Hkv, int d,
+                                  float scale, int causal, const int32_t* cu_seqlens,
+                                  int max_seqlen, const gqa_attn_options_t* opt, void* workspace,
+                                  size_t workspace_bytes, gqa_dtype_t dtype, hipStream_t stream) {
   if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return GQA_ERR_NULL_PTR;
   if (B <= 0 || Tq <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_SHAPE;
   if (!resolve_scale(scale, d)) return GQA_ERR_SHAPE;
-  if (causal && Tq > Tkv) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0) return GQA_ERR_GROUPING;
   if (dtype != GQA_DTYPE_BF16 || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
+  if (opt) {
+    // the backward of the rotary embedding and of QK-norm is not built
+    if (opt->rope_cos || opt->rope_sin || opt->q_norm_w || opt->k_norm_w || opt->keys_prepared)
+      return GQA_ERR_UNSUPPORTED;
+    if (opt->window < 0 || opt->n_sink < 0) return GQA_ERR_SHAPE;
+  }
+  const int window = opt ? opt->window : 0;
+  const int n_sink = opt ? opt->n_sink : 0;
+  if ((window > 0 || n_sink > 0) && !causal) return GQA_ERR_SHAPE;  // windows are causal
+  int max_len;
+  if (cu_seqlens) {
+    if (Tq != Tkv || max_seqlen <= 0 || max_seqlen > Tq) return GQA_ERR_SHAPE;
+    max_len = max_seqlen;
+  } else {
+    if (causal && Tq > Tkv) return GQA_ERR_SHAPE;
+    max_len = Tq > Tkv ? Tq : Tkv;
+  }
   const void* ptrs[] = {q, k, v, out, dout, lse, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return GQA_ERR_UNSUPPORTED;
-  const size_t need = gqa_attn_backward_workspace_bytes(B, Tq, Hq);
+  // packed: one [1, total, ., d] batch; its rows and keys count once
+  const int64_t qrows = cu_seqlens ? static_cast<int64_t>(Tq) : static_cast<int64_t>(B) * Tq;
+  const int64_t krows = cu_seqlens ? static_cast<int64_t>(Tkv) : static_cast<int64_t>(B) * Tkv;
+  const size_t need = gqa_attn_backward_workspace_bytes(1, static_cast<int>(qrows), Hq);
   if (!workspace || workspace_bytes < need) return GQA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return GQA_ERR_UNSUPPORTED;
   // the largest of the three launches: rows / (256 / (d / 8)), key tiles of 32, query tiles
-  const int64_t rows = static_cast<int64_t>(B) * Tq * Hq;
+  const int64_t rows = qrows * Hq;
   const int64_t wgs = std::max({rows * (d / 8) / 256 + 1,
-                                static_cast<int64_t>(B) * Hkv * ((Tkv + 31) / 32),
-                                rows / 128 + static_cast<int64_t>(B) * Hkv + 1});
+                                static_cast<int64_t>(B) * Hkv * ((max_len + 31) / 32),
+                                static_cast<int64_t>(B) * max_len * Hq / 128 +
+                                    static_cast<int64_t>(B) * Hkv + 1});
   // one sequence's q / dout and k / v rows are addressed with 32-bit byte offsets
-  const bool seq_fits = static_cast<int64_t>(Tq) * Hq * d * 2 < (1LL << 31) &&
-                        static_cast<int64_t>(Tkv) * Hkv * d * 2 < (1LL << 31);
+  const int64_t tq_item = cu_seqlens ? max_len : Tq, tkv_item = cu_seqlens ? max_len : Tkv;
+  const bool seq_fits = tq_item * Hq * d * 2 < (1LL << 31) && tkv_item * Hkv * d * 2 < (1LL << 31);
   if (wgs > kMaxFlatWorkgroups256 || rows * d > INT32_MAX * 8LL || !seq_fits)
     return GQA_ERR_UNSUPPORTED;
-  const size_t nq = static_cast<size_t>(B) * Tq * Hq * d * 2;
-  const size_t nk = static_cast<size_t>(B) * Tkv * Hkv * d * 2;
-  const size_t nl = static_cast<size_t>(B) * Tq * Hq * sizeof(float);
+  const size_t nq = static_cast<size_t>(qrows) * Hq * d * 2;
+  const size_t nk = static_cast<size_t>(krows) * Hkv * d * 2;
+  const size_t nl = static_cast<size_t>(qrows) * Hq * sizeof(float);
   // every output (and the workspace) must be disjoint from every input and from each other
   const void* outs[] = {dq, dk, dv, workspace};
   const size_t outn[] = {nq, nk, nk, need};
@@ -522,7 +543,33 @@ gqa_status_t gqa_attn_backward(const void* q, const void* k, const void* v, cons
   a.d = d;
   a.scale = scale;
   a.causal = causal ? 1 : 0;
+  a.items.cu = cu_seqlens;
+  a.items.Tq = Tq;
+  a.items.Tkv = Tkv;
+  a.max_len = max_len;
+  a.window = window;
+  a.n_sink = window > 0 ? n_sink : 0;  // without a window every past key is visible anyway
   return from_hip(gqa::launch_backward_bf16(a, stream));
+}
+
+gqa_status_t gqa_attn_backward(const void* q, const void* k, const void* v, const void* out,
+                               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                               int B, int Tq, int Tkv, int Hq, int Hkv, int d, float scale,
+                               int causal, void* workspace, size_t workspace_bytes,
+                               gqa_dtype_t dtype, hipStream_t stream) {
+  return backward_impl(q, k, v, out, dout, lse, dq, dk, dv, B, Tq, Tkv, Hq, Hkv, d, scale, causal,
+                       nullptr, 0, nullptr, workspace, workspace_bytes, dtype, stream);
+}
+
+gqa_status_t gqa_attn_backward_ex(const void* q, const void* k, const void* v, const void* out,
+                                  const void* dout, const float* lse, void* dq, void* dk,
+                                  void* dv, int B, int Tq, int Tkv, int Hq, int Hkv, int d,
+                                  float scale, int causal, const int32_t* cu_seqlens,
+                                  int max_seqlen, const gqa_attn_options_t* options,
+                                  void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
+                                  hipStream_t stream) {
+  return backward_impl(q, k, v, out, dout, lse, dq, dk, dv, B, Tq, Tkv, Hq, Hkv, d, scale, causal,
+                       cu_seqlens, max_seqlen, options, workspace, workspace_bytes, dtype, stream);
 }
 
 gqa_status_t gqa_prepare_keys(const void* k, void* k_out, int B, int T, int Hkv, int d,

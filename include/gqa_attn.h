@@ -270,6 +270,25 @@ gqa_status_t gqa_attn_backward(const void* q, const void* k, const void* v, cons
                                gqa_dtype_t dtype, hipStream_t stream);
 
 /*
+ * Backward with the options of the forward (course page "Week 7. Attention", step 3): a causal
+ * sliding window with sinks (options->window, n_sink, as for gqa_attn_prefill_ex; NULL options:
+ * none) and packed variable-length batches (cu_seqlens / max_seqlen as for gqa_attn_prefill:
+ * q, out, dout, dq [1, total, Hq, d], k, v, dk, dv [1, total, Hkv, d], lse [1, total, Hq], each
+ * sequence differentiated on its own). The forward must have used the same window, sinks and
+ * packing. Rotary tables, QK-norm weights and keys_prepared are GQA_ERR_UNSUPPORTED here (their
+ * backward is not built). Workspace: gqa_attn_backward_workspace_bytes(B, Tq, Hq) for a dense
+ * batch, gqa_attn_backward_workspace_bytes(1, total, Hq) for a packed one. Other arguments and
+ * errors as for gqa_attn_backward.
+ */
+gqa_status_t gqa_attn_backward_ex(const void* q, const void* k, const void* v, const void* out,
+                                  const void* dout, const float* lse, void* dq, void* dk,
+                                  void* dv, int B, int Tq, int Tkv, int Hq, int Hkv, int d,
+                                  float scale, int causal, const int32_t* cu_seqlens,
+                                  int max_seqlen, const gqa_attn_options_t* options,
+                                  void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
+                                  hipStream_t stream);
+
+/*
  * Fold key/value heads: src [B, T, H, d] -> dst [B, T, g, d] with
  *   dst[b,t,j,:] = (sum of src[b,t,j*s + i,:] for i < s) / s,   s = H / g,
  * summed in fp32 in head order, divided in fp32, rounded to `dtype`. g == H copies the input.

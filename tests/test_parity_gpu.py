@@ -92,7 +92,10 @@ BF16_CASES = [
     (1, 77, 333, 4, 4, 64, False),
     (2, 200, 200, 32, 1, 128, True),     # MQA, G=32
     (1, 150, 150, 6, 2, 128, True),      # G=3: columns not a power of two
-    (1, 65, 65, 192, 1, 64, True),       # G=192 > 128 columns: two head tiles
+    (1, 65, 65, 192, 1, 64, True),       # G=192: one head tile of 192 of the 256 columns
+    (1, 40, 40, 320, 1, 64, True),       # G=320 > 256 columns: two head tiles (256 + 64 heads)
+    (1, 33, 70, 512, 1, 128, False),     # G=512: two full head tiles, one position per tile
+    (2, 17, 17, 300, 2, 128, True),      # G=150 per head, two key/value heads
     (3, 1, 513, 16, 4, 128, False),      # one query row per item
     (1, 129, 129, 1, 1, 128, True),      # single head
 ]
