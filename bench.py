@@ -139,6 +139,9 @@ def time_launches(fn, steps, warmup, torch, per_launch=50):
     return avg, wall, median, (each[0] if each else avg)
 
 
+PER_LAUNCH = 50  # separately timed launches for the median and minimum (set by --median-launches)
+
+
 def bench_prefill(gqa, w, steps, warmup, torch, seed, rope=False, qk_norm=False,
                   prepared=False):
     """rope: turn q and k inside the kernel with (cos, sin) tables (rotary embedding); qk_norm:
@@ -175,7 +178,7 @@ def bench_prefill(gqa, w, steps, warmup, torch, seed, rope=False, qk_norm=False,
         else:
             gqa.gqa_attn_prefill(q, k, v, causal=w.causal, cu_seqlens=cu, max_seqlen=msl, out=out)
 
-    avg, wall, med, mn = time_launches(step, steps, warmup, torch)
+    avg, wall, med, mn = time_launches(step, steps, warmup, torch, PER_LAUNCH)
     flops = prefill_flops(w)
     res = {"workload": w.name, "flops_per_launch": flops, "avg_ms": avg,
            "median_ms": med, "min_ms": mn,
@@ -250,7 +253,7 @@ def bench_decode(gqa, w, steps, warmup, torch, seed):
         else:
             gqa.gqa_attn_decode(q, k, v, workspace=ws, out=out)
 
-    avg, wall, med, mn = time_launches(step, steps, warmup, torch)
+    avg, wall, med, mn = time_launches(step, steps, warmup, torch, PER_LAUNCH)
     entries = sum(w.cache_lens) if w.cache_lens is not None else w.B * w.Tkv
     kv_bytes = 2 * entries * w.Hkv * w.d * 2
     qo_bytes = 2 * w.B * w.Hq * w.d * 2
@@ -404,6 +407,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="time only the headline workload")
+    ap.add_argument("--median-launches", type=int, default=50,
+                    help="separately timed launches for the median and minimum (0: none)")
     ap.add_argument("--only", choices=["varlen", "prefill", "decode", "mqa", "window",
                                        "ragged", "rope", "qknorm", "backward", "gva",
                                        "fold", "copy"],
@@ -440,6 +445,8 @@ def main():
         print(json.dumps(res), flush=True)
         return
 
+    global PER_LAUNCH
+    PER_LAUNCH = max(0, args.median_launches)
     S, Wu = args.steps, args.warmup
     headline = args.only or "varlen"
     legs = {}      # name -> (result, roofline, config)

@@ -105,7 +105,8 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restr
 }
 
 
-template <int D>
+// WIN: a sliding window (with sinks) is on; the plain kernels carry none of its tests.
+template <int D, bool WIN>
 __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int tile_wgs) {
   using C = BwdCfg<D>;
   constexpr int NS = C::kNS, NMT = C::kNMT;
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int tile_
   const int n = lane & 31, hh = lane >> 5;
   const int off = tkv - tq;
   const float sl2 = a.scale * kLog2e;
-  const int W = a.window;
+  const int W = WIN ? a.window : 0;
 
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* K = static_cast<const uint16_t*>(a.k);
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int tile_
     // With a sliding window (course page "Week 7. Attention", step 3) the rows end at the last
     // one whose window still reaches the tile's last key, unless the tile holds sink keys.
     const int qstart = a.causal ? max(0, kb0 - off) / kRows * kRows : 0;
-    const int qlast = (W > 0 && kb0 >= a.n_sink) ? min(tq - 1, kb0 + 63 + W - 1 - off) : tq - 1;
+    const int qlast = (WIN && kb0 >= a.n_sink) ? min(tq - 1, kb0 + 63 + W - 1 - off) : tq - 1;
     const int nchunk = qstart <= qlast ? (qlast - qstart) / kRows + 1 : 0;
     const int nitems = G * nchunk;
     const int nsteps = (nitems + 1) / 2;
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int tile_
       // a chunk whose last row cannot see this wave's first key, or whose first row's window
       // starts past this wave's keys (none of them a sink), contributes nothing
       const bool work = it < nitems && (!a.causal || qc + kRows - 1 + off >= kfirst) &&
-                        (W == 0 || kfirst < a.n_sink || kfirst + 31 > qc + off - W);
+                        (!WIN || kfirst < a.n_sink || kfirst + 31 > qc + off - W);
       if (work) {
         char* sq = smem + (st & 1) * kStageBytes + slot * kSlotBytes;
         char* sg = sq + C::kChunkBytes;
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int tile_
         for (int i = 0; i < 16; ++i) {
           const int p = qc + (i >> 2) * 8 + 4 * hh + (i & 3);
           const bool vis = key_ok && (!a.causal || key <= p + off) &&
-                           (W == 0 || key > p + off - W || key < a.n_sink);
+                           (!WIN || key > p + off - W || key < a.n_sink);
           const float e = fast_exp2(fmaf(s_acc[i], sl2, -lrow[i]));
           pr[i] = vis ? e : 0.f;
           ds[i] = pr[i] * (p_acc[i] - drow[i]);
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int tile_
   }
 }
 
-template <int D>
+template <int D, bool WIN>
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per_wg,
                                                           int heads_per_wg, int head_tiles,
                                                           int gz) {
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
   const int n = lane & 31, hh = lane >> 5;
   const int off = tkv - tq;
   const float sl2 = a.scale * kLog2e;
-  const int W = a.window;
+  const int W = WIN ? a.window : 0;
   // causal: each workgroup takes the query tile pair (pos_tiles-1-z, z), equal work per pair
   int tiles[2];
   int ntile_here;
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
     // window start of the tile's first row up; step ci works on chunk kchunk(ci)
     const int kc_end = (kend + kRows - 1) / kRows;
     int nsc = 0, wc0 = 0;
-    if (W > 0) {
+    if (WIN) {
       wc0 = max(0, p0 + off - W + 1) / kRows;
       nsc = min((min(a.n_sink, kend) + kRows - 1) / kRows, wc0);
     }
@@ -512,7 +513,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
       for (int i = 0; i < 16; ++i) {
         const int kk = kc + (i >> 2) * 8 + 4 * hh + (i & 3);
         const bool vis = kk < tkv && (!a.causal || kk <= pos + off) &&
-                         (W == 0 || kk > pos + off - W || kk < a.n_sink);
+                         (!WIN || kk > pos + off - W || kk < a.n_sink);
         const float pv2 = vis ? fast_exp2(fmaf(s_acc[i], sl2, -Lr)) : 0.f;
         ds[i] = pv2 * (p_acc[i] - Dq);
       }
@@ -561,8 +562,12 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const int max_tq = a.items.cu ? a.max_len : a.Tq;
   const int key_tiles = (max_tkv + 63) / 64;
   const int tile_wgs = a.causal ? (key_tiles + 1) / 2 : key_tiles;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv * tile_wgs), dim3(kThreads), 0, s, a,
-                     tile_wgs);
+  if (a.window > 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(a.B * a.Hkv * tile_wgs), dim3(kThreads), 0,
+                       s, a, tile_wgs);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(a.B * a.Hkv * tile_wgs), dim3(kThreads),
+                       0, s, a, tile_wgs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;
@@ -572,8 +577,13 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const int head_tiles = (G + heads_per_wg - 1) / heads_per_wg;
   const int pos_tiles = (max_tq + pos_per_wg - 1) / pos_per_wg;
   const int gz = a.causal ? (pos_tiles + 1) / 2 : pos_tiles;
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.B * a.Hkv * head_tiles * gz), dim3(kThreads), 0, s,
-                     a, pos_per_wg, heads_per_wg, head_tiles, gz);
+  const dim3 qgrid(a.B * a.Hkv * head_tiles * gz);
+  if (a.window > 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), qgrid, dim3(kThreads), 0, s, a, pos_per_wg,
+                       heads_per_wg, head_tiles, gz);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), qgrid, dim3(kThreads), 0, s, a, pos_per_wg,
+                       heads_per_wg, head_tiles, gz);
   return hipGetLastError();
 }
 
