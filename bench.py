@@ -78,9 +78,13 @@ def prefill_flops(w):
     return 4 * w.d * w.Hq * pairs
 
 
+# kernel sources of legs that have no traffic record
+SOURCES = {"backward": ("backward.hip", "common.hpp")}
+
+
 def kernel_source_sha(which="prefill"):
     h = hashlib.sha256()
-    for name in TRAFFIC[which][1]:
+    for name in (TRAFFIC[which][1] if which in TRAFFIC else SOURCES[which]):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -365,10 +369,10 @@ def traffic_for(which):
 KERNEL_PLAIN = "prefill_pp_kernel<128, 128, false, false, false>"
 
 
-def mfma_roofline(res, kernel, traffic_key=None):
+def mfma_roofline(res, kernel, traffic_key=None, sha_key=None):
     """Roofline record of an MFMA-bound leg: algorithmic flops per launch over the measured
     average launch time, against the bf16 dense peak."""
-    sha_key = traffic_key if traffic_key in TRAFFIC else "prefill"
+    sha_key = sha_key or (traffic_key if traffic_key in TRAFFIC else "prefill")
     return {"bound": "mfma", "achieved": res["tflops"], "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": res["tflops"] / PEAK_BF16_TFLOPS,
             "traffic": traffic_for(traffic_key) if traffic_key else None, "kernel": kernel,
@@ -511,7 +515,8 @@ def main():
             bw = bench_backward(gqa, workloads.LLAMA_PREFILL, S, Wu, torch, 2000)
             log(f"backward: {bw['avg_ms'] * 1e3:.1f} us, {bw['tflops']:.1f} TFLOP/s")
             legs["backward"] = (bw, mfma_roofline(
-                bw, "bwd_rowdot + bwd_dkdv_kernel<128> + bwd_dq_kernel<128>"),
+                bw, "bwd_rowdot + bwd_dkdv_kernel<128, false> + bwd_dq_kernel<128, false>",
+                sha_key="backward"),
                 prefill_config(workloads.LLAMA_PREFILL))
         elif name == "gva":
             gv = bench_gva(gqa, workloads.GVA_PREFILL, S, Wu, torch, 8000)
