@@ -26,6 +26,8 @@
 // All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace gqa {
@@ -34,12 +36,13 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32;  // rows of a streamed chunk
+constexpr int kDkdvSlots = 4;  // query items per dK/dV step (two waves each)
 // LDS layout of a [rows][D] chunk: rows of 2*D bytes, the 16-byte pieces of row r stored at
 // piece index c ^ swz(r). The two readers of a chunk -- 16-byte reads down a column of rows (an
 // MFMA operand with the rows as its M index) and transposing 8-byte reads of 4 rows x 64 bytes --
 // then both hit 64 distinct banks per pass, which no plain row padding achieves for both.
 template <int D>
-__device__ __forceinline__ int swz(int r) {
+__host__ __device__ constexpr int swz(int r) {
   if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
 }
@@ -81,11 +84,14 @@ __device__ __forceinline__ bf16x8 pack_rows(const float* x, int ks) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// D = dout . out per row; rows = B*Tq*Hq, one 64-lane wave per 4 rows (16 lanes per row).
+// Per row: D = dout . out and L2 = lse log2 e (the log-sum-exp in base 2); rows = B*Tq*Hq, one
+// 64-lane wave per 4 rows (16 lanes per row).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restrict__ out,
                                                          const uint16_t* __restrict__ dout,
-                                                         float* __restrict__ Dr, int64_t rows) {
+                                                         const float* __restrict__ lse,
+                                                         float* __restrict__ Dr,
+                                                         float* __restrict__ L2r, int64_t rows) {
   constexpr int LPR = D / 8;  // lanes per row
   const int64_t row = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) / LPR;
   const int c = threadIdx.x % LPR;
@@ -101,22 +107,60 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restr
   }
 #pragma unroll
   for (int m = LPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
-  if (row < rows && c == 0) Dr[row] = acc;
+  if (row < rows && c == 0) {
+    Dr[row] = acc;
+    L2r[row] = lse[row] * kLog2e;
+  }
 }
 
 
+// XOR pattern that the swizzle adds to the pieces of the rows i*R .. i*R+R-1 of a chunk relative
+// to rows 0 .. R-1 (R rows per 1 KiB block), the same for every row of the block.
+template <int D>
+constexpr int block_xor(int i) {
+  constexpr int R = 64 / BwdCfg<D>::kLoadsPerRow;
+  return swz<D>(i * R) ^ swz<D>(0);
+}
+template <int D>
+constexpr bool block_xor_is_uniform() {
+  constexpr int R = 64 / BwdCfg<D>::kLoadsPerRow;
+  for (int i = 0; i < kRows / R; ++i)
+    for (int r = 0; r < R; ++r)
+      if ((swz<D>(i * R + r) ^ swz<D>(r)) != block_xor<D>(i)) return false;
+  return true;
+}
+
 // WIN: a sliding window (with sinks) is on; the plain kernels carry none of its tests.
-template <int D, bool WIN>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int tile_wgs) {
+// SL: query items per step (wave pairs); the workgroup has 2 SL waves.
+template <int D, bool WIN, int SL>
+__global__ __launch_bounds__(128 * SL) void bwd_dkdv_kernel(BwdArgs a, int tile_wgs) {
   using C = BwdCfg<D>;
   constexpr int NS = C::kNS, NMT = C::kNMT;
-  constexpr int kSlotBytes = 2 * C::kChunkBytes + 2 * kRows * 4;  // q, dout, L, D of a chunk
-  constexpr int kStageBytes = 2 * kSlotBytes;                     // the two items of a step
-  constexpr int kRedBytes = 2 * 2 * 32 * D * 4;                   // two waves' dK^T, dV^T
-  constexpr int kSmem = 2 * kStageBytes > kRedBytes ? 2 * kStageBytes : kRedBytes;
-  constexpr int kMatPieces = kRows * C::kLoadsPerRow;             // 16-byte pieces per matrix
-  constexpr int kPieces = 2 * 2 * kMatPieces / kThreads;          // per thread and step
-  static_assert(kMatPieces % kThreads == 0, "a piece index decides its matrix uniformly");
+  constexpr int CB = C::kChunkBytes;
+  // LDS: chunk (slot, matrix (0: q, 1: dout), stage) at ((slot * 2 + matrix) * 2 + stage) * CB,
+  // so that a wave's chunks lie within the reach of a DS instruction's offset field; then the
+  // rows' L2 (matrix 0) and D (matrix 1): 32 floats each, in 256-byte regions at
+  // kRowsOff + ((stage * 2 + matrix) * SL + slot) * 256
+  // (the tile's V rows follow at kVOff: [64][D], swizzled as a chunk)
+  constexpr int kRowsOff = SL * 4 * CB;
+  constexpr int kVOff = kRowsOff + 4 * SL * 256;
+  // and with D = 128 the second half (d >= 64) of the tile's K rows at kKOff: [64][64], swizzled
+  // as the rows of a d = 64 chunk; the first half (all of K with D = 64) stays in registers
+  constexpr int NSR = D == 128 ? NS / 2 : NS;  // k-steps with K in registers
+  constexpr int kKOff = kVOff + 2 * CB;
+  constexpr int kStagesBytes = kKOff + (NSR < NS ? CB : 0);
+  constexpr int kWaveRed = 2 * 32 * D * 4;  // one wave's dK^T, dV^T
+  constexpr int kRedBytes = SL * kWaveRed;  // the upper half's waves
+  constexpr int kSmem = kStagesBytes > kRedBytes ? kStagesBytes : kRedBytes;
+  constexpr int kBlocks = C::kChunkBytes / 1024;      // 1 KiB blocks per chunk
+  constexpr int kBlockRows = 64 / C::kLoadsPerRow;    // rows per block
+  static_assert(C::kChunkBytes % 1024 == 0 && block_xor_is_uniform<D>(),
+                "a block's loads differ from the first block's by one XOR pattern");
+  static_assert(SL == 2 || SL == 4, "the cross-wave sums pair the slots");
+  static_assert((2 * kBlocks) % (2 * SL) == 0, "the V tile's blocks split evenly over the waves");
+  static_assert(3 * CB + CB <= 65536, "offset field reach");
+  static_assert(swz<D>(32) == swz<D>(0) && swz<D>(kRows) == swz<D>(0),
+                "the V tile's row 32 + n swizzles as chunk row n");
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
 
   // key/value heads fastest: consecutive workgroups go round-robin to the XCDs, so with 8 heads
@@ -133,28 +177,53 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int tile_
   const int G = a.Hq / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kh = wave & 1;    // which 32 keys of the 64-key tile
-  const int slot = wave >> 1;  // which item of each step (waves 0, 1: the first; 2, 3: the second)
+  const int kh = wave & 1;     // which 32 keys of the 64-key tile; also which matrix it loads
+  const int slot = wave >> 1;  // which item of each step
   const int n = lane & 31, hh = lane >> 5;
   const int off = tkv - tq;
   const float sl2 = a.scale * kLog2e;
   const int W = WIN ? a.window : 0;
 
-  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* K = static_cast<const uint16_t*>(a.k);
-  const uint16_t* V = static_cast<const uint16_t*>(a.v);
-  const uint16_t* GO = static_cast<const uint16_t*>(a.dout);
-  // this sequence's q, dout, L and D (each below 2 GiB: checked by the entry point)
+  // this sequence's q or dout (the wave's matrix) and its rows' L2 or D; K and V
   const int64_t qe0 = q0 * a.Hq;
-  const int qbytes = tq * a.Hq * D * 2, lbytes = tq * a.Hq * 4;
-  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(Q + qe0 * D), 0, qbytes, kBufWord3);
-  const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(GO + qe0 * D), 0, qbytes, kBufWord3);
-  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(a.lse + qe0), 0, lbytes, kBufWord3);
-  const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc(a.Drow + qe0, 0, lbytes,
-                                                                       kBufWord3);
+  const uint16_t* mat = static_cast<const uint16_t*>(kh ? a.dout : a.q) + qe0 * D;
+  const float* rowv = (kh ? a.Drow : a.L2row) + qe0;
+  const int kbytes = tkv * a.Hkv * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(static_cast<const void*>(static_cast<const uint16_t*>(a.k) + k0 * a.Hkv * D)),
+      0, kbytes, kBufWord3);
+  // V goes through LDS (the tile's 64 rows, loaded straight into LDS by all waves)
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(static_cast<const void*>(static_cast<const uint16_t*>(a.v) + k0 * a.Hkv * D)),
+      0, kbytes, kBufWord3);
+
+  // lane constants of the LDS addresses (byte offsets within the wave's slot region):
+  //   row reads (A operands with the chunk rows as M): piece 2s + hh of row n lies at
+  //   rb + ((s << 5) ^ x1) (the swizzle's upper bits move whole 32-byte pairs);
+  //   transposed reads: rows 4 hh + (j >> 2) (+8), pieces 4 mt + 2 sub + ((j >> 1) & 1), half
+  //   j & 1, at tb + ((mt << 6) ^ t6) (+ 16 rows per k-step: 16 row pitches)
+  const int sw = swz<D>(n);
+  int x1 = (sw >> 1) << 5;
+  int rb = slot * 4 * CB + n * C::kPitch + 16 * (hh ^ (sw & 1));
+  //   the V tile's row 32 kh + n (the lane's key) likewise at vb + ((s << 5) ^ x1)
+  int vb = kVOff + (32 * kh + n) * C::kPitch + 16 * (hh ^ (sw & 1));
+  //   the K half-tile's row 32 kh + n: piece 2 (s - NSR) + hh at kb + ((s - NSR) << 5 ^ xk)
+  const int swk = swz<64>(32 * kh + n);
+  int xk = (swk >> 1) << 5;
+  int kb = kKOff + (32 * kh + n) * (C::kPitch / 2) + 16 * (hh ^ (swk & 1));
+  const int j = lane & 15, sub = (lane >> 4) & 1;
+  const int trow = 4 * hh + (j >> 2), tp = 2 * sub + ((j >> 1) & 1);
+  const int swl = swz<D>(trow), swh = swz<D>(trow + 8);
+  int tbl = slot * 4 * CB + trow * C::kPitch + 16 * (tp ^ (swl & 3)) + 8 * (j & 1);
+  int tbh = slot * 4 * CB + (trow + 8) * C::kPitch + 16 * (tp ^ (swh & 3)) + 8 * (j & 1);
+  int t6l = (swl >> 2) << 6, t6h = (swh >> 2) << 6;
+  //   L2 / D of rows 8 g + 4 hh + 0..3 (the lane's accumulator rows): 16 bytes at lrow + 32 g
+  int lrow = kRowsOff + slot * 256 + 16 * hh;
+  // lane constants of the loads: piece i of the wave's chunk, 16-byte position 64 i + lane, holds
+  // row i * kBlockRows + lane / kLoadsPerRow, piece (lane % kLoadsPerRow) ^ swz(row)
+  const int lr = lane / C::kLoadsPerRow;
+  int v0 = lr * a.Hq * D * 2 + 16 * ((lane % C::kLoadsPerRow) ^ swz<D>(lr));
+  int vrow = (lane & 31) * a.Hq * 4;
 
   // causal: a workgroup takes the key tile pair (z, key_tiles-1-z), equal work per pair
   int tiles[2];
@@ -171,17 +240,36 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int tile_
     const int key = kfirst + n;        // this lane's key column
     const bool key_ok = key < tkv;
 
-    bf16x8 kop[NS], vop[NS];
-    {
-      const int64_t kr = ((k0 + (key_ok ? key : 0)) * a.Hkv + kvh) * D;
+    __syncthreads();  // the previous tile's cross-wave sums and V reads are done with the LDS
+    bf16x8 kop[NSR];
+    {  // keys past the end read zeros
+      const unsigned kr = static_cast<unsigned>((key * a.Hkv + kvh) * D) * 2u;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const u32x4 wk = key_ok ? *reinterpret_cast<const u32x4*>(K + kr + 16 * s + 8 * hh)
-                                : u32x4{0, 0, 0, 0};
-        const u32x4 wv = key_ok ? *reinterpret_cast<const u32x4*>(V + kr + 16 * s + 8 * hh)
-                                : u32x4{0, 0, 0, 0};
-        kop[s] = __builtin_bit_cast(bf16x8, wk);
-        vop[s] = __builtin_bit_cast(bf16x8, wv);
+      for (int s = 0; s < NSR; ++s) {
+        const unsigned o = key_ok ? kr + 32 * s + 16 * hh : kOutside;
+        kop[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, o, 0, 0));
+      }
+      // the K half-tile: rows of 8 pieces, kBlocks 1 KiB blocks
+      constexpr int KL = 8;
+#pragma unroll
+      for (int i = 0; i < (NSR < NS ? (kBlocks + 2 * SL - 1) / (2 * SL) : 0); ++i) {
+        const int blk = i * 2 * SL + wave;
+        if (blk < kBlocks) {
+          const int pos = blk * 64 + lane;
+          const int r = pos / KL, c = (pos % KL) ^ swz<64>(r);
+          const unsigned o =
+              static_cast<unsigned>(((kb0 + r) * a.Hkv + kvh) * D + D / 2 + 8 * c) * 2u;
+          buffer_load_lds16(krs, smem + kKOff + blk * 1024, o);
+        }
+      }
+      // the V tile: 2 kBlocks 1 KiB blocks over the 2 SL waves, lane l at 16 l of its block
+#pragma unroll
+      for (int i = 0; i < 2 * kBlocks / (2 * SL); ++i) {
+        const int blk = i * 2 * SL + wave;
+        const int pos = blk * 64 + lane;
+        const int r = pos / C::kLoadsPerRow, c = (pos % C::kLoadsPerRow) ^ swz<D>(r);
+        const unsigned o = static_cast<unsigned>(((kb0 + r) * a.Hkv + kvh) * D + 8 * c) * 2u;
+        buffer_load_lds16(vrs, smem + kVOff + blk * 1024, o);
       }
     }
     f32x16 dk[NMT], dv[NMT];
@@ -192,179 +280,202 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a, int tile_
 
     // items: (32-row chunk from the first row that can see the tile's first key, query head of
     // the group), chunks from the last one down and heads inner, so that every workgroup walks
-    // the rows in the same order; step s holds items 2s (waves 0, 1) and 2s+1 (waves 2, 3)
+    // the rows in the same order; step s holds items SL s .. SL s + SL-1, item SL s + j on the
+    // wave pair j
     // With a sliding window (course page "Week 7. Attention", step 3) the rows end at the last
     // one whose window still reaches the tile's last key, unless the tile holds sink keys.
     const int qstart = a.causal ? max(0, kb0 - off) / kRows * kRows : 0;
     const int qlast = (WIN && kb0 >= a.n_sink) ? min(tq - 1, kb0 + 63 + W - 1 - off) : tq - 1;
     const int nchunk = qstart <= qlast ? (qlast - qstart) / kRows + 1 : 0;
-    const int nitems = G * nchunk;
-    const int nsteps = (nitems + 1) / 2;
+    const int nsteps = (G * nchunk + SL - 1) / SL;
 
-    // the next step's loads: two chunks of q and dout (kPieces 16-byte pieces per thread), and
-    // L and D of their rows (threads 0..63). Buffer loads with the range check doing the
-    // padding: rows past the end get an offset past the buffer and read zeros.
-    u32x4 pr_[kPieces];
-    float pL = 0.f, pD = 0.f;
-    bool pvalid = false;
-    auto load = [&](int st) {
-      int soff[2], srow[2], nrows[2];  // per slot: element offset / row index of the chunk's
-                                       // first row (head h), rows present
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        const int it = 2 * st + sl;
-        const int h = it % G, ci = nchunk - 1 - it / G;
-        const int p0 = qstart + ci * kRows;
-        const bool ok = it < nitems;
-        srow[sl] = ok ? p0 * a.Hq + kvh * G + h : 0;
-        soff[sl] = srow[sl] * D;
-        nrows[sl] = ok ? min(kRows, tq - p0) : 0;
-      }
-#pragma unroll
-      for (int i = 0; i < kPieces; ++i) {
-        constexpr int kSlotPieces = 2 * kMatPieces;
-        const int sl = (i * kThreads) / kSlotPieces;           // the same for the whole workgroup
-        const int mat = ((i * kThreads) / kMatPieces) & 1;     // 0: q, 1: dout
-        const int pc = (i * kThreads) % kMatPieces + tid;
-        const int r = pc / C::kLoadsPerRow, c = pc % C::kLoadsPerRow;
-        const unsigned vo =
-            r < nrows[sl] ? static_cast<unsigned>(soff[sl] + r * a.Hq * D + 8 * c) * 2u : kOutside;
-        pr_[i] = __builtin_amdgcn_raw_buffer_load_b128(mat ? grs : qrs, vo, 0, 0);
-      }
-      if (tid < 2 * kRows) {
-        const int sl = tid / kRows, r = tid % kRows;
-        pvalid = r < nrows[sl];
-        const unsigned vo = pvalid ? static_cast<unsigned>(srow[sl] + r * a.Hq) * 4u : kOutside;
-        pL = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, vo, 0, 0));
-        pD = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(drs, vo, 0, 0));
-      }
+    // (query head, chunk counted from the last one) of this wave pair's item: item it has head
+    // it % G and chunk it / G, followed from step to step without divisions
+    struct ItemPos {
+      int h, c;
     };
-    auto store = [&](int stage) {
-      char* base = smem + stage * kStageBytes;
-#pragma unroll
-      for (int i = 0; i < kPieces; ++i) {
-        const int sl = (i * kThreads) / (2 * kMatPieces);
-        const int mat = ((i * kThreads) / kMatPieces) & 1;
-        const int pc = (i * kThreads) % kMatPieces + tid;
-        const int r = pc / C::kLoadsPerRow, c = pc % C::kLoadsPerRow;
-        *reinterpret_cast<u32x4*>(base + sl * kSlotBytes + mat * C::kChunkBytes +
-                                  chunk_off<D>(r, c)) = pr_[i];
+    auto advance = [&](ItemPos p, int by) {
+      for (int i = 0; i < by; ++i) {
+        p.h = p.h + 1 == G ? 0 : p.h + 1;
+        p.c += p.h == 0;
       }
-      if (tid < 2 * kRows) {
-        const int sl = tid / kRows, r = tid % kRows;
-        float* ld = reinterpret_cast<float*>(base + sl * kSlotBytes + 2 * C::kChunkBytes);
-        ld[r] = pvalid ? pL * kLog2e : INFINITY;  // rows past the end: P = 0
-        ld[kRows + r] = pD;
-      }
+      return p;
     };
 
-    __syncthreads();  // the previous tile's reduction is done with the LDS
-    if (nsteps > 0) {
-      load(0);
-      store(0);
-    }
+    // a step's loads, straight into its LDS stage: the wave loads its pair's item's chunk of its
+    // matrix (q for the tile's first 32 keys, dout for the others) and the rows' L2 or D. Each
+    // 16-byte load fills 1 KiB of the chunk, lane l at 16 l, with the piece that the swizzle puts
+    // there. The buffer starts at the chunk's first row and ends at the sequence's end, so rows
+    // past the end read zeros (and add nothing below: their q and dout rows are zero); a step
+    // without an item for the pair reads zeros only.
+    auto load = [&](int stage, ItemPos ip) {
+      const bool ok = ip.c < nchunk;
+      const int p0 = qstart + (nchunk - 1 - ip.c) * kRows;
+      const int srow = ok ? p0 * a.Hq + kvh * G + ip.h : 0;
+      const int left = ok ? (tq - p0) * a.Hq - (kvh * G + ip.h) : 0;  // rows of the buffer
+      const __amdgpu_buffer_rsrc_t ms = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(mat + static_cast<int64_t>(srow) * D), 0, left * D * 2,
+          kBufWord3);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(rowv + srow), 0, left * 4, kBufWord3);
+      char* chunk = smem + ((slot * 2 + kh) * 2 + stage) * CB;
+#pragma unroll
+      for (int i = 0; i < kBlocks; ++i) {
+        const unsigned vo = static_cast<unsigned>((v0 ^ (16 * block_xor<D>(i))) +
+                                                  i * kBlockRows * a.Hq * D * 2);
+        buffer_load_lds16(ms, chunk + i * 1024, vo);
+      }
+      // 64 lanes write the 256-byte region: the 32 rows, then the same 32 rows again (unused)
+      buffer_load_lds4(rs, smem + kRowsOff + ((stage * 2 + kh) * SL + slot) * 256,
+                       static_cast<unsigned>(vrow));
+    };
+
+    ItemPos cur = advance(ItemPos{0, 0}, slot);  // item `slot` of step 0
+    if (nsteps > 0) load(0, cur);
     // nothing in flight from here on (the K/V operands included), so that the loop below waits
     // only for its own loads
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
     for (int st = 0; st < nsteps; ++st) {
-      if (st + 1 < nsteps) load(st + 1);  // in flight during this step
-      const int it = 2 * st + slot;
-      const int ci = nchunk - 1 - it / G;
-      const int qc = qstart + ci * kRows;
+      const int stage = st & 1;
+      const ItemPos nxt = advance(cur, SL);
+      // in flight during this step; the stage it fills was last read in step st-1, before the
+      // previous barrier
+      if (st + 1 < nsteps) load(stage ^ 1, nxt);
+      const int qc = qstart + (nchunk - 1 - cur.c) * kRows;
       // a chunk whose last row cannot see this wave's first key, or whose first row's window
       // starts past this wave's keys (none of them a sink), contributes nothing
-      const bool work = it < nitems && (!a.causal || qc + kRows - 1 + off >= kfirst) &&
+      const bool work = cur.c < nchunk && (!a.causal || qc + kRows - 1 + off >= kfirst) &&
                         (!WIN || kfirst < a.n_sink || kfirst + 31 > qc + off - W);
+      cur = nxt;
       if (work) {
-        char* sq = smem + (st & 1) * kStageBytes + slot * kSlotBytes;
-        char* sg = sq + C::kChunkBytes;
-        const float* sl = reinterpret_cast<const float*>(sg + C::kChunkBytes);
-        const float* sd = sl + kRows;
+        // the lane constants, opaque to the compiler for this step: the addresses below are
+        // formed per step (one instruction each) instead of being held in registers
+        asm volatile("" : "+v"(x1), "+v"(rb), "+v"(vb), "+v"(xk), "+v"(kb), "+v"(tbl), "+v"(tbh),
+                     "+v"(t6l), "+v"(t6h), "+v"(lrow));
+        // S = Q K^T and dP = dO V^T (the chunk rows as M, the wave's keys as N)
+        const int rbs = rb + stage * CB;
         f32x16 s_acc = {}, p_acc = {};
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const bf16x8 qa = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(sq + chunk_off<D>(n, 2 * s + hh)));
-          const bf16x8 ga = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(sg + chunk_off<D>(n, 2 * s + hh)));
-          s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[s], s_acc, 0, 0, 0);
-          p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vop[s], p_acc, 0, 0, 0);
+          const int o = ((s << 5) ^ x1) + rbs, ov = ((s << 5) ^ x1) + vb;
+          const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + o));
+          const bf16x8 ga =
+              __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + o + 2 * CB));
+          const bf16x8 vo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + ov));
+          bf16x8 ko;
+          if (s < NSR)
+            ko = kop[s < NSR ? s : 0];
+          else
+            ko = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(smem + ((((s - NSR) & 7) << 5) ^ xk) + kb));
+          s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, ko, s_acc, 0, 0, 0);
+          p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vo, p_acc, 0, 0, 0);
         }
-        float lrow[16], drow[16], pr[16], ds[16];
+        // P = 2^(S scale log2 e - L2) and dS = P (dP - D) for the lane's rows 8 g + 4 hh + t;
+        // the masks only in chunks where some (row, key) pair is hidden. Keys past the end need
+        // none: each lane's accumulator column is its own key, which is not written.
+        const int lrs = lrow + stage * 2 * SL * 256;
+        float pr[16], ds[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = (i >> 2) * 8 + 4 * hh + (i & 3);
-          lrow[i] = sl[r];
-          drow[i] = sd[r];
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(smem + lrs + 32 * g);
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            pr[4 * g + t] = fast_exp2(fmaf(s_acc[4 * g + t], sl2, -l2[t]));
+        }
+        const bool hide_causal = a.causal && kfirst + 31 > qc + off;
+        const bool hide_window =
+            WIN && !(kfirst + 31 < a.n_sink || kfirst > qc + kRows - 1 + off - W);
+        if (hide_causal || hide_window) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int p = qc + (i >> 2) * 8 + 4 * hh + (i & 3);
+            const bool vis = (!a.causal || key <= p + off) &&
+                             (!WIN || key > p + off - W || key < a.n_sink);
+            pr[i] = vis ? pr[i] : 0.f;
+          }
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int p = qc + (i >> 2) * 8 + 4 * hh + (i & 3);
-          const bool vis = key_ok && (!a.causal || key <= p + off) &&
-                           (!WIN || key > p + off - W || key < a.n_sink);
-          const float e = fast_exp2(fmaf(s_acc[i], sl2, -lrow[i]));
-          pr[i] = vis ? e : 0.f;
-          ds[i] = pr[i] * (p_acc[i] - drow[i]);
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 dd = *reinterpret_cast<const f32x4*>(smem + lrs + SL * 256 + 32 * g);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) ds[4 * g + t] = pr[4 * g + t] * (p_acc[4 * g + t] - dd[t]);
         }
+        // dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read transposed (k = the chunk
+        // rows in the accumulator order)
+        const int tls = tbl + stage * CB, ths = tbh + stage * CB;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const bf16x8 pb = pack_rows(pr, ks);
           const bf16x8 db = pack_rows(ds, ks);
 #pragma unroll
           for (int mt = 0; mt < NMT; ++mt) {
-            dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(sg, lane, 32 * mt, ks),
-                                                             pb, dv[mt], 0, 0, 0);
-            dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(sq, lane, 32 * mt, ks),
-                                                             db, dk[mt], 0, 0, 0);
+            const int ol = ((mt << 6) ^ t6l) + tls + ks * 16 * C::kPitch;
+            const int oh = ((mt << 6) ^ t6h) + ths + ks * 16 * C::kPitch;
+            const u32x2 gl = lds_read_tr(smem, ol + 2 * CB), gh = lds_read_tr(smem, oh + 2 * CB);
+            dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, u32x4{gl[0], gl[1], gh[0], gh[1]}), pb, dv[mt], 0, 0,
+                0);
+            const u32x2 ql = lds_read_tr(smem, ol), qh = lds_read_tr(smem, oh);
+            dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, u32x4{ql[0], ql[1], qh[0], qh[1]}), db, dk[mt], 0, 0,
+                0);
           }
         }
       }
-      // the other stage was last read in step st-1, before the previous barrier
-      if (st + 1 < nsteps) store((st + 1) & 1);
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the next stage is in place
       __syncthreads();
     }
 
-    // waves 2, 3 hand their partial dK^T, dV^T to waves 0, 1 (same keys), which write them
-    float* red = reinterpret_cast<float*>(smem);
-    if (slot == 1) {
-      float* base = red + kh * 2 * 32 * D;
+    // cross-wave sums over the slots (same keys): the upper half of the slots hands its partial
+    // dK^T, dV^T to the lower half through LDS, halving until slot 0 holds the sum
+    // (a wave's area: kWaveRed bytes at its lane's float, the values 256 bytes apart)
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          base[(mt * 16 + i) * 64 + lane] = dk[mt][i];
-          base[32 * D + (mt * 16 + i) * 64 + lane] = dv[mt][i];
-        }
-    }
-    __syncthreads();
-    if (slot == 0) {
-      const float* base = red + kh * 2 * 32 * D;
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          dk[mt][i] += base[(mt * 16 + i) * 64 + lane];
-          dv[mt][i] += base[32 * D + (mt * 16 + i) * 64 + lane];
-        }
-      if (key_ok) {
-        uint16_t* DK = static_cast<uint16_t*>(a.dk);
-        uint16_t* DV = static_cast<uint16_t*>(a.dv);
-        const int64_t orow = ((k0 + key) * a.Hkv + kvh) * D;
+    for (int half = SL / 2; half > 0; half >>= 1) {
+      // the area of wave pair (slot mod half), kept opaque so that the addresses stay one
+      // register plus the instructions' offsets
+      int area = ((slot & (half - 1)) * 2 + kh) * kWaveRed + 4 * lane;
+      asm volatile("" : "+v"(area));
+      if (slot >= half && slot < 2 * half) {
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int dd = mt * 32 + g4 * 8 + hh * 4;
-            u32x2 wk, wv;
-            wk[0] = pack_bf16x2(dk[mt][4 * g4] * a.scale, dk[mt][4 * g4 + 1] * a.scale);
-            wk[1] = pack_bf16x2(dk[mt][4 * g4 + 2] * a.scale, dk[mt][4 * g4 + 3] * a.scale);
-            wv[0] = pack_bf16x2(dv[mt][4 * g4], dv[mt][4 * g4 + 1]);
-            wv[1] = pack_bf16x2(dv[mt][4 * g4 + 2], dv[mt][4 * g4 + 3]);
-            *reinterpret_cast<u32x2*>(DK + orow + dd) = wk;
-            *reinterpret_cast<u32x2*>(DV + orow + dd) = wv;
+          for (int i = 0; i < 16; ++i) {
+            *reinterpret_cast<float*>(smem + area + (mt * 16 + i) * 256) = dk[mt][i];
+            *reinterpret_cast<float*>(smem + area + 32 * D * 4 + (mt * 16 + i) * 256) = dv[mt][i];
           }
       }
+      __syncthreads();
+      if (slot < half) {
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            dk[mt][i] += *reinterpret_cast<const float*>(smem + area + (mt * 16 + i) * 256);
+            dv[mt][i] +=
+                *reinterpret_cast<const float*>(smem + area + 32 * D * 4 + (mt * 16 + i) * 256);
+          }
+      }
+      if (half > 1) __syncthreads();  // read before the next round overwrites
+    }
+    if (slot == 0 && key_ok) {
+      uint16_t* DK = static_cast<uint16_t*>(a.dk);
+      uint16_t* DV = static_cast<uint16_t*>(a.dv);
+      const int64_t orow = ((k0 + key) * a.Hkv + kvh) * D;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int dd = mt * 32 + g4 * 8 + hh * 4;
+          u32x2 wk, wv;
+          wk[0] = pack_bf16x2(dk[mt][4 * g4] * a.scale, dk[mt][4 * g4 + 1] * a.scale);
+          wk[1] = pack_bf16x2(dk[mt][4 * g4 + 2] * a.scale, dk[mt][4 * g4 + 3] * a.scale);
+          wv[0] = pack_bf16x2(dv[mt][4 * g4], dv[mt][4 * g4 + 1]);
+          wv[1] = pack_bf16x2(dv[mt][4 * g4 + 2], dv[mt][4 * g4 + 3]);
+          *reinterpret_cast<u32x2*>(DK + orow + dd) = wk;
+          *reinterpret_cast<u32x2*>(DV + orow + dd) = wv;
+        }
     }
   }
 }
@@ -441,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
       qop[s] = __builtin_bit_cast(bf16x8, wq);
       gop[s] = __builtin_bit_cast(bf16x8, wg);
     }
-    const float Lr = valid ? a.lse[qrow] * kLog2e : INFINITY;
+    const float Lr = valid ? a.L2row[qrow] : INFINITY;
     const float Dq = valid ? a.Drow[qrow] : 0.f;
     f32x16 dq[NMT];
 #pragma unroll
@@ -554,7 +665,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const int64_t rblocks = (rows * (D / 8) + 255) / 256;
   hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3(static_cast<unsigned>(rblocks)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(a.out), static_cast<const uint16_t*>(a.dout),
-                     a.Drow, rows);
+                     a.lse, a.Drow, a.L2row, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the grid covers the longest item; workgroups past a shorter item's tiles return at once
@@ -563,11 +674,11 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const int key_tiles = (max_tkv + 63) / 64;
   const int tile_wgs = a.causal ? (key_tiles + 1) / 2 : key_tiles;
   if (a.window > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(a.B * a.Hkv * tile_wgs), dim3(kThreads), 0,
-                       s, a, tile_wgs);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, kDkdvSlots>), dim3(a.B * a.Hkv * tile_wgs),
+                       dim3(128 * kDkdvSlots), 0, s, a, tile_wgs);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(a.B * a.Hkv * tile_wgs), dim3(kThreads),
-                       0, s, a, tile_wgs);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, kDkdvSlots>), dim3(a.B * a.Hkv * tile_wgs),
+                       dim3(128 * kDkdvSlots), 0, s, a, tile_wgs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;

@@ -457,9 +457,12 @@ gqa_status_t gqa_attn_decode_ex(const void* q, const void* k_cache, const void* 
                      workspace, workspace_bytes, dtype, stream);
 }
 
+// two per-row float arrays (dout . out, then lse log2 e), each rounded up to 256 bytes
+static size_t backward_row_array_bytes(size_t rows) { return (rows * sizeof(float) + 255) / 256 * 256; }
+
 size_t gqa_attn_backward_workspace_bytes(int B, int Tq, int Hq) {
   if (B <= 0 || Tq <= 0 || Hq <= 0) return 0;
-  return (static_cast<size_t>(B) * Tq * Hq * sizeof(float) + 15) / 16 * 16;
+  return 2 * backward_row_array_bytes(static_cast<size_t>(B) * Tq * Hq);
 }
 
 static gqa_status_t backward_impl(const void* q, const void* k, const void* v, const void* out,
@@ -532,6 +535,8 @@ static gqa_status_t backward_impl(const void* q, const void* k, const void* v, c
   a.dout = dout;
   a.lse = lse;
   a.Drow = static_cast<float*>(workspace);
+  a.L2row = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                     backward_row_array_bytes(static_cast<size_t>(rows)));
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
