@@ -330,103 +330,126 @@ __global__ __launch_bounds__(128 * SL) void bwd_dkdv_kernel(BwdArgs a, int tile_
                        static_cast<unsigned>(vrow));
     };
 
+    // One item's work in two parts. m1v: S = Q K^T and dP = dO V^T (the chunk rows as M, the
+    // wave's keys as N), then P = 2^(S scale log2 e - L2) and dS = P (dP - D), packed as the B
+    // operands of the second part; returns whether the item contributes. m3: dV^T += dO^T P and
+    // dK^T += Q^T dS, with dO^T and Q^T read transposed (k = the chunk rows in the accumulator
+    // order). The lane constants are opaque to the compiler at each call: the addresses are
+    // formed per call (one instruction each) instead of being held in registers.
+    bf16x8 pk[2], dsk[2];
+    auto m1v = [&](int stage, ItemPos ip) {
+      const int qc = qstart + (nchunk - 1 - ip.c) * kRows;
+      // a chunk whose last row cannot see this wave's first key, or whose first row's window
+      // starts past this wave's keys (none of them a sink), contributes nothing
+      const bool work = ip.c < nchunk && (!a.causal || qc + kRows - 1 + off >= kfirst) &&
+                        (!WIN || kfirst < a.n_sink || kfirst + 31 > qc + off - W);
+      if (!work) return false;
+      asm volatile("" : "+v"(x1), "+v"(rb), "+v"(vb), "+v"(xk), "+v"(kb), "+v"(lrow));
+      const int rbs = rb + stage * CB;
+      f32x16 s_acc = {}, p_acc = {};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int o = ((s << 5) ^ x1) + rbs, ov = ((s << 5) ^ x1) + vb;
+        const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + o));
+        const bf16x8 ga =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + o + 2 * CB));
+        const bf16x8 vo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + ov));
+        bf16x8 ko;
+        if (s < NSR)
+          ko = kop[s < NSR ? s : 0];
+        else
+          ko = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(smem + ((((s - NSR) & 7) << 5) ^ xk) + kb));
+        s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, ko, s_acc, 0, 0, 0);
+        p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vo, p_acc, 0, 0, 0);
+      }
+      // the lane's rows are 8 g + 4 hh + t; the masks only in chunks where some (row, key) pair
+      // is hidden. Keys past the end need none: each lane's accumulator column is its own key,
+      // which is not written.
+      const int lrs = lrow + stage * 2 * SL * 256;
+      float pr[16], ds[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(smem + lrs + 32 * g);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          pr[4 * g + t] = fast_exp2(fmaf(s_acc[4 * g + t], sl2, -l2[t]));
+      }
+      const bool hide_causal = a.causal && kfirst + 31 > qc + off;
+      const bool hide_window =
+          WIN && !(kfirst + 31 < a.n_sink || kfirst > qc + kRows - 1 + off - W);
+      if (hide_causal || hide_window) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int p = qc + (i >> 2) * 8 + 4 * hh + (i & 3);
+          const bool vis = (!a.causal || key <= p + off) &&
+                           (!WIN || key > p + off - W || key < a.n_sink);
+          pr[i] = vis ? pr[i] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 dd = *reinterpret_cast<const f32x4*>(smem + lrs + SL * 256 + 32 * g);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ds[4 * g + t] = pr[4 * g + t] * (p_acc[4 * g + t] - dd[t]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        pk[ks] = pack_rows(pr, ks);
+        dsk[ks] = pack_rows(ds, ks);
+      }
+      return true;
+    };
+    auto m3 = [&](int stage) {
+      asm volatile("" : "+v"(tbl), "+v"(tbh), "+v"(t6l), "+v"(t6h));
+      const int tls = tbl + stage * CB, ths = tbh + stage * CB;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+          const int ol = ((mt << 6) ^ t6l) + tls + ks * 16 * C::kPitch;
+          const int oh = ((mt << 6) ^ t6h) + ths + ks * 16 * C::kPitch;
+          const u32x2 gl = lds_read_tr(smem, ol + 2 * CB), gh = lds_read_tr(smem, oh + 2 * CB);
+          dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, u32x4{gl[0], gl[1], gh[0], gh[1]}), pk[ks], dv[mt], 0, 0,
+              0);
+          const u32x2 ql = lds_read_tr(smem, ol), qh = lds_read_tr(smem, oh);
+          dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, u32x4{ql[0], ql[1], qh[0], qh[1]}), dsk[ks], dk[mt], 0,
+              0, 0);
+        }
+      }
+    };
+
+    // Two groups of wave pairs, half a step apart, so that on each SIMD (one wave of each group)
+    // one wave's softmax runs beside the other's matrix products: group 0 (slots 0 .. SL/2-1)
+    // does m1v of step st's item in the first half of step st and m3 in the second half; group 1
+    // does m1v in the second half and m3 in the first half of step st+1. Each slot's two stages
+    // are refilled one step ahead, at the start of the slot's m1v, into the stage that its m3 of
+    // the previous step finished reading before the last barrier.
+    // Every wave runs the same steps (m1v, barrier, m3, barrier); group 1 passes one barrier
+    // before its first step and group 0 one after its last, so the groups' barriers pair up half
+    // a step apart.
+    const int lag = slot < SL / 2 ? 0 : 1;
     ItemPos cur = advance(ItemPos{0, 0}, slot);  // item `slot` of step 0
     if (nsteps > 0) load(0, cur);
     // nothing in flight from here on (the K/V operands included), so that the loop below waits
     // only for its own loads
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
+    if (lag) __syncthreads();
     for (int st = 0; st < nsteps; ++st) {
       const int stage = st & 1;
       const ItemPos nxt = advance(cur, SL);
-      // in flight during this step; the stage it fills was last read in step st-1, before the
-      // previous barrier
       if (st + 1 < nsteps) load(stage ^ 1, nxt);
-      const int qc = qstart + (nchunk - 1 - cur.c) * kRows;
-      // a chunk whose last row cannot see this wave's first key, or whose first row's window
-      // starts past this wave's keys (none of them a sink), contributes nothing
-      const bool work = cur.c < nchunk && (!a.causal || qc + kRows - 1 + off >= kfirst) &&
-                        (!WIN || kfirst < a.n_sink || kfirst + 31 > qc + off - W);
+      const bool work = m1v(stage, cur);
       cur = nxt;
-      if (work) {
-        // the lane constants, opaque to the compiler for this step: the addresses below are
-        // formed per step (one instruction each) instead of being held in registers
-        asm volatile("" : "+v"(x1), "+v"(rb), "+v"(vb), "+v"(xk), "+v"(kb), "+v"(tbl), "+v"(tbh),
-                     "+v"(t6l), "+v"(t6h), "+v"(lrow));
-        // S = Q K^T and dP = dO V^T (the chunk rows as M, the wave's keys as N)
-        const int rbs = rb + stage * CB;
-        f32x16 s_acc = {}, p_acc = {};
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const int o = ((s << 5) ^ x1) + rbs, ov = ((s << 5) ^ x1) + vb;
-          const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + o));
-          const bf16x8 ga =
-              __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + o + 2 * CB));
-          const bf16x8 vo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + ov));
-          bf16x8 ko;
-          if (s < NSR)
-            ko = kop[s < NSR ? s : 0];
-          else
-            ko = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4*>(smem + ((((s - NSR) & 7) << 5) ^ xk) + kb));
-          s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, ko, s_acc, 0, 0, 0);
-          p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vo, p_acc, 0, 0, 0);
-        }
-        // P = 2^(S scale log2 e - L2) and dS = P (dP - D) for the lane's rows 8 g + 4 hh + t;
-        // the masks only in chunks where some (row, key) pair is hidden. Keys past the end need
-        // none: each lane's accumulator column is its own key, which is not written.
-        const int lrs = lrow + stage * 2 * SL * 256;
-        float pr[16], ds[16];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 l2 = *reinterpret_cast<const f32x4*>(smem + lrs + 32 * g);
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            pr[4 * g + t] = fast_exp2(fmaf(s_acc[4 * g + t], sl2, -l2[t]));
-        }
-        const bool hide_causal = a.causal && kfirst + 31 > qc + off;
-        const bool hide_window =
-            WIN && !(kfirst + 31 < a.n_sink || kfirst > qc + kRows - 1 + off - W);
-        if (hide_causal || hide_window) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int p = qc + (i >> 2) * 8 + 4 * hh + (i & 3);
-            const bool vis = (!a.causal || key <= p + off) &&
-                             (!WIN || key > p + off - W || key < a.n_sink);
-            pr[i] = vis ? pr[i] : 0.f;
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 dd = *reinterpret_cast<const f32x4*>(smem + lrs + SL * 256 + 32 * g);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) ds[4 * g + t] = pr[4 * g + t] * (p_acc[4 * g + t] - dd[t]);
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read transposed (k = the chunk
-        // rows in the accumulator order)
-        const int tls = tbl + stage * CB, ths = tbh + stage * CB;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 pb = pack_rows(pr, ks);
-          const bf16x8 db = pack_rows(ds, ks);
-#pragma unroll
-          for (int mt = 0; mt < NMT; ++mt) {
-            const int ol = ((mt << 6) ^ t6l) + tls + ks * 16 * C::kPitch;
-            const int oh = ((mt << 6) ^ t6h) + ths + ks * 16 * C::kPitch;
-            const u32x2 gl = lds_read_tr(smem, ol + 2 * CB), gh = lds_read_tr(smem, oh + 2 * CB);
-            dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, u32x4{gl[0], gl[1], gh[0], gh[1]}), pb, dv[mt], 0, 0,
-                0);
-            const u32x2 ql = lds_read_tr(smem, ol), qh = lds_read_tr(smem, oh);
-            dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, u32x4{ql[0], ql[1], qh[0], qh[1]}), db, dk[mt], 0, 0,
-                0);
-          }
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the next stage is in place
+      __syncthreads();
+      if (work) m3(stage);
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the next step's stage is in place
       __syncthreads();
     }
+    if (!lag) __syncthreads();
 
     // cross-wave sums over the slots (same keys): the upper half of the slots hands its partial
     // dK^T, dV^T to the lower half through LDS, halving until slot 0 holds the sum
