@@ -79,7 +79,7 @@ def prefill_flops(w):
 
 
 # kernel sources of legs that have no traffic record
-SOURCES = {"backward": ("backward.hip", "common.hpp")}
+SOURCES = {"backward": ("backward.hip", "backward.hpp", "common.hpp")}
 
 
 def kernel_source_sha(which="prefill"):
@@ -515,7 +515,7 @@ def main():
             bw = bench_backward(gqa, workloads.LLAMA_PREFILL, S, Wu, torch, 2000)
             log(f"backward: {bw['avg_ms'] * 1e3:.1f} us, {bw['tflops']:.1f} TFLOP/s")
             legs["backward"] = (bw, mfma_roofline(
-                bw, "bwd_rowdot + bwd_dkdv_kernel<128, false> + bwd_dq_kernel<128, false>",
+                bw, "bwd_rowdot + bwd_dkdv_kernel<128, false, 4> + bwd_dq_kernel<128, false>",
                 sha_key="backward"),
                 prefill_config(workloads.LLAMA_PREFILL))
         elif name == "gva":

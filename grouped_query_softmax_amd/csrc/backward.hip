@@ -29,9 +29,25 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "backward.hpp"
 
 namespace gqa {
 namespace {
+
+// Buffer loads that write LDS directly (buffer_load ... lds): the wave's data goes to the
+// (wave-uniform) LDS address `lds` plus the load size times the lane index; voff is the lane's
+// byte offset in the buffer (range-checked: past num_records the lane writes zeros).
+__device__ __forceinline__ __attribute__((address_space(3))) void* to_lds(char* p) {
+  return (__attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, char* lds,
+                                                  unsigned voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, to_lds(lds), 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t rs, char* lds,
+                                                 unsigned voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, to_lds(lds), 4, voff, 0, 0, 0);
+}
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -133,7 +149,8 @@ constexpr bool block_xor_is_uniform() {
 // WIN: a sliding window (with sinks) is on; the plain kernels carry none of its tests.
 // SL: query items per step (wave pairs); the workgroup has 2 SL waves.
 template <int D, bool WIN, int SL>
-__global__ __launch_bounds__(128 * SL) void bwd_dkdv_kernel(BwdArgs a, int tile_wgs) {
+__global__ __launch_bounds__(128 * SL) void bwd_dkdv_kernel(BwdArgs a, const float* L2row,
+                                                            int tile_wgs) {
   using C = BwdCfg<D>;
   constexpr int NS = C::kNS, NMT = C::kNMT;
   constexpr int CB = C::kChunkBytes;
@@ -187,7 +204,7 @@ __global__ __launch_bounds__(128 * SL) void bwd_dkdv_kernel(BwdArgs a, int tile_
   // this sequence's q or dout (the wave's matrix) and its rows' L2 or D; K and V
   const int64_t qe0 = q0 * a.Hq;
   const uint16_t* mat = static_cast<const uint16_t*>(kh ? a.dout : a.q) + qe0 * D;
-  const float* rowv = (kh ? a.Drow : a.L2row) + qe0;
+  const float* rowv = (kh ? a.Drow : L2row) + qe0;
   const int kbytes = tkv * a.Hkv * D * 2;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(static_cast<const void*>(static_cast<const uint16_t*>(a.k) + k0 * a.Hkv * D)),
@@ -437,19 +454,22 @@ __global__ __launch_bounds__(128 * SL) void bwd_dkdv_kernel(BwdArgs a, int tile_
     // only for its own loads
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    if (lag) __syncthreads();
+    if (lag) __builtin_amdgcn_s_barrier();
     for (int st = 0; st < nsteps; ++st) {
       const int stage = st & 1;
       const ItemPos nxt = advance(cur, SL);
       if (st + 1 < nsteps) load(stage ^ 1, nxt);
       const bool work = m1v(stage, cur);
       cur = nxt;
-      __syncthreads();
+      // only pairs the groups' halves (no data passes here): a bare barrier, without the fence
+      // that would wait for the loads just issued
+      __builtin_amdgcn_s_barrier();
       if (work) m3(stage);
       __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the next step's stage is in place
       __syncthreads();
     }
-    if (!lag) __syncthreads();
+    if (!lag) __builtin_amdgcn_s_barrier();
+    __syncthreads();  // every wave's m3 is done before the LDS is reused below
 
     // cross-wave sums over the slots (same keys): the upper half of the slots hands its partial
     // dK^T, dV^T to the lower half through LDS, halving until slot 0 holds the sum
@@ -504,9 +524,9 @@ __global__ __launch_bounds__(128 * SL) void bwd_dkdv_kernel(BwdArgs a, int tile_
 }
 
 template <int D, bool WIN>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per_wg,
-                                                          int heads_per_wg, int head_tiles,
-                                                          int gz) {
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, const float* L2row,
+                                                          int pos_per_wg, int heads_per_wg,
+                                                          int head_tiles, int gz) {
   using C = BwdCfg<D>;
   constexpr int NS = C::kNS, NMT = C::kNMT;
   __shared__ __attribute__((aligned(16))) char smem[4 * C::kChunkBytes];  // 2 x (K, V) chunks
@@ -575,7 +595,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, int pos_per
       qop[s] = __builtin_bit_cast(bf16x8, wq);
       gop[s] = __builtin_bit_cast(bf16x8, wg);
     }
-    const float Lr = valid ? a.L2row[qrow] : INFINITY;
+    const float Lr = valid ? L2row[qrow] : INFINITY;
     const float Dq = valid ? a.Drow[qrow] : 0.f;
     f32x16 dq[NMT];
 #pragma unroll
@@ -686,9 +706,10 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const int64_t rows =
       (a.items.cu ? static_cast<int64_t>(a.Tq) : static_cast<int64_t>(a.B) * a.Tq) * a.Hq;
   const int64_t rblocks = (rows * (D / 8) + 255) / 256;
+  float* L2row = a.Drow + backward_row_array_floats(static_cast<size_t>(rows));
   hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3(static_cast<unsigned>(rblocks)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(a.out), static_cast<const uint16_t*>(a.dout),
-                     a.lse, a.Drow, a.L2row, rows);
+                     a.lse, a.Drow, L2row, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the grid covers the longest item; workgroups past a shorter item's tiles return at once
@@ -698,10 +719,10 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const int tile_wgs = a.causal ? (key_tiles + 1) / 2 : key_tiles;
   if (a.window > 0)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, kDkdvSlots>), dim3(a.B * a.Hkv * tile_wgs),
-                       dim3(128 * kDkdvSlots), 0, s, a, tile_wgs);
+                       dim3(128 * kDkdvSlots), 0, s, a, L2row, tile_wgs);
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, kDkdvSlots>), dim3(a.B * a.Hkv * tile_wgs),
-                       dim3(128 * kDkdvSlots), 0, s, a, tile_wgs);
+                       dim3(128 * kDkdvSlots), 0, s, a, L2row, tile_wgs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;
@@ -713,11 +734,11 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const int gz = a.causal ? (pos_tiles + 1) / 2 : pos_tiles;
   const dim3 qgrid(a.B * a.Hkv * head_tiles * gz);
   if (a.window > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), qgrid, dim3(kThreads), 0, s, a, pos_per_wg,
-                       heads_per_wg, head_tiles, gz);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), qgrid, dim3(kThreads), 0, s, a, L2row,
+                       pos_per_wg, heads_per_wg, head_tiles, gz);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), qgrid, dim3(kThreads), 0, s, a, pos_per_wg,
-                       heads_per_wg, head_tiles, gz);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), qgrid, dim3(kThreads), 0, s, a, L2row,
+                       pos_per_wg, heads_per_wg, head_tiles, gz);
   return hipGetLastError();
 }
 

@@ -69,21 +69,6 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* base, int byte_off) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-// Buffer loads that write LDS directly (buffer_load ... lds): the wave's data goes to the
-// (wave-uniform) LDS address `lds` plus the load size times the lane index; voff is the lane's
-// byte offset in the buffer (range-checked: past num_records the lane writes zeros).
-__device__ __forceinline__ __attribute__((address_space(3))) void* to_lds(char* p) {
-  return (__attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, char* lds,
-                                                  unsigned voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, to_lds(lds), 16, voff, 0, 0, 0);
-}
-__device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t rs, char* lds,
-                                                 unsigned voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, to_lds(lds), 4, voff, 0, 0, 0);
-}
-
 // Keeps the compiler from moving LDS accesses across this point. For an LDS region written and
 // read back only by one wave, whose LDS instructions execute in program order, this is all the
 // ordering needed (no wait, no workgroup barrier).
@@ -251,7 +236,6 @@ struct BwdArgs {
   const void* dout;
   const float* lse;  // [B, Tq, Hq] natural-log log-sum-exp of the forward rows
   float* Drow;       // workspace [B, Tq, Hq]: dout . out
-  float* L2row;      // workspace [B, Tq, Hq]: lse log2 e
   void* dq;
   void* dk;
   void* dv;

@@ -10,6 +10,7 @@
 
 #include "gqa_attn.h"
 #include "common.hpp"
+#include "backward.hpp"
 
 static_assert(GQA_DECODE_SCRATCH_BYTES == gqa::kDecodeScratchBytes,
               "the header's scratch limit is the size of the library's array");
@@ -457,12 +458,9 @@ gqa_status_t gqa_attn_decode_ex(const void* q, const void* k_cache, const void* 
                      workspace, workspace_bytes, dtype, stream);
 }
 
-// two per-row float arrays (dout . out, then lse log2 e), each rounded up to 256 bytes
-static size_t backward_row_array_bytes(size_t rows) { return (rows * sizeof(float) + 255) / 256 * 256; }
-
 size_t gqa_attn_backward_workspace_bytes(int B, int Tq, int Hq) {
   if (B <= 0 || Tq <= 0 || Hq <= 0) return 0;
-  return 2 * backward_row_array_bytes(static_cast<size_t>(B) * Tq * Hq);
+  return 2 * gqa::backward_row_array_floats(static_cast<size_t>(B) * Tq * Hq) * sizeof(float);
 }
 
 static gqa_status_t backward_impl(const void* q, const void* k, const void* v, const void* out,
@@ -535,8 +533,6 @@ static gqa_status_t backward_impl(const void* q, const void* k, const void* v, c
   a.dout = dout;
   a.lse = lse;
   a.Drow = static_cast<float*>(workspace);
-  a.L2row = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                     backward_row_array_bytes(static_cast<size_t>(rows)));
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

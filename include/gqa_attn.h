@@ -259,7 +259,8 @@ gqa_status_t gqa_attn_decode_ex(const void* q, const void* k_cache, const void* 
  * The gradient of a key/value head is the SUM of the gradients of the G query heads that read it
  * (K3 notes, section 4, backward: the backward of a replication sums over the copies).
  * workspace: caller-owned device memory of at least gqa_attn_backward_workspace_bytes(B, Tq, Hq)
- * bytes (per-row dout . out). bf16 only, d in {64, 128}. Outputs must not overlap the inputs,
+ * bytes, 16-byte aligned (two per-row float arrays: dout . out and lse log2 e). bf16 only,
+ * d in {64, 128}. Outputs must not overlap the inputs,
  * the workspace or each other (GQA_ERR_ALIAS). Errors as for gqa_attn_prefill.
  */
 size_t gqa_attn_backward_workspace_bytes(int B, int Tq, int Hq);
