@@ -582,6 +582,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, const float
     const int hi = ht * heads_per_wg + col % heads_per_wg;
     const bool valid = pl < pos_per_wg && p0 + pl < tq && hi < G;
     const int pos = min(p0 + pl, tq - 1);
+    const int pmin = p0 + (wave * 32) / heads_per_wg;  // the wave's first position
     const int hq = kvh * G + min(hi, G - 1);
     const int64_t qrow = (q0 + pos) * a.Hq + hq;
 
@@ -662,15 +663,23 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a, const float
         s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[s], s_acc, 0, 0, 0);
         p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gop[s], p_acc, 0, 0, 0);
       }
+      // P (in place of S) and dS; the masks only in chunks that cross the diagonal of some of the
+      // wave's positions (or with a window). Keys past the end need none: their K and V rows
+      // read zeros, so they add nothing to dQ.
       float ds[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kk = kc + (i >> 2) * 8 + 4 * hh + (i & 3);
-        const bool vis = kk < tkv && (!a.causal || kk <= pos + off) &&
-                         (!WIN || kk > pos + off - W || kk < a.n_sink);
-        const float pv2 = vis ? fast_exp2(fmaf(s_acc[i], sl2, -Lr)) : 0.f;
-        ds[i] = pv2 * (p_acc[i] - Dq);
+      for (int i = 0; i < 16; ++i) s_acc[i] = fast_exp2(fmaf(s_acc[i], sl2, -Lr));
+      if (WIN || (a.causal && kc + kRows - 1 > pmin + off)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kk = kc + (i >> 2) * 8 + 4 * hh + (i & 3);
+          const bool vis = kk < tkv && (!a.causal || kk <= pos + off) &&
+                           (!WIN || kk > pos + off - W || kk < a.n_sink);
+          s_acc[i] = vis ? s_acc[i] : 0.f;
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] = s_acc[i] * (p_acc[i] - Dq);
       // dQ^T += K^T dS^T (K^T read transposed in the accumulator's key order)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
