@@ -209,12 +209,13 @@ __global__ __launch_bounds__(128 * SL) void bwd_dkdv_kernel(BwdArgs a, const flo
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(static_cast<const void*>(static_cast<const uint16_t*>(a.k) + k0 * a.Hkv * D)),
       0, kbytes, kBufWord3);
-  // V goes through LDS (the tile's 64 rows, loaded straight into LDS by all waves)
+  // (V, and half of K with D = 128, go through per-tile LDS tiles loaded by all waves)
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(static_cast<const void*>(static_cast<const uint16_t*>(a.v) + k0 * a.Hkv * D)),
       0, kbytes, kBufWord3);
 
-  // lane constants of the LDS addresses (byte offsets within the wave's slot region):
+  // lane constants of the LDS addresses (byte offsets into smem; stage and matrix are added as
+  // multiples of the chunk size):
   //   row reads (A operands with the chunk rows as M): piece 2s + hh of row n lies at
   //   rb + ((s << 5) ^ x1) (the swizzle's upper bits move whole 32-byte pairs);
   //   transposed reads: rows 4 hh + (j >> 2) (+8), pieces 4 mt + 2 sub + ((j >> 1) & 1), half
@@ -239,8 +240,8 @@ __global__ __launch_bounds__(128 * SL) void bwd_dkdv_kernel(BwdArgs a, const flo
   // lane constants of the loads: piece i of the wave's chunk, 16-byte position 64 i + lane, holds
   // row i * kBlockRows + lane / kLoadsPerRow, piece (lane % kLoadsPerRow) ^ swz(row)
   const int lr = lane / C::kLoadsPerRow;
-  int v0 = lr * a.Hq * D * 2 + 16 * ((lane % C::kLoadsPerRow) ^ swz<D>(lr));
-  int vrow = (lane & 31) * a.Hq * 4;
+  const int v0 = lr * a.Hq * D * 2 + 16 * ((lane % C::kLoadsPerRow) ^ swz<D>(lr));
+  const int vrow = (lane & 31) * a.Hq * 4;
 
   // causal: a workgroup takes the key tile pair (z, key_tiles-1-z), equal work per pair
   int tiles[2];
