@@ -8,17 +8,19 @@
 // backward: the backward of a replication is a sum over the copies).
 //
 // Three kernels:
-//   * bwd_rowdot: D = dout.out per query row (fp32).
-//   * bwd_dkdv: one workgroup of 4 waves per (sequence, key/value head, 64-key tile; causal: a
-//     pair of tiles, heavy and light). Waves 0 and 2 own the tile's first 32 keys, waves 1 and 3
-//     the other 32, each with the keys' K^T, V^T operands and its own dK^T, dV^T accumulators in
-//     registers. The 32-row chunks of (q, dout, L, D) of all query heads of the group stream
-//     through two LDS stages two at a time (the next pair's loads in flight): waves 0, 1 take the
-//     first chunk of a pair, waves 2, 3 the second, so every chunk read from memory feeds 64
-//     keys. Waves 2, 3 hand their partial sums to waves 0, 1 through LDS at the end of a tile.
-//     Per chunk: S = Q K^T and dP = dO V^T with the keys as MFMA columns, P and dS in fp32,
-//     then dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T read transposed from LDS
-//     (ds_read_b64_tr_b16) in the key order of the accumulators.
+//   * bwd_rowdot: per query row D = dout.out and L2 = L log2 e (fp32, into the workspace).
+//   * bwd_dkdv: one workgroup of 8 waves (two per SIMD) per (sequence, key/value head, 64-key
+//     tile; causal: a pair of tiles, heavy and light). Even waves own the tile's first 32 keys,
+//     odd waves the other 32, each with its own dK^T, dV^T accumulators in registers; K (half
+//     of it with d = 128) sits in registers as MFMA operands, V and the other half of K in
+//     per-tile LDS tiles. The items -- 32-row chunks of q and dout with their rows' L2 and D,
+//     for every query head of the group -- go four per step, one per wave pair, loaded straight
+//     into double-buffered LDS stages a step ahead; every chunk read from memory feeds 64 keys.
+//     Per item: S = Q K^T and dP = dO V^T with the keys as MFMA columns, P and dS in fp32, then
+//     dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T read transposed from LDS
+//     (ds_read_b64_tr_b16) in the key order of the accumulators. The two halves of the wave
+//     pairs run half a step apart (one's softmax beside the other's products), and the four
+//     slots' partial sums are added through LDS at the end of a tile.
 //   * bwd_dq: one workgroup of 4 waves per (sequence, key/value head, 128 (position, head) query
 //     columns; causal: a pair of such tiles, heavy and light); 32-key chunks of K and V stream
 //     through two LDS buffers with the next chunk's loads in flight. Per chunk: S^T = K Q^T and
