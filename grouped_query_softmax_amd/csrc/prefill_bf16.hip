@@ -495,11 +495,14 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
         m_run = m_new;
       }
       const float mref = m_run == -INFINITY ? 0.f : m_run;
-      float psum = 0.f;
+      // the row sum in four independent partial sums (a chain of 16 dependent dot products
+      // would pace the phase)
+      float psum4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
+          float& psum = psum4[2 * h + h2];
           uint32_t pw[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -515,7 +518,7 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
           const u32x4 w = {pw[0], pw[1], pw[2], pw[3]};
           pb[2 * h + h2] = __builtin_bit_cast(bf16x8, w);
         }
-      l_run += psum;
+      l_run += (psum4[0] + psum4[1]) + (psum4[2] + psum4[3]);
     };
 
     __syncthreads();  // the previous query tile's readers are done with every stage
