@@ -79,7 +79,7 @@ def prefill_flops(w):
 
 
 # kernel sources of legs that have no traffic record
-SOURCES = {"backward": ("backward.hip", "backward.hpp", "common.hpp")}
+SOURCES = {"backward": ("backward.hip", "backward.hpp", "common.hpp"), "fold": ("fold.hip", "common.hpp")}
 
 
 def kernel_source_sha(which="prefill"):
