@@ -34,6 +34,8 @@
 //   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
 #include <math.h>
 
+#include <algorithm>
+
 #include <mutex>
 
 #include "common.hpp"
@@ -91,7 +93,8 @@ struct DecCfg {
 // every K/V operand read from LDS then feeds both chunks' MFMAs, and the cache is read once for
 // up to 32 heads)
 template <int D, int NCH>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, int head_chunks) {
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, int head_chunks,
+                                                                const int* __restrict__ order) {
   using C = DecCfg<D>;
   constexpr int NS = C::kSteps;
   constexpr int NDT = C::kDT;
@@ -102,7 +105,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   const int split = lin % S;
   const int rest = lin / S;
   const int y = rest % (a.Hkv * head_chunks);
-  const int b = rest / (a.Hkv * head_chunks);
+  // sequence: in launch order, or from the balanced order of a ragged cache
+  const int b = order ? order[rest / (a.Hkv * head_chunks)] : rest / (a.Hkv * head_chunks);
   const int kvh = y / head_chunks;
   const int hc = y % head_chunks;
   const int G = a.Hq / a.Hkv;
@@ -427,6 +431,52 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   static_cast<uint16_t*>(a.out)[static_cast<int64_t>(bh) * D + d] = f32_to_bf16(num / den);
 }
 
+// Ragged caches: an order of the sequences that balances the compute units. With equal splits a
+// sequence's work grows with its visible entries, and the workgroups go out in rows of about one
+// per compute unit, the rows that fit at once all resident together: a unit that gets two long
+// sequences finishes last. Ranked longest first (ties by index), the sequences are laid out in
+// rows of `row` sequences with every other row reversed (a snake), so the unit that holds a row's
+// longest also holds the next row's shortest. order[position] = sequence; up to kMaxOrdered
+// sequences, one workgroup.
+constexpr int kMaxOrdered = 512;
+__global__ __launch_bounds__(256) void decode_order_kernel(DecodeArgs a, int row,
+                                                           int* __restrict__ order) {
+  __shared__ int vis[kMaxOrdered];
+  for (int b = threadIdx.x; b < a.B; b += 256) {
+    const int L = min(max(a.lens[b], 0), a.Tkv);
+    const int w_start = a.window > 0 ? max(0, L - a.window) : 0;
+    vis[b] = min(a.n_sink, w_start) + (L - w_start);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < a.B; b += 256) {
+    const int v = vis[b];
+    int rank = 0;
+    for (int j = 0; j < a.B; ++j) rank += (vis[j] > v) || (vis[j] == v && j < b);
+    const int r = rank / row, c = rank % row;
+    const int len = min(row, a.B - r * row);  // the last row may be short
+    order[r * row + ((r & 1) ? len - 1 - c : c)] = b;
+  }
+}
+
+// floats of the split partials in the workspace (a ragged cache's sequence order follows them)
+int64_t partial_floats(int B, int Hq, int S, int d) {
+  return static_cast<int64_t>(B) * Hq * S * (d + 2);
+}
+
+// compute units of the current device (cached per device)
+int g_units[kMaxDevices] = {};
+int device_units() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_units[dev]) {
+    int n = 0;
+    g_units[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                               hipSuccess && n > 0 ? n : 256;
+  }
+  return g_units[dev];
+}
+
 // 16-head chunks per workgroup: two when a group has more than 16 query heads
 int chunks_per_wg(int G) { return G > kHeadCols ? 2 : 1; }
 int head_chunks_of(int G) {
@@ -439,10 +489,19 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int hcs = head_chunks_of(G);
   const dim3 grid(a.nsplit * a.Hkv * hcs * a.B);
+  int* order = nullptr;
+  if (a.lens && a.B > 1 && a.B <= kMaxOrdered) {
+    // a row: the sequences whose workgroups take about one per compute unit
+    const int row = std::max(1, device_units() / (a.nsplit * a.Hkv * hcs));
+    order = reinterpret_cast<int*>(a.ws + partial_floats(a.B, a.Hq, a.nsplit, D));
+    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(256), 0, s, a, row, order);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (chunks_per_wg(G) == 2)
-    hipLaunchKernelGGL((decode_split_kernel<D, 2>), grid, dim3(kThreads), 0, s, a, hcs);
+    hipLaunchKernelGGL((decode_split_kernel<D, 2>), grid, dim3(kThreads), 0, s, a, hcs, order);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, dim3(kThreads), 0, s, a, hcs);
+    hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, dim3(kThreads), 0, s, a, hcs, order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.B * a.Hq), dim3(D), 0, s, a);
@@ -469,8 +528,10 @@ int decode_num_splits(int B, int Tkv, int Hq, int Hkv, int d) {
 }
 
 size_t decode_workspace_bytes(int B, int Tkv, int Hq, int Hkv, int d) {
-  const int64_t S = decode_num_splits(B, Tkv, Hq, Hkv, d);
-  return static_cast<size_t>(static_cast<int64_t>(B) * Hq * S * (d + 2)) * sizeof(float);
+  const int S = decode_num_splits(B, Tkv, Hq, Hkv, d);
+  // the split partials, then room for a ragged cache's sequence order
+  return static_cast<size_t>(partial_floats(B, Hq, S, d)) * sizeof(float) +
+         static_cast<size_t>(B) * sizeof(int);
 }
 
 hipError_t decode_scratch(void** ptr) {

@@ -98,6 +98,11 @@ DECODE_RAGGED_CASES = [
     (4, 600, 32, 8, 128, (0, 1, 0, 600), 0, 0),
     (2, 9000, 16, 2, 64, (0, 8999), 0, 0),
     (3, 4000, 32, 8, 128, (0, 3000, 17), 512, 3),
+    # many sequences: up to 512 their work goes out in a balanced order (ranked by length, ties
+    # by index, rows snaking), more than 512 in launch order
+    (300, 96, 8, 2, 64, tuple((i % 7) * 13 for i in range(300)), 0, 0),
+    (600, 96, 8, 2, 64, tuple((i * 37) % 97 for i in range(600)), 40, 2),
+    (130, 3000, 32, 4, 128, tuple((i * 613) % 3001 for i in range(130)), 0, 0),
 ]
 
 
