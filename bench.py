@@ -42,6 +42,8 @@ TRAFFIC = {
                ("decode.hip", "common.hpp")),
     "gva": (os.path.join(ROOT, "profiles", "gva_prefill_B2_T4096_H16_HV32_d64_traffic.json"),
             ("prefill_bf16.hip", "common.hpp")),
+    "fold": (os.path.join(ROOT, "profiles", "fold_bf16_B8_T4096_H32_g8_d128_traffic.json"),
+             ("fold.hip", "common.hpp")),
 }
 
 
@@ -79,7 +81,7 @@ def prefill_flops(w):
 
 
 # kernel sources of legs that have no traffic record
-SOURCES = {"backward": ("backward.hip", "backward.hpp", "common.hpp"), "fold": ("fold.hip", "common.hpp")}
+SOURCES = {"backward": ("backward.hip", "backward.hpp", "common.hpp")}
 
 
 def kernel_source_sha(which="prefill"):
@@ -293,9 +295,9 @@ def bench_fold(gqa, steps, warmup, torch):
             "config": {"workload": f"fold_B{B}_T{T}_H{H}_g{g}_d{d}", "B": B, "T": T, "H": H,
                        "g": g, "d": d},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": traffic_for("fold"),
                          "kernel": "fold_kernel<BF16>", "bytes_per_launch": nbytes,
-                         "avg_launch_ms": avg},
+                         "avg_launch_ms": avg, "kernel_source_sha": kernel_source_sha("fold")},
             "cpu_baseline": None, "wall_s": wall}
 
 
