@@ -481,19 +481,13 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
       const float r4d = fmaxf(r3[9], r3[10]);
       float tmax = fmaxf(fmaxf(r4a, r4b), fmaxf(r4c, r4d));
       tmax = pair_max32(tmax) * sl2;
+      // The new reference is chosen without a branch, so the exponentials follow the maximum in
+      // one block; only the rare rescale of O and of the running sum sits in a branch, after
+      // them. Lanes that keep their reference keep their sums (alpha = 1; their m may still be
+      // -inf, since with a sliding window a row can see nothing in the first tiles).
       const bool move = tmax > m_run + kRescaleSlack;
-      if (__any(move)) {
-        const float m_new = move ? tmax : m_run;
-        // lanes that keep their reference keep their sums (their m may still be -inf, since
-        // with a sliding window a row can see nothing in the first tiles of the workgroup)
-        const float alpha = move ? fast_exp2(m_run - m_new) : 1.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc_o[mt][i] *= alpha;
-        m_run = m_new;
-      }
+      const float m_old = m_run;
+      m_run = move ? tmax : m_run;
       const float mref = m_run == -INFINITY ? 0.f : m_run;
       // the row sum in four independent partial sums (a chain of 16 dependent dot products
       // would pace the phase)
@@ -518,6 +512,14 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
           const u32x4 w = {pw[0], pw[1], pw[2], pw[3]};
           pb[2 * h + h2] = __builtin_bit_cast(bf16x8, w);
         }
+      if (__any(move)) {
+        const float alpha = move ? fast_exp2(m_old - m_run) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc_o[mt][i] *= alpha;
+      }
       l_run += (psum4[0] + psum4[1]) + (psum4[2] + psum4[3]);
     };
 
@@ -613,7 +615,11 @@ __global__ __launch_bounds__(512) void prefill_pp_kernel(PrefillArgs a, int head
           if (rpos[j] >= 0) {
             uint16_t* orow = Op + (q0 + rpos[j]) * a.o_row +
                              static_cast<int64_t>(rhq[j]) * a.o_head + vsl * DV;
-            *reinterpret_cast<u32x4*>(orow + 64 * h + 8 * (lane & 7)) = x;
+            // non-temporal: nothing here reads the output back; kept out of the caches the
+            // stores retire sooner, and the next query tile's first loads, which share the
+            // memory counter with them, wait less
+            __builtin_nontemporal_store(x,
+                                        reinterpret_cast<u32x4*>(orow + 64 * h + 8 * (lane & 7)));
           }
         }
         asm volatile("" ::: "memory");
