@@ -269,7 +269,7 @@ def bench_decode(gqa, w, steps, warmup, torch, seed):
             "splits": gqa.gqa_attn_decode_workspace_bytes_hkv(w.B, w.Tkv, w.Hq, w.Hkv, w.d)
             // (w.B * w.Hq * (w.d + 2) * 4),
             "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "wall_s": wall,
-            "traffic": traffic_for("decode") if w.cache_lens is None else None}
+            "traffic": traffic_for("decode", w.name)}
 
 
 FOLD_SHAPE = (8, 4096, 32, 128, 8)  # B, T, H, d, g: a 32-head K (or V) folded to 8 heads
@@ -356,14 +356,17 @@ def cpu_baseline(w, tensors, torch, target_s=15.0):
                       f"{t:.1f} s, fp64"}
 
 
-def traffic_for(which):
-    """Calibrated HBM bytes per launch, or None when no counters exist for the current source."""
+def traffic_for(which, workload=None):
+    """Calibrated HBM bytes per launch, or None when no counters exist for the current source
+    (or, when `workload` is given, for that workload)."""
     path = TRAFFIC[which][0]
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_sha") != kernel_source_sha(which):
+        return None
+    if workload is not None and rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -416,15 +419,15 @@ def main():
     ap.add_argument("--median-launches", type=int, default=50,
                     help="separately timed launches for the median and minimum (0: none)")
     ap.add_argument("--only", choices=["varlen", "prefill", "decode", "mqa", "window",
-                                       "ragged", "rope", "qknorm", "backward", "gva",
-                                       "fold", "copy"],
+                                       "ragged", "longdecode", "rope", "qknorm", "backward",
+                                       "gva", "fold", "copy"],
                     default=None,
                     help="time a single workload as the line's headline (for profiling); "
                          "'copy' times a plain 1 GiB device copy, the calibration kernel for the "
                          "HBM byte counters; 'fold' times gqa_fold_kv")
     ap.add_argument("--all", action="store_true",
-                    help="also time the variant legs (window, ragged decode, RoPE, QK-norm, "
-                         "backward, grouped values)")
+                    help="also time the variant legs (window, ragged decode, long-context "
+                         "decode, RoPE, QK-norm, backward, grouped values)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -487,8 +490,8 @@ def main():
     elif args.only not in (None, "varlen"):
         plan.append(args.only)
     if args.all:
-        plan += [x for x in ("window", "ragged", "rope", "qknorm", "backward", "gva")
-                 if x not in plan]
+        plan += [x for x in ("window", "ragged", "longdecode", "rope", "qknorm", "backward",
+                             "gva") if x not in plan]
 
     for name in plan:
         if name == "varlen":
@@ -531,6 +534,8 @@ def main():
             run_decode("decode", workloads.DECODE, 3000)
         elif name == "ragged":
             run_decode("ragged", workloads.RAGGED_DECODE, 7000)
+        elif name == "longdecode":
+            run_decode("longdecode", workloads.LONG_DECODE, 9000)
 
     head_key = {"prefill": "prefill"}.get(headline, headline)
     res, roofline, config = legs.pop(head_key)

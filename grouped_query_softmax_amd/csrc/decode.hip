@@ -400,8 +400,39 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   }
 }
 
+// Largest number of splits a launch uses (decode_num_splits aims at kTargetBlocks workgroups).
+constexpr int kMaxSplits = kTargetBlocks;
+
+// Reductions over the D threads of a combine workgroup (D / 64 waves), through LDS.
+template <int D>
+__device__ __forceinline__ float block_max(float x, float* red) {
+  for (int m = 32; m > 0; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < D / 64; ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+template <int D>
+__device__ __forceinline__ float block_sum(float x, float* red) {
+  for (int m = 32; m > 0; m >>= 1) x += __shfl_xor(x, m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < D / 64; ++w) r += red[w];
+  __syncthreads();
+  return r;
+}
+
+// One workgroup of D threads per (sequence, query head): the splits' (m, l) pairs are reduced by
+// the whole workgroup and their weights kept in LDS, then each thread forms one output column
+// from four independent partial sums, so that the split partials' loads overlap instead of
+// following one another.
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+  __shared__ float wsh[kMaxSplits];
+  __shared__ float red[D / 64];
   const float* __restrict__ ws = a.ws;
   const int nsplit = a.nsplit;
   const int nbh = a.B * a.Hq;
@@ -420,14 +451,24 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const int64_t ntot = static_cast<int64_t>(nbh) * nsplit;
   const float* wm = ws + ntot * D + static_cast<int64_t>(bh) * nsplit;
   const float* wl = ws + ntot * D + ntot + static_cast<int64_t>(bh) * nsplit;
-  float M = -INFINITY;
-  for (int s = 0; s < nvalid; ++s) M = fmaxf(M, wm[s]);
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < nvalid; ++s) {
+  float m = -INFINITY;
+  for (int s = d; s < nvalid; s += D) m = fmaxf(m, wm[s]);
+  const float M = block_max<D>(m, red);
+  float dl = 0.f;
+  for (int s = d; s < nvalid; s += D) {
     const float w = (wm[s] == -INFINITY) ? 0.f : fast_exp2(wm[s] - M);
-    num = fmaf(w, ws[(static_cast<int64_t>(bh) * nsplit + s) * D + d], num);
-    den = fmaf(w, wl[s], den);
+    wsh[s] = w;
+    dl = fmaf(w, wl[s], dl);
   }
+  const float den = block_sum<D>(dl, red);  // its barriers also publish wsh
+  const float* o = ws + static_cast<int64_t>(bh) * nsplit * D + d;
+  float n4[4] = {0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 4 <= nvalid; s += 4)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) n4[j] = fmaf(wsh[s + j], o[static_cast<int64_t>(s + j) * D], n4[j]);
+  for (; s < nvalid; ++s) n4[0] = fmaf(wsh[s], o[static_cast<int64_t>(s) * D], n4[0]);
+  const float num = (n4[0] + n4[1]) + (n4[2] + n4[3]);
   static_cast<uint16_t*>(a.out)[static_cast<int64_t>(bh) * D + d] = f32_to_bf16(num / den);
 }
 
@@ -486,6 +527,7 @@ int head_chunks_of(int G) {
 
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
+  if (a.nsplit < 1 || a.nsplit > kMaxSplits) return hipErrorInvalidValue;  // the combine's LDS
   const int G = a.Hq / a.Hkv;
   const int hcs = head_chunks_of(G);
   const dim3 grid(a.nsplit * a.Hkv * hcs * a.B);

@@ -1,8 +1,9 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark times.
 
-The four benchmark workloads (the 4096-token 32/8 prefill, the 64-sequence decode, the multi-query
-prefill with its x30 rows and the packed 16k/8k/4k/1k prefill) are compared with the fp64 oracle
-over the whole output, every head, row and column (the GQA lab's max_gap, step 5; the course
+The benchmark workloads (the 4096-token 32/8 prefill, the 64-sequence decode, the multi-query
+prefill with its x30 rows, the packed 16k/8k/4k/1k prefill and the long-context decode of one
+131072-entry cache, which runs split and merges its partial results) are compared with the fp64
+oracle over the whole output, every head, row and column (the GQA lab's max_gap, step 5; the course
 page's whole-output comparison with torch's scaled_dot_product_attention). The variant workloads
 (window, ragged decode, rotary embedding, grouped values, backward) are checked on seeded
 samples of rows, sequences or head groups; rows are independent, so each sampled row is an exact
@@ -85,6 +86,26 @@ def test_full_decode_whole_output(gqa):
     for b0 in range(0, w.B, step):
         say(f"full-size decode: oracle on sequences {b0} .. {b0 + step - 1}")
         ref[b0:b0 + step] = orc.attention(qh[b0:b0 + step], kh[b0:b0 + step], vh[b0:b0 + step])
+    _whole(got, ref, w.name)
+
+
+def test_full_long_decode_whole_output(gqa):
+    """One sequence against a 131072-entry cache: the cache is split across the compute units and
+    the partial results are merged by the combine kernel; every head and column is compared."""
+    w = workloads.LONG_DECODE
+    splits = (gqa.raw_library().gqa_attn_decode_workspace_bytes_hkv(w.B, w.Tkv, w.Hq, w.Hkv, w.d)
+              // (w.B * w.Hq * (w.d + 2) * 4))
+    assert splits > 1, "the long-context decode must run split (and merge the partials)"
+    say(f"full-size long decode {w.name}: generating inputs")
+    q, k, v, _ = workloads.make_inputs(w)
+    ws = torch.empty(gqa.gqa_attn_decode_workspace_bytes(w.B, w.Tkv, w.Hq, w.d),
+                     dtype=torch.uint8, device="cuda")
+    say(f"full-size long decode: launching ({splits} splits)")
+    out = gqa.gqa_attn_decode(to_dev(q), to_dev(k), to_dev(v), workspace=ws)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    say("full-size long decode: oracle on the whole output")
+    ref = oracle.default().attention(host_view(q), host_view(k), host_view(v))
     _whole(got, ref, w.name)
 
 

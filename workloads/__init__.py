@@ -180,9 +180,14 @@ RAGGED_DECODE = Workload("ragged_decode_B64_max8192", B=64, Tq=1, Tkv=8192, Hq=3
 GVA_PREFILL = Workload("gva_prefill_B2_T4096_H16_HV32_d64", B=2, Tq=4096, Tkv=4096, Hq=32, Hkv=16,
                        d=64, dtype="bf16", causal=True, seeds=(8000, 8001, 8002))
 
+# Long-context decode: one sequence against a 131072-entry cache (32/8 heads, d = 128). The
+# cache is split across the compute units, so the partial results go through the combine step.
+LONG_DECODE = Workload("decode_B1_kv131072", B=1, Tq=1, Tkv=131072, Hq=32, Hkv=8, d=128,
+                       dtype="bf16", causal=False, seeds=(9000, 9001, 9002))
+
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in
                                   (TINY, LLAMA_PREFILL, DECODE, MQA_PREFILL, VARLEN_PREFILL,
-                                   WINDOW_PREFILL, RAGGED_DECODE, GVA_PREFILL)}
+                                   WINDOW_PREFILL, RAGGED_DECODE, GVA_PREFILL, LONG_DECODE)}
 
 
 def tiny_lab_inputs(x1000: bool = False) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
