@@ -89,24 +89,58 @@ struct DecCfg {
 };
 
 
+// Ragged caches: a balanced order of the sequences. With equal splits a sequence's work grows with
+// its visible entries, and the workgroups go out in rows of about one per compute unit, the rows
+// that fit at once all resident together: a unit that gets two long sequences finishes last.
+// Ranked longest first (ties by index), the sequences are laid out in rows of `row` with every
+// other row reversed (a snake), so the unit that holds a row's longest also holds the next row's
+// shortest. Each split workgroup finds the sequence at its position of that layout itself (up to
+// kMaxOrdered sequences, ranked in LDS: B^2 / 256 comparisons per thread).
+constexpr int kMaxOrdered = 512;
+__device__ int balanced_sequence(const DecodeArgs& a, int pos, int row, int* vis) {
+  for (int j = threadIdx.x; j < a.B; j += kThreads) {
+    const int L = min(max(a.lens[j], 0), a.Tkv);
+    const int w_start = a.window > 0 ? max(0, L - a.window) : 0;
+    vis[j] = min(a.n_sink, w_start) + (L - w_start);
+  }
+  __syncthreads();
+  // the rank that the snake layout puts at this position (the last row may be short)
+  const int r = pos / row, c = pos % row;
+  const int len = min(row, a.B - r * row);
+  const int k = r * row + ((r & 1) ? len - 1 - c : c);
+  for (int j = threadIdx.x; j < a.B; j += kThreads) {
+    const int v = vis[j];
+    int rank = 0;
+    for (int i = 0; i < a.B; ++i) rank += (vis[i] > v) || (vis[i] == v && i < j);
+    if (rank == k) vis[kMaxOrdered] = j;  // each rank belongs to exactly one sequence
+  }
+  __syncthreads();
+  const int b = vis[kMaxOrdered];
+  __syncthreads();  // the LDS is the key/value tiles' from here on
+  return b;
+}
+
 // NCH: 16-head chunks of query heads per workgroup (1, or 2 when a group has more than 16 heads:
 // every K/V operand read from LDS then feeds both chunks' MFMAs, and the cache is read once for
 // up to 32 heads)
 template <int D, int NCH>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, int head_chunks,
-                                                                const int* __restrict__ order) {
+                                                                int order_row) {
   using C = DecCfg<D>;
   constexpr int NS = C::kSteps;
   constexpr int NDT = C::kDT;
   __shared__ __attribute__((aligned(16))) char smem[C::kSmemBytes];
+  static_assert(C::kSmemBytes >= (kMaxOrdered + 1) * 4, "the ragged order's ranks fit the LDS");
 
   const int S = a.nsplit;
   const int lin = blockIdx.x;
   const int split = lin % S;
   const int rest = lin / S;
   const int y = rest % (a.Hkv * head_chunks);
-  // sequence: in launch order, or from the balanced order of a ragged cache
-  const int b = order ? order[rest / (a.Hkv * head_chunks)] : rest / (a.Hkv * head_chunks);
+  // sequence: in launch order, or from the balanced order of a ragged cache (rows of order_row)
+  const int pos = rest / (a.Hkv * head_chunks);
+  const int b =
+      order_row > 0 ? balanced_sequence(a, pos, order_row, reinterpret_cast<int*>(smem)) : pos;
   const int kvh = y / head_chunks;
   const int hc = y % head_chunks;
   const int G = a.Hq / a.Hkv;
@@ -472,34 +506,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   static_cast<uint16_t*>(a.out)[static_cast<int64_t>(bh) * D + d] = f32_to_bf16(num / den);
 }
 
-// Ragged caches: an order of the sequences that balances the compute units. With equal splits a
-// sequence's work grows with its visible entries, and the workgroups go out in rows of about one
-// per compute unit, the rows that fit at once all resident together: a unit that gets two long
-// sequences finishes last. Ranked longest first (ties by index), the sequences are laid out in
-// rows of `row` sequences with every other row reversed (a snake), so the unit that holds a row's
-// longest also holds the next row's shortest. order[position] = sequence; up to kMaxOrdered
-// sequences, one workgroup.
-constexpr int kMaxOrdered = 512;
-__global__ __launch_bounds__(256) void decode_order_kernel(DecodeArgs a, int row,
-                                                           int* __restrict__ order) {
-  __shared__ int vis[kMaxOrdered];
-  for (int b = threadIdx.x; b < a.B; b += 256) {
-    const int L = min(max(a.lens[b], 0), a.Tkv);
-    const int w_start = a.window > 0 ? max(0, L - a.window) : 0;
-    vis[b] = min(a.n_sink, w_start) + (L - w_start);
-  }
-  __syncthreads();
-  for (int b = threadIdx.x; b < a.B; b += 256) {
-    const int v = vis[b];
-    int rank = 0;
-    for (int j = 0; j < a.B; ++j) rank += (vis[j] > v) || (vis[j] == v && j < b);
-    const int r = rank / row, c = rank % row;
-    const int len = min(row, a.B - r * row);  // the last row may be short
-    order[r * row + ((r & 1) ? len - 1 - c : c)] = b;
-  }
-}
-
-// floats of the split partials in the workspace (a ragged cache's sequence order follows them)
+// floats of the split partials in the workspace
 int64_t partial_floats(int B, int Hq, int S, int d) {
   return static_cast<int64_t>(B) * Hq * S * (d + 2);
 }
@@ -531,19 +538,17 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int hcs = head_chunks_of(G);
   const dim3 grid(a.nsplit * a.Hkv * hcs * a.B);
-  int* order = nullptr;
-  if (a.lens && a.B > 1 && a.B <= kMaxOrdered) {
-    // a row: the sequences whose workgroups take about one per compute unit
-    const int row = std::max(1, device_units() / (a.nsplit * a.Hkv * hcs));
-    order = reinterpret_cast<int*>(a.ws + partial_floats(a.B, a.Hq, a.nsplit, D));
-    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(256), 0, s, a, row, order);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  // a ragged cache's balanced order: rows of the sequences whose workgroups take about one per
+  // compute unit (0: launch order)
+  const int order_row = (a.lens && a.B > 1 && a.B <= kMaxOrdered)
+                            ? std::max(1, device_units() / (a.nsplit * a.Hkv * hcs))
+                            : 0;
   if (chunks_per_wg(G) == 2)
-    hipLaunchKernelGGL((decode_split_kernel<D, 2>), grid, dim3(kThreads), 0, s, a, hcs, order);
+    hipLaunchKernelGGL((decode_split_kernel<D, 2>), grid, dim3(kThreads), 0, s, a, hcs,
+                       order_row);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, dim3(kThreads), 0, s, a, hcs, order);
+    hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, dim3(kThreads), 0, s, a, hcs,
+                       order_row);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.B * a.Hq), dim3(D), 0, s, a);
@@ -571,9 +576,8 @@ int decode_num_splits(int B, int Tkv, int Hq, int Hkv, int d) {
 
 size_t decode_workspace_bytes(int B, int Tkv, int Hq, int Hkv, int d) {
   const int S = decode_num_splits(B, Tkv, Hq, Hkv, d);
-  // the split partials, then room for a ragged cache's sequence order
-  return static_cast<size_t>(partial_floats(B, Hq, S, d)) * sizeof(float) +
-         static_cast<size_t>(B) * sizeof(int);
+  // the split partials
+  return static_cast<size_t>(partial_floats(B, Hq, S, d)) * sizeof(float);
 }
 
 hipError_t decode_scratch(void** ptr) {

@@ -194,8 +194,8 @@ gqa_status_t gqa_attn_prefill_gva(const void* q, const void* k, const void* v, v
  * kernel with Tq = 1 and needs no workspace (workspace may then be NULL).
  *
  * gqa_attn_decode_workspace_bytes: an upper bound valid for every Hkv that divides Hq (the
- * split count, and so the fp32 partials [B, Hq, splits, d + 2], depends on Hkv; B ints follow
- * them, the work order of a ragged cache); 0 for non-positive sizes. gqa_attn_decode_workspace_bytes_hkv: the exact requirement for one Hkv
+ * split count, and so the fp32 partials [B, Hq, splits, d + 2], depends on Hkv); 0 for
+ * non-positive sizes. gqa_attn_decode_workspace_bytes_hkv: the exact requirement for one Hkv
  * (0 for non-positive sizes or Hq not divisible by Hkv); never above the bound.
  */
 size_t gqa_attn_decode_workspace_bytes(int B, int Tkv, int Hq, int d);
