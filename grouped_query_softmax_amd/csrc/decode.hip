@@ -22,7 +22,9 @@
 // Ragged caches and sliding windows (course page "Week 7. Attention", step 3): sequence b uses
 // its first lens[b] cache entries; with a window it sees only the last `window` of them plus the
 // first n_sink (sink) entries. The visible entries form one list (sinks, then window) over which
-// the splits and tiles run, so nothing outside it is read.
+// the splits and tiles run, so nothing outside it is read. With up to 512 sequences, each
+// workgroup takes its sequence from a balanced order (longest and shortest sequences paired on
+// the compute units) that it works out itself at its start.
 // Each lane owns one query head (one accumulator column), so the softmax reference and the
 // rescale factor are per lane; the row maximum of a tile is combined over the 4 lane groups that
 // hold that head's keys. Online softmax in the base-2 domain with a lazily moved reference
@@ -30,7 +32,7 @@
 // reference is used for both the output and the running sum). The 4 waves are merged in LDS and
 // the split's partial (reference m, running sum l, unnormalised output o) goes to the workspace,
 // or, when the cache is not split, the normalised output goes straight to `out`.
-// Kernel 2 (combine, only with more than one split):
+// Kernel 2 (combine, only with more than one split), one workgroup per (sequence, query head):
 //   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.
 #include <math.h>
 
