@@ -1,5 +1,6 @@
-"""Host-side checks of bench.py (no GPU): the one-GPU contract and the algorithmic work counts
-its roofline divides by.
+"""Host-side checks of bench.py (no GPU): the one-GPU contract, the algorithmic work counts its
+roofline divides by, and the rule that a measured HBM traffic figure is reported only for the
+kernel sources and the workload its counters were taken on.
 
 The counts are pinned to independent arithmetic: a brute-force count of the visible (query,
 key) pairs of small masks, and the closed forms for the benchmark shapes (4·d·Hq flops per
@@ -60,3 +61,44 @@ def test_headline_decode_reads_every_cached_element_once():
     w = workloads.DECODE
     kv_bytes = 2 * w.B * w.Tkv * w.Hkv * w.d * 2
     assert kv_bytes == 2_147_483_648
+
+
+def _record(tmp_path, sha, workload, nbytes):
+    import json
+    p = tmp_path / "traffic.json"
+    p.write_text(json.dumps({"kernel_source_sha": sha, "workload": workload,
+                             "hbm_bytes_per_launch": nbytes}))
+    return str(p)
+
+
+def test_traffic_is_reported_only_for_the_sources_and_workload_it_was_measured_on(
+        tmp_path, monkeypatch):
+    # the roofline's measured traffic must go null as soon as the kernel's sources change after
+    # the counters were taken, and must never be borrowed from another workload's record
+    sources = bench.TRAFFIC["prefill"][1]
+    sha = bench.kernel_source_sha("prefill")
+    name = workloads.LLAMA_PREFILL.name
+    monkeypatch.setitem(bench.TRAFFIC, "prefill", (_record(tmp_path, sha, name, 123), sources))
+    assert bench.traffic_for("prefill") == 123
+    assert bench.traffic_for("prefill", name) == 123
+    assert bench.traffic_for("prefill", workloads.MQA_PREFILL.name) is None
+    stale = "0" * 16 if sha != "0" * 16 else "1" * 16
+    monkeypatch.setitem(bench.TRAFFIC, "prefill", (_record(tmp_path, stale, name, 123), sources))
+    assert bench.traffic_for("prefill") is None
+    monkeypatch.setitem(bench.TRAFFIC, "prefill", (str(tmp_path / "missing.json"), sources))
+    assert bench.traffic_for("prefill") is None
+
+
+def test_source_hash_follows_every_file_of_the_kernel(tmp_path, monkeypatch):
+    # the hash covers each listed source: a change to any one of them (the shared header
+    # included) changes it
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    (tmp_path / "a.hip").write_text("kernel a\n")
+    (tmp_path / "common.hpp").write_text("shared\n")
+    monkeypatch.setitem(bench.TRAFFIC, "probe", ("unused", ("a.hip", "common.hpp")))
+    h0 = bench.kernel_source_sha("probe")
+    (tmp_path / "common.hpp").write_text("shared, changed\n")
+    h1 = bench.kernel_source_sha("probe")
+    (tmp_path / "a.hip").write_text("kernel a, changed\n")
+    h2 = bench.kernel_source_sha("probe")
+    assert len({h0, h1, h2}) == 3 and all(len(h) == 16 for h in (h0, h1, h2))
