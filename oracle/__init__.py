@@ -8,7 +8,9 @@ heads"): ``group_of`` / ``group_members`` (step 1), ``fold_kv`` (step 2), ``expa
 ``attention`` (step 4 per head, run over all heads as in step 5's ``heads_out``), ``max_gap``
 (step 5), and the counts ``kv_cache_elems`` / ``kv_table`` / ``mults`` (steps 6-7, in
 :mod:`oracle.counts`). As on the page, a head count that does not divide evenly raises
-``ValueError``.
+``ValueError``. ``window_cache_slot`` / ``window_cache_visible`` / ``unroll_window_cache`` read a
+decode cache bounded to the sliding window (course page "Week 7. Attention", step 3) back in
+arrival order, for ``attention`` to run on.
 
 Array conventions: numpy arrays; float64 and float32 are taken as values, uint16 as bfloat16 bit
 patterns. Outputs are float64.
@@ -308,6 +310,57 @@ class Oracle:
         vf = self.fold_kv(v, g)
         return self.attention(np.asarray(q, dtype=np.float64) if q.dtype != np.uint16 else
                               _bf16_to_f64(q), kf, vf, causal=causal)
+
+
+def _window_slots(entries: np.ndarray, window: int, n_sink: int) -> np.ndarray:
+    """Slots of cache entries in a cache bounded to the window: an entry below n_sink keeps its
+    own slot; a later entry e goes to slot n_sink + (e - n_sink) mod window, the slot of the entry
+    `window` places before it, which has left the window (course page "Week 7. Attention",
+    step 3: the window bounds the cache to its size, and the sink tokens are never dropped)."""
+    e = np.asarray(entries, dtype=np.int64)
+    return np.where(e < n_sink, e, n_sink + (e - n_sink) % window)
+
+
+def window_cache_slot(entry: int, window: int, n_sink: int) -> int:
+    """Slot (0 .. n_sink + window - 1) that keeps cache entry ``entry`` (0-based, in arrival
+    order) of a cache bounded to ``window`` entries plus ``n_sink`` sink entries."""
+    if window < 1 or n_sink < 0 or entry < 0:
+        raise ValueError("window_cache_slot: window >= 1, n_sink >= 0, entry >= 0")
+    return int(_window_slots(np.array([entry]), window, n_sink)[0])
+
+
+def window_cache_visible(length: int, window: int, n_sink: int) -> np.ndarray:
+    """Entries that the newest query of a sequence of ``length`` entries sees (it sits at
+    position length - 1): the sinks 0 .. n_sink - 1 and the last ``window`` entries (course
+    page, step 3; the same visibility as ``attention(..., causal=True, window, n_sink)``)."""
+    e = np.arange(max(int(length), 0), dtype=np.int64)
+    return e[(e < n_sink) | (e >= length - window)]
+
+
+def unroll_window_cache(ring: np.ndarray, lengths, window: int, n_sink: int,
+                        compact: bool = False) -> List[np.ndarray]:
+    """Each sequence's cache in arrival order, read out of its window-bounded cache
+    ``ring`` [B, n_sink + window, Hkv, d]: every visible entry from its slot.
+
+    compact=False: [1, length, Hkv, d] with the entries that the window hides set to zero (they
+    are never looked at by a windowed query at position length - 1); compact=True: only the
+    visible entries, in arrival order, [1, n_visible, Hkv, d]."""
+    ring = np.asarray(ring)
+    if window < 1 or n_sink < 0 or ring.ndim != 4 or ring.shape[1] != n_sink + window:
+        raise ValueError("unroll_window_cache: ring must be [B, n_sink + window, Hkv, d]")
+    if len(lengths) != ring.shape[0]:
+        raise ValueError("unroll_window_cache: one length per sequence")
+    out = []
+    for b, length in enumerate(lengths):
+        vis = window_cache_visible(length, window, n_sink)
+        rows = ring[b, _window_slots(vis, window, n_sink)]
+        if compact:
+            out.append(rows[None].copy())
+        else:
+            full = np.zeros((1, max(int(length), 0)) + ring.shape[2:], dtype=ring.dtype)
+            full[0, vis] = rows
+            out.append(full)
+    return out
 
 
 def _bf16_to_f64(bits: np.ndarray) -> np.ndarray:

@@ -31,6 +31,8 @@ import os
 
 import numpy as np
 
+import oracle
+
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
@@ -500,6 +502,81 @@ def check_window_limits(orc):
         raise AssertionError("a window without the causal flag must be rejected")
 
 
+def _fill_window_cache(k, window, n_sink):
+    """Writes the entries of a full cache k [B, L, ...] one at a time into a cache bounded to the
+    window, the way a decoder fills it: the first n_sink entries into their own slots, then a
+    cursor that steps through the window's slots and starts over at the first of them when it
+    passes the last; a first-in-first-out queue of at most `window` entries records which
+    entries the bounded cache should still hold. Returns the cache and the queue's entries plus
+    the sinks. Shares nothing with the oracle's closed-form slot rule."""
+    from collections import deque
+    B, L = k.shape[:2]
+    ring = np.zeros((B, n_sink + window) + k.shape[2:], dtype=k.dtype)
+    held = np.full(n_sink + window, -1)
+    fifo = deque(maxlen=window)
+    cur = n_sink
+    for e in range(L):
+        if e < n_sink:
+            slot = e
+        else:
+            slot = cur
+            cur = cur + 1 if cur + 1 < n_sink + window else n_sink
+            fifo.append(e)
+        ring[:, slot] = k[:, e]
+        held[slot] = e
+    kept = sorted(list(range(min(L, n_sink))) + list(fifo))
+    return ring, held, kept
+
+
+def check_window_cache_layout(orc):
+    """The bounded cache's layout: after a writer fills it entry by entry (cursor and queue, above),
+    the entries it holds are exactly the ones a windowed query at the last position sees (course
+    step 3: the window bounds the cache, the sinks stay), each at the slot the oracle reads it
+    from; for every window, sink count and length up to three times the capacity."""
+    del orc
+    for W, S in [(1, 0), (1, 3), (4, 0), (4, 2), (7, 5), (16, 1), (3, 9)]:
+        for L in range(0, 3 * (W + S) + 5):
+            _, held, kept = _fill_window_cache(np.arange(L).reshape(1, L), W, S)
+            vis = oracle.window_cache_visible(L, W, S)
+            assert list(vis) == kept, (W, S, L, list(vis), kept)
+            assert sorted(int(x) for x in held if x >= 0) == kept, (W, S, L)
+            for e in vis:
+                assert held[oracle.window_cache_slot(int(e), W, S)] == e, (W, S, L, e)
+
+
+def check_window_cache_attention(orc):
+    """Decode from a bounded cache equals the windowed decode of the full cache bit for bit,
+    unrolled (hidden entries zero) and compact (visible entries only, no window), for plain,
+    rotary (query turned at the last position, keys turned when written) and QK-norm queries."""
+    rng = _rng(31)
+    for (L, W, S, Hq, Hkv) in [(1, 4, 0, 4, 2), (3, 4, 2, 4, 2), (6, 4, 2, 4, 1), (23, 5, 3, 6, 3),
+                               (40, 7, 0, 2, 2), (40, 1, 1, 4, 2), (9, 16, 4, 4, 2)]:
+        d = 8
+        q = rng.standard_normal((1, 1, Hq, d))
+        k = rng.standard_normal((1, L, Hkv, d))
+        v = rng.standard_normal((1, L, Hkv, d))
+        rk, _, _ = _fill_window_cache(k, W, S)
+        rv, _, _ = _fill_window_cache(v, W, S)
+        ref = orc.attention(q, k, v, causal=True, window=W, n_sink=S)
+        ku = oracle.unroll_window_cache(rk, [L], W, S)[0]
+        vu = oracle.unroll_window_cache(rv, [L], W, S)[0]
+        assert np.array_equal(orc.attention(q, ku, vu, causal=True, window=W, n_sink=S), ref)
+        kc = oracle.unroll_window_cache(rk, [L], W, S, compact=True)[0]
+        vc = oracle.unroll_window_cache(rv, [L], W, S, compact=True)[0]
+        assert kc.shape[1] == min(L, W + S)
+        assert np.array_equal(orc.attention(q, kc, vc), ref), (L, W, S)
+        cos, sin = rope_tables(L, d)
+        rref = orc.attention(q, k, v, causal=True, window=W, n_sink=S, rope=(cos, sin),
+                             rope_mode="q")
+        assert np.array_equal(orc.attention(q, ku, vu, causal=True, window=W, n_sink=S,
+                                            rope=(cos, sin), rope_mode="q"), rref)
+        norm = (rng.standard_normal(d).astype(np.float32), np.ones(d, dtype=np.float32), 1e-6)
+        nref = orc.attention(q, k, v, causal=True, window=W, n_sink=S, qk_norm=norm,
+                             qk_norm_mode="q")
+        assert np.array_equal(orc.attention(q, ku, vu, causal=True, window=W, n_sink=S,
+                                            qk_norm=norm, qk_norm_mode="q"), nref)
+
+
 # ------------------------------------------------------------------------------------------------
 # course step 3: rotary position embedding
 # ------------------------------------------------------------------------------------------------
@@ -860,6 +937,8 @@ ALL_CHECKS = [
     check_causality,
     check_window_matches_masked_sdpa,
     check_window_limits,
+    check_window_cache_layout,
+    check_window_cache_attention,
     check_rope_worked_example,
     check_rope_matches_complex_torch,
     check_rope_relative_positions,

@@ -3,6 +3,7 @@ plausible error, compiled into a temporary library; at least one pin must fail f
 This shows the pins constrain the oracle and are not a restatement of it."""
 import os
 
+import numpy as np
 import pytest
 
 import oracle
@@ -126,3 +127,38 @@ def test_count_mutant_is_caught(name):
         except (AssertionError, ValueError):
             failed.append(check.__name__)
     assert failed, f"no count pin caught mutant {name}"
+
+
+# Mistakes in the window-bounded cache's slot rule and visibility (course page "Week 7. Attention",
+# step 3), planted in the Python oracle functions for the duration of one check.
+WINDOW_CACHE_MUTANTS = {
+    # the window's slots start one place late
+    "slot_rotated": lambda e, w, s: np.where(e < s, e, s + (e - s + 1) % w),
+    # the sinks are not kept apart: every entry cycles through the whole cache
+    "slot_ignores_sinks": lambda e, w, s: e % (w + s),
+    # the modulo taken from entry 0 instead of from the first non-sink entry
+    "slot_from_zero": lambda e, w, s: np.where(e < s, e, s + e % w),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WINDOW_CACHE_MUTANTS))
+def test_window_cache_mutant_is_caught(name, monkeypatch):
+    monkeypatch.setattr(oracle, "_window_slots", WINDOW_CACHE_MUTANTS[name])
+    orc = oracle.default()
+    failed = []
+    for check in (pins.check_window_cache_layout, pins.check_window_cache_attention):
+        try:
+            check(orc)
+        except (AssertionError, ValueError, IndexError):
+            failed.append(check.__name__)
+    assert failed, f"no pin caught window-cache mutant {name}"
+
+
+def test_window_cache_visibility_mutant_is_caught(monkeypatch):
+    """A window one entry too wide."""
+    def wide(length, window, n_sink):
+        e = np.arange(max(int(length), 0), dtype=np.int64)
+        return e[(e < n_sink) | (e >= length - window - 1)]
+    monkeypatch.setattr(oracle, "window_cache_visible", wide)
+    with pytest.raises(AssertionError):
+        pins.check_window_cache_layout(oracle.default())
