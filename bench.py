@@ -39,7 +39,7 @@ TRAFFIC = {
     "mqa": (os.path.join(ROOT, "profiles", "prefill_bf16_mqa_B8_T2048_traffic.json"),
             ("prefill_bf16.hip", "common.hpp")),
     "decode": (os.path.join(ROOT, "profiles", "decode_bf16_B64_kv8192_traffic.json"),
-               ("decode.hip", "common.hpp")),
+               ("decode.hip", "decode.hpp", "common.hpp")),
     "gva": (os.path.join(ROOT, "profiles", "gva_prefill_B2_T4096_H16_HV32_d64_traffic.json"),
             ("prefill_bf16.hip", "common.hpp")),
     "fold": (os.path.join(ROOT, "profiles", "fold_bf16_B8_T4096_H32_g8_d128_traffic.json"),
@@ -254,13 +254,19 @@ def bench_decode(gqa, w, steps, warmup, torch, seed):
     def step():
         q, k, v = sets[it[0] & 1]
         it[0] += 1
-        if lens is not None:
+        if w.window_cache:
+            gqa.gqa_attn_decode_window_cache(q, k, v, lens, window=w.window, n_sink=w.n_sink,
+                                             workspace=ws, out=out)
+        elif lens is not None:
             gqa.gqa_attn_decode_ragged(q, k, v, cache_lens=lens, workspace=ws, out=out)
         else:
             gqa.gqa_attn_decode(q, k, v, workspace=ws, out=out)
 
     avg, wall, med, mn = time_launches(step, steps, warmup, torch, PER_LAUNCH)
-    entries = sum(w.cache_lens) if w.cache_lens is not None else w.B * w.Tkv
+    if w.window_cache:   # the visible entries: the sinks and the window of each sequence
+        entries = sum(min(L, w.n_sink + w.window) for L in w.cache_lens)
+    else:
+        entries = sum(w.cache_lens) if w.cache_lens is not None else w.B * w.Tkv
     kv_bytes = 2 * entries * w.Hkv * w.d * 2
     qo_bytes = 2 * w.B * w.Hq * w.d * 2
     gbs = (kv_bytes + qo_bytes) / (avg * 1e-3) / 1e9
@@ -419,7 +425,8 @@ def main():
     ap.add_argument("--median-launches", type=int, default=50,
                     help="separately timed launches for the median and minimum (0: none)")
     ap.add_argument("--only", choices=["varlen", "prefill", "decode", "mqa", "window",
-                                       "ragged", "longdecode", "rope", "qknorm", "backward",
+                                       "ragged", "longdecode", "windowcache", "rope", "qknorm",
+                                       "backward",
                                        "gva", "fold", "copy"],
                     default=None,
                     help="time a single workload as the line's headline (for profiling); "
@@ -475,9 +482,12 @@ def main():
         log(f"{name}: {res['avg_ms'] * 1e3:.1f} us, {res['gbs']:.0f} GB/s")
         cfg = {"workload": w.name, "B": w.B, "Tkv": w.Tkv, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
                "parallelism": "single-gpu"}
-        if w.cache_lens is not None:
+        if w.window_cache:
+            cfg.update({"window": w.window, "n_sink": w.n_sink,
+                        "entries_per_sequence": w.cache_lens[0]})
+        elif w.cache_lens is not None:
             cfg["cache_lens"] = "uniform 1..Tkv (seeded)"
-        kern = "decode_split_kernel<128, 1>"
+        kern = "decode_split_kernel<128, 1, {}>".format("true" if w.window_cache else "false")
         if res["splits"] > 1:
             kern += " + decode_combine_kernel<128>"
         legs[name] = (res, hbm_roofline(res, kern), cfg)
@@ -490,8 +500,8 @@ def main():
     elif args.only not in (None, "varlen"):
         plan.append(args.only)
     if args.all:
-        plan += [x for x in ("window", "ragged", "longdecode", "rope", "qknorm", "backward",
-                             "gva") if x not in plan]
+        plan += [x for x in ("window", "ragged", "longdecode", "windowcache", "rope", "qknorm",
+                             "backward", "gva") if x not in plan]
 
     for name in plan:
         if name == "varlen":
@@ -536,6 +546,8 @@ def main():
             run_decode("ragged", workloads.RAGGED_DECODE, 7000)
         elif name == "longdecode":
             run_decode("longdecode", workloads.LONG_DECODE, 9000)
+        elif name == "windowcache":
+            run_decode("windowcache", workloads.WINDOW_CACHE_DECODE, 9500)
 
     head_key = {"prefill": "prefill"}.get(headline, headline)
     res, roofline, config = legs.pop(head_key)

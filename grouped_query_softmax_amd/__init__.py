@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     gqa_attn_decode_ex,
     gqa_attn_decode_noalloc,
     gqa_attn_decode_ragged,
+    gqa_attn_decode_window_cache,
     gqa_attn_decode_workspace_bytes,
     gqa_attn_decode_workspace_bytes_hkv,
     GQA_SCALE_DEFAULT,

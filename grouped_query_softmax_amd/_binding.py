@@ -116,6 +116,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gqa_prepare_keys.restype = I
     lib.gqa_attn_decode_ex.argtypes = [P, P, P, P, I, I, I, I, I, F, P, OP, P, SZ, I, P]
     lib.gqa_attn_decode_ex.restype = I
+    lib.gqa_attn_decode_window_cache.argtypes = [P, P, P, P, I, I, I, I, F, P, OP, P, SZ, I,
+                                                 P]
+    lib.gqa_attn_decode_window_cache.restype = I
     lib.gqa_attn_backward_workspace_bytes.argtypes = [I, I, I]
     lib.gqa_attn_backward_workspace_bytes.restype = SZ
     lib.gqa_attn_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, SZ, I,
@@ -457,6 +460,36 @@ def gqa_attn_decode_ex(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                                  lens_ptr, ctypes.byref(opt), ws_ptr, ws_bytes, _dtype_code(q),
                                  _stream(stream))
     _check(rc, "gqa_attn_decode_ex")
+    return out
+
+
+def gqa_attn_decode_window_cache(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 cache_lens: torch.Tensor, window: int, n_sink: int = 0,
+                                 rope=None, scale: Optional[float] = None,
+                                 workspace: Optional[torch.Tensor] = None,
+                                 out: Optional[torch.Tensor] = None, qk_norm=None,
+                                 stream=None) -> torch.Tensor:
+    """Decode against caches bounded to the window: k_cache, v_cache [B, n_sink + window, Hkv, d]
+    with entry e of a sequence in slot e (e < n_sink) or n_sink + (e - n_sink) % window;
+    cache_lens (int32 device [B]) counts every entry a sequence has had. rope / qk_norm as for
+    :func:`gqa_attn_decode_ex`. bf16 only."""
+    if window < 1 or n_sink < 0:
+        raise ValueError("window must be >= 1 and n_sink >= 0")
+    if k_cache.dim() != 4 or k_cache.shape[1] != n_sink + window:
+        raise ValueError("k_cache, v_cache must hold n_sink + window slots per sequence")
+    q, k, v, out, dims, ws_ptr, ws_bytes, _ = _decode_args(q, k_cache, v_cache, scale, workspace,
+                                                           out)
+    lens = _dev(cache_lens, "cache_lens")
+    if lens.dtype != torch.int32 or lens.dim() != 1 or lens.numel() != q.shape[0]:
+        raise ValueError("cache_lens must be a 1-D int32 device tensor with one entry per "
+                         "sequence")
+    B, _, Hq, Hkv, d, sc = dims
+    opt = _options(window, n_sink, rope, d, None, qk_norm)
+    rc = _lib.gqa_attn_decode_window_cache(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                           out.data_ptr(), B, Hq, Hkv, d, sc, lens.data_ptr(),
+                                           ctypes.byref(opt), ws_ptr, ws_bytes, _dtype_code(q),
+                                           _stream(stream))
+    _check(rc, "gqa_attn_decode_window_cache")
     return out
 
 

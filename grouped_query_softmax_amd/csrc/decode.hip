@@ -22,7 +22,10 @@
 // Ragged caches and sliding windows (course page "Week 7. Attention", step 3): sequence b uses
 // its first lens[b] cache entries; with a window it sees only the last `window` of them plus the
 // first n_sink (sink) entries. The visible entries form one list (sinks, then window) over which
-// the splits and tiles run, so nothing outside it is read. With up to 512 sequences, each
+// the splits and tiles run, so nothing outside it is read. A cache bounded to the window (the
+// same page: the window bounds the cache to its size) holds n_sink + window slots per sequence:
+// the sinks in their own slots, and entry e >= n_sink in slot n_sink + (e - n_sink) mod window,
+// where it replaced the entry that left the window; the list is then mapped to those slots. With up to 512 sequences, each
 // workgroup takes its sequence from a balanced order (longest and shortest sequences paired on
 // the compute units) that it works out itself at its start.
 // Each lane owns one query head (one accumulator column), so the softmax reference and the
@@ -40,7 +43,7 @@
 
 #include <mutex>
 
-#include "common.hpp"
+#include "decode.hpp"
 
 // Scratch for callers that cannot allocate: the fp32 split partials of gqa_attn_decode_noalloc
 // live in this fixed device array (one copy per GPU, for the life of the process) instead of a
@@ -99,9 +102,10 @@ struct DecCfg {
 // shortest. Each split workgroup finds the sequence at its position of that layout itself (up to
 // kMaxOrdered sequences, ranked in LDS: B^2 / 256 comparisons per thread).
 constexpr int kMaxOrdered = 512;
+template <bool RING>
 __device__ int balanced_sequence(const DecodeArgs& a, int pos, int row, int* vis) {
   for (int j = threadIdx.x; j < a.B; j += kThreads) {
-    const int L = min(max(a.lens[j], 0), a.Tkv);
+    const int L = RING ? max(a.lens[j], 0) : min(max(a.lens[j], 0), a.Tkv);
     const int w_start = a.window > 0 ? max(0, L - a.window) : 0;
     vis[j] = min(a.n_sink, w_start) + (L - w_start);
   }
@@ -124,8 +128,8 @@ __device__ int balanced_sequence(const DecodeArgs& a, int pos, int row, int* vis
 
 // NCH: 16-head chunks of query heads per workgroup (1, or 2 when a group has more than 16 heads:
 // every K/V operand read from LDS then feeds both chunks' MFMAs, and the cache is read once for
-// up to 32 heads)
-template <int D, int NCH>
+// up to 32 heads). RING: the cache is bounded to the window (launch_decode_window_cache_bf16).
+template <int D, int NCH, bool RING>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, int head_chunks,
                                                                 int order_row) {
   using C = DecCfg<D>;
@@ -141,8 +145,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   const int y = rest % (a.Hkv * head_chunks);
   // sequence: in launch order, or from the balanced order of a ragged cache (rows of order_row)
   const int pos = rest / (a.Hkv * head_chunks);
-  const int b =
-      order_row > 0 ? balanced_sequence(a, pos, order_row, reinterpret_cast<int*>(smem)) : pos;
+  const int b = order_row > 0
+                    ? balanced_sequence<RING>(a, pos, order_row, reinterpret_cast<int*>(smem))
+                    : pos;
   const int kvh = y / head_chunks;
   const int hc = y % head_chunks;
   const int G = a.Hq / a.Hkv;
@@ -153,8 +158,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
   const int g = lane >> 4;
   // The visible cache entries of this sequence, as one list: the sink entries below the window
   // [0, a_end) followed by the window [w_start, L). Splits and tiles run over list positions.
-  // L = 0 (an empty cache) leaves nothing visible: the output row is zero
-  const int L = a.lens ? min(max(a.lens[b], 0), a.Tkv) : a.Tkv;
+  // L = 0 (an empty cache) leaves nothing visible: the output row is zero. A bounded cache's
+  // length counts every entry the sequence has had.
+  const int L = RING ? max(a.lens[b], 0) : a.lens ? min(max(a.lens[b], 0), a.Tkv) : a.Tkv;
   const int w_start = a.window > 0 ? max(0, L - a.window) : 0;
   const int a_end = min(a.n_sink, w_start);
   const int nvis = a_end + (L - w_start);
@@ -195,8 +201,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
     for (int s = 0; s < NS; ++s) {
       u32x4 w = wq[s];
       // rotary embedding of the query at its position L - 1 (the cache holds turned keys);
-      // this lane's dimensions 32s + 8g .. +7 are the pairs 16s + 4g .. +3
-      const int ti = max(L - 1, 0) * (D / 2) + 16 * s + 4 * g;
+      // this lane's dimensions 32s + 8g .. +7 are the pairs 16s + 4g .. +3. A bounded cache's
+      // length is not bounded by the tables: past their last row the query takes that row.
+      const int qpos = RING ? min(L, a.rope_rows) - 1 : L - 1;
+      const int ti = max(qpos, 0) * (D / 2) + 16 * s + 4 * g;
       if (a.qn_w) {
         float x[8];
         unpack8(w, x);
@@ -216,14 +224,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
 
   const int64_t seq_elem = (static_cast<int64_t>(b) * a.Tkv * a.Hkv + kvh) * D;
   // bytes from the head's first entry to the end of its last visible one (0 for an empty cache,
-  // so every load of that sequence is out of range and reads zeros)
-  const int nrec = L > 0 ? (L - 1) * row_bytes + D * 2 : 0;
+  // so every load of that sequence is out of range and reads zeros); a bounded cache uses at
+  // most its Tkv slots
+  const int nslot = RING ? min(L, a.Tkv) : L;
+  const int nrec = nslot > 0 ? (nslot - 1) * row_bytes + D * 2 : 0;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k) + seq_elem), 0, nrec, kBufWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(static_cast<const uint16_t*>(a.v) + seq_elem), 0, nrec, kBufWord3);
   const int vend = kb + max(nkeys, 0);    // list positions of this split: [kb, vend)
   const int shift = w_start - a_end;      // list position -> cache entry, past the sinks
+  // bounded cache: the window's entries e >= e0 = max(w_start, n_sink) sit in slot
+  // n_sink + (r0 + e - e0) mod window with r0 = (e0 - n_sink) mod window; they span fewer than
+  // `window` entries, so the sum wraps at most once
+  [[maybe_unused]] const int e0 = max(w_start, a.n_sink);
+  [[maybe_unused]] const int r0 = RING ? (e0 - a.n_sink) % a.window : 0;
 
   // Loads: kLPR lanes cover one whole key row (16 bytes each), so every load instruction reads
   // whole 128-byte lines; K and V go to this wave's LDS tiles as they arrived. The K operand is
@@ -256,7 +271,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int vpos = v0 + (blk * NS + s) * C::kRPI;
-        const int entry = vpos < a_end ? vpos : vpos + shift;
+        int entry = vpos < a_end ? vpos : vpos + shift;
+        if constexpr (RING) {
+          if (entry >= a.n_sink) {
+            const int r = r0 + (entry - e0);
+            entry = a.n_sink + (r >= a.window ? r - a.window : r);
+          }
+        }
         const int off = vpos < vend
                             ? static_cast<int>(static_cast<unsigned>(entry) * row_bytes) + 16 * lcol
                             : nrec;
@@ -535,7 +556,7 @@ int head_chunks_of(int G) {
 }
 
 template <int D>
-hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_d(const DecodeArgs& a, hipStream_t s, bool ring) {
   if (a.nsplit < 1 || a.nsplit > kMaxSplits) return hipErrorInvalidValue;  // the combine's LDS
   const int G = a.Hq / a.Hkv;
   const int hcs = head_chunks_of(G);
@@ -545,12 +566,20 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   const int order_row = (a.lens && a.B > 1 && a.B <= kMaxOrdered)
                             ? std::max(1, device_units() / (a.nsplit * a.Hkv * hcs))
                             : 0;
-  if (chunks_per_wg(G) == 2)
-    hipLaunchKernelGGL((decode_split_kernel<D, 2>), grid, dim3(kThreads), 0, s, a, hcs,
+  if (ring) {
+    if (chunks_per_wg(G) == 2)
+      hipLaunchKernelGGL((decode_split_kernel<D, 2, true>), grid, dim3(kThreads), 0, s, a, hcs,
+                         order_row);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<D, 1, true>), grid, dim3(kThreads), 0, s, a, hcs,
+                         order_row);
+  } else if (chunks_per_wg(G) == 2) {
+    hipLaunchKernelGGL((decode_split_kernel<D, 2, false>), grid, dim3(kThreads), 0, s, a, hcs,
                        order_row);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, dim3(kThreads), 0, s, a, hcs,
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<D, 1, false>), grid, dim3(kThreads), 0, s, a, hcs,
                        order_row);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.B * a.Hq), dim3(D), 0, s, a);
@@ -600,8 +629,17 @@ hipError_t decode_scratch(void** ptr) {
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   switch (a.d) {
-    case 64: return launch_d<64>(a, s);
-    case 128: return launch_d<128>(a, s);
+    case 64: return launch_d<64>(a, s, false);
+    case 128: return launch_d<128>(a, s, false);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_window_cache_bf16(const DecodeArgs& a, hipStream_t s) {
+  if (!a.lens || a.window < 1) return hipErrorInvalidValue;
+  switch (a.d) {
+    case 64: return launch_d<64>(a, s, true);
+    case 128: return launch_d<128>(a, s, true);
     default: return hipErrorInvalidValue;
   }
 }

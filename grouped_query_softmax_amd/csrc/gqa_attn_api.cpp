@@ -11,6 +11,7 @@
 #include "gqa_attn.h"
 #include "common.hpp"
 #include "backward.hpp"
+#include "decode.hpp"
 
 static_assert(GQA_DECODE_SCRATCH_BYTES == gqa::kDecodeScratchBytes,
               "the header's scratch limit is the size of the library's array");
@@ -317,17 +318,22 @@ size_t gqa_attn_decode_workspace_bytes(int B, int Tkv, int Hq, int d) {
   return most;
 }
 
+// ring: k_cache / v_cache are bounded to the window (Tkv = n_sink + window slots per sequence,
+// cache_lens counting every entry a sequence has had); see gqa_attn_decode_window_cache.
 static gqa_status_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
                                 void* out, int B, int Tkv, int Hq, int Hkv, int d, float scale,
                                 const int32_t* cache_lens, const gqa_attn_options_t* opt,
                                 void* workspace, size_t workspace_bytes, gqa_dtype_t dtype,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool ring = false) {
   if (!q || !k_cache || !v_cache || !out) return GQA_ERR_NULL_PTR;
+  if (ring && (!cache_lens || !opt)) return GQA_ERR_NULL_PTR;
   if (B <= 0 || Tkv <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return GQA_ERR_SHAPE;
   if (!resolve_scale(scale, d)) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0) return GQA_ERR_GROUPING;
   if (!dtype_ok(dtype) || !attn_d_supported(dtype, d)) return GQA_ERR_UNSUPPORTED;
-  if (const gqa_status_t st = check_options(opt, dtype, Tkv, true)) return st;
+  // the query's table row of a bounded cache is clamped to the tables (its length is on the
+  // device and unbounded): one row is the least they need
+  if (const gqa_status_t st = check_options(opt, dtype, ring ? 1 : Tkv, true)) return st;
   if (cache_lens && dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
   const int window = opt ? opt->window : 0;
   const int n_sink = opt ? opt->n_sink : 0;
@@ -407,7 +413,8 @@ static gqa_status_t decode_impl(const void* q, const void* k_cache, const void* 
   a.rope_rows = opt ? opt->rope_rows : 0;
   a.qn_w = opt ? opt->q_norm_w : nullptr;  // the cache holds normalised keys
   a.norm_eps = opt ? opt->norm_eps : 0.f;
-  return from_hip(gqa::launch_decode_bf16(a, stream));
+  return from_hip(ring ? gqa::launch_decode_window_cache_bf16(a, stream)
+                       : gqa::launch_decode_bf16(a, stream));
 }
 
 gqa_status_t gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
@@ -456,6 +463,21 @@ gqa_status_t gqa_attn_decode_ex(const void* q, const void* k_cache, const void* 
                                 hipStream_t stream) {
   return decode_impl(q, k_cache, v_cache, out, B, Tmax, Hq, Hkv, d, scale, cache_lens, options,
                      workspace, workspace_bytes, dtype, stream);
+}
+
+gqa_status_t gqa_attn_decode_window_cache(const void* q, const void* k_cache, const void* v_cache,
+                                          void* out, int B, int Hq, int Hkv, int d, float scale,
+                                          const int32_t* cache_lens,
+                                          const gqa_attn_options_t* options, void* workspace,
+                                          size_t workspace_bytes, gqa_dtype_t dtype,
+                                          hipStream_t stream) {
+  if (!options || !cache_lens) return GQA_ERR_NULL_PTR;
+  if (options->window < 1 || options->n_sink < 0 ||
+      static_cast<int64_t>(options->window) + options->n_sink > INT32_MAX)
+    return GQA_ERR_SHAPE;
+  if (dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+  return decode_impl(q, k_cache, v_cache, out, B, options->window + options->n_sink, Hq, Hkv, d,
+                     scale, cache_lens, options, workspace, workspace_bytes, dtype, stream, true);
 }
 
 size_t gqa_attn_backward_workspace_bytes(int B, int Tq, int Hq) {

@@ -252,6 +252,33 @@ gqa_status_t gqa_attn_decode_ex(const void* q, const void* k_cache, const void* 
                                 hipStream_t stream);
 
 /*
+ * Decode against caches bounded to the sliding window (course page "Week 7. Attention", step 3:
+ * the window bounds the cache to its size, and the first tokens, the attention sinks, are never
+ * dropped from it). The query sees what gqa_attn_decode_ex with the same window and sinks sees on
+ * the whole cache, entries 0 .. n_sink-1 and the last `window` entries, and the cache keeps only
+ * those.
+ *   q [B, 1, Hq, d]     k_cache, v_cache [B, n_sink + window, Hkv, d]     out [B, 1, Hq, d]
+ * Slots: entry e of a sequence (0-based, in the order its tokens arrived) lives in slot e when
+ * e < n_sink and in slot n_sink + (e - n_sink) mod window otherwise, so each new entry overwrites
+ * the one `window` places before it, which has just left the window.
+ * cache_lens: DEVICE int32[B], required (else GQA_ERR_NULL_PTR): the number of entries sequence b
+ * has had, which may exceed n_sink + window (a negative count is taken as 0: a zero output row);
+ * its query sits at position cache_lens[b]-1.
+ * options: required (else GQA_ERR_NULL_PTR) with window >= 1 (else GQA_ERR_SHAPE) and
+ * n_sink >= 0; the query's rotary embedding and QK-norm as for gqa_attn_decode_ex (the cache
+ * holds turned and normalised keys). The query takes table row min(cache_lens[b], rope_rows) - 1,
+ * so the tables must reach the positions decoded (rope_rows >= 1). Workspace as for
+ * gqa_attn_decode with Tkv = n_sink + window: gqa_attn_decode_workspace_bytes(B, n_sink + window,
+ * Hq, d). Only the visible slots are read. bf16 only (else GQA_ERR_UNSUPPORTED).
+ */
+gqa_status_t gqa_attn_decode_window_cache(const void* q, const void* k_cache, const void* v_cache,
+                                          void* out, int B, int Hq, int Hkv, int d, float scale,
+                                          const int32_t* cache_lens,
+                                          const gqa_attn_options_t* options, void* workspace,
+                                          size_t workspace_bytes, gqa_dtype_t dtype,
+                                          hipStream_t stream);
+
+/*
  * Backward of gqa_attn_prefill (dense batches): gradients of sum(out * dout).
  *   q, out, dout [B, Tq, Hq, d]; k, v [B, Tkv, Hkv, d]; lse [B, Tq, Hq] fp32 from the forward
  *   (gqa_attn_options_t.lse of gqa_attn_prefill_ex, same q, k, v, scale, causal);

@@ -114,6 +114,42 @@ int main() {
   EXPECT(gqa_attn_decode_ragged(Q, K, V, O, 4, 1024, 32, 8, 128, 0.1f, nullptr, -3, 0, W, need, BF,
                                 nullptr),
          GQA_ERR_SHAPE);
+  {
+    // decode against caches bounded to the window
+    gqa_attn_options_t wo = {};
+    wo.window = 64;
+    wo.n_sink = 4;
+    const int32_t* lens = static_cast<const int32_t*>(P(6));
+    const size_t wneed = gqa_attn_decode_workspace_bytes_hkv(4, 68, 32, 8, 128);
+    EXPECT(gqa_attn_decode_window_cache(Q, K, V, O, 4, 32, 8, 128, 0.1f, nullptr, &wo, W, wneed,
+                                        BF, nullptr),
+           GQA_ERR_NULL_PTR);
+    EXPECT(gqa_attn_decode_window_cache(Q, K, V, O, 4, 32, 8, 128, 0.1f, lens, nullptr, W, wneed,
+                                        BF, nullptr),
+           GQA_ERR_NULL_PTR);
+    EXPECT(gqa_attn_decode_window_cache(Q, K, V, O, 4, 32, 8, 128, 0.1f, lens, &wo, W, wneed - 1,
+                                        BF, nullptr),
+           GQA_ERR_WORKSPACE);
+    EXPECT(gqa_attn_decode_window_cache(Q, K, V, O, 4, 32, 8, 16, 0.1f, lens, &wo, W, wneed, F32,
+                                        nullptr),
+           GQA_ERR_UNSUPPORTED);
+    EXPECT(gqa_attn_decode_window_cache(Q, K, V, O, 4, 32, 5, 128, 0.1f, lens, &wo, W, wneed, BF,
+                                        nullptr),
+           GQA_ERR_GROUPING);
+    wo.window = 0;
+    EXPECT(gqa_attn_decode_window_cache(Q, K, V, O, 4, 32, 8, 128, 0.1f, lens, &wo, W, wneed, BF,
+                                        nullptr),
+           GQA_ERR_SHAPE);
+    wo.window = std::numeric_limits<int>::max();
+    EXPECT(gqa_attn_decode_window_cache(Q, K, V, O, 4, 32, 8, 128, 0.1f, lens, &wo, W, wneed, BF,
+                                        nullptr),
+           GQA_ERR_SHAPE);  // n_sink + window beyond int
+    wo.window = 64;
+    wo.n_sink = -1;
+    EXPECT(gqa_attn_decode_window_cache(Q, K, V, O, 4, 32, 8, 128, 0.1f, lens, &wo, W, wneed, BF,
+                                        nullptr),
+           GQA_ERR_SHAPE);
+  }
   EXPECT(gqa_attn_decode_noalloc(Q, K, V, O, 1024, 1, 32, 8, 128, 0.1f, 0, BF, nullptr),
          GQA_ERR_WORKSPACE);  // partials beyond the fixed scratch: refused first
   EXPECT(gqa_attn_decode_noalloc(nullptr, K, V, O, 4, 1024, 32, 8, 128, 0.1f, 0, F32, nullptr),

@@ -146,6 +146,25 @@ def test_window_and_ragged_validation(lib):
     assert rag(Tmax=1 << 22) == B.GQA_ERR_UNSUPPORTED
 
 
+def test_window_cache_validation(lib):
+    Opt = B.AttnOptions
+    need = lib.gqa_attn_decode_workspace_bytes_hkv(4, 68, 32, 8, 128)
+
+    def wc(window=64, n_sink=4, dt=BF16, d=128, lens=W + 4096, opt=True, ws=W, wsb=need, hkv=8):
+        o = Opt(window, n_sink, None, None, 0, None, None, None, 0.0, 0)
+        return lib.gqa_attn_decode_window_cache(Q, K, V, O, 4, 32, hkv, d, 0.1, lens,
+                                                ctypes.byref(o) if opt else None, ws, wsb, dt,
+                                                None)
+    assert wc(lens=None) == B.GQA_ERR_NULL_PTR            # the entry counts are required
+    assert wc(opt=False) == B.GQA_ERR_NULL_PTR            # so is the window
+    assert wc(window=0) == B.GQA_ERR_SHAPE
+    assert wc(n_sink=-1) == B.GQA_ERR_SHAPE
+    assert wc(window=2**31 - 1) == B.GQA_ERR_SHAPE        # n_sink + window past int
+    assert wc(dt=F32, d=16) == B.GQA_ERR_UNSUPPORTED
+    assert wc(hkv=5) == B.GQA_ERR_GROUPING
+    assert wc(wsb=need - 1) == B.GQA_ERR_WORKSPACE        # sized for n_sink + window slots
+
+
 def test_extended_options_validation(lib):
     Opt = B.AttnOptions
     T = W + 8192   # fake 16-byte aligned table addresses

@@ -105,6 +105,8 @@ class Workload:
     window: int = 0                             # causal sliding window (0: none)
     n_sink: int = 0                             # sink keys kept visible below the window
     cache_lens: Optional[Tuple[int, ...]] = None  # ragged decode: entries used per sequence
+    window_cache: bool = False  # decode cache bounded to the window: Tkv = n_sink + window slots,
+                                # cache_lens count every entry a sequence has had
 
     @property
     def G(self) -> int:
@@ -185,9 +187,18 @@ GVA_PREFILL = Workload("gva_prefill_B2_T4096_H16_HV32_d64", B=2, Tq=4096, Tkv=40
 LONG_DECODE = Workload("decode_B1_kv131072", B=1, Tq=1, Tkv=131072, Hq=32, Hkv=8, d=128,
                        dtype="bf16", causal=False, seeds=(9000, 9001, 9002))
 
+# Decode against caches bounded to the window (course page "Week 7. Attention", step 3): 64
+# sequences of 32768 entries each, 32/8 heads, d = 128, a window of 4096 entries and 4 sinks, so
+# each cache holds 4100 slots (written over about eight times).
+WINDOW_CACHE_DECODE = Workload("window_cache_decode_B64_W4096_S4", B=64, Tq=1, Tkv=4100, Hq=32,
+                               Hkv=8, d=128, dtype="bf16", causal=False,
+                               seeds=(9500, 9501, 9502), window=4096, n_sink=4,
+                               cache_lens=(32768,) * 64, window_cache=True)
+
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in
                                   (TINY, LLAMA_PREFILL, DECODE, MQA_PREFILL, VARLEN_PREFILL,
-                                   WINDOW_PREFILL, RAGGED_DECODE, GVA_PREFILL, LONG_DECODE)}
+                                   WINDOW_PREFILL, RAGGED_DECODE, GVA_PREFILL, LONG_DECODE,
+                                   WINDOW_CACHE_DECODE)}
 
 
 def tiny_lab_inputs(x1000: bool = False) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
