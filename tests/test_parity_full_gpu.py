@@ -1,8 +1,9 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark times.
 
 The benchmark workloads (the 4096-token 32/8 prefill, the 64-sequence decode, the multi-query
-prefill with its x30 rows, the packed 16k/8k/4k/1k prefill and the long-context decode of one
-131072-entry cache, which runs split and merges its partial results) are compared with the fp64
+prefill with its x30 rows, the packed 16k/8k/4k/1k prefill, the long-context decode of one
+131072-entry cache, which runs split and merges its partial results, and the decode against caches
+bounded to the window) are compared with the fp64
 oracle over the whole output, every head, row and column (the GQA lab's max_gap, step 5; the course
 page's whole-output comparison with torch's scaled_dot_product_attention). The variant workloads
 (window, ragged decode, rotary embedding, grouped values, backward) are checked on seeded
@@ -106,6 +107,29 @@ def test_full_long_decode_whole_output(gqa):
     got = to_f64(out)
     say("full-size long decode: oracle on the whole output")
     ref = oracle.default().attention(host_view(q), host_view(k), host_view(v))
+    _whole(got, ref, w.name)
+
+
+def test_full_window_cache_decode_whole_output(gqa):
+    """64 sequences of 32768 entries each in caches bounded to a 4096-entry window and 4 sinks
+    (4100 slots, written over about eight times): every sequence, head and column against the
+    oracle, which reads each visible entry back from its slot (course page "Week 7. Attention",
+    step 3)."""
+    w = workloads.WINDOW_CACHE_DECODE
+    say(f"full-size window-cache decode {w.name}: generating inputs")
+    q, k, v, _ = workloads.make_inputs(w)
+    lens = torch.tensor(w.cache_lens, dtype=torch.int32, device="cuda")
+    say("full-size window-cache decode: launching")
+    out = gqa.gqa_attn_decode_window_cache(to_dev(q), to_dev(k), to_dev(v), lens,
+                                           window=w.window, n_sink=w.n_sink)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    qh = host_view(q)
+    kc = oracle.unroll_window_cache(host_view(k), w.cache_lens, w.window, w.n_sink, compact=True)
+    vc = oracle.unroll_window_cache(host_view(v), w.cache_lens, w.window, w.n_sink, compact=True)
+    say("full-size window-cache decode: oracle on every sequence")
+    orc = oracle.default()
+    ref = np.concatenate([orc.attention(qh[b:b + 1], kc[b], vc[b]) for b in range(w.B)])
     _whole(got, ref, w.name)
 
 
