@@ -1,5 +1,6 @@
 """Seeded random shapes against the oracle, through the C ABI: dense, packed and sliding-window
-prefill, plain, ragged and windowed decode, grouped value attention, RoPE and QK-norm (fused or
+prefill, plain, ragged and windowed decode, decode against caches bounded to the window, grouped
+value attention, RoPE and QK-norm (fused or
 applied to the keys ahead) and the backward, over head counts, group
 sizes, lengths and head dims that the hand-picked cases do not name. The seed fixes the list, so
 a failure names a reproducible case (its id carries every size). Inputs are N(0, 1) rounded to
@@ -142,6 +143,56 @@ def test_random_shape_vs_oracle(gqa, orc, c):
         ref = orc.attention_gva(host_view(q), host_view(k), host_view(v), causal=c["causal"])
     torch.cuda.synchronize()
     assert_bf16_close(to_f64(got), ref, what=_id(c))
+
+
+def _wc_cases(n, seed):
+    """Decode against caches bounded to the window: window, sinks and entry counts drawn so that
+    some caches are empty, some not yet full, some written over many times."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        hkv = int(rng.choice([1, 2, 3, 4, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 5, 8, 16, 24, 40]))
+        while hkv * g > 64:
+            g = max(1, g // 2)
+        B = int(rng.integers(1, 6))
+        W = int(rng.integers(1, 1500))
+        S = int(rng.integers(0, 9)) if rng.integers(0, 3) else int(rng.integers(0, 200))
+        lens = tuple(int(x) for x in rng.integers(0, 4 * (W + S) + 2, size=B))
+        out.append({"d": d, "Hkv": hkv, "G": g, "B": B, "window": W, "n_sink": S, "lens": lens,
+                    "seed": 9100 + 10 * i})
+    return out
+
+
+WC_CASES = _wc_cases(12, 20261206)
+
+
+def _wc_id(c):
+    return "wc_B{B}_W{window}_S{n_sink}_Hkv{Hkv}_G{G}_d{d}_s{seed}".format(**c)
+
+
+@pytest.mark.parametrize("c", WC_CASES, ids=_wc_id)
+def test_random_window_cache_vs_oracle(gqa, orc, c):
+    B, W, S, d, seed = c["B"], c["window"], c["n_sink"], c["d"], c["seed"]
+    hkv, hq = c["Hkv"], c["Hkv"] * c["G"]
+    say(_wc_id(c))
+    q = workloads.randn_bf16((B, 1, hq, d), seed)
+    k = workloads.randn_bf16((B, S + W, hkv, d), seed + 1)
+    v = workloads.randn_bf16((B, S + W, hkv, d), seed + 2)
+    lens = np.asarray(c["lens"], dtype=np.int32)
+    got = to_f64(gqa.gqa_attn_decode_window_cache(to_dev(q), to_dev(k), to_dev(v), to_dev(lens),
+                                                  window=W, n_sink=S))
+    torch.cuda.synchronize()
+    qh = host_view(q)
+    kc = oracle.unroll_window_cache(host_view(k), c["lens"], W, S, compact=True)
+    vc = oracle.unroll_window_cache(host_view(v), c["lens"], W, S, compact=True)
+    for b, L in enumerate(c["lens"]):
+        if L == 0:
+            assert np.array_equal(got[b], np.zeros_like(got[b])), f"{_wc_id(c)} seq {b}: empty"
+            continue
+        ref = orc.attention(qh[b:b + 1], kc[b], vc[b])
+        assert_bf16_close(got[b:b + 1], ref, what=f"{_wc_id(c)} seq {b} len {L}")
 
 
 def _bwd_cases(n, seed):
