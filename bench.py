@@ -236,6 +236,15 @@ def bench_gva(gqa, w, steps, warmup, torch, seed):
             "frac_mfma": flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "wall_s": wall}
 
 
+def decode_entries(w):
+    """Cache entries a decode step reads once, over all sequences: every entry of a plain cache,
+    each sequence's first cache_lens[b] entries of a ragged one, and of a cache bounded to the
+    window its sinks and window (the entries its query sees; the rest were written over)."""
+    if w.window_cache:
+        return sum(min(L, w.n_sink + w.window) for L in w.cache_lens)
+    return sum(w.cache_lens) if w.cache_lens is not None else w.B * w.Tkv
+
+
 def bench_decode(gqa, w, steps, warmup, torch, seed):
     """Alternates two distinct caches (4 GiB together) so no run rides the previous one's
     last-level cache."""
@@ -263,10 +272,7 @@ def bench_decode(gqa, w, steps, warmup, torch, seed):
             gqa.gqa_attn_decode(q, k, v, workspace=ws, out=out)
 
     avg, wall, med, mn = time_launches(step, steps, warmup, torch, PER_LAUNCH)
-    if w.window_cache:   # the visible entries: the sinks and the window of each sequence
-        entries = sum(min(L, w.n_sink + w.window) for L in w.cache_lens)
-    else:
-        entries = sum(w.cache_lens) if w.cache_lens is not None else w.B * w.Tkv
+    entries = decode_entries(w)
     kv_bytes = 2 * entries * w.Hkv * w.d * 2
     qo_bytes = 2 * w.B * w.Hq * w.d * 2
     gbs = (kv_bytes + qo_bytes) / (avg * 1e-3) / 1e9

@@ -102,3 +102,15 @@ def test_source_hash_follows_every_file_of_the_kernel(tmp_path, monkeypatch):
     (tmp_path / "a.hip").write_text("kernel a, changed\n")
     h2 = bench.kernel_source_sha("probe")
     assert len({h0, h1, h2}) == 3 and all(len(h) == 16 for h in (h0, h1, h2))
+
+
+def test_decode_entries_match_a_brute_force_count():
+    """Entries each decode leg reads: for the bounded cache, the entries a query at the last
+    position sees (sinks and window) counted one by one."""
+    w = workloads.WINDOW_CACHE_DECODE
+    assert w.Tkv == w.n_sink + w.window
+    seen = sum(int(np.count_nonzero((np.arange(L) < w.n_sink) | (np.arange(L) >= L - w.window)))
+               for L in w.cache_lens)
+    assert bench.decode_entries(w) == seen == 64 * 4100
+    assert bench.decode_entries(workloads.DECODE) == 64 * 8192
+    assert bench.decode_entries(workloads.RAGGED_DECODE) == sum(workloads.RAGGED_DECODE.cache_lens)
