@@ -25,9 +25,9 @@
 // the splits and tiles run, so nothing outside it is read. A cache bounded to the window (the
 // same page: the window bounds the cache to its size) holds n_sink + window slots per sequence:
 // the sinks in their own slots, and entry e >= n_sink in slot n_sink + (e - n_sink) mod window,
-// where it replaced the entry that left the window; the list is then mapped to those slots. With up to 512 sequences, each
-// workgroup takes its sequence from a balanced order (longest and shortest sequences paired on
-// the compute units) that it works out itself at its start.
+// where it replaced the entry that left the window; the list is then mapped to those slots.
+// With up to 512 sequences, each workgroup takes its sequence from a balanced order (longest and
+// shortest sequences paired on the compute units) that it works out itself at its start.
 // Each lane owns one query head (one accumulator column), so the softmax reference and the
 // rescale factor are per lane; the row maximum of a tile is combined over the 4 lane groups that
 // hold that head's keys. Online softmax in the base-2 domain with a lazily moved reference
@@ -273,7 +273,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, in
         const int vpos = v0 + (blk * NS + s) * C::kRPI;
         int entry = vpos < a_end ? vpos : vpos + shift;
         if constexpr (RING) {
-          if (entry >= a.n_sink) {
+          // (rows past the list read zeros below whatever their entry)
+          if (vpos < vend && entry >= a.n_sink) {
             const int r = r0 + (entry - e0);
             entry = a.n_sink + (r >= a.window ? r - a.window : r);
           }
