@@ -64,3 +64,21 @@ def test_packed_prefill_needs_max_seqlen(gqa):
     with pytest.raises(ValueError):
         gqa.gqa_prepare_keys(k, qk_norm=(None, _t(128, dtype=torch.float32), 1e-6),
                              cu_seqlens=cu)
+
+
+def test_window_cache_decode_rejects_bad_arguments(gqa):
+    say("binding: bounded-cache decode checks")
+    q, ring = _t(2, 1, 8, 128), _t(2, 68, 2, 128)   # 4 sinks + a window of 64 slots
+    lens = torch.tensor([5, 500], dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):   # the cache must hold n_sink + window slots
+        gqa.gqa_attn_decode_window_cache(q, ring, ring, lens, window=64, n_sink=5)
+    with pytest.raises(ValueError):
+        gqa.gqa_attn_decode_window_cache(q, ring, ring, lens, window=0, n_sink=68)
+    with pytest.raises(ValueError):
+        gqa.gqa_attn_decode_window_cache(q, ring, ring, lens, window=64, n_sink=-1)
+    for bad in (lens[:1], lens.to(torch.int64), lens.cpu()):
+        with pytest.raises((ValueError, TypeError)):
+            gqa.gqa_attn_decode_window_cache(q, ring, ring, bad, window=64, n_sink=4)
+    with pytest.raises(ValueError):
+        gqa.gqa_attn_decode_window_cache(q, ring, ring, lens, window=64, n_sink=4,
+                                         out=_t(2, 1, 4, 128))
